@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for the hard-selection PD-SSM forward pass.
+
+TEST INFRASTRUCTURE: imported only by the tests, the smoke check and the
+benchmark's CPU-baseline leg; never by the product path."""
+
+from .pdssm_oracle import (  # noqa: F401
+    forward,
+    forward_inputs,
+    pd_apply,
+    pd_compose,
+    scan,
+    scores,
+    select,
+    sigmoid,
+    three_phase,
+    transition_matrix,
+)

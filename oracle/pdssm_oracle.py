@@ -1,0 +1,206 @@
+"""fp64 CPU oracle for the hard-selection PD-SSM forward pass.
+
+TEST INFRASTRUCTURE.  Only the test-suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The product path (the HIP library
+and its Python binding) never calls it, and this module imports nothing from
+the product path.
+
+It is the plain definition, written out slowly:
+
+* selection -- "Flash PD-SSM: Memory-Optimized Structured Sparse State-Space
+  Models" (gist.science explainer), technical summary, methodology item 1
+  (hard selection): a linear map of u_t gives K scores, the highest-scoring
+  precomputed sparse matrix is taken (argmax) and used as is.  Ties go to the
+  lowest index (numpy's argmax returns the first maximum).
+* the selected matrix is a one-hot column selector (same item, complexity
+  paragraph).  Reading: P[idx[j], j] = 1, i.e. column j carries its one in
+  row idx[j]; the transition is A_t = P^(k*) D_t with the diagonal
+  D_t = sigmoid(W_d u_t + b_d) scaling column j before it moves.
+* the recurrence of a linear SSM (problem statement of the same summary):
+  h_t = A_t h_{t-1} + Bu_t, y_t = C h_t, with h0 the state before step 0,
+  y_t read after the update and h_L the state after the last step.
+
+Everything is upcast exactly to fp64 first.  ``scan`` builds the dense N x N
+transition of every step and multiplies; it never uses the sparse structure.
+
+``three_phase`` is a separate fp64 evaluation that follows the pages' kernel
+description (same summary, methodology item 3: phase A runs independent
+sequential recurrences inside chunks, phase B prefix-scans the chunk
+summaries into carry states, phase C applies the carry corrections), with
+dense matrices.  It exists so that the chunked identity can be checked against
+``scan``.  ``pd_compose`` / ``pd_apply`` state the O(N) algebra of these maps
+(composition by an index gather and a scale product, application by a
+scatter-add) so that it can be checked against dense products.
+"""
+
+import numpy as np
+
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# selection
+# --------------------------------------------------------------------------
+
+def sigmoid(z):
+    """Logistic function 1 / (1 + exp(-z)) in fp64."""
+    z = np.asarray(z, dtype=F64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def scores(u, W, u_shared):
+    """Linear forms of every input row: out[b,h,t,k] = sum_c W[h,k,c] u[b,(h),t,c].
+
+    u: [B,H,L,d] (per head) or [B,L,d] (shared by all heads); W: [H,M,d].
+    Returns fp64 [B,H,L,M]."""
+    u = np.asarray(u, dtype=F64)
+    W = np.asarray(W, dtype=F64)
+    if u_shared:
+        # [B,1,L,d] @ [1,H,d,M]
+        return np.matmul(u[:, None], np.swapaxes(W, -1, -2)[None])
+    return np.matmul(u, np.swapaxes(W, -1, -2)[None])
+
+
+def select(u, W_sel, W_d, b_d, u_shared=False):
+    """Hard selection and input-dependent diagonal.
+
+    Returns (k_star int32 [B,H,L], D fp64 [B,H,L,N], s fp64 [B,H,L,K])."""
+    s = scores(u, W_sel, u_shared)
+    k_star = np.argmax(s, axis=-1).astype(np.int32)      # first maximum wins
+    z = scores(u, W_d, u_shared) + np.asarray(b_d, dtype=F64)[None, :, None, :]
+    return k_star, sigmoid(z), s
+
+
+# --------------------------------------------------------------------------
+# transitions and the sequential scan
+# --------------------------------------------------------------------------
+
+def transition_matrix(idx, dvals):
+    """Dense A = P D for one map: A[..., idx[j], j] = dvals[j], zeros elsewhere.
+
+    idx: int [..., N]; dvals: [..., N].  Returns fp64 [..., N, N]."""
+    idx = np.asarray(idx)
+    dvals = np.asarray(dvals, dtype=F64)
+    N = idx.shape[-1]
+    lead = idx.shape[:-1]
+    A = np.zeros(lead + (N, N), dtype=F64)
+    flat_idx = idx.reshape(-1, N)
+    flat_d = dvals.reshape(-1, N)
+    Af = A.reshape(-1, N, N)
+    cols = np.arange(N)
+    for r in range(flat_idx.shape[0]):
+        Af[r, flat_idx[r], cols] = flat_d[r]
+    return A
+
+
+def scan(k_star, dict_idx, D, Bu, C, h0=None):
+    """Sequential recurrence with dense transitions.
+
+    k_star [B,H,L] int; dict_idx [H,K,N] int; D [B,H,L,N]; Bu [B,H,L,N];
+    C [H,N]; h0 [B,H,N] or None (zeros).  Returns (y fp64 [B,H,L],
+    h_L fp64 [B,H,N])."""
+    k_star = np.asarray(k_star)
+    dict_idx = np.asarray(dict_idx)
+    D = np.asarray(D, dtype=F64)
+    Bu = np.asarray(Bu, dtype=F64)
+    C = np.asarray(C, dtype=F64)
+    B, H, L = k_star.shape
+    N = dict_idx.shape[-1]
+    x = np.zeros((B, H, N), dtype=F64) if h0 is None else np.array(h0, dtype=F64)
+    y = np.zeros((B, H, L), dtype=F64)
+    heads = np.arange(H)[None, :]
+    bi = np.arange(B)[:, None, None]
+    hi = np.arange(H)[None, :, None]
+    cols = np.arange(N)[None, None, :]
+    for t in range(L):
+        rows = dict_idx[heads, k_star[:, :, t]]            # [B,H,N]: row of column j
+        A = np.zeros((B, H, N, N), dtype=F64)
+        A[bi, hi, rows, cols] = D[:, :, t]
+        x = np.matmul(A, x[..., None])[..., 0] + Bu[:, :, t]
+        y[:, :, t] = (C[None] * x).sum(-1)
+    return y, x
+
+
+def forward(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0=None, u_shared=False):
+    """Selection followed by the sequential scan.
+
+    Returns dict(k_star, D, scores, y, h_L)."""
+    k_star, D, s = select(u, W_sel, W_d, b_d, u_shared)
+    y, hL = scan(k_star, dict_idx, D, Bu, C, h0)
+    return {"k_star": k_star, "D": D, "scores": s, "y": y, "h_L": hL}
+
+
+def forward_inputs(inp, L=None):
+    """``forward`` on a generated input bundle, optionally on its first L steps."""
+    c = inp.cfg
+    L = c.L if L is None else L
+    u = inp.u[:, :L] if c.u_shared else inp.u[:, :, :L]
+    return forward(u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d,
+                   inp.Bu[:, :, :L], inp.C, inp.h0, c.u_shared)
+
+
+# --------------------------------------------------------------------------
+# PD-map algebra (stated for checking, used by nothing above)
+# --------------------------------------------------------------------------
+
+def pd_apply(idx, scale, x, b=None):
+    """(P D) x + b by scatter-add: out[idx[j]] += scale[j] * x[j]."""
+    idx = np.asarray(idx)
+    out = np.zeros(np.shape(x), dtype=F64) if b is None else np.array(b, dtype=F64)
+    np.add.at(out, idx, np.asarray(scale, dtype=F64) * np.asarray(x, dtype=F64))
+    return out
+
+
+def pd_compose(later, earlier):
+    """Composition later o earlier of two maps (idx, scale): the product of
+    their dense matrices, later @ earlier, is again column-one-hot times a
+    diagonal, with idx = idx_later[idx_earlier] and
+    scale = scale_later[idx_earlier] * scale_earlier."""
+    i2, s2 = np.asarray(later[0]), np.asarray(later[1], dtype=F64)
+    i1, s1 = np.asarray(earlier[0]), np.asarray(earlier[1], dtype=F64)
+    return i2[i1], s2[i1] * s1
+
+
+# --------------------------------------------------------------------------
+# chunked evaluation (phases A, B, C) with dense matrices
+# --------------------------------------------------------------------------
+
+def three_phase(k_star, dict_idx, D, Bu, C, h0=None, chunk=64):
+    """Chunked evaluation in the pages' three phases, fp64, dense.
+
+    Phase A: each chunk, on its own and from a zero state, runs its steps in
+    order, recording local states and the running product of its
+    transitions.  Phase B: carries H_c = Phi_c H_{c-1} + b_c from H_{-1} = h0.
+    Phase C: h_t = hloc_t + Phi_{c,t} H_{c-1}, y_t = C h_t.
+    Returns (y, h_L) like ``scan``."""
+    k_star = np.asarray(k_star)
+    D = np.asarray(D, dtype=F64)
+    Bu = np.asarray(Bu, dtype=F64)
+    C = np.asarray(C, dtype=F64)
+    B, H, L = k_star.shape
+    N = dict_idx.shape[-1]
+    starts = list(range(0, L, chunk))
+    hloc = np.zeros((B, H, L, N))
+    prefix = np.zeros((B, H, L, N, N))          # Phi_{c,t} = A_t ... A_{c0}
+    for c0 in starts:                            # phase A (chunks independent)
+        x = np.zeros((B, H, N))
+        P = np.broadcast_to(np.eye(N), (B, H, N, N)).copy()
+        for t in range(c0, min(c0 + chunk, L)):
+            A = transition_matrix(np.asarray(dict_idx)[np.arange(H)[None, :], k_star[:, :, t]],
+                                  D[:, :, t])
+            x = np.matmul(A, x[..., None])[..., 0] + Bu[:, :, t]
+            P = np.matmul(A, P)
+            hloc[:, :, t] = x
+            prefix[:, :, t] = P
+    carry = np.zeros((B, H, N)) if h0 is None else np.array(h0, dtype=F64)
+    carries = []
+    for c0 in starts:                            # phase B
+        carries.append(carry)
+        e = min(c0 + chunk, L) - 1
+        carry = np.matmul(prefix[:, :, e], carry[..., None])[..., 0] + hloc[:, :, e]
+    y = np.zeros((B, H, L))
+    for c0, Hc in zip(starts, carries):          # phase C
+        for t in range(c0, min(c0 + chunk, L)):
+            h = hloc[:, :, t] + np.matmul(prefix[:, :, t], Hc[..., None])[..., 0]
+            y[:, :, t] = (C[None] * h).sum(-1)
+    return y, carry

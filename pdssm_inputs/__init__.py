@@ -1,0 +1,25 @@
+"""Seeded synthetic inputs for the hard-selection PD-SSM forward pass.
+
+This module is shared by the tests, the benchmark and the oracle's checks.  It
+draws random numbers and lays them out; it does not evaluate the method (no
+selection, no transition, no scan).  Two input-preparation steps do touch the
+parameters, and both are described where they happen:
+
+* the top-2 score-margin rule, which redraws any input row whose two largest
+  linear scores are closer than ``GAP`` (so that an argmax is well posed in any
+  reasonable floating-point precision);
+* the driving term ``Bu = W_b u``, which the forward pass receives as an input.
+
+Workloads follow the pages' experiment descriptions only loosely (they print no
+inputs); the recipes are synthetic stand-ins, see ``configs.py``.
+"""
+
+from .configs import CONFIGS, Config, get_config  # noqa: F401
+from .gen import (  # noqa: F401
+    GAP,
+    Inputs,
+    bf16_bits,
+    bf16_round,
+    generate,
+    top2_margin,
+)
