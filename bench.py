@@ -1,0 +1,203 @@
+"""Throughput of the fused PD-SSM forward pass (selection + chunked scan) on one
+MI355X, in state-updates per second, with its HBM roofline fraction and the
+fp64 CPU oracle timed beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload impulse]
+                    [--no-cpu-baseline]
+
+Prints one JSON line.  A step is one pdssm_fwd call over the whole workload
+(selection outputs not materialised), with every input already resident in
+HBM.  The default workload is the 131072-step impulse-response shape
+(B=1, H=32, L=131072, N=16, K=8, d=64, chunk=512, fp32).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (matrix / packed vector)
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+METRIC = "state-updates/sec (B·H·L·N) PD-SSM fwd select+scan; achieved HBM GB/s vs peak"
+KERNEL_SOURCES = ("structured_sparse_state_pdssm_amd/csrc/pdscan_kernels.hip",
+                  "structured_sparse_state_pdssm_amd/csrc/pdscan_plan.h",
+                  "structured_sparse_state_pdssm_amd/csrc/pdscan_api.cpp")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(cfg):
+    """Minimum traffic: every input read once, outputs written once; and the
+    score-GEMM flops 2 (K + N) d per (b, h, t)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    B, H, L, N, K, d = cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, cfg.d
+    u = B * (1 if cfg.u_shared else H) * L * d * es
+    params = H * K * d * es + H * N * d * es + H * N * 4 + H * K * N * 4 + H * N * 4
+    total = u + B * H * L * N * 4 + B * H * L * 4 + 2 * B * H * N * 4 + params
+    flops = 2 * (K + N) * d * B * H * L
+    return total, flops
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pdssm_fused_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp):
+    """The fp64 oracle, as it is, on the host cores: selection plus the dense
+    sequential scan over the whole workload (inputs already generated)."""
+    import numpy as np  # noqa: F401
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=cores)
+    except Exception:                       # threadpoolctl missing: numpy defaults
+        import contextlib
+        ctx = contextlib.nullcontext()
+    c = inp.cfg
+    with ctx:
+        t0 = time.perf_counter()
+        oracle.forward_inputs(inp)
+        dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": c.state_updates / dt, "unit": "state-updates/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3), "cpu": model,
+            "sample": f"whole {c.name} workload ({c.B}x{c.H}x{c.L} steps, N={c.N}), one run; "
+                      "BLAS threads = cores (the step loop itself is single-threaded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="impulse")
+    ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward pass shards over independent sequences with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import structured_sparse_state_pdssm_amd as P
+    from pdssm_inputs import generate, get_config
+
+    torch.cuda.set_device(0)
+    cfg = get_config(args.workload)
+    chunk = args.chunk or cfg.chunk
+    t0 = time.time()
+    inp = generate(cfg)
+    print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    bf = cfg.dtype == "bf16"
+    pdt = torch.bfloat16 if bf else torch.float32
+
+    def dev(x, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+
+    u, W_sel, W_d = dev(inp.u, pdt), dev(inp.W_sel, pdt), dev(inp.W_d, pdt)
+    b_d, dic, Bu, C, h0 = dev(inp.b_d), dev(inp.dict_idx), dev(inp.Bu), dev(inp.C), dev(inp.h0)
+    dims = P.make_dims(cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, cfg.d, cfg.u_shared, bf)
+    ws = torch.empty(P.fwd_workspace_bytes(dims, chunk), dtype=torch.uint8, device="cuda")
+    out = {"y": torch.empty((cfg.B, cfg.H, cfg.L), device="cuda"),
+           "h_L": torch.empty((cfg.B, cfg.H, cfg.N), device="cuda")}
+
+    def step():
+        P.pdssm_fwd(u, W_sel, dic, W_d, b_d, Bu, C, h0, chunk=chunk, workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if P.workspace_error_flag(ws):
+        raise RuntimeError("look-back wait gave up during warm-up")
+    # per-launch durations with events on the stream the kernels run on
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_step = wall * 1e3 / args.steps
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+
+    alg_bytes, flops = algorithmic(cfg)
+    # the dominant cost: HBM traffic, except where the score GEMM outweighs it
+    t_hbm = alg_bytes / (PEAK_HBM_GBPS * 1e9)
+    t_mma = flops / ((PEAK_BF16_TFLOPS if (bf and cfg.d >= 128) else PEAK_FP32_TFLOPS) * 1e12)
+    if t_mma > t_hbm:
+        peak = PEAK_BF16_TFLOPS if (bf and cfg.d >= 128) else PEAK_FP32_TFLOPS
+        achieved = flops / avg_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s"}
+    else:
+        achieved = alg_bytes / avg_launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic_from_profile(cfg.name)
+    roof["algorithmic_bytes"] = alg_bytes
+    roof["launch_us"] = round(avg_launch_s * 1e6, 2)
+
+    rec = {
+        "metric": METRIC,
+        "value": cfg.state_updates / (ms_step / 1e3),
+        "unit": "state-updates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} L={cfg.L} N={cfg.N} K={cfg.K} "
+                               f"d={cfg.d} chunk={chunk} u={'shared' if cfg.u_shared else 'per-head'}",
+                   "B": cfg.B, "H": cfg.H, "L": cfg.L, "N": cfg.N, "K": cfg.K, "d_in": cfg.d,
+                   "chunk": chunk, "u_dtype": cfg.dtype, "state_dtype": "f32"},
+        "hbm_GBps": round(alg_bytes / avg_launch_s / 1e9, 1),
+        "roofline": roof,
+        "kernel_hash": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

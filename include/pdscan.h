@@ -1,0 +1,131 @@
+/*
+ * libpdscan -- hard-selection PD-SSM forward pass for AMD Instinct MI355X
+ * (gfx950).  C ABI: plain pointers and sizes, no C++ or framework types.
+ *
+ * What is computed (per batch element b, head h, step t):
+ *   scores  s_t[k] = sum_c W_sel[h,k,c] u_t[c]                 (k < K)
+ *   select  k*_t   = lowest k with s_t[k] = max_j s_t[j]
+ *   diag    D_t[n] = 1 / (1 + exp(-(sum_c W_d[h,n,c] u_t[c] + b_d[h,n])))
+ *   step    h_t[i] = Bu_t[i] + sum_{j : dict[h,k*_t,j] = i} D_t[j] h_{t-1}[j]
+ *   output  y_t    = sum_i C[h,i] h_t[i]
+ * with h_{-1} = h0 and h_L the state after the last step.
+ *
+ * Sources: "Flash PD-SSM: Memory-Optimized Structured Sparse State-Space
+ * Models" (gist.science explainer), technical summary -- methodology item 1
+ * (scores from a linear map of u_t, argmax over a precomputed dictionary of K
+ * sparse matrices, the chosen matrix a one-hot column selector, O(LN) memory)
+ * and item 3 (three-phase chunked kernel: per-chunk sequential recurrences,
+ * an inter-chunk prefix scan of carry states, a carry correction).  Readings
+ * where the pages are silent: column j of the selected matrix carries its one
+ * in row dict[h,k*,j]; the transition is that selector times diag(D_t); D_t
+ * is the logistic of a second linear map; Bu is supplied by the caller; C has
+ * one output per head.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a caller-owned DEVICE pointer, row-major and
+ *     contiguous, 16-byte aligned.  Shapes are given below in brackets.
+ *   - u, W_sel and W_d are fp32 (dims.in_dtype = PDSSM_F32) or bf16
+ *     (PDSSM_BF16, stored as raw 16-bit words).  Everything else is fp32
+ *     (int32 for indices).
+ *   - u is [B,H,L,d_in] when dims.u_shared = 0, or [B,L,d_in] shared by all
+ *     heads when dims.u_shared = 1.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  PDSSM_OK means "enqueued".  Faults surface at the caller's
+ *     next synchronisation.
+ *   - The library allocates nothing, never synchronises the device and holds
+ *     no global mutable state: scratch memory comes from the caller's
+ *     workspace.  Two calls that share one workspace must be ordered on one
+ *     stream.
+ *   - Arguments are validated on the host before any HIP call.  On failure
+ *     nothing is enqueued and a negative pdssm_status is returned; the
+ *     calling thread's pdssm_last_error() then describes the problem.
+ *   - Preconditions NOT checked on the device: dict values lie in [0, N);
+ *     inputs are finite.
+ *   - Shape limits (else PDSSM_EUNSUPPORTED): 1 <= N <= 64, 1 <= K <= 64,
+ *     K + N <= 128, d_in % 8 == 0, d_in <= 8192, and the per-chunk on-chip
+ *     footprint (about chunk * (N + 2) * 4 bytes) within 64 KiB.
+ */
+#ifndef PDSCAN_H
+#define PDSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PDSSM_ABI_VERSION 1
+
+typedef enum {
+  PDSSM_OK = 0,
+  PDSSM_EINVAL = -1,        /* bad argument: NULL, size <= 0, misaligned, aliasing */
+  PDSSM_EUNSUPPORTED = -2,  /* valid but outside the shape limits above           */
+  PDSSM_EWORKSPACE = -3,    /* workspace smaller than the matching *_workspace_bytes */
+  PDSSM_EHIP = -4           /* a HIP launch or runtime call failed                */
+} pdssm_status;
+
+typedef enum { PDSSM_F32 = 0, PDSSM_BF16 = 1 } pdssm_dtype;
+
+typedef struct {
+  int32_t B, H, L, N, K, d_in;
+  int32_t u_shared; /* 0: u is [B,H,L,d_in]; 1: u is [B,L,d_in], read by every head */
+  int32_t in_dtype; /* pdssm_dtype of u, W_sel and W_d                               */
+} pdssm_dims;
+
+/* Selection: scores, argmax and the logistic diagonal for every (b,h,t).
+ *   u [B,H,L,d] | [B,L,d]; W_sel [H,K,d]; W_d [H,N,d]; b_d [H,N]
+ *   k_star [B,H,L] int32 (out, required); D [B,H,L,N] fp32 (out, required)
+ *   dict_idx [H,K,N] int32 and P_idx [B,H,L,N] int32: optional pair.  When
+ *   P_idx is non-NULL it receives dict_idx[h, k*_t, :] (the selected matrix as
+ *   its N row indices) and dict_idx must be non-NULL; otherwise both may be
+ *   NULL.
+ * Score GEMMs run as fp32 MFMA for fp32 inputs and for bf16 inputs with
+ * d_in < 128 (bf16 products are exact in fp32), and as bf16 MFMA with fp32
+ * accumulation for bf16 inputs with d_in >= 128. */
+int pdssm_select(const pdssm_dims* dims, const void* u, const void* W_sel,
+                 const int32_t* dict_idx, const void* W_d, const float* b_d,
+                 int32_t* k_star, float* D, int32_t* P_idx, void* stream);
+
+/* Bytes of workspace pdssm_scan_fwd needs for these dims and chunk length. */
+int pdssm_scan_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes);
+
+/* Chunked scan given selections: phases A, B and C.
+ *   k_star [B,H,L] int32; dict_idx [H,K,N] int32; D [B,H,L,N]; Bu [B,H,L,N];
+ *   C [H,N]; h0 [B,H,N] or NULL (zero state)
+ *   y [B,H,L] (out); h_L [B,H,N] (out)
+ *   chunk >= 1: steps per chunk (the last chunk may be shorter).  Results do
+ *   not depend on chunk beyond floating-point rounding.
+ *   workspace: device scratch of at least pdssm_scan_workspace_bytes bytes;
+ *   its contents on entry do not matter. */
+int pdssm_scan_fwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
+                   const int32_t* dict_idx, const float* D, const float* Bu,
+                   const float* C, const float* h0, float* y, float* h_L,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pdssm_fwd needs for these dims and chunk length. */
+int pdssm_fwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes);
+
+/* Fused selection + chunked scan in one pass over u and Bu.  Arguments as in
+ * pdssm_select and pdssm_scan_fwd; k_star [B,H,L] and D [B,H,L,N] are
+ * optional outputs (NULL: not written). */
+int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
+              const int32_t* dict_idx, const void* W_d, const float* b_d,
+              const float* Bu, const float* C, const float* h0,
+              int32_t* k_star, float* D, float* y, float* h_L,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* pdssm_status_str(int status);
+
+/* Description of the calling thread's most recent failure ("" if none). */
+const char* pdssm_last_error(void);
+
+/* PDSSM_ABI_VERSION of the loaded library. */
+int pdssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDSCAN_H */

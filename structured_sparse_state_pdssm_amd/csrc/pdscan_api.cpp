@@ -1,0 +1,250 @@
+// C ABI of libpdscan: argument validation (host only, before any HIP call),
+// plan construction and kernel dispatch.  Declarations and the contract of
+// every entry point are in include/pdscan.h.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "pdscan.h"
+#include "pdscan_plan.h"
+
+namespace pdscan {
+hipError_t launch(int mode, const Args& a, hipStream_t st);
+}
+
+using pdscan::Plan;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+struct Range {
+  const char* name;
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Shape checks common to all entry points.  `chunk` < 0 means "not used".
+int check_dims(const pdssm_dims* d, int32_t chunk) {
+  if (!d) return fail(PDSSM_EINVAL, "dims is NULL");
+  if (d->B < 1 || d->H < 1 || d->L < 1 || d->N < 1 || d->K < 1 || d->d_in < 1)
+    return fail(PDSSM_EINVAL, "dims must be >= 1 (B=%d H=%d L=%d N=%d K=%d d_in=%d)", d->B, d->H,
+                d->L, d->N, d->K, d->d_in);
+  if (d->u_shared != 0 && d->u_shared != 1)
+    return fail(PDSSM_EINVAL, "u_shared must be 0 or 1 (got %d)", d->u_shared);
+  if (d->in_dtype != PDSSM_F32 && d->in_dtype != PDSSM_BF16)
+    return fail(PDSSM_EINVAL, "in_dtype must be PDSSM_F32 or PDSSM_BF16 (got %d)", d->in_dtype);
+  if (chunk != -1 && chunk < 1) return fail(PDSSM_EINVAL, "chunk must be >= 1 (got %d)", chunk);
+  if (d->N > 64) return fail(PDSSM_EUNSUPPORTED, "N=%d > 64 (one lane owns one state row)", d->N);
+  if (d->K > 64) return fail(PDSSM_EUNSUPPORTED, "K=%d > 64", d->K);
+  if (d->K + d->N > 128) return fail(PDSSM_EUNSUPPORTED, "K+N=%d > 128", d->K + d->N);
+  if (d->d_in % 8 != 0) return fail(PDSSM_EUNSUPPORTED, "d_in=%d is not a multiple of 8", d->d_in);
+  if (d->d_in > 8192) return fail(PDSSM_EUNSUPPORTED, "d_in=%d > 8192", d->d_in);
+  const uint64_t rows = (uint64_t)d->B * d->H * d->L;
+  if (rows > 0x7fffffffull)
+    return fail(PDSSM_EUNSUPPORTED, "B*H*L=%llu exceeds 2^31-1", (unsigned long long)rows);
+  return PDSSM_OK;
+}
+
+int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk) {
+  const int c = (mode == pdscan::kModeSelect) ? pdscan::kSelectRows : chunk;
+  if (!pdscan::make_plan(p, mode, d->B, d->H, d->L, d->N, d->K, d->d_in, d->u_shared,
+                         d->in_dtype == PDSSM_BF16, c))
+    return fail(PDSSM_EUNSUPPORTED,
+                "chunk=%d with N=%d needs %d bytes of on-chip memory per workgroup (limit %d)", c,
+                d->N, p.lds_bytes, pdscan::kMaxLds);
+  if ((uint64_t)p.nC * d->B * d->H > 0x7fffffffull)
+    return fail(PDSSM_EUNSUPPORTED, "too many chunks");
+  return PDSSM_OK;
+}
+
+struct Sizes {
+  size_t u, Wsel, Wd, bd, dict, Bu, C, h0, k, D, P, y, hL;
+};
+
+Sizes sizes(const pdssm_dims* d) {
+  const size_t es = d->in_dtype == PDSSM_BF16 ? 2 : 4;
+  const size_t B = d->B, H = d->H, L = d->L, N = d->N, K = d->K, din = d->d_in;
+  Sizes s;
+  s.u = B * (d->u_shared ? 1 : H) * L * din * es;
+  s.Wsel = H * K * din * es;
+  s.Wd = H * N * din * es;
+  s.bd = H * N * 4;
+  s.dict = H * K * N * 4;
+  s.Bu = B * H * L * N * 4;
+  s.C = H * N * 4;
+  s.h0 = B * H * N * 4;
+  s.k = B * H * L * 4;
+  s.D = B * H * L * N * 4;
+  s.P = s.D;
+  s.y = B * H * L * 4;
+  s.hL = B * H * N * 4;
+  return s;
+}
+
+// NULL (if required), alignment and aliasing checks.
+int check_ptrs(const Range* in, int nin, const Range* out, int nout, const char* const* required) {
+  for (int r = 0; required[r]; ++r) {
+    for (int q = 0; q < nin; ++q)
+      if (!strcmp(in[q].name, required[r]) && !in[q].p)
+        return fail(PDSSM_EINVAL, "%s is NULL", in[q].name);
+    for (int q = 0; q < nout; ++q)
+      if (!strcmp(out[q].name, required[r]) && !out[q].p)
+        return fail(PDSSM_EINVAL, "%s is NULL", out[q].name);
+  }
+  for (int q = 0; q < nin; ++q)
+    if (in[q].p && ((uintptr_t)in[q].p & 15))
+      return fail(PDSSM_EINVAL, "%s is not 16-byte aligned", in[q].name);
+  for (int q = 0; q < nout; ++q)
+    if (out[q].p && ((uintptr_t)out[q].p & 15))
+      return fail(PDSSM_EINVAL, "%s is not 16-byte aligned", out[q].name);
+  for (int q = 0; q < nout; ++q) {
+    for (int r = 0; r < nin; ++r)
+      if (overlap(out[q], in[r]))
+        return fail(PDSSM_EINVAL, "output %s overlaps input %s", out[q].name, in[r].name);
+    for (int r = q + 1; r < nout; ++r)
+      if (overlap(out[q], out[r]))
+        return fail(PDSSM_EINVAL, "outputs %s and %s overlap", out[q].name, out[r].name);
+  }
+  return PDSSM_OK;
+}
+
+int dispatch(int mode, const pdscan::Args& a, void* stream) {
+  const hipError_t e = pdscan::launch(mode, a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return PDSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pdssm_abi_version(void) { return PDSSM_ABI_VERSION; }
+
+const char* pdssm_last_error(void) { return g_err; }
+
+const char* pdssm_status_str(int status) {
+  switch (status) {
+    case PDSSM_OK: return "ok";
+    case PDSSM_EINVAL: return "invalid argument";
+    case PDSSM_EUNSUPPORTED: return "unsupported shape";
+    case PDSSM_EWORKSPACE: return "workspace too small";
+    case PDSSM_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int pdssm_select(const pdssm_dims* dims, const void* u, const void* W_sel,
+                 const int32_t* dict_idx, const void* W_d, const float* b_d, int32_t* k_star,
+                 float* D, int32_t* P_idx, void* stream) {
+  int rc = check_dims(dims, -1);
+  if (rc) return rc;
+  if (P_idx && !dict_idx) return fail(PDSSM_EINVAL, "P_idx requested but dict_idx is NULL");
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"u", u, z.u}, {"W_sel", W_sel, z.Wsel}, {"W_d", W_d, z.Wd},
+                      {"b_d", b_d, z.bd}, {"dict_idx", dict_idx, z.dict}};
+  const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"P_idx", P_idx, z.P}};
+  static const char* const req[] = {"u", "W_sel", "W_d", "b_d", "k_star", "D", nullptr};
+  if ((rc = check_ptrs(in, 5, out, 3, req))) return rc;
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeSelect, dims, -1))) return rc;
+  pdscan::Args a = {};
+  a.p = p;
+  a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx;
+  a.k_out = k_star; a.D_out = D; a.P_out = P_idx;
+  return dispatch(pdscan::kModeSelect, a, stream);
+}
+
+int pdssm_scan_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  if (!bytes) return fail(PDSSM_EINVAL, "bytes is NULL");
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk))) return rc;
+  *bytes = p.ws_bytes;
+  return PDSSM_OK;
+}
+
+int pdssm_fwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  if (!bytes) return fail(PDSSM_EINVAL, "bytes is NULL");
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk))) return rc;
+  *bytes = p.ws_bytes;
+  return PDSSM_OK;
+}
+
+int pdssm_scan_fwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
+                   const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
+                   const float* h0, float* y, float* h_L, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk))) return rc;
+  if (workspace_bytes < p.ws_bytes)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"k_star", k_star, z.k}, {"dict_idx", dict_idx, z.dict}, {"D", D, z.D},
+                      {"Bu", Bu, z.Bu}, {"C", C, z.C}, {"h0", h0, z.h0}};
+  const Range out[] = {{"y", y, z.y}, {"h_L", h_L, z.hL}, {"workspace", workspace, p.ws_bytes}};
+  static const char* const req[] = {"k_star", "dict_idx", "D", "Bu", "C", "y", "h_L", "workspace",
+                                    nullptr};
+  if ((rc = check_ptrs(in, 6, out, 3, req))) return rc;
+  pdscan::Args a = {};
+  a.p = p;
+  a.dict = dict_idx; a.k_in = k_star; a.D_in = D; a.Bu = Bu; a.C = C; a.h0 = h0;
+  a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
+  return dispatch(pdscan::kModeScan, a, stream);
+}
+
+int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
+              const int32_t* dict_idx, const void* W_d, const float* b_d, const float* Bu,
+              const float* C, const float* h0, int32_t* k_star, float* D, float* y, float* h_L,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk))) return rc;
+  if (workspace_bytes < p.ws_bytes)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"u", u, z.u},         {"W_sel", W_sel, z.Wsel}, {"dict_idx", dict_idx, z.dict},
+                      {"W_d", W_d, z.Wd},    {"b_d", b_d, z.bd},       {"Bu", Bu, z.Bu},
+                      {"C", C, z.C},         {"h0", h0, z.h0}};
+  const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y},
+                       {"h_L", h_L, z.hL},      {"workspace", workspace, p.ws_bytes}};
+  static const char* const req[] = {"u",  "W_sel", "dict_idx", "W_d", "b_d",      "Bu",
+                                    "C",  "y",     "h_L",      "workspace", nullptr};
+  if ((rc = check_ptrs(in, 8, out, 5, req))) return rc;
+  pdscan::Args a = {};
+  a.p = p;
+  a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx;
+  a.Bu = Bu; a.C = C; a.h0 = h0; a.k_out = k_star; a.D_out = D;
+  a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
+  return dispatch(pdscan::kModeFused, a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Launch plan shared by the host dispatcher and the kernels: work split,
+// on-chip (LDS) layout and workspace layout for one call.
+//
+// Work split.  One workgroup (256 lanes, 4 waves) owns one chunk of one
+// (b, h) sequence.  Inside it the chunk's steps are cut into G consecutive
+// sub-chunks of S steps, one per lane group; a lane group is NP = next power
+// of two >= N lanes, so each lane owns one state row and G * NP = 256.
+// Phase A runs the G sub-chunks side by side; their summaries are combined in
+// order in LDS to form the chunk summary that enters the inter-chunk scan.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pdscan {
+
+constexpr int kThreads = 256;          // lanes per workgroup
+constexpr int kWaves = kThreads / 64;  // wave64
+constexpr int kSelectRows = 256;       // rows per workgroup for selection alone
+constexpr int kMaxLds = 64 * 1024;     // bytes of LDS one workgroup may use
+
+enum Mode : int { kModeSelect = 0, kModeScan = 1, kModeFused = 2 };
+
+struct Plan {
+  // problem
+  int B, H, L, N, K, d, u_shared, in_bf16, chunk;
+  // work split
+  int NP;    // lanes per group
+  int G;     // groups per workgroup
+  int S;     // steps per group
+  int nC;    // chunks per sequence
+  int NC;    // GEMM columns (K scores then N pre-activations), padded to 16
+  int KP;    // score staging width
+  int mma_bf16;  // score GEMM on bf16 MFMA (else fp32 MFMA)
+  int tasks;     // workgroups
+  // LDS byte offsets
+  int off_D, off_k, off_yl, off_dict, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
+      off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_stage, off_misc, lds_bytes;
+  // workspace byte offsets (scan / fused)
+  size_t ws_agg, ws_inc, ws_bytes;
+};
+
+inline int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+inline int align_up(int x, int a) { return (x + a - 1) / a * a; }
+
+// Fills `p` for one call.  `mode` selects which parts exist.  Returns false
+// when the plan needs more than kMaxLds bytes of LDS.
+inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int d, int u_shared,
+                      int in_bf16, int chunk) {
+  p.B = B; p.H = H; p.L = L; p.N = N; p.K = K; p.d = d;
+  p.u_shared = u_shared; p.in_bf16 = in_bf16;
+  // a chunk longer than the sequence behaves exactly like chunk = L
+  p.chunk = (mode == kModeSelect) ? kSelectRows : (chunk < L ? chunk : L);
+  p.NP = next_pow2(N);
+  p.G = kThreads / p.NP;
+  p.S = (p.chunk + p.G - 1) / p.G;
+  p.nC = (L + p.chunk - 1) / p.chunk;
+  p.NC = align_up(K + N, 16);
+  p.KP = align_up(K, 4) + 1;            // +1 word breaks power-of-two row strides
+  p.mma_bf16 = (in_bf16 && d >= 128) ? 1 : 0;
+  p.tasks = p.nC * B * H;
+
+  const int T = p.chunk;
+  int off = 0;
+  auto take = [&](int bytes) { int o = off; off = align_up(off + bytes, 16); return o; };
+  const bool scan = mode != kModeSelect;
+  p.off_D = scan ? take(T * N * 4) : 0;
+  p.off_k = scan ? take(T * 4) : 0;
+  p.off_yl = scan ? take(T * 4) : 0;
+  p.off_dict = take(K * N * 4);
+  p.off_C = take(N * 4);
+  p.off_bd = take(N * 4);
+  p.off_slot = take(kThreads * 4);
+  p.off_sIdx = scan ? take(p.G * N * 4) : 0;
+  p.off_sSc = scan ? take(p.G * N * 4) : 0;
+  p.off_sB = scan ? take(p.G * N * 4) : 0;
+  p.off_pIdx = scan ? take(p.G * N * 4) : 0;
+  p.off_pSc = scan ? take(p.G * N * 4) : 0;
+  p.off_pB = scan ? take(p.G * N * 4) : 0;
+  p.off_H = take(64 * 4);
+  p.off_tmp = take(64 * 4);
+  p.off_stage = (mode != kModeScan) ? take(kWaves * 16 * p.KP * 4) : 0;
+  p.off_misc = take(16);
+  p.lds_bytes = off;
+
+  // workspace: header (ticket counter, error word) then tagged chunk
+  // aggregates (3N words per chunk and sequence) and inclusive states (N).
+  const size_t seqchunks = (size_t)p.nC * B * H;
+  p.ws_agg = 256;
+  p.ws_inc = p.ws_agg + seqchunks * 3 * N * sizeof(uint64_t);
+  p.ws_bytes = (mode == kModeSelect) ? 0 : p.ws_inc + seqchunks * N * sizeof(uint64_t);
+  return p.lds_bytes <= kMaxLds;
+}
+
+// Everything a kernel launch reads.
+struct Args {
+  Plan p;
+  const void* u;
+  const void* W_sel;
+  const void* W_d;
+  const float* b_d;
+  const int32_t* dict;
+  const float* Bu;
+  const float* C;
+  const float* h0;
+  const int32_t* k_in;   // scan mode
+  const float* D_in;     // scan mode
+  int32_t* k_out;        // optional
+  float* D_out;          // optional
+  int32_t* P_out;        // optional (selection mode)
+  float* y;
+  float* hL;
+  unsigned char* ws;     // workspace base
+};
+
+// Workspace header words.
+constexpr int kWsTicket = 0;   // uint32 ticket counter
+constexpr int kWsError = 1;    // uint32: nonzero if a look-back wait gave up
+
+}  // namespace pdscan
