@@ -14,6 +14,11 @@
 // scale[j] in row idx[j] of column j; applying it is a scatter-add, and two
 // maps compose by an index gather and a scale product.
 //
+// On-chip layout of one chunk (T steps): D and then w live in one [N][TS]
+// buffer (t contiguous), so the selection epilogue stores four steps of one
+// column with one 16-byte write, phase A reads four steps per lane at once,
+// and phase C reads consecutive steps on consecutive lanes.
+//
 // Phase B is a single-pass decoupled look-back: workgroups take chunk tickets
 // in (chunk, sequence) order, publish their chunk aggregate, then walk back
 // over predecessors until an inclusive state is found.  Every word published
@@ -34,9 +39,12 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+typedef int i4v __attribute__((ext_vector_type(4)));
+typedef int i2v __attribute__((ext_vector_type(2)));
 
 constexpr uint64_t kTagValid = 1ull << 32;
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kBuBlock = 32;   // phase-A steps whose drive terms sit in registers
 
 // Compiler-level ordering point between LDS accesses of different lanes of
 // one wave.  The hardware executes one wave's LDS instructions in order.
@@ -61,105 +69,322 @@ __device__ __forceinline__ uint64_t get_tagged(uint64_t* p) {
 
 __device__ __forceinline__ bool tag_ok(uint64_t w) { return (w >> 32) == 1u; }
 
-// ---------------------------------------------------------------------------
-// Score GEMM for one 16-row tile: acc[ct] holds rows row0 + 4*(lane/16) + r,
-// column 16*ct + lane%16 of [scores | pre-activations].
-//
-// fp32 MFMA (v_mfma_f32_16x16x4_f32): lane (i = lane%16, g = lane/16) feeds
-// A = u[row0+i][c] and B = W[col][c] for the channel c = m + 4g + q of step q
-// of group m; bf16 MFMA (v_mfma_f32_16x16x32_bf16): 8 channels m + 8g .. +7
-// per lane.  Both operands use the same channel order, so the sum is the
-// full contraction.
-// ---------------------------------------------------------------------------
-template <int IN_BF16, int MMA_BF16>
-__device__ __forceinline__ void score_tile(const Args& a, int s_u, int h, int c0, int row0,
-                                           int rowlim, int lane, f4v acc[8]) {
-  const Plan& p = a.p;
-  const int i = lane & 15, g = lane >> 4;
-  const int row = row0 + i;
-  const bool rv = row < rowlim;
-  const int NCT = p.NC >> 4;
-  const size_t urow = ((size_t)s_u * p.L + c0 + row) * p.d;
-  for (int ct = 0; ct < 8; ++ct) acc[ct] = f4v{0.f, 0.f, 0.f, 0.f};
+// DPP lane permutations inside 16-lane rows.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within each 16 lanes
 
-  const int K = p.K, N = p.N, d = p.d;
-  if constexpr (!MMA_BF16) {
-    for (int m = 0; m < d; m += 16) {
-      const int ch = m + 4 * g;
-      f4v av = {0.f, 0.f, 0.f, 0.f};
-      if (rv && ch < d) {
-        if constexpr (IN_BF16) {
-          u2v w = *(const u2v*)((const uint16_t*)a.u + urow + ch);
-          av = f4v{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-        } else {
-          av = *(const f4v*)((const float*)a.u + urow + ch);
-        }
-      }
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        if (ct < NCT) {
-          const int col = ct * 16 + i;
-          f4v bv = {0.f, 0.f, 0.f, 0.f};
-          if (ch < d && col < K + N) {
-            const size_t wo = (col < K) ? ((size_t)h * K + col) * d : ((size_t)h * N + col - K) * d;
-            const void* wb = (col < K) ? a.W_sel : a.W_d;
-            if constexpr (IN_BF16) {
-              u2v w = *(const u2v*)((const uint16_t*)wb + wo + ch);
-              bv = f4v{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-            } else {
-              bv = *(const f4v*)((const float*)wb + wo + ch);
-            }
-          }
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[ct], 0, 0, 0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[ct], 0, 0, 0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[ct], 0, 0, 0);
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[ct], 0, 0, 0);
-        }
-      }
-    }
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+
+// (value, index) pair order: larger value first, then the lower index.
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& k) {
+  const float ov = dpp_f<CTRL>(v);
+  const int ok = dpp_i<CTRL>(k);
+  const bool take = (ov > v) || (ov == v && ok < k);
+  v = take ? ov : v;
+  k = take ? ok : k;
+}
+
+// Sum over a lane group of NP lanes (NP a power of two); every lane of the
+// group gets the same value.
+__device__ __forceinline__ float group_sum(float v, int NP) {
+  if (NP >= 2) v += dpp_f<kDppXor1>(v);
+  if (NP >= 4) v += dpp_f<kDppXor2>(v);
+  if (NP >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (NP >= 16) v += dpp_f<kDppMirror>(v);
+  if (NP >= 32) v += __shfl_xor(v, 16, 64);
+  if (NP >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Selection of one wave's rows.
+//
+// MFMA tiles of 16 rows: lane (i = lane%16, g = lane/16) feeds A = u[row0+i][c]
+// and B = W[col][c]; fp32 (v_mfma_f32_16x16x4_f32) takes channel m + 4g + q at
+// step q of channel block m, bf16 (v_mfma_f32_16x16x32_bf16) channels
+// m + 8g .. +7.  Both operands use the same channel order, so each output is
+// the full contraction.  acc[ct] holds rows row0 + 4g + r, column 16 ct + i
+// of [scores | pre-activations].
+//
+// FAST = true: W lives in registers for the whole wave (KCH channel blocks,
+// NCT column tiles known at compile time) and the next tile's u is loaded
+// while the current one is multiplied.  FAST = false: any shape, operands
+// loaded per tile.
+// ---------------------------------------------------------------------------
+struct SelDst {
+  int* kbuf;      // chunk-local k* (fused) or nullptr
+  float* Dbuf;    // [N][TS] (fused) or nullptr
+  int TS;
+  int32_t* k_out; // global, optional
+  float* D_out;   // global, optional
+  int32_t* P_out; // global, optional
+  const int* dic; // LDS dictionary [K][N] (for P_out)
+  size_t gbase;   // global row index of chunk row 0 = s*L + c0
+};
+
+template <int IN_BF16, int MMA_BF16>
+struct Frag;
+template <>
+struct Frag<0, 0> { typedef f4v T; };
+template <>
+struct Frag<1, 0> { typedef u2v T; };
+template <>
+struct Frag<1, 1> { typedef u4v T; };
+
+template <int IN_BF16, int MMA_BF16>
+__device__ __forceinline__ typename Frag<IN_BF16, MMA_BF16>::T load_frag(const void* base, size_t off,
+                                                                         bool ok) {
+  typedef typename Frag<IN_BF16, MMA_BF16>::T T;
+  T z = {};
+  if (!ok) return z;
+  if constexpr (!IN_BF16) return *(const T*)((const float*)base + off);
+  else return *(const T*)((const uint16_t*)base + off);
+}
+
+template <int IN_BF16, int MMA_BF16>
+__device__ __forceinline__ void mma_step(f4v& acc, typename Frag<IN_BF16, MMA_BF16>::T a,
+                                         typename Frag<IN_BF16, MMA_BF16>::T b) {
+  if constexpr (MMA_BF16) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a),
+                                                  __builtin_bit_cast(bf8v, b), acc, 0, 0, 0);
+  } else if constexpr (IN_BF16) {
+    const float a0 = __uint_as_float(a.x << 16), a1 = __uint_as_float(a.x & 0xffff0000u);
+    const float a2 = __uint_as_float(a.y << 16), a3 = __uint_as_float(a.y & 0xffff0000u);
+    const float b0 = __uint_as_float(b.x << 16), b1 = __uint_as_float(b.x & 0xffff0000u);
+    const float b2 = __uint_as_float(b.y << 16), b3 = __uint_as_float(b.y & 0xffff0000u);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, b2, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, b3, acc, 0, 0, 0);
   } else {
-    for (int m = 0; m < d; m += 32) {
-      const int ch = m + 8 * g;
-      u4v ar = {0u, 0u, 0u, 0u};
-      if (rv && ch < d) ar = *(const u4v*)((const uint16_t*)a.u + urow + ch);
-      const bf8v av = __builtin_bit_cast(bf8v, ar);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+  }
+}
+
+// channels per fragment block: 16 (fp32 MFMA, 4 per lane group) or 32 (bf16)
+template <int MMA_BF16>
+constexpr int kChanBlock = MMA_BF16 ? 32 : 16;
+
+// Epilogue of one tile: argmax over score columns, logistic of the
+// pre-activations, stores.  rows >= rlim are not stored.
+template <int NCT>
+__device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, const float* bdr,
+                                              int row0, int rlim, int lane, const SelDst& o) {
+  const int i = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N;
+  float bv[4];
+  int bk[4];
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        if (ct < NCT) {
-          const int col = ct * 16 + i;
-          u4v br = {0u, 0u, 0u, 0u};
-          if (ch < d && col < K + N) {
-            const size_t wo = (col < K) ? ((size_t)h * K + col) * d : ((size_t)h * N + col - K) * d;
-            const void* wb = (col < K) ? a.W_sel : a.W_d;
-            br = *(const u4v*)((const uint16_t*)wb + wo + ch);
-          }
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf8v, br),
-                                                            acc[ct], 0, 0, 0);
-        }
-      }
+  for (int r = 0; r < 4; ++r) { bv[r] = -__builtin_inff(); bk[r] = 0x7fffffff; }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ct + i;
+    if (col < K) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (acc[ct][r] > bv[r]) { bv[r] = acc[ct][r]; bk[r] = col; }   // columns rise with ct
     }
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    argmax_step<kDppXor1>(bv[r], bk[r]);
+    argmax_step<kDppXor2>(bv[r], bk[r]);
+    argmax_step<kDppHalfMirror>(bv[r], bk[r]);
+    argmax_step<kDppMirror>(bv[r], bk[r]);
+  }
+  const int rb = row0 + 4 * g;   // first of this lane's four rows
+  const bool full = rb + 4 <= rlim;
+  if (i == 0) {
+    if (o.kbuf) {
+      if (full) *(i4v*)(o.kbuf + rb) = i4v{bk[0], bk[1], bk[2], bk[3]};
+      else
+        for (int r = 0; r < 4; ++r) if (rb + r < rlim) o.kbuf[rb + r] = bk[r];
+    }
+    if (o.k_out)
+      for (int r = 0; r < 4; ++r) if (rb + r < rlim) o.k_out[o.gbase + rb + r] = bk[r];
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ct + i;
+    if (col >= K && col < K + N) {
+      const int n = col - K;
+      f4v dv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dv[r] = logistic(acc[ct][r] + bdr[ct]);
+      if (o.Dbuf) {
+        float* dst = o.Dbuf + n * o.TS + rb;
+        if (full) *(f4v*)dst = dv;
+        else
+          for (int r = 0; r < 4; ++r) if (rb + r < rlim) dst[r] = dv[r];
+      }
+      if (o.D_out)
+        for (int r = 0; r < 4; ++r)
+          if (rb + r < rlim) o.D_out[(o.gbase + rb + r) * N + n] = dv[r];
+    }
+  }
+  if (o.P_out) {
+    for (int r = 0; r < 4; ++r)
+      for (int gg = 0; gg < 4; ++gg) {
+        const int kr = __shfl(bk[r], 16 * gg, 64);
+        const int row = row0 + 4 * gg + r;
+        if (row < rlim)
+          for (int n = lane; n < N; n += 64) o.P_out[(o.gbase + row) * N + n] = o.dic[kr * N + n];
+      }
+  }
+}
+
+template <int IN_BF16, int MMA_BF16, int KCH, int NCT>
+__device__ __forceinline__ void select_rows(const Args& a, int s_u, int h, int c0, int rbeg,
+                                            int rend, int lane, const SelDst& o) {
+  typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
+  constexpr int CB = kChanBlock<MMA_BF16>;
+  constexpr int PER = MMA_BF16 ? 8 : 4;           // channels per lane per block
+  const Plan& p = a.p;
+  const int i = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N, d = p.d;
+
+  // W fragments and logistic biases, in registers for the whole wave
+  FT wf[NCT][KCH];
+  float bdr[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ct + i;
+    const bool sc = col < K, zc = col >= K && col < K + N;
+    const void* wb = sc ? a.W_sel : a.W_d;
+    const size_t wrow = sc ? ((size_t)h * K + col) * d : ((size_t)h * N + (col - K)) * d;
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) {
+      const int ch = m * CB + PER * g;
+      wf[ct][m] = load_frag<IN_BF16, MMA_BF16>(wb, wrow + ch, (sc || zc) && ch < d);
+    }
+    bdr[ct] = zc ? a.b_d[(size_t)h * N + col - K] : 0.f;
+  }
+
+  const size_t ubase = ((size_t)s_u * p.L + c0) * d;
+  FT cur[KCH], nxt[KCH];
+  {
+    const int row = rbeg + i;
+#pragma unroll
+    for (int m = 0; m < KCH; ++m)
+      cur[m] = load_frag<IN_BF16, MMA_BF16>(a.u, ubase + (size_t)row * d + m * CB + PER * g,
+                                            row < rend);
+  }
+  for (int row0 = rbeg; row0 < rend; row0 += 16) {
+    const int nrow = row0 + 16 + i;
+#pragma unroll
+    for (int m = 0; m < KCH; ++m)
+      nxt[m] = load_frag<IN_BF16, MMA_BF16>(a.u, ubase + (size_t)nrow * d + m * CB + PER * g,
+                                            nrow < rend);
+    f4v acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < KCH; ++m)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) mma_step<IN_BF16, MMA_BF16>(acc[ct], cur[m], wf[ct][m]);
+    tile_epilogue<NCT>(p, acc, bdr, row0, rend, lane, o);
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) cur[m] = nxt[m];
+  }
+}
+
+// Any shape: operands loaded per 16-row tile, up to 8 column tiles.
+template <int IN_BF16, int MMA_BF16>
+__device__ __forceinline__ void select_rows_any(const Args& a, int s_u, int h, int c0, int rbeg,
+                                                int rend, int lane, const SelDst& o) {
+  typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
+  constexpr int CB = kChanBlock<MMA_BF16>;
+  constexpr int PER = MMA_BF16 ? 8 : 4;
+  const Plan& p = a.p;
+  const int i = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N, d = p.d;
+  const int NCT = p.NC >> 4;
+  float bdr[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const int col = 16 * ct + i;
+    bdr[ct] = (ct < NCT && col >= K && col < K + N) ? a.b_d[(size_t)h * N + col - K] : 0.f;
+  }
+  const size_t ubase = ((size_t)s_u * p.L + c0) * d;
+  for (int row0 = rbeg; row0 < rend; row0 += 16) {
+    const int row = row0 + i;
+    f4v acc[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[ct] = f4v{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m * CB < d; ++m) {
+      const int ch = m * CB + PER * g;
+      const FT av = load_frag<IN_BF16, MMA_BF16>(a.u, ubase + (size_t)row * d + ch,
+                                                 row < rend && ch < d);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        if (ct < NCT) {
+          const int col = 16 * ct + i;
+          const bool sc = col < K, zc = col >= K && col < K + N;
+          const void* wb = sc ? a.W_sel : a.W_d;
+          const size_t wrow = sc ? ((size_t)h * K + col) * d : ((size_t)h * N + (col - K)) * d;
+          const FT bw = load_frag<IN_BF16, MMA_BF16>(wb, wrow + ch, (sc || zc) && ch < d);
+          mma_step<IN_BF16, MMA_BF16>(acc[ct], av, bw);
+        }
+      }
+    }
+    switch (NCT) {
+      case 1: tile_epilogue<1>(p, acc, bdr, row0, rend, lane, o); break;
+      case 2: tile_epilogue<2>(p, acc, bdr, row0, rend, lane, o); break;
+      case 3: tile_epilogue<3>(p, acc, bdr, row0, rend, lane, o); break;
+      case 4: tile_epilogue<4>(p, acc, bdr, row0, rend, lane, o); break;
+      case 5: tile_epilogue<5>(p, acc, bdr, row0, rend, lane, o); break;
+      case 6: tile_epilogue<6>(p, acc, bdr, row0, rend, lane, o); break;
+      case 7: tile_epilogue<7>(p, acc, bdr, row0, rend, lane, o); break;
+      default: tile_epilogue<8>(p, acc, bdr, row0, rend, lane, o); break;
+    }
+  }
+}
+
+// Shapes with a register-resident fast path.
+enum SelPath : int { kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3 };
+
+template <int IN_BF16, int MMA_BF16, int PATH>
+__device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, int c0, int rbeg,
+                                                int rend, int lane, const SelDst& o) {
+  if constexpr (PATH == kSelF32D64N2 && !IN_BF16 && !MMA_BF16)
+    select_rows<0, 0, 4, 2>(a, s_u, h, c0, rbeg, rend, lane, o);
+  else if constexpr (PATH == kSelF32D16N1 && !IN_BF16 && !MMA_BF16)
+    select_rows<0, 0, 1, 1>(a, s_u, h, c0, rbeg, rend, lane, o);
+  else if constexpr (PATH == kSelBF16D128N3 && IN_BF16 && MMA_BF16)
+    select_rows<1, 1, 4, 3>(a, s_u, h, c0, rbeg, rend, lane, o);
+  else
+    select_rows_any<IN_BF16, MMA_BF16>(a, s_u, h, c0, rbeg, rend, lane, o);
 }
 
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <int MODE, int IN_BF16, int MMA_BF16>
-__global__ __launch_bounds__(kThreads) void pdssm_kernel(Args a) {
-  extern __shared__ __align__(16) unsigned char smem[];
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH>
+__device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   const Plan& p = a.p;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = p.N, K = p.K, NP = p.NP, S = p.S, T = p.chunk;
+  const int N = p.N, K = p.K, NP = p.NP, S = p.S, T = p.chunk, TS = p.TS;
   const int BH = p.B * p.H;
 
   float* Dbuf = (float*)(smem + p.off_D);
   int* kbuf = (int*)(smem + p.off_k);
   float* yloc = (float*)(smem + p.off_yl);
   int* dic = (int*)(smem + p.off_dict);
+  i2v* DC = (i2v*)(smem + p.off_DC);
   float* Cs = (float*)(smem + p.off_C);
-  float* bds = (float*)(smem + p.off_bd);
   float* slots = (float*)(smem + p.off_slot);
   int* sIdx = (int*)(smem + p.off_sIdx);
   float* sSc = (float*)(smem + p.off_sSc);
@@ -169,7 +394,6 @@ __global__ __launch_bounds__(kThreads) void pdssm_kernel(Args a) {
   float* pB = (float*)(smem + p.off_pB);
   float* Hs = (float*)(smem + p.off_H);
   float* tmp = (float*)(smem + p.off_tmp);
-  float* stage = (float*)(smem + p.off_stage);
   int* misc = (int*)(smem + p.off_misc);
 
   uint32_t* hdr = (uint32_t*)a.ws;
@@ -189,138 +413,119 @@ __global__ __launch_bounds__(kThreads) void pdssm_kernel(Args a) {
   const int b = s / p.H, h = s % p.H;
   const int c0 = c * T;
   const int Tc = min(T, p.L - c0);
+  const size_t gbase = (size_t)s * p.L + c0;
+
+  const int gpw = 64 / NP;                 // lane groups per wave
+  const int gl = lane / NP, j = lane % NP;
+  const int gam = wave * gpw + gl;         // this lane's group (sub-chunk)
+  const int tb = gam * S, te = min(tb + S, Tc);
+  const bool act = j < N;
+
+  // ---- phase-A drive terms of the first block: issued first, used last
+  float bu[kBuBlock];
+  if constexpr (MODE != kModeSelect) {
+#pragma unroll
+    for (int q = 0; q < kBuBlock; ++q) {
+      const int t = tb + q;
+      bu[q] = (act && t < te) ? a.Bu[(gbase + t) * N + j] : 0.f;
+    }
+  }
 
   // ---- per-head constants
-  const bool need_dict = (MODE != kModeSelect) || (a.P_out != nullptr);
-  if (need_dict)
-    for (int q = tid; q < K * N; q += kThreads) dic[q] = a.dict[(size_t)h * K * N + q];
-  for (int q = tid; q < N; q += kThreads) {
-    if (MODE != kModeScan) bds[q] = a.b_d[(size_t)h * N + q];
-    if (MODE != kModeSelect) Cs[q] = a.C[(size_t)h * N + q];
+  if constexpr (MODE == kModeSelect) {
+    if (a.P_out)
+      for (int q = tid; q < K * N; q += kThreads) dic[q] = a.dict[(size_t)h * K * N + q];
+  } else {
+    for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
+    __syncthreads();
+    // DC[k][m] = (dict[k][m], C[dict[k][m]]): target row and its output weight
+    for (int q = tid; q < K * N; q += kThreads) {
+      const int r = a.dict[(size_t)h * K * N + q];
+      DC[q] = i2v{r, __float_as_int(Cs[r])};
+    }
   }
   if constexpr (MODE == kModeScan) {
-    const size_t base = (size_t)s * p.L + c0;
-    for (int q = tid; q < Tc; q += kThreads) kbuf[q] = a.k_in[base + q];
-    const f4v* src = (const f4v*)(a.D_in + base * N);
-    if ((N & 3) == 0) {
-      for (int q = tid; q < Tc * N / 4; q += kThreads) ((f4v*)Dbuf)[q] = src[q];
-    } else {
-      for (int q = tid; q < Tc * N; q += kThreads) Dbuf[q] = a.D_in[base * N + q];
+    for (int q = tid; q < Tc; q += kThreads) kbuf[q] = a.k_in[gbase + q];
+    for (int q = tid; q < Tc * N; q += kThreads) {
+      const int t = q / N, n = q - t * N;
+      Dbuf[n * TS + t] = a.D_in[gbase * N + q];
     }
   }
   __syncthreads();
 
-  const int gpw = 64 / NP;                       // groups per wave
-  const int wrow0 = wave * gpw * S;              // this wave's rows [wrow0, wrow1)
-  const int wrow1 = min(wrow0 + gpw * S, Tc);
-
   // ---- selection for this wave's rows
   if constexpr (MODE != kModeScan) {
     const int s_u = p.u_shared ? b : s;
-    const int i = lane & 15, g = lane >> 4;
-    float* st = stage + wave * 16 * p.KP;
-    for (int row0 = wrow0; row0 < wrow1; row0 += 16) {
-      f4v acc[8];
-      score_tile<IN_BF16, MMA_BF16>(a, s_u, h, c0, row0, wrow1, lane, acc);
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        if (ct < (p.NC >> 4)) {
-          const int col = ct * 16 + i;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int lr = 4 * g + r, row = row0 + lr;
-            if (row < wrow1) {
-              const float v = acc[ct][r];
-              if (col < K) {
-                st[lr * p.KP + col] = v;
-              } else if (col < K + N) {
-                const int n = col - K;
-                const float dv = logistic(v + bds[n]);
-                if constexpr (MODE == kModeFused) Dbuf[row * N + n] = dv;
-                if (a.D_out) a.D_out[((size_t)s * p.L + c0 + row) * N + n] = dv;
-              }
-            }
-          }
-        }
-      }
-      WAVE_SYNC();
-      int kk = 0;
-      if (lane < 16 && row0 + lane < wrow1) {
-        const float* sr = st + lane * p.KP;
-        float best = sr[0];
-        for (int k = 1; k < K; ++k) {
-          const float v = sr[k];
-          if (v > best) { best = v; kk = k; }        // strict: lowest index wins ties
-        }
-        const int row = row0 + lane;
-        if constexpr (MODE == kModeFused) kbuf[row] = kk;
-        if (a.k_out) a.k_out[(size_t)s * p.L + c0 + row] = kk;
-      }
-      if (a.P_out) {
-        // lane r (< 16) holds k* of row row0 + r
-        for (int r = 0; r < 16; ++r) {
-          const int kr = __shfl(kk, r, 64);
-          const int row = row0 + r;
-          if (row < wrow1)
-            for (int n = lane; n < N; n += 64)
-              a.P_out[((size_t)s * p.L + c0 + row) * N + n] = dic[kr * N + n];
-        }
-      }
-      WAVE_SYNC();
-    }
+    SelDst o;
+    o.kbuf = (MODE == kModeFused) ? kbuf : nullptr;
+    o.Dbuf = (MODE == kModeFused) ? Dbuf : nullptr;
+    o.TS = TS;
+    o.k_out = a.k_out;
+    o.D_out = a.D_out;
+    o.P_out = a.P_out;
+    o.dic = dic;
+    o.gbase = gbase;
+    const int wr0 = min(wave * gpw * S, Tc), wr1 = min(wr0 + gpw * S, Tc);
+    select_dispatch<IN_BF16, MMA_BF16, PATH>(a, s_u, h, c0, wr0, wr1, lane, o);
   }
   if constexpr (MODE == kModeSelect) return;
+  WAVE_SYNC();   // this wave's k* / D rows are read back by its own lane groups
 
-  // ---- phase A: G sub-chunks of S steps, one per lane group
-  const int gl = lane / NP, j = lane % NP;
-  const int gam = wave * gpw + gl;
-  const int tb = gam * S;
-  const bool act = j < N;
+  // ---- phase A: each lane group runs its sub-chunk [tb, te) from a zero state
   float* slot = slots + gam * NP;
   const float cj = act ? Cs[j] : 0.f;
   float hl = 0.f, msc = 1.f;
   int midx = j;
-  {
-    const size_t bub = ((size_t)s * p.L + c0) * N + j;
-    constexpr int PF = 16;
-    float cur[PF], nxt[PF];
+  for (int blk = 0; blk < S; blk += kBuBlock) {
+    if (blk > 0) {
 #pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      const int t = tb + q;
-      cur[q] = (act && q < S && t < Tc) ? a.Bu[bub + (size_t)t * N] : 0.f;
+      for (int q = 0; q < kBuBlock; ++q) {
+        const int t = tb + blk + q;
+        bu[q] = (act && t < te) ? a.Bu[(gbase + t) * N + j] : 0.f;
+      }
     }
-    for (int t0 = 0; t0 < S; t0 += PF) {
 #pragma unroll
-      for (int q = 0; q < PF; ++q) {
-        const int tt = t0 + PF + q, t = tb + tt;
-        nxt[q] = (act && tt < S && t < Tc) ? a.Bu[bub + (size_t)t * N] : 0.f;
+    for (int q4 = 0; q4 < kBuBlock; q4 += 4) {
+      const int t0 = tb + blk + q4;
+      if (blk + q4 >= S) break;               // uniform across the workgroup
+      const bool gv0 = t0 < te;               // uniform within the group
+      // state-independent inputs of the next four steps
+      i4v k4 = {0, 0, 0, 0};
+      f4v d4 = {0.f, 0.f, 0.f, 0.f};
+      if (gv0) {
+        k4 = *(const i4v*)(kbuf + t0);
+        if (act) d4 = *(const f4v*)(Dbuf + j * TS + t0);
       }
+      int id4[4];
 #pragma unroll
-      for (int q = 0; q < PF; ++q) {
-        const int tt = t0 + q, t = tb + tt;
-        const bool gv = tt < S && t < Tc;          // uniform within the group
+      for (int r = 0; r < 4; ++r) id4[r] = (act && t0 + r < te) ? DC[k4[r] * N + j].x : 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + r;
+        const bool gv = t < te;
         const bool v = act && gv;
-        const int k = gv ? kbuf[t] : 0;
-        const int idx = v ? dic[k * N + j] : 0;
-        const float dj = v ? Dbuf[t * N + j] : 0.f;
-        if (v) slot[j] = cur[q];
-        WAVE_SYNC();
-        if (v) atomicAdd(&slot[idx], dj * hl);
-        WAVE_SYNC();
-        if (v) hl = slot[j];
-        float yl = v ? cj * hl : 0.f;
-        for (int off = NP >> 1; off > 0; off >>= 1) yl += __shfl_xor(yl, off, NP);
-        if (gv && j == 0) yloc[t] = yl;
+        // the running map's next factor, gathered at its current rows
+        i2v e = {0, 0};
+        float dm = 0.f;
         if (v) {
-          const int nidx = dic[k * N + midx];
-          msc *= Dbuf[t * N + midx];
-          midx = nidx;
+          e = DC[k4[r] * N + midx];
+          dm = Dbuf[midx * TS + t];
         }
-        WAVE_SYNC();
-        if (v) Dbuf[t * N + j] = Cs[midx] * msc;   // w_t = C Phi_t (row t no longer read)
+        // h' = Bu + scatter(D h): one wave, so its LDS operations stay in order
+        if (v) slot[j] = bu[q4 + r];
+        if (v) atomicAdd(&slot[id4[r]], d4[r] * hl);
+        if (v) hl = slot[j];
+        // compose, and record w_t = C Phi_t over column t (every lane of the
+        // group has read column t above)
+        if (v) {
+          msc *= dm;
+          midx = e.x;
+          Dbuf[j * TS + t] = __int_as_float(e.y) * msc;
+        }
+        // local output C h'
+        const float yl = group_sum(v ? cj * hl : 0.f, NP);
+        if (gv && j == 0) yloc[t] = yl;
       }
-#pragma unroll
-      for (int q = 0; q < PF; ++q) cur[q] = nxt[q];
     }
   }
   if (act) {
@@ -331,46 +536,45 @@ __global__ __launch_bounds__(kThreads) void pdssm_kernel(Args a) {
   __syncthreads();
 
   // ---- combine the sub-chunk summaries in order (wave 0)
-  uint32_t aggI = 0;
-  float aggS = 1.f, aggB = 0.f;
   if (wave == 0) {
     const bool on = lane < N;
     int ai = lane;
     float as = 1.f, ab = 0.f;
     for (int gm = 0; gm < p.G; ++gm) {
+      int gi = 0;
+      float gs = 0.f, gb = 0.f;
       if (on) {
         pIdx[gm * N + lane] = ai;
         pSc[gm * N + lane] = as;
         pB[gm * N + lane] = ab;
+        gi = sIdx[gm * N + lane];
+        gs = sSc[gm * N + lane];
+        gb = sB[gm * N + lane];
       }
       const int ni = on ? sIdx[gm * N + ai] : 0;
       const float ns = on ? sSc[gm * N + ai] * as : 0.f;
-      if (on) tmp[lane] = sB[gm * N + lane];
+      if (on) tmp[lane] = gb;
       WAVE_SYNC();
-      if (on) atomicAdd(&tmp[sIdx[gm * N + lane]], sSc[gm * N + lane] * ab);
+      if (on) atomicAdd(&tmp[gi], gs * ab);
       WAVE_SYNC();
       if (on) ab = tmp[lane];
       WAVE_SYNC();
       ai = ni;
       as = ns;
     }
-    aggI = (uint32_t)ai;
-    aggS = as;
-    aggB = ab;
 
     // ---- publish this chunk's aggregate
     uint64_t* my = agg + ((size_t)c * BH + s) * 3 * N;
     if (on) {
-      put_tagged(my + lane, aggI);
-      put_tagged(my + N + lane, __float_as_uint(aggS));
-      put_tagged(my + 2 * N + lane, __float_as_uint(aggB));
+      put_tagged(my + lane, (uint32_t)ai);
+      put_tagged(my + N + lane, __float_as_uint(as));
+      put_tagged(my + 2 * N + lane, __float_as_uint(ab));
     }
 
     // ---- look back for the carry into this chunk
     float x = (on && a.h0) ? a.h0[(size_t)s * N + lane] : 0.f;
-    int start = 0;                         // first chunk whose aggregate must be applied
     if (c > 0) {
-      int q = c - 1, spins = 0;
+      int q = c - 1, spins = 0, start = 0;
       while (true) {
         const uint64_t wi = on ? get_tagged(inc + ((size_t)q * BH + s) * N + lane) : kTagValid;
         if (__all(tag_ok(wi))) {
@@ -383,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void pdssm_kernel(Args a) {
         if (on) okq = tag_ok(get_tagged(pa + lane)) && tag_ok(get_tagged(pa + N + lane)) &&
                       tag_ok(get_tagged(pa + 2 * N + lane));
         if (__all(okq)) {
-          if (q == 0) { start = 0; break; }  // x already holds h0
+          if (q == 0) { start = 0; break; }  // x holds h0
           --q;
           continue;
         }
@@ -411,11 +615,11 @@ __global__ __launch_bounds__(kThreads) void pdssm_kernel(Args a) {
       }
     }
     // inclusive state of this chunk, with the same arithmetic
-    if (on) tmp[lane] = aggB;
+    if (on) tmp[lane] = ab;
     WAVE_SYNC();
-    if (on) atomicAdd(&tmp[aggI], aggS * x);
+    if (on) atomicAdd(&tmp[ai], as * x);
     WAVE_SYNC();
-    float xo = on ? tmp[lane] : 0.f;
+    const float xo = on ? tmp[lane] : 0.f;
     WAVE_SYNC();
     if (on) {
       put_tagged(inc + ((size_t)c * BH + s) * N + lane, __float_as_uint(xo));
@@ -435,12 +639,26 @@ __global__ __launch_bounds__(kThreads) void pdssm_kernel(Args a) {
     __syncthreads();
   }
   for (int t = tid; t < Tc; t += kThreads) {
-    const float* w = Dbuf + t * N;
     const float* cr = slots + (t / S) * NP;
     float acc = yloc[t];
-    for (int n = 0; n < N; ++n) acc += w[n] * cr[n];
-    a.y[(size_t)s * p.L + c0 + t] = acc;
+    for (int n = 0; n < N; ++n) acc += Dbuf[n * TS + t] * cr[n];
+    a.y[gbase + t] = acc;
   }
+}
+
+// Two entry points over one body: the register-resident fp32 selection paths
+// fit three waves per SIMD; the other paths get the larger register budget
+// of two waves per SIMD.
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH>
+__global__ __launch_bounds__(kThreads, 3) void pdssm_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH>(a, smem);
+}
+
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH>
+__global__ __launch_bounds__(kThreads, 2) void pdssm_kernel_wide(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH>(a, smem);
 }
 
 // Zero the workspace words the scan reads (header, aggregates, inclusive states).
@@ -453,21 +671,55 @@ __global__ void clear_kernel(uint64_t* w, size_t n) {
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+static int sel_path(const Plan& p) {
+  const int nct = p.NC >> 4;
+  if (!p.in_bf16 && p.d == 64 && nct == 2) return kSelF32D64N2;
+  if (!p.in_bf16 && p.d == 16 && nct == 1) return kSelF32D16N1;
+  if (p.in_bf16 && p.mma_bf16 && p.d == 128 && nct == 3) return kSelBF16D128N3;
+  return kSelAny;
+}
+
+template <int MODE, int IN_BF16, int MMA_BF16>
+static void launch_path(const Args& a, int path, dim3 grid, hipStream_t st) {
+  const dim3 block(kThreads);
+  const int lds = a.p.lds_bytes;
+  switch (path) {
+    case kSelF32D64N2:
+      hipLaunchKernelGGL((pdssm_kernel<MODE, IN_BF16, MMA_BF16, kSelF32D64N2>), grid, block, lds, st, a);
+      break;
+    case kSelF32D16N1:
+      hipLaunchKernelGGL((pdssm_kernel<MODE, IN_BF16, MMA_BF16, kSelF32D16N1>), grid, block, lds, st, a);
+      break;
+    case kSelBF16D128N3:
+      hipLaunchKernelGGL((pdssm_kernel_wide<MODE, IN_BF16, MMA_BF16, kSelBF16D128N3>), grid, block, lds, st, a);
+      break;
+    default:
+      if (MODE == kModeScan)
+        hipLaunchKernelGGL((pdssm_kernel<MODE, IN_BF16, MMA_BF16, kSelAny>), grid, block, lds, st, a);
+      else
+        hipLaunchKernelGGL((pdssm_kernel_wide<MODE, IN_BF16, MMA_BF16, kSelAny>), grid, block, lds, st, a);
+  }
+}
+
 template <int MODE>
 static hipError_t launch_mode(const Args& a, hipStream_t st) {
   const Plan& p = a.p;
-  dim3 grid(p.tasks), block(kThreads);
+  const dim3 grid(p.tasks);
   if (MODE != kModeSelect) {
     const size_t words = p.ws_bytes / 8;
-    const int cb = (int)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096);
-    hipLaunchKernelGGL(clear_kernel, dim3(cb > 0 ? cb : 1), dim3(256), 0, st, (uint64_t*)a.ws, words);
+    size_t cb = (words + 255) / 256;
+    if (cb > 4096) cb = 4096;
+    if (cb < 1) cb = 1;
+    hipLaunchKernelGGL(clear_kernel, dim3((unsigned)cb), dim3(256), 0, st, (uint64_t*)a.ws, words);
   }
-  if (p.in_bf16 && p.mma_bf16)
-    hipLaunchKernelGGL((pdssm_kernel<MODE, 1, 1>), grid, block, p.lds_bytes, st, a);
-  else if (p.in_bf16)
-    hipLaunchKernelGGL((pdssm_kernel<MODE, 1, 0>), grid, block, p.lds_bytes, st, a);
-  else
-    hipLaunchKernelGGL((pdssm_kernel<MODE, 0, 0>), grid, block, p.lds_bytes, st, a);
+  if constexpr (MODE == kModeScan) {
+    launch_path<MODE, 0, 0>(a, kSelAny, grid, st);   // no selection in this mode
+  } else {
+    const int path = sel_path(p);
+    if (p.in_bf16 && p.mma_bf16) launch_path<MODE, 1, 1>(a, path, grid, st);
+    else if (p.in_bf16) launch_path<MODE, 1, 0>(a, path, grid, st);
+    else launch_path<MODE, 0, 0>(a, path, grid, st);
+  }
   return hipGetLastError();
 }
 

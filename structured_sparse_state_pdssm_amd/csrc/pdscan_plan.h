@@ -27,15 +27,16 @@ struct Plan {
   // work split
   int NP;    // lanes per group
   int G;     // groups per workgroup
-  int S;     // steps per group
+  int S;     // steps per group (a multiple of 4)
+  int TS;    // row stride of the on-chip [N][TS] diagonal / output-weight buffer
   int nC;    // chunks per sequence
   int NC;    // GEMM columns (K scores then N pre-activations), padded to 16
   int KP;    // score staging width
   int mma_bf16;  // score GEMM on bf16 MFMA (else fp32 MFMA)
   int tasks;     // workgroups
   // LDS byte offsets
-  int off_D, off_k, off_yl, off_dict, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
-      off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_stage, off_misc, lds_bytes;
+  int off_D, off_k, off_yl, off_dict, off_DC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
+      off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_misc, lds_bytes;
   // workspace byte offsets (scan / fused)
   size_t ws_agg, ws_inc, ws_bytes;
 };
@@ -58,10 +59,14 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.chunk = (mode == kModeSelect) ? kSelectRows : (chunk < L ? chunk : L);
   p.NP = next_pow2(N);
   p.G = kThreads / p.NP;
-  p.S = (p.chunk + p.G - 1) / p.G;
+  p.S = align_up((p.chunk + p.G - 1) / p.G, 4);
+  // t-contiguous rows; a stride of 4 (mod 32) words spreads the rows of one
+  // column over distinct LDS banks while keeping 16-byte alignment
+  p.TS = align_up(p.chunk, 4);
+  if (p.TS % 32 != 4) p.TS += (36 - p.TS % 32) % 32;
   p.nC = (L + p.chunk - 1) / p.chunk;
   p.NC = align_up(K + N, 16);
-  p.KP = align_up(K, 4) + 1;            // +1 word breaks power-of-two row strides
+  p.KP = align_up(K, 4);
   p.mma_bf16 = (in_bf16 && d >= 128) ? 1 : 0;
   p.tasks = p.nC * B * H;
 
@@ -69,10 +74,11 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   int off = 0;
   auto take = [&](int bytes) { int o = off; off = align_up(off + bytes, 16); return o; };
   const bool scan = mode != kModeSelect;
-  p.off_D = scan ? take(T * N * 4) : 0;
-  p.off_k = scan ? take(T * 4) : 0;
+  p.off_D = scan ? take(N * p.TS * 4) : 0;
+  p.off_k = scan ? take(align_up(T, 4) * 4) : 0;
   p.off_yl = scan ? take(T * 4) : 0;
-  p.off_dict = take(K * N * 4);
+  p.off_dict = scan ? 0 : take(K * N * 4);   // selection: P_idx gathers
+  p.off_DC = scan ? take(K * N * 8) : 0;      // scan: (row, C[row]) pairs
   p.off_C = take(N * 4);
   p.off_bd = take(N * 4);
   p.off_slot = take(kThreads * 4);
@@ -84,7 +90,6 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.off_pB = scan ? take(p.G * N * 4) : 0;
   p.off_H = take(64 * 4);
   p.off_tmp = take(64 * 4);
-  p.off_stage = (mode != kModeScan) ? take(kWaves * 16 * p.KP * 4) : 0;
   p.off_misc = take(16);
   p.lds_bytes = off;
 
