@@ -25,16 +25,18 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (matrix / packed vector)
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 METRIC = "state-updates/sec (B·H·L·N) PD-SSM fwd select+scan; achieved HBM GB/s vs peak"
-KERNEL_SOURCES = ("structured_sparse_state_pdssm_amd/csrc/pdscan_kernels.hip",
-                  "structured_sparse_state_pdssm_amd/csrc/pdscan_plan.h",
-                  "structured_sparse_state_pdssm_amd/csrc/pdscan_api.cpp")
+CSRC = os.path.join(ROOT, "structured_sparse_state_pdssm_amd", "csrc")
 
 
 def kernel_hash() -> str:
+    """Hash of the library sources: ties a stored counter summary to the
+    kernel it was measured on."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -15,16 +15,18 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpdscan.so")
 
-SOURCES = ["pdscan_api.cpp", "pdscan_kernels.hip"]
-HEADERS = ["pdscan_plan.h"]
+SOURCES = ["pdscan_api.cpp", "pdscan_launch_select.hip", "pdscan_launch_scan.hip",
+           "pdscan_launch_fused.hip"]
+HEADERS = ["pdscan_plan.h", "pdscan_device.h"]
 
-FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared",
+COMPILE_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC",
     "--offload-arch=gfx950",
     # packed fp32 VALU forms stay disabled in all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+LINK_FLAGS = ["-shared", "-fPIC", "--offload-arch=gfx950"]
 
 
 def hipcc() -> str:
@@ -34,24 +36,46 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpdscan)")
 
 
+def _run(cmd, cwd):
+    r = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
+    msgs = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops" not in ln)   # the host pass does not know it
+    return r.returncode, msgs
+
+
 def build(verbose: bool = False, save_temps: str | None = None) -> str:
-    """Compile every source into libpdscan.so (always recompiles)."""
-    out_tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", out_tmp]
-    if save_temps:
-        os.makedirs(save_temps, exist_ok=True)
-        cmd.insert(1, f"-save-temps={'obj'}")
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, cwd=save_temps or CSRC, capture_output=True, text=True)
-    msgs = "\n".join(
-        ln for ln in (r.stdout + r.stderr).splitlines()
-        if "packed-fp32-ops" not in ln)          # the host pass does not know the feature
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
-    if verbose and msgs.strip():
-        print(msgs, flush=True)
+    """Compile every source (in parallel, one process per translation unit)
+    and link libpdscan.so.  Always recompiles."""
+    import concurrent.futures as cf
+    import tempfile
+
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="pdscan_build_") as tmp:
+        objs, cmds = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            cmd = [cc, *COMPILE_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+                   os.path.join(CSRC, src), "-o", obj]
+            if save_temps:
+                cmd.insert(1, "-save-temps=obj")
+            objs.append(obj)
+            cmds.append(cmd)
+        cwd = save_temps or tmp
+        if save_temps:
+            os.makedirs(save_temps, exist_ok=True)
+        with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+            results = list(ex.map(lambda c: _run(c, cwd), cmds))
+        for cmd, (rc, msgs) in zip(cmds, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed ({rc}):\n{msgs}")
+            if verbose and msgs.strip():
+                print(msgs, flush=True)
+        out_tmp = LIB + ".tmp"
+        rc, msgs = _run([cc, *LINK_FLAGS, *objs, "-o", out_tmp], tmp)
+        if rc != 0:
+            raise RuntimeError(f"link failed ({rc}):\n{msgs}")
     os.replace(out_tmp, LIB)
     return LIB
 

@@ -13,7 +13,11 @@
 #include "pdscan_plan.h"
 
 namespace pdscan {
-hipError_t launch(int mode, const Args& a, hipStream_t st);
+// One launcher per mode, each in its own translation unit.  They enqueue on
+// `st` and return the launch status; scan and fused clear the workspace first.
+hipError_t launch_select(const Args& a, hipStream_t st);
+hipError_t launch_scan(const Args& a, hipStream_t st);
+hipError_t launch_fused(const Args& a, hipStream_t st);
 }
 
 using pdscan::Plan;
@@ -128,7 +132,10 @@ int check_ptrs(const Range* in, int nin, const Range* out, int nout, const char*
 }
 
 int dispatch(int mode, const pdscan::Args& a, void* stream) {
-  const hipError_t e = pdscan::launch(mode, a, (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = mode == pdscan::kModeSelect ? pdscan::launch_select(a, st)
+                       : mode == pdscan::kModeScan ? pdscan::launch_scan(a, st)
+                                                   : pdscan::launch_fused(a, st);
   if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_err[0] = 0;
   return PDSSM_OK;

@@ -1,0 +1,998 @@
+// Device code for gfx950 (CDNA4): selection, chunked scan, and the fused pass.
+// Included by the three launcher translation units (one per mode), which are
+// compiled in parallel.
+//
+// One kernel template serves three modes (pdscan_plan.h):
+//   select : score GEMM + argmax + logistic, results to global memory
+//   scan   : selections read from global memory, then phases A, B, C
+//   fused  : score GEMM feeding phases A, B, C on chip (the hot path)
+//
+// Sources: "Flash PD-SSM: Memory-Optimized Structured Sparse State-Space
+// Models" (gist.science explainer), technical summary, methodology item 1
+// (hard selection by argmax over K linear scores; the selected matrix is a
+// one-hot column selector) and item 3 (phase A: sequential recurrences inside
+// chunks; phase B: prefix scan of chunk summaries into carry states; phase C:
+// carry correction).  A map (idx, scale) stands for the matrix with
+// scale[j] in row idx[j] of column j; applying it is a scatter-add, and two
+// maps compose by an index gather and a scale product.
+//
+// On-chip layout of one chunk (T steps): D and then w live in one [N][TS]
+// buffer (t contiguous), so the selection epilogue stores four steps of one
+// column with one 16-byte write, phase A reads four steps per lane at once,
+// and phase C reads consecutive steps on consecutive lanes.
+//
+// Phase B is a single-pass decoupled look-back: workgroups take chunk tickets
+// in (chunk, sequence) order, publish their chunk aggregate, then walk back
+// over predecessors until an inclusive state is found.  Every word published
+// to other workgroups is a 64-bit (tag, payload) pair written and read with
+// device-scope atomics, so no fences are needed and a reader never sees half
+// a record.  Inclusive states are always produced by applying aggregates to a
+// state vector in chunk order with the same arithmetic, so the result does
+// not depend on how far a look-back had to walk.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pdscan_plan.h"
+
+namespace pdscan {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+typedef int i4v __attribute__((ext_vector_type(4)));
+typedef int i2v __attribute__((ext_vector_type(2)));
+
+constexpr uint64_t kTagValid = 1ull << 32;
+constexpr int kSpinLimit = 1 << 22;
+constexpr int kBuBlock = 16;   // phase-A steps whose drive terms sit in registers
+
+// Compiler-level ordering point between LDS accesses of different lanes of
+// one wave.  The hardware executes one wave's LDS instructions in order.
+#define WAVE_SYNC()                          \
+  do {                                       \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST); \
+    __builtin_amdgcn_wave_barrier();         \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST); \
+  } while (0)
+
+__device__ __forceinline__ float logistic(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+__device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t payload) {
+  __hip_atomic_store(p, kTagValid | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t get_tagged(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool tag_ok(uint64_t w) { return (w >> 32) == 1u; }
+
+// Raw buffer loads through a per-workgroup resource: a scalar base, 32-bit
+// lane offsets, and reads past the end return zero without touching memory
+// (kNoLoad is such an offset).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;     // 32-bit data format, raw access
+constexpr uint32_t kNoLoad = 0xFFFFFFF0u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ float buf_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// DPP lane permutations inside 16-lane rows.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within each 16 lanes
+
+// Every pattern here reads a valid lane; bound_ctrl with a zero "old" lets
+// the compiler fold the move into the consuming VALU instruction.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+
+// Order-preserving integer key of a finite float (-0 folded onto +0, so
+// equal scores give equal keys).
+__device__ __forceinline__ int order_key(float v) {
+  const int b = __float_as_int(v + 0.0f);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+
+// Max / min over the 16 lanes of a DPP row; every lane gets the result.
+__device__ __forceinline__ int row_max(int v) {
+  v = max(v, dpp_i<kDppXor1>(v));
+  v = max(v, dpp_i<kDppXor2>(v));
+  v = max(v, dpp_i<kDppHalfMirror>(v));
+  return max(v, dpp_i<kDppMirror>(v));
+}
+__device__ __forceinline__ int row_min(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppHalfMirror>(v));
+  return min(v, dpp_i<kDppMirror>(v));
+}
+
+// Sum over a lane group of NP lanes (a power of two); every lane of the group
+// gets the same value (the partial sums meet in the same order on every lane).
+template <int NP>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (NP >= 2) v += dpp_f<kDppXor1>(v);
+  if constexpr (NP >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (NP >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (NP >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (NP >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (NP >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ float group_sum_rt(float v, int NP) {
+  switch (NP) {
+    case 1: return v;
+    case 2: return group_sum<2>(v);
+    case 4: return group_sum<4>(v);
+    case 8: return group_sum<8>(v);
+    case 16: return group_sum<16>(v);
+    case 32: return group_sum<32>(v);
+    default: return group_sum<64>(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection of one wave's rows.
+//
+// MFMA tiles of 16 rows: lane (i = lane%16, g = lane/16) feeds A = u[row0+i][c]
+// and B = W[col][c]; fp32 (v_mfma_f32_16x16x4_f32) takes channel m + 4g + q at
+// step q of channel block m, bf16 (v_mfma_f32_16x16x32_bf16) channels
+// m + 8g .. +7.  Both operands use the same channel order, so each output is
+// the full contraction.  acc[ct] holds rows row0 + 4g + r, column 16 ct + i
+// of [scores | pre-activations].
+//
+// FAST = true: W lives in registers for the whole wave (KCH channel blocks,
+// NCT column tiles known at compile time) and the next tile's u is loaded
+// while the current one is multiplied.  FAST = false: any shape, operands
+// loaded per tile.
+// ---------------------------------------------------------------------------
+struct SelDst {
+  int* kbuf;      // chunk-local k* (fused) or nullptr
+  float* Dbuf;    // [N][TS] (fused) or nullptr
+  int TS;
+  int32_t* k_out; // global, optional
+  float* D_out;   // global, optional
+  int32_t* P_out; // global, optional
+  const int* dic; // LDS dictionary [K][N] (for P_out)
+  size_t gbase;   // global row index of chunk row 0 = s*L + c0
+};
+
+template <int IN_BF16, int MMA_BF16>
+struct Frag;
+template <>
+struct Frag<0, 0> { typedef f4v T; };
+template <>
+struct Frag<1, 0> { typedef u2v T; };
+template <>
+struct Frag<1, 1> { typedef u4v T; };
+
+template <int IN_BF16, int MMA_BF16>
+__device__ __forceinline__ typename Frag<IN_BF16, MMA_BF16>::T load_frag(const void* base, size_t off,
+                                                                         bool ok) {
+  typedef typename Frag<IN_BF16, MMA_BF16>::T T;
+  T z = {};
+  if (!ok) return z;
+  if constexpr (!IN_BF16) return *(const T*)((const float*)base + off);
+  else return *(const T*)((const uint16_t*)base + off);
+}
+
+template <int IN_BF16, int MMA_BF16>
+__device__ __forceinline__ typename Frag<IN_BF16, MMA_BF16>::T load_frag_buf(rsrc_t r, uint32_t off) {
+  typedef typename Frag<IN_BF16, MMA_BF16>::T T;
+  if constexpr (IN_BF16 && !MMA_BF16)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int IN_BF16, int MMA_BF16>
+__device__ __forceinline__ void mma_step(f4v& acc, typename Frag<IN_BF16, MMA_BF16>::T a,
+                                         typename Frag<IN_BF16, MMA_BF16>::T b) {
+  if constexpr (MMA_BF16) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a),
+                                                  __builtin_bit_cast(bf8v, b), acc, 0, 0, 0);
+  } else if constexpr (IN_BF16) {
+    const float a0 = __uint_as_float(a.x << 16), a1 = __uint_as_float(a.x & 0xffff0000u);
+    const float a2 = __uint_as_float(a.y << 16), a3 = __uint_as_float(a.y & 0xffff0000u);
+    const float b0 = __uint_as_float(b.x << 16), b1 = __uint_as_float(b.x & 0xffff0000u);
+    const float b2 = __uint_as_float(b.y << 16), b3 = __uint_as_float(b.y & 0xffff0000u);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, b2, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, b3, acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+  }
+}
+
+// channels per fragment block: 16 (fp32 MFMA, 4 per lane group) or 32 (bf16)
+template <int MMA_BF16>
+constexpr int kChanBlock = MMA_BF16 ? 32 : 16;
+
+// Epilogue of one tile: argmax over score columns, logistic of the
+// pre-activations, stores.  rows >= rlim are not stored.
+template <int NCT>
+__device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, const float* bdr,
+                                              int row0, int rlim, int lane, const SelDst& o) {
+  const int i = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N;
+  // argmax per row: the largest score over the row's lanes, then the lowest
+  // column holding it (lowest index wins ties)
+  int bv[4];
+  int bk[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    bv[r] = (int)0x80000000;
+    bk[r] = 0x7fffffff;
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ct + i;
+    if (16 * ct < K) {                     // uniform: tile holds score columns
+      const bool sc = col < K;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = sc ? order_key(acc[ct][r]) : (int)0x80000000;
+        const bool gt = v > bv[r];         // columns rise with ct: keep the first
+        bv[r] = gt ? v : bv[r];
+        bk[r] = gt ? col : bk[r];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = row_max(bv[r]);
+    bk[r] = row_min(bv[r] == m ? bk[r] : 0x7fffffff);
+  }
+  const int rb = row0 + 4 * g;   // first of this lane's four rows
+  const bool full = rb + 4 <= rlim;
+  if (i == 0) {
+    if (o.kbuf) {
+      if (full) *(i4v*)(o.kbuf + rb) = i4v{bk[0], bk[1], bk[2], bk[3]};
+      else
+        for (int r = 0; r < 4; ++r) if (rb + r < rlim) o.kbuf[rb + r] = bk[r];
+    }
+    if (o.k_out)
+      for (int r = 0; r < 4; ++r) if (rb + r < rlim) o.k_out[o.gbase + rb + r] = bk[r];
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ct + i;
+    if (col >= K && col < K + N) {
+      const int n = col - K;
+      f4v dv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dv[r] = logistic(acc[ct][r] + bdr[ct]);
+      if (o.Dbuf) {
+        float* dst = o.Dbuf + n * o.TS + rb;
+        if (full) *(f4v*)dst = dv;
+        else
+          for (int r = 0; r < 4; ++r) if (rb + r < rlim) dst[r] = dv[r];
+      }
+      if (o.D_out)
+        for (int r = 0; r < 4; ++r)
+          if (rb + r < rlim) o.D_out[(o.gbase + rb + r) * N + n] = dv[r];
+    }
+  }
+  if (o.P_out) {
+    for (int r = 0; r < 4; ++r)
+      for (int gg = 0; gg < 4; ++gg) {
+        const int kr = __shfl(bk[r], 16 * gg, 64);
+        const int row = row0 + 4 * gg + r;
+        if (row < rlim)
+          for (int n = lane; n < N; n += 64) o.P_out[(o.gbase + row) * N + n] = o.dic[kr * N + n];
+      }
+  }
+}
+
+template <int IN_BF16, int MMA_BF16, int KCH, int NCT>
+__device__ __forceinline__ void select_rows(const Args& a, int s_u, int h, int c0, int rbeg,
+                                            int rend, int lane, const SelDst& o) {
+  typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
+  constexpr int CB = kChanBlock<MMA_BF16>;
+  constexpr int PER = MMA_BF16 ? 8 : 4;           // channels per lane per block
+  const Plan& p = a.p;
+  const int i = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N, d = p.d;
+
+  // W fragments and logistic biases, in registers for the whole wave
+  FT wf[NCT][KCH];
+  float bdr[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ct + i;
+    const bool sc = col < K, zc = col >= K && col < K + N;
+    const void* wb = sc ? a.W_sel : a.W_d;
+    const size_t wrow = sc ? ((size_t)h * K + col) * d : ((size_t)h * N + (col - K)) * d;
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) {
+      const int ch = m * CB + PER * g;
+      wf[ct][m] = load_frag<IN_BF16, MMA_BF16>(wb, wrow + ch, (sc || zc) && ch < d);
+    }
+    bdr[ct] = zc ? a.b_d[(size_t)h * N + col - K] : 0.f;
+  }
+
+  // this chunk's rows of u through one buffer resource (rows past the
+  // chunk read as zero)
+  constexpr int ES = IN_BF16 ? 2 : 4;
+  const int Tc = min(p.chunk, p.L - c0);
+  const rsrc_t ur = make_rsrc((const unsigned char*)a.u + ((size_t)s_u * p.L + c0) * d * ES,
+                              (uint32_t)(Tc * d * ES));
+  // one tile in flight while the previous one is multiplied
+  FT r0[KCH], r1[KCH];
+  auto load_tile = [&](FT* dst, int row0) {
+    const int row = row0 + i;
+    const uint32_t rb = row < rend ? (uint32_t)(row * d + PER * g) * ES : kNoLoad;
+#pragma unroll
+    for (int m = 0; m < KCH; ++m)
+      dst[m] = load_frag_buf<IN_BF16, MMA_BF16>(ur, rb == kNoLoad ? kNoLoad : rb + m * CB * ES);
+  };
+  auto do_tile = [&](const FT* src, int row0) {
+    f4v acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < KCH; ++m)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) mma_step<IN_BF16, MMA_BF16>(acc[ct], src[m], wf[ct][m]);
+    tile_epilogue<NCT>(p, acc, bdr, row0, rend, lane, o);
+  };
+  load_tile(r0, rbeg);
+  for (int row0 = rbeg; row0 < rend; row0 += 32) {
+    load_tile(r1, row0 + 16);
+    do_tile(r0, row0);
+    load_tile(r0, row0 + 32);
+    if (row0 + 16 < rend) do_tile(r1, row0 + 16);
+  }
+}
+
+// Any shape: operands loaded per 16-row tile, up to 8 column tiles.
+template <int IN_BF16, int MMA_BF16>
+__device__ __forceinline__ void select_rows_any(const Args& a, int s_u, int h, int c0, int rbeg,
+                                                int rend, int lane, const SelDst& o) {
+  typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
+  constexpr int CB = kChanBlock<MMA_BF16>;
+  constexpr int PER = MMA_BF16 ? 8 : 4;
+  const Plan& p = a.p;
+  const int i = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N, d = p.d;
+  const int NCT = p.NC >> 4;
+  float bdr[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const int col = 16 * ct + i;
+    bdr[ct] = (ct < NCT && col >= K && col < K + N) ? a.b_d[(size_t)h * N + col - K] : 0.f;
+  }
+  const size_t ubase = ((size_t)s_u * p.L + c0) * d;
+  for (int row0 = rbeg; row0 < rend; row0 += 16) {
+    const int row = row0 + i;
+    f4v acc[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[ct] = f4v{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m * CB < d; ++m) {
+      const int ch = m * CB + PER * g;
+      const FT av = load_frag<IN_BF16, MMA_BF16>(a.u, ubase + (size_t)row * d + ch,
+                                                 row < rend && ch < d);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        if (ct < NCT) {
+          const int col = 16 * ct + i;
+          const bool sc = col < K, zc = col >= K && col < K + N;
+          const void* wb = sc ? a.W_sel : a.W_d;
+          const size_t wrow = sc ? ((size_t)h * K + col) * d : ((size_t)h * N + (col - K)) * d;
+          const FT bw = load_frag<IN_BF16, MMA_BF16>(wb, wrow + ch, (sc || zc) && ch < d);
+          mma_step<IN_BF16, MMA_BF16>(acc[ct], av, bw);
+        }
+      }
+    }
+    switch (NCT) {
+      case 1: tile_epilogue<1>(p, acc, bdr, row0, rend, lane, o); break;
+      case 2: tile_epilogue<2>(p, acc, bdr, row0, rend, lane, o); break;
+      case 3: tile_epilogue<3>(p, acc, bdr, row0, rend, lane, o); break;
+      case 4: tile_epilogue<4>(p, acc, bdr, row0, rend, lane, o); break;
+      case 5: tile_epilogue<5>(p, acc, bdr, row0, rend, lane, o); break;
+      case 6: tile_epilogue<6>(p, acc, bdr, row0, rend, lane, o); break;
+      case 7: tile_epilogue<7>(p, acc, bdr, row0, rend, lane, o); break;
+      default: tile_epilogue<8>(p, acc, bdr, row0, rend, lane, o); break;
+    }
+  }
+}
+
+// Shapes with a register-resident fast path.
+enum SelPath : int { kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3 };
+
+template <int IN_BF16, int MMA_BF16, int PATH>
+__device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, int c0, int rbeg,
+                                                int rend, int lane, const SelDst& o) {
+  if constexpr (PATH == kSelF32D64N2 && !IN_BF16 && !MMA_BF16)
+    select_rows<0, 0, 4, 2>(a, s_u, h, c0, rbeg, rend, lane, o);
+  else if constexpr (PATH == kSelF32D16N1 && !IN_BF16 && !MMA_BF16)
+    select_rows<0, 0, 1, 1>(a, s_u, h, c0, rbeg, rend, lane, o);
+  else if constexpr (PATH == kSelBF16D128N3 && IN_BF16 && MMA_BF16)
+    select_rows<1, 1, 4, 3>(a, s_u, h, c0, rbeg, rend, lane, o);
+  else
+    select_rows_any<IN_BF16, MMA_BF16>(a, s_u, h, c0, rbeg, rend, lane, o);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Everything after phase A, shared by the scan bodies: combine the sub-chunk
+// summaries, phase B (publish, look back, publish), phase C.  Each lane
+// brings the summary (midx, msc, hl) of its group's sub-chunk; w_t is in the
+// [N][TS] buffer and the local outputs in yloc.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, int c, int s, int Tc,
+                                           size_t gbase, int NP, int gam, int j, bool act,
+                                           int midx, float msc, float hl) {
+  const Plan& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = p.N, S = p.S, TS = p.TS, G = p.G;
+  const int BH = p.B * p.H;
+  float* Dbuf = (float*)(smem + p.off_D);
+  float* yloc = (float*)(smem + p.off_yl);
+  float* slots = (float*)(smem + p.off_slot);
+  int* sIdx = (int*)(smem + p.off_sIdx);
+  float* sSc = (float*)(smem + p.off_sSc);
+  float* sB = (float*)(smem + p.off_sB);
+  int* pIdx = (int*)(smem + p.off_pIdx);
+  float* pSc = (float*)(smem + p.off_pSc);
+  float* pB = (float*)(smem + p.off_pB);
+  float* Hs = (float*)(smem + p.off_H);
+  float* tmp = (float*)(smem + p.off_tmp);
+  uint32_t* hdr = (uint32_t*)a.ws;
+  uint64_t* agg = (uint64_t*)(a.ws + p.ws_agg);
+  uint64_t* inc = (uint64_t*)(a.ws + p.ws_inc);
+  float* slot = slots + gam * NP;
+
+  // ---- combine the sub-chunk summaries: inclusive prefix over the groups
+  // (Hillis-Steele), each step composing with the summary `o` groups back
+  int ci = midx;
+  float cs = msc, cb = hl;
+  for (int o = 1; o < G; o <<= 1) {
+    if (act) {
+      sIdx[gam * N + j] = ci;
+      sSc[gam * N + j] = cs;
+      sB[gam * N + j] = cb;
+    }
+    __syncthreads();
+    const bool up = act && gam >= o;
+    int ni = 0;
+    float ns = 0.f, pb = 0.f;
+    if (up) {
+      const int q = (gam - o) * N + j;
+      const int pi = sIdx[q];
+      pb = sB[q];
+      ni = sIdx[gam * N + pi];
+      ns = sSc[gam * N + pi] * sSc[q];
+    }
+    if (act) slot[j] = cb;
+    __syncthreads();
+    if (up) atomicAdd(&slot[ci], cs * pb);
+    __syncthreads();
+    if (up) {
+      cb = slot[j];
+      ci = ni;
+      cs = ns;
+    }
+  }
+  if (act) {
+    pIdx[gam * N + j] = ci;
+    pSc[gam * N + j] = cs;
+    pB[gam * N + j] = cb;
+  }
+  __syncthreads();
+
+  // ---- phase B (wave 0): publish the chunk aggregate, look back for the
+  // carry into this chunk, publish the inclusive state
+  if (wave == 0) {
+    const bool on = lane < N;
+    const int lq = (G - 1) * N + (on ? lane : 0);
+    const int ai = pIdx[lq];
+    const float as = pSc[lq], ab = pB[lq];
+    uint64_t* my = agg + ((size_t)c * BH + s) * 3 * N;
+    if (on) {
+      put_tagged(my + lane, (uint32_t)ai);
+      put_tagged(my + N + lane, __float_as_uint(as));
+      put_tagged(my + 2 * N + lane, __float_as_uint(ab));
+    }
+
+    float x = (on && a.h0) ? a.h0[(size_t)s * N + lane] : 0.f;
+    if (c > 0) {
+      // Poll up to 64 predecessors at once (lane l looks at chunk c-1-l) for
+      // the nearest inclusive state with every aggregate after it present.
+      const int win = min(c, 64);
+      int stop = 0, spins = 0;
+      while (true) {
+        const int q = c - 1 - lane;
+        bool iv = false, av = false;
+        if (lane < win) {
+          iv = tag_ok(get_tagged(inc + ((size_t)q * BH + s) * N));
+          av = tag_ok(get_tagged(agg + ((size_t)q * BH + s) * 3 * N));
+        }
+        const uint64_t mi = __ballot(iv), ma = __ballot(av);
+        const int li = mi ? __builtin_ctzll(mi) : 64;
+        const int need = li < win ? li : win;
+        const uint64_t nm = need >= 64 ? ~0ull : ((1ull << need) - 1ull);
+        if ((ma & nm) == nm && (li < win || c <= 64)) {
+          stop = need;
+          break;
+        }
+        if (++spins > kSpinLimit) {
+          if (lane == 0) atomicOr(&hdr[kWsError], 1u);
+          stop = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      // base state: the inclusive state `stop` chunks back, or h0
+      if (stop < c) {
+        uint64_t* pw = inc + ((size_t)(c - 1 - stop) * BH + s) * N;
+        if (on) {
+          uint64_t w = get_tagged(pw + lane);
+          for (int n = 0; !tag_ok(w) && n < kSpinLimit; ++n) w = get_tagged(pw + lane);
+          x = __uint_as_float((uint32_t)w);
+        }
+      }
+      // apply the aggregates after it, oldest first, loading eight at a time
+      for (int r0 = c - stop; r0 < c; r0 += 8) {
+        uint64_t wv[8][3];
+#pragma unroll
+        for (int u8 = 0; u8 < 8; ++u8) {
+          uint64_t* pa = agg + ((size_t)(r0 + u8) * BH + s) * 3 * N;
+#pragma unroll
+          for (int f = 0; f < 3; ++f)
+            wv[u8][f] = (on && r0 + u8 < c) ? get_tagged(pa + f * N + lane) : kTagValid;
+        }
+#pragma unroll
+        for (int u8 = 0; u8 < 8; ++u8) {
+          if (r0 + u8 >= c) break;
+          uint64_t* pa = agg + ((size_t)(r0 + u8) * BH + s) * 3 * N;
+#pragma unroll
+          for (int f = 0; f < 3; ++f)
+            for (int n = 0; on && !tag_ok(wv[u8][f]) && n < kSpinLimit; ++n)
+              wv[u8][f] = get_tagged(pa + f * N + lane);
+          if (on) tmp[lane] = __uint_as_float((uint32_t)wv[u8][2]);
+          WAVE_SYNC();
+          if (on)
+            atomicAdd(&tmp[(int)(uint32_t)wv[u8][0]], __uint_as_float((uint32_t)wv[u8][1]) * x);
+          WAVE_SYNC();
+          if (on) x = tmp[lane];
+          WAVE_SYNC();
+        }
+      }
+    }
+    // inclusive state of this chunk, with the same arithmetic
+    if (on) tmp[lane] = ab;
+    WAVE_SYNC();
+    if (on) atomicAdd(&tmp[ai], as * x);
+    WAVE_SYNC();
+    const float xo = on ? tmp[lane] : 0.f;
+    WAVE_SYNC();
+    if (on) {
+      put_tagged(inc + ((size_t)c * BH + s) * N + lane, __float_as_uint(xo));
+      Hs[lane] = x;
+      if (c == p.nC - 1) a.hL[(size_t)s * N + lane] = xo;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase C: state entering every sub-chunk (apply the inclusive prefix
+  // of the groups before it to the carry), then the corrected outputs
+  {
+    float* srow = slots + gam * NP;
+    if (gam == 0) {
+      if (act) srow[j] = Hs[j];
+    } else if (act) {
+      srow[j] = pB[(gam - 1) * N + j];
+    }
+    __syncthreads();
+    if (gam > 0 && act) atomicAdd(&srow[pIdx[(gam - 1) * N + j]], pSc[(gam - 1) * N + j] * Hs[j]);
+    __syncthreads();
+  }
+  for (int t = tid; t < Tc; t += kThreads) {
+    const float* cr = slots + (t / S) * NP;
+    float acc = yloc[t];
+    for (int n = 0; n < N; ++n) acc += Dbuf[n * TS + t] * cr[n];
+    a.y[gbase + t] = acc;
+  }
+}
+
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT>
+__device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
+  const Plan& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = p.N, K = p.K, S = p.S, T = p.chunk, TS = p.TS, G = p.G;
+  // NPT != 0: compile-time group width equal to N (every lane owns a row)
+  const int NP = NPT ? NPT : p.NP;
+  const int BH = p.B * p.H;
+
+  float* Dbuf = (float*)(smem + p.off_D);
+  int* kbuf = (int*)(smem + p.off_k);
+  float* yloc = (float*)(smem + p.off_yl);
+  int* dic = (int*)(smem + p.off_dict);
+  i2v* DC = (i2v*)(smem + p.off_DC);
+  float* Cs = (float*)(smem + p.off_C);
+  float* slots = (float*)(smem + p.off_slot);
+  int* sIdx = (int*)(smem + p.off_sIdx);
+  float* sSc = (float*)(smem + p.off_sSc);
+  float* sB = (float*)(smem + p.off_sB);
+  int* pIdx = (int*)(smem + p.off_pIdx);
+  float* pSc = (float*)(smem + p.off_pSc);
+  float* pB = (float*)(smem + p.off_pB);
+  float* Hs = (float*)(smem + p.off_H);
+  float* tmp = (float*)(smem + p.off_tmp);
+  int* misc = (int*)(smem + p.off_misc);
+
+  uint32_t* hdr = (uint32_t*)a.ws;
+  uint64_t* agg = (uint64_t*)(a.ws + p.ws_agg);
+  uint64_t* inc = (uint64_t*)(a.ws + p.ws_inc);
+
+  // ---- task: chunk-major tickets so that predecessors always started first
+  int task;
+  if constexpr (MODE == kModeSelect) {
+    task = blockIdx.x;
+  } else {
+    if (tid == 0) misc[0] = (int)atomicAdd(&hdr[kWsTicket], 1u);
+    __syncthreads();
+    task = misc[0];
+  }
+  const int c = task / BH, s = task % BH;
+  const int b = s / p.H, h = s % p.H;
+  const int c0 = c * T;
+  const int Tc = min(T, p.L - c0);
+  const size_t gbase = (size_t)s * p.L + c0;
+
+  const int gpw = 64 / NP;                 // lane groups per wave
+  const int gl = lane / NP, j = lane % NP;
+  const int gam = wave * gpw + gl;         // this lane's group (sub-chunk)
+  const int tb = gam * S, te = min(tb + S, Tc);
+  const int nst = max(te - tb, 0);         // steps of this group
+  const bool act = NPT ? true : (j < N);
+  const int jj = act ? j : 0;              // row index that is safe to look up
+
+  // ---- phase-A drive terms of the first block: issued first, used last
+  // (selection mode never reads Bu; its pointer may be null there)
+  const rsrc_t bur = make_rsrc(MODE == kModeSelect ? (const float*)nullptr : a.Bu + gbase * N,
+                               MODE == kModeSelect ? 0u : (uint32_t)(Tc * N * 4));
+  float bu[kBuBlock];
+  if constexpr (MODE != kModeSelect) {
+#pragma unroll
+    for (int q = 0; q < kBuBlock; ++q)
+      bu[q] = buf_f32(bur, (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad);
+  }
+
+  // ---- per-head constants
+  if constexpr (MODE == kModeSelect) {
+    if (a.P_out)
+      for (int q = tid; q < K * N; q += kThreads) dic[q] = a.dict[(size_t)h * K * N + q];
+  } else {
+    for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
+    __syncthreads();
+    // DC[k][m] = (dict[k][m], C[dict[k][m]]): target row and its output weight
+    for (int q = tid; q < K * N; q += kThreads) {
+      const int r = a.dict[(size_t)h * K * N + q];
+      DC[q] = i2v{r, __float_as_int(Cs[r])};
+    }
+  }
+  if constexpr (MODE == kModeScan) {
+    for (int q = tid; q < Tc; q += kThreads) kbuf[q] = a.k_in[gbase + q];
+    for (int q = tid; q < Tc * N; q += kThreads) {
+      const int t = q / N, n = q - t * N;
+      Dbuf[n * TS + t] = a.D_in[gbase * N + q];
+    }
+  }
+  __syncthreads();
+
+  // ---- selection for this wave's rows
+  if constexpr (MODE != kModeScan) {
+    const int s_u = p.u_shared ? b : s;
+    SelDst o;
+    o.kbuf = (MODE == kModeFused) ? kbuf : nullptr;
+    o.Dbuf = (MODE == kModeFused) ? Dbuf : nullptr;
+    o.TS = TS;
+    o.k_out = a.k_out;
+    o.D_out = a.D_out;
+    o.P_out = a.P_out;
+    o.dic = dic;
+    o.gbase = gbase;
+    const int wr0 = min(wave * gpw * S, Tc), wr1 = min(wr0 + gpw * S, Tc);
+    select_dispatch<IN_BF16, MMA_BF16, PATH>(a, s_u, h, c0, wr0, wr1, lane, o);
+  }
+  if constexpr (MODE == kModeSelect) return;
+  WAVE_SYNC();   // this wave's k* / D rows are read back by its own lane groups
+
+  // ---- phase A: each lane group runs its sub-chunk [tb, te) from a zero
+  // state.  Padding steps (past te) act as the identity map.
+  float* slot = slots + gam * NP;
+  const float cj = act ? Cs[j] : 0.f;
+  float hl = 0.f, msc = 1.f;
+  int midx = jj;
+  for (int blk = 0; blk < nst; blk += kBuBlock) {
+    float bn[kBuBlock];
+#pragma unroll
+    for (int q = 0; q < kBuBlock; ++q) {
+      const int tt = blk + kBuBlock + q;
+      bn[q] = buf_f32(bur, (act && tt < nst) ? (uint32_t)((tb + tt) * N + j) * 4u : kNoLoad);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < kBuBlock; q4 += 4) {
+      const int nb = nst - blk - q4;          // steps left, uniform in the group
+      if (nb <= 0) break;
+      const int t0 = tb + blk + q4;
+      const i4v k4 = *(const i4v*)(kbuf + t0);
+      const f4v d4 = act ? *(const f4v*)(Dbuf + j * TS + t0) : f4v{1.f, 1.f, 1.f, 1.f};
+      int own[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) own[r] = DC[(r < nb ? k4[r] : 0) * N + jj].x;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = r < nb;
+        const int t = t0 + r;
+        const int k = valid ? k4[r] : 0;
+        // next factor of the running map, gathered at its current rows
+        const i2v e = DC[k * N + midx];
+        const float dm = Dbuf[midx * TS + t];
+        // h' = Bu + scatter(D h); one wave, so its LDS operations stay in order
+        slot[j] = valid ? bu[q4 + r] : 0.f;
+        atomicAdd(&slot[(valid && act) ? own[r] : j], (valid ? d4[r] : 1.f) * hl);
+        hl = slot[j];
+        // compose, and record w_t = C Phi_t over column t (all lanes of the
+        // group have read column t above)
+        if (valid) {
+          msc *= dm;
+          midx = e.x;
+        }
+        if (valid && act) Dbuf[j * TS + t] = __int_as_float(e.y) * msc;
+        // local output C h'
+        const float yl = NPT ? group_sum<NPT ? NPT : 1>(cj * hl) : group_sum_rt(cj * hl, NP);
+        if (valid && j == 0) yloc[t] = yl;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kBuBlock; ++q) bu[q] = bn[q];
+  }
+
+  chunk_tail(a, smem, c, s, Tc, gbase, NP, gam, j, act, midx, msc, hl);
+}
+
+// ---------------------------------------------------------------------------
+// Fused pass with step-major tiles (N <= 16, K <= 16, per-head u).
+//
+// A wave holds four lane groups of 16 (group = lane / 16, state row j =
+// lane % 16).  MFMA tile k of a wave takes, as its 16 rows, steps 4k .. 4k+3
+// of each of the wave's four sub-chunks (row i <-> group i / 4, step
+// 4k + i % 4).  The 16x16 output puts rows 4g .. 4g+3 of column i in lane
+// (g, i): with the pre-activation columns first, lane (g, j) receives D_t[j]
+// of its own group's four steps, and a row argmax over the score columns
+// gives every lane of the group its k*_t.  Selections therefore never pass
+// through LDS, and the next tile's MFMAs are issued before the current
+// tile's scan steps so that the two overlap.
+// ---------------------------------------------------------------------------
+template <int IN_BF16, int MMA_BF16, int KCH>
+__device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem) {
+  typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
+  constexpr int CB = kChanBlock<MMA_BF16>;
+  constexpr int PER = MMA_BF16 ? 8 : 4;
+  constexpr int ES = IN_BF16 ? 2 : 4;
+  constexpr int SMAX = 32;                         // steps per group
+  const Plan& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = p.N, K = p.K, S = p.S, T = p.chunk, TS = p.TS, d = p.d;
+  const int BH = p.B * p.H;
+
+  float* Dbuf = (float*)(smem + p.off_D);          // holds w_t
+  float* yloc = (float*)(smem + p.off_yl);
+  i2v* DC = (i2v*)(smem + p.off_DC);
+  float* Cs = (float*)(smem + p.off_C);
+  float* slots = (float*)(smem + p.off_slot);
+  int* misc = (int*)(smem + p.off_misc);
+  uint32_t* hdr = (uint32_t*)a.ws;
+
+  if (tid == 0) misc[0] = (int)atomicAdd(&hdr[kWsTicket], 1u);
+  __syncthreads();
+  const int task = misc[0];
+  const int c = task / BH, s = task % BH;
+  const int h = s % p.H;
+  const int c0 = c * T;
+  const int Tc = min(T, p.L - c0);
+  const size_t gbase = (size_t)s * p.L + c0;
+
+  const int gl = lane >> 4, j = lane & 15;
+  const int gam = wave * 4 + gl;
+  const int tb = gam * S;
+  const int nst = max(min(tb + S, Tc) - tb, 0);
+  const bool act = j < N;
+  const int jj = act ? j : 0;
+
+  // drive terms of this lane's steps, issued first
+  const rsrc_t bur = make_rsrc(a.Bu + gbase * N, (uint32_t)(Tc * N * 4));
+  float bu[SMAX];
+#pragma unroll
+  for (int q = 0; q < SMAX; ++q)
+    bu[q] = buf_f32(bur, (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad);
+
+  // per-head tables
+  for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
+  __syncthreads();
+  for (int q = tid; q < K * N; q += kThreads) {
+    const int r = a.dict[(size_t)h * K * N + q];
+    DC[q] = i2v{r, __float_as_int(Cs[r])};
+  }
+
+  // weight fragments: tile 0 = pre-activation columns, tile 1 = score columns
+  const int i = lane & 15, g = lane >> 4;
+  FT wz[KCH], wsel[KCH];
+  {
+    const size_t zrow = ((size_t)h * N + (i < N ? i : 0)) * d;
+    const size_t srow = ((size_t)h * K + (i < K ? i : 0)) * d;
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) {
+      const int ch = m * CB + PER * g;
+      wz[m] = load_frag<IN_BF16, MMA_BF16>(a.W_d, zrow + ch, i < N && ch < d);
+      wsel[m] = load_frag<IN_BF16, MMA_BF16>(a.W_sel, srow + ch, i < K && ch < d);
+    }
+  }
+  const float bdz = i < N ? a.b_d[(size_t)h * N + i] : 0.f;
+  const float cj = act ? Cs[j] : 0.f;
+
+  // u rows of tile k for this lane's A operand: group i / 4 of the wave,
+  // step 4k + i % 4 of that group's sub-chunk
+  const rsrc_t ur = make_rsrc((const unsigned char*)a.u + gbase * d * ES, (uint32_t)(Tc * d * ES));
+  const int rg_tb = (wave * 4 + (i >> 2)) * S;
+  const int rg_nst = max(min(rg_tb + S, Tc) - rg_tb, 0);
+  auto load_tile = [&](FT* dst, int k) {
+    const int st = 4 * k + (i & 3);
+    const bool ok = st < rg_nst;
+    const uint32_t rb = (uint32_t)(((rg_tb + st) * d + PER * g) * ES);
+#pragma unroll
+    for (int m = 0; m < KCH; ++m)
+      dst[m] = load_frag_buf<IN_BF16, MMA_BF16>(ur, ok ? rb + (uint32_t)(m * CB * ES) : kNoLoad);
+  };
+  auto mma_tile = [&](f4v* acc, const FT* src) {
+    acc[0] = f4v{0.f, 0.f, 0.f, 0.f};
+    acc[1] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) {
+      mma_step<IN_BF16, MMA_BF16>(acc[0], src[m], wz[m]);
+      mma_step<IN_BF16, MMA_BF16>(acc[1], src[m], wsel[m]);
+    }
+  };
+
+  __syncthreads();                                 // DC ready
+
+  float* slot = slots + gam * 16;
+  float hl = 0.f, msc = 1.f;
+  int midx = jj;
+  const int wave_nst = max(min(wave * 4 * S + S, Tc) - wave * 4 * S, 0);
+  const int nblk = (wave_nst + 3) >> 2;            // uniform in the wave
+  FT U[2][KCH];
+  f4v A[2][2];
+  if (nblk > 0) {
+    load_tile(U[0], 0);
+    if (nblk > 1) load_tile(U[1], 1);
+    mma_tile(A[0], U[0]);
+    if (nblk > 2) load_tile(U[0], 2);
+  }
+#pragma unroll
+  for (int k = 0; k < SMAX / 4; ++k) {
+    if (k >= nblk) break;
+    const int cu = k & 1, nx = cu ^ 1;
+    if (k + 1 < nblk) {
+      mma_tile(A[nx], U[nx]);                      // next tile, overlaps the scan below
+      if (k + 3 < nblk) load_tile(U[nx], k + 3);
+    }
+    // selections of this tile: D for this lane's row, k* for its group
+    float Dr[4];
+    int ks[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      Dr[r] = logistic(A[cu][0][r] + bdz);
+      const int key = i < K ? order_key(A[cu][1][r]) : (int)0x80000000;
+      const int m = row_max(key);
+      ks[r] = row_min(key == m ? i : 0x7fffffff);
+    }
+    const int nb = nst - 4 * k;                    // steps left in this group
+    if (a.k_out && j == 0)
+      for (int r = 0; r < 4 && r < nb; ++r) a.k_out[gbase + tb + 4 * k + r] = ks[r];
+    if (a.D_out && act)
+      for (int r = 0; r < 4 && r < nb; ++r) a.D_out[(gbase + tb + 4 * k + r) * N + j] = Dr[r];
+    int own[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) own[r] = DC[(r < nb ? ks[r] : 0) * N + jj].x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool valid = r < nb;
+      const int t = tb + 4 * k + r;
+      const int kk = valid ? ks[r] : 0;
+      const i2v e = DC[kk * N + midx];
+      const float dm = __int_as_float(
+          __builtin_amdgcn_ds_bpermute(((lane & ~15) + midx) << 2, __float_as_int(Dr[r])));
+      slot[j] = valid ? bu[4 * k + r] : 0.f;
+      atomicAdd(&slot[(valid && act) ? own[r] : j], (valid ? Dr[r] : 1.f) * hl);
+      hl = slot[j];
+      if (valid) {
+        msc *= dm;
+        midx = e.x;
+      }
+      if (valid && act) Dbuf[j * TS + t] = __int_as_float(e.y) * msc;
+      const float yl = group_sum<16>(cj * hl);
+      if (valid && j == 0) yloc[t] = yl;
+    }
+  }
+  chunk_tail(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
+}
+
+template <int IN_BF16, int MMA_BF16, int KCH>
+__global__ __launch_bounds__(kThreads, 3) void pdssm_fused16_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  fused16_body<IN_BF16, MMA_BF16, KCH>(a, smem);
+}
+
+// Two entry points over one body: the register-resident fp32 selection paths
+// fit three waves per SIMD; the other paths get the larger register budget
+// of two waves per SIMD.
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT>
+__global__ __launch_bounds__(kThreads, 3) void pdssm_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT>(a, smem);
+}
+
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT>
+__global__ __launch_bounds__(kThreads, 2) void pdssm_kernel_wide(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT>(a, smem);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+static inline int sel_path(const Plan& p) {
+  const int nct = p.NC >> 4;
+  if (!p.in_bf16 && p.d == 64 && nct == 2) return kSelF32D64N2;
+  if (!p.in_bf16 && p.d == 16 && nct == 1) return kSelF32D16N1;
+  if (p.in_bf16 && p.mma_bf16 && p.d == 128 && nct == 3) return kSelBF16D128N3;
+  return kSelAny;
+}
+
+// Group width fixed at compile time when N is a power of two (the common
+// case); otherwise the runtime-width body with per-lane guards.
+static inline int npt_of(const Plan& p) {
+  return (p.N == p.NP && (p.N == 8 || p.N == 16 || p.N == 32 || p.N == 64)) ? p.N : 0;
+}
+
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, bool WIDE>
+static inline void launch_kernel(const Args& a, hipStream_t st) {
+  if constexpr (WIDE)
+    hipLaunchKernelGGL((pdssm_kernel_wide<MODE, IN_BF16, MMA_BF16, PATH, NPT>), dim3(a.p.tasks),
+                       dim3(kThreads), a.p.lds_bytes, st, a);
+  else
+    hipLaunchKernelGGL((pdssm_kernel<MODE, IN_BF16, MMA_BF16, PATH, NPT>), dim3(a.p.tasks),
+                       dim3(kThreads), a.p.lds_bytes, st, a);
+}
+
+}  // namespace pdscan

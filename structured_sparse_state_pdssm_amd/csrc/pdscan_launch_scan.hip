@@ -1,0 +1,35 @@
+// Launcher for the scan mode (selections given), and the workspace clear
+// that precedes every scan or fused launch.
+#include "pdscan_device.h"
+
+namespace pdscan {
+
+// Zero the workspace words the look-back reads (header, aggregates,
+// inclusive states): every word starts untagged.
+__global__ void clear_kernel(uint64_t* w, size_t n) {
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < n;
+       q += (size_t)gridDim.x * blockDim.x)
+    w[q] = 0;
+}
+
+void launch_clear(const Args& a, hipStream_t st) {
+  const size_t words = a.p.ws_bytes / 8;
+  size_t cb = (words + 255) / 256;
+  if (cb > 4096) cb = 4096;
+  if (cb < 1) cb = 1;
+  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)cb), dim3(256), 0, st, (uint64_t*)a.ws, words);
+}
+
+hipError_t launch_scan(const Args& a, hipStream_t st) {
+  launch_clear(a, st);
+  switch (npt_of(a.p)) {
+    case 8: launch_kernel<kModeScan, 0, 0, kSelAny, 8, false>(a, st); break;
+    case 16: launch_kernel<kModeScan, 0, 0, kSelAny, 16, false>(a, st); break;
+    case 32: launch_kernel<kModeScan, 0, 0, kSelAny, 32, false>(a, st); break;
+    case 64: launch_kernel<kModeScan, 0, 0, kSelAny, 64, false>(a, st); break;
+    default: launch_kernel<kModeScan, 0, 0, kSelAny, 0, false>(a, st); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pdscan

@@ -33,6 +33,7 @@ struct Plan {
   int NC;    // GEMM columns (K scores then N pre-activations), padded to 16
   int KP;    // score staging width
   int mma_bf16;  // score GEMM on bf16 MFMA (else fp32 MFMA)
+  int fused16;   // fused pass with step-major MFMA tiles (N, K <= 16; see below)
   int tasks;     // workgroups
   // LDS byte offsets
   int off_D, off_k, off_yl, off_dict, off_DC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
@@ -57,7 +58,14 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.u_shared = u_shared; p.in_bf16 = in_bf16;
   // a chunk longer than the sequence behaves exactly like chunk = L
   p.chunk = (mode == kModeSelect) ? kSelectRows : (chunk < L ? chunk : L);
-  p.NP = next_pow2(N);
+  // Step-major fused path: 16-lane groups, each MFMA tile holding four steps
+  // of each of a wave's four groups, so D and k* land in the lanes that use
+  // them.  Per-head inputs, N and K up to 16, the register-resident weight
+  // shapes, at most 32 steps per group.
+  const int kch = in_bf16 ? (d >= 128 ? (d == 128 ? 4 : 0) : 0) : (d == 16 || d == 32 || d == 64 ? d / 16 : 0);
+  p.fused16 = (mode == kModeFused && !u_shared && N <= 16 && K <= 16 && kch > 0 &&
+               (chunk < L ? chunk : L) <= 512) ? 1 : 0;
+  p.NP = p.fused16 ? 16 : next_pow2(N);
   p.G = kThreads / p.NP;
   p.S = align_up((p.chunk + p.G - 1) / p.G, 4);
   // t-contiguous rows; a stride of 4 (mod 32) words spreads the rows of one
