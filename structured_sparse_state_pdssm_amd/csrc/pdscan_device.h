@@ -126,6 +126,35 @@ __device__ __forceinline__ int row_min(int v) {
   return min(v, dpp_i<kDppMirror>(v));
 }
 
+// Apply a map inside one 16-lane DPP row without atomics: lane i returns
+// base + sum of v_j over the lanes j of its row whose idx_j == i, visiting
+// j = i, i+1, ... (mod 16) in a fixed order.
+template <int S>
+__device__ __forceinline__ void gather_rot(float& acc, int idx, float v, int i) {
+  const int ix = dpp_i<0x120 + S>(idx);      // row_ror:S
+  const float vs = dpp_f<0x120 + S>(v);
+  acc += (ix == i) ? vs : 0.f;
+}
+__device__ __forceinline__ float row_gather_add(float base, int idx, float v, int i) {
+  float acc = base + ((idx == i) ? v : 0.f);
+  gather_rot<1>(acc, idx, v, i);
+  gather_rot<2>(acc, idx, v, i);
+  gather_rot<3>(acc, idx, v, i);
+  gather_rot<4>(acc, idx, v, i);
+  gather_rot<5>(acc, idx, v, i);
+  gather_rot<6>(acc, idx, v, i);
+  gather_rot<7>(acc, idx, v, i);
+  gather_rot<8>(acc, idx, v, i);
+  gather_rot<9>(acc, idx, v, i);
+  gather_rot<10>(acc, idx, v, i);
+  gather_rot<11>(acc, idx, v, i);
+  gather_rot<12>(acc, idx, v, i);
+  gather_rot<13>(acc, idx, v, i);
+  gather_rot<14>(acc, idx, v, i);
+  gather_rot<15>(acc, idx, v, i);
+  return acc;
+}
+
 // Sum over a lane group of NP lanes (a power of two); every lane of the group
 // gets the same value (the partial sums meet in the same order on every lane).
 template <int NP>
@@ -446,6 +475,7 @@ __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, i
 // brings the summary (midx, msc, hl) of its group's sub-chunk; w_t is in the
 // [N][TS] buffer and the local outputs in yloc.
 // ---------------------------------------------------------------------------
+template <bool ROW16>
 __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, int c, int s, int Tc,
                                            size_t gbase, int NP, int gam, int j, bool act,
                                            int midx, float msc, float hl) {
@@ -490,14 +520,25 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
       ni = sIdx[gam * N + pi];
       ns = sSc[gam * N + pi] * sSc[q];
     }
-    if (act) slot[j] = cb;
-    __syncthreads();
-    if (up) atomicAdd(&slot[ci], cs * pb);
-    __syncthreads();
-    if (up) {
-      cb = slot[j];
-      ci = ni;
-      cs = ns;
+    if constexpr (ROW16) {
+      // 16-lane groups: apply the map by a DPP gather inside the row
+      const float nb = row_gather_add(cb, up ? ci : -1, up ? cs * pb : 0.f, j);
+      __syncthreads();
+      if (up) {
+        cb = nb;
+        ci = ni;
+        cs = ns;
+      }
+    } else {
+      if (act) slot[j] = cb;
+      __syncthreads();
+      if (up) atomicAdd(&slot[ci], cs * pb);
+      __syncthreads();
+      if (up) {
+        cb = slot[j];
+        ci = ni;
+        cs = ns;
+      }
     }
   }
   if (act) {
@@ -576,23 +617,35 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
           for (int f = 0; f < 3; ++f)
             for (int n = 0; on && !tag_ok(wv[u8][f]) && n < kSpinLimit; ++n)
               wv[u8][f] = get_tagged(pa + f * N + lane);
-          if (on) tmp[lane] = __uint_as_float((uint32_t)wv[u8][2]);
-          WAVE_SYNC();
-          if (on)
-            atomicAdd(&tmp[(int)(uint32_t)wv[u8][0]], __uint_as_float((uint32_t)wv[u8][1]) * x);
-          WAVE_SYNC();
-          if (on) x = tmp[lane];
-          WAVE_SYNC();
+          const float rb = __uint_as_float((uint32_t)wv[u8][2]);
+          const int ri = on ? (int)(uint32_t)wv[u8][0] : -1;
+          const float rv = on ? __uint_as_float((uint32_t)wv[u8][1]) * x : 0.f;
+          if constexpr (ROW16) {
+            const float xn = row_gather_add(rb, ri, rv, lane);
+            if (on) x = xn;
+          } else {
+            if (on) tmp[lane] = rb;
+            WAVE_SYNC();
+            if (on) atomicAdd(&tmp[ri], rv);
+            WAVE_SYNC();
+            if (on) x = tmp[lane];
+            WAVE_SYNC();
+          }
         }
       }
     }
     // inclusive state of this chunk, with the same arithmetic
-    if (on) tmp[lane] = ab;
-    WAVE_SYNC();
-    if (on) atomicAdd(&tmp[ai], as * x);
-    WAVE_SYNC();
-    const float xo = on ? tmp[lane] : 0.f;
-    WAVE_SYNC();
+    float xo;
+    if constexpr (ROW16) {
+      xo = row_gather_add(ab, on ? ai : -1, on ? as * x : 0.f, lane);
+    } else {
+      if (on) tmp[lane] = ab;
+      WAVE_SYNC();
+      if (on) atomicAdd(&tmp[ai], as * x);
+      WAVE_SYNC();
+      xo = on ? tmp[lane] : 0.f;
+      WAVE_SYNC();
+    }
     if (on) {
       put_tagged(inc + ((size_t)c * BH + s) * N + lane, __float_as_uint(xo));
       Hs[lane] = x;
@@ -605,19 +658,31 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
   // of the groups before it to the carry), then the corrected outputs
   {
     float* srow = slots + gam * NP;
-    if (gam == 0) {
-      if (act) srow[j] = Hs[j];
-    } else if (act) {
-      srow[j] = pB[(gam - 1) * N + j];
+    if constexpr (ROW16) {
+      const bool on = act && gam > 0;
+      const int q = (gam - 1) * N + j;
+      const float hj = act ? Hs[j] : 0.f;
+      const float cv = row_gather_add(on ? pB[q] : hj, on ? pIdx[q] : -1,
+                                      on ? pSc[q] * hj : 0.f, j);
+      if (act) srow[j] = cv;
+      __syncthreads();
+    } else {
+      if (gam == 0) {
+        if (act) srow[j] = Hs[j];
+      } else if (act) {
+        srow[j] = pB[(gam - 1) * N + j];
+      }
+      __syncthreads();
+      if (gam > 0 && act) atomicAdd(&srow[pIdx[(gam - 1) * N + j]], pSc[(gam - 1) * N + j] * Hs[j]);
+      __syncthreads();
     }
-    __syncthreads();
-    if (gam > 0 && act) atomicAdd(&srow[pIdx[(gam - 1) * N + j]], pSc[(gam - 1) * N + j] * Hs[j]);
-    __syncthreads();
   }
   for (int t = tid; t < Tc; t += kThreads) {
-    const float* cr = slots + (t / S) * NP;
-    float acc = yloc[t];
-    for (int n = 0; n < N; ++n) acc += Dbuf[n * TS + t] * cr[n];
+    const int gt = t / S;
+    const int col = t + (p.skew ? gt : 0);
+    const float* cr = slots + gt * NP;
+    float acc = yloc[col];
+    for (int n = 0; n < N; ++n) acc += Dbuf[n * TS + col] * cr[n];
     a.y[gbase + t] = acc;
   }
 }
@@ -696,7 +761,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     // DC[k][m] = (dict[k][m], C[dict[k][m]]): target row and its output weight
     for (int q = tid; q < K * N; q += kThreads) {
       const int r = a.dict[(size_t)h * K * N + q];
-      DC[q] = i2v{r, __float_as_int(Cs[r])};
+      DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
     }
   }
   if constexpr (MODE == kModeScan) {
@@ -748,14 +813,14 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
       const f4v d4 = act ? *(const f4v*)(Dbuf + j * TS + t0) : f4v{1.f, 1.f, 1.f, 1.f};
       int own[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) own[r] = DC[(r < nb ? k4[r] : 0) * N + jj].x;
+      for (int r = 0; r < 4; ++r) own[r] = DC[(r < nb ? k4[r] : 0) * p.DCS + jj].x;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool valid = r < nb;
         const int t = t0 + r;
         const int k = valid ? k4[r] : 0;
         // next factor of the running map, gathered at its current rows
-        const i2v e = DC[k * N + midx];
+        const i2v e = DC[k * p.DCS + midx];
         const float dm = Dbuf[midx * TS + t];
         // h' = Bu + scatter(D h); one wave, so its LDS operations stay in order
         slot[j] = valid ? bu[q4 + r] : 0.f;
@@ -777,7 +842,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     for (int q = 0; q < kBuBlock; ++q) bu[q] = bn[q];
   }
 
-  chunk_tail(a, smem, c, s, Tc, gbase, NP, gam, j, act, midx, msc, hl);
+  chunk_tail<false>(a, smem, c, s, Tc, gbase, NP, gam, j, act, midx, msc, hl);
 }
 
 // ---------------------------------------------------------------------------
@@ -841,7 +906,25 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   __syncthreads();
   for (int q = tid; q < K * N; q += kThreads) {
     const int r = a.dict[(size_t)h * K * N + q];
-    DC[q] = i2v{r, __float_as_int(Cs[r])};
+    DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
+  }
+  __syncthreads();
+  // SRC[k][i]: the source columns j (ascending) whose one sits in row i under
+  // dictionary entry k, as nibbles (x: first eight, y: next eight), and
+  // their count (z)
+  i4v* SRC = (i4v*)(smem + p.off_SRC);
+  for (int q = tid; q < K * 16; q += kThreads) {
+    const int kq = q >> 4, iq = q & 15;
+    unsigned lo = 0, hi = 0;
+    int n = 0;
+    for (int jq = 0; jq < N; ++jq) {
+      if (DC[kq * p.DCS + jq].x == iq) {
+        if (n < 8) lo |= (unsigned)jq << (4 * n);
+        else hi |= (unsigned)jq << (4 * (n - 8));
+        ++n;
+      }
+    }
+    SRC[q] = i4v{(int)lo, (int)hi, n, 0};
   }
 
   // weight fragments: tile 0 = pre-activation columns, tile 1 = score columns
@@ -885,7 +968,6 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
 
   __syncthreads();                                 // DC ready
 
-  float* slot = slots + gam * 16;
   float hl = 0.f, msc = 1.f;
   int midx = jj;
   const int wave_nst = max(min(wave * 4 * S + S, Tc) - wave * 4 * S, 0);
@@ -921,30 +1003,58 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       for (int r = 0; r < 4 && r < nb; ++r) a.k_out[gbase + tb + 4 * k + r] = ks[r];
     if (a.D_out && act)
       for (int r = 0; r < 4 && r < nb; ++r) a.D_out[(gbase + tb + 4 * k + r) * N + j] = Dr[r];
-    int own[4];
+    i4v srl[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) own[r] = DC[(r < nb ? ks[r] : 0) * N + jj].x;
+    for (int r = 0; r < 4; ++r) srl[r] = SRC[(r < nb ? ks[r] : 0) * 16 + j];
+    const int lbase = (lane & ~15) << 2;
+    float yp[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool valid = r < nb;
       const int t = tb + 4 * k + r;
       const int kk = valid ? ks[r] : 0;
-      const i2v e = DC[kk * N + midx];
+      const i2v e = DC[kk * p.DCS + midx];
       const float dm = __int_as_float(
-          __builtin_amdgcn_ds_bpermute(((lane & ~15) + midx) << 2, __float_as_int(Dr[r])));
-      slot[j] = valid ? bu[4 * k + r] : 0.f;
-      atomicAdd(&slot[(valid && act) ? own[r] : j], (valid ? Dr[r] : 1.f) * hl);
-      hl = slot[j];
+          __builtin_amdgcn_ds_bpermute(lbase + (midx << 2), __float_as_int(Dr[r])));
+      // h'_i = Bu_i + sum over the sources j of row i of D_j h_j, gathered
+      // from their lanes in ascending j
+      const int vj = __float_as_int(Dr[r] * hl);
+      const int deg = act ? srl[r].z : 0;
+      const unsigned lo = (unsigned)srl[r].x;
+      float g[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        g[m] = __int_as_float(
+            __builtin_amdgcn_ds_bpermute(lbase + (int)(((lo >> (4 * m)) & 15u) << 2), vj));
+      float hn = bu[4 * k + r];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) hn += m < deg ? g[m] : 0.f;
+      if (__builtin_amdgcn_ballot_w64(deg > 4)) {
+        for (int m = 4; m < 16; ++m) {
+          const unsigned w = m < 8 ? lo >> (4 * m) : (unsigned)srl[r].y >> (4 * (m - 8));
+          const float gm = __int_as_float(
+              __builtin_amdgcn_ds_bpermute(lbase + (int)((w & 15u) << 2), vj));
+          hn += m < deg ? gm : 0.f;
+          if (!__builtin_amdgcn_ballot_w64(m + 1 < deg)) break;
+        }
+      }
+      if (valid) hl = hn;
       if (valid) {
         msc *= dm;
         midx = e.x;
       }
-      if (valid && act) Dbuf[j * TS + t] = __int_as_float(e.y) * msc;
-      const float yl = group_sum<16>(cj * hl);
-      if (valid && j == 0) yloc[t] = yl;
+      if (valid && act) Dbuf[j * TS + t + gam] = __int_as_float(e.y) * msc;
+      yp[r] = cj * hl;
+    }
+    // local outputs of the four steps, summed over the group off the scan's
+    // critical path
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float yl = group_sum<16>(yp[r]);
+      if (r < nb && j == 0) yloc[tb + 4 * k + r + gam] = yl;
     }
   }
-  chunk_tail(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
+  chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
 }
 
 template <int IN_BF16, int MMA_BF16, int KCH>

@@ -29,6 +29,8 @@ struct Plan {
   int G;     // groups per workgroup
   int S;     // steps per group (a multiple of 4)
   int TS;    // row stride of the on-chip [N][TS] diagonal / output-weight buffer
+  int skew;  // 1: step t of group g sits in column t + g (fused16 layout)
+  int DCS;   // row stride of the (row, C[row]) dictionary table
   int nC;    // chunks per sequence
   int NC;    // GEMM columns (K scores then N pre-activations), padded to 16
   int KP;    // score staging width
@@ -36,7 +38,7 @@ struct Plan {
   int fused16;   // fused pass with step-major MFMA tiles (N, K <= 16; see below)
   int tasks;     // workgroups
   // LDS byte offsets
-  int off_D, off_k, off_yl, off_dict, off_DC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
+  int off_D, off_k, off_yl, off_dict, off_DC, off_SRC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
       off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_misc, lds_bytes;
   // workspace byte offsets (scan / fused)
   size_t ws_agg, ws_inc, ws_bytes;
@@ -70,8 +72,19 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.S = align_up((p.chunk + p.G - 1) / p.G, 4);
   // t-contiguous rows; a stride of 4 (mod 32) words spreads the rows of one
   // column over distinct LDS banks while keeping 16-byte alignment
-  p.TS = align_up(p.chunk, 4);
-  if (p.TS % 32 != 4) p.TS += (36 - p.TS % 32) % 32;
+  // Column layout.  fused16: group g's step t goes to column t + g and the
+  // row stride is 2 (mod 32), so the 64 lanes of a wave writing one step of
+  // four groups hit 64 distinct banks in every 32-lane half.  Otherwise
+  // t-contiguous rows with a stride of 4 (mod 32) for 16-byte accesses.
+  p.skew = p.fused16;
+  if (p.skew) {
+    p.TS = p.chunk + p.G;
+    p.TS += ((2 - p.TS % 32) + 32) % 32;
+  } else {
+    p.TS = align_up(p.chunk, 4);
+    if (p.TS % 32 != 4) p.TS += (36 - p.TS % 32) % 32;
+  }
+  p.DCS = N + 1;
   p.nC = (L + p.chunk - 1) / p.chunk;
   p.NC = align_up(K + N, 16);
   p.KP = align_up(K, 4);
@@ -84,9 +97,10 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   const bool scan = mode != kModeSelect;
   p.off_D = scan ? take(N * p.TS * 4) : 0;
   p.off_k = scan ? take(align_up(T, 4) * 4) : 0;
-  p.off_yl = scan ? take(T * 4) : 0;
+  p.off_yl = scan ? take((T + p.G) * 4) : 0;
   p.off_dict = scan ? 0 : take(K * N * 4);   // selection: P_idx gathers
-  p.off_DC = scan ? take(K * N * 8) : 0;      // scan: (row, C[row]) pairs
+  p.off_DC = scan ? take(K * p.DCS * 8) : 0;  // scan: (row, C[row]) pairs
+  p.off_SRC = p.fused16 ? take(K * 16 * 16) : 0;  // fused16: source columns of each row
   p.off_C = take(N * 4);
   p.off_bd = take(N * 4);
   p.off_slot = take(kThreads * 4);
