@@ -873,8 +873,6 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   float* Dbuf = (float*)(smem + p.off_D);          // holds w_t
   float* yloc = (float*)(smem + p.off_yl);
   i2v* DC = (i2v*)(smem + p.off_DC);
-  float* Cs = (float*)(smem + p.off_C);
-  float* slots = (float*)(smem + p.off_slot);
   int* misc = (int*)(smem + p.off_misc);
   uint32_t* hdr = (uint32_t*)a.ws;
 
@@ -894,54 +892,20 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   const bool act = j < N;
   const int jj = act ? j : 0;
 
-  // drive terms of this lane's steps, issued first
-  const rsrc_t bur = make_rsrc(a.Bu + gbase * N, (uint32_t)(Tc * N * 4));
-  float bu[SMAX];
-#pragma unroll
-  for (int q = 0; q < SMAX; ++q)
-    bu[q] = buf_f32(bur, (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad);
-
-  // per-head tables
-  for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
-  __syncthreads();
-  for (int q = tid; q < K * N; q += kThreads) {
-    const int r = a.dict[(size_t)h * K * N + q];
-    DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
-  }
-  __syncthreads();
-  // SRC[k][i]: the source columns j (ascending) whose one sits in row i under
-  // dictionary entry k, as nibbles (x: first eight, y: next eight), and
-  // their count (z)
-  i4v* SRC = (i4v*)(smem + p.off_SRC);
-  for (int q = tid; q < K * 16; q += kThreads) {
-    const int kq = q >> 4, iq = q & 15;
-    unsigned lo = 0, hi = 0;
-    int n = 0;
-    for (int jq = 0; jq < N; ++jq) {
-      if (DC[kq * p.DCS + jq].x == iq) {
-        if (n < 8) lo |= (unsigned)jq << (4 * n);
-        else hi |= (unsigned)jq << (4 * (n - 8));
-        ++n;
-      }
-    }
-    SRC[q] = i4v{(int)lo, (int)hi, n, 0};
-  }
-
-  // weight fragments: tile 0 = pre-activation columns, tile 1 = score columns
   const int i = lane & 15, g = lane >> 4;
-  FT wz[KCH], wsel[KCH];
-  {
-    const size_t zrow = ((size_t)h * N + (i < N ? i : 0)) * d;
-    const size_t srow = ((size_t)h * K + (i < K ? i : 0)) * d;
+  i2v* SRC = (i2v*)(smem + p.off_SRC);
+  int* SRC2 = (int*)(smem + p.off_SRC + K * 16 * 8);
+
+  // ---- every global load of this chunk is issued before anything waits
+  // drive terms: a ring of four blocks of four steps; each block's slots are
+  // refilled four blocks ahead
+  const rsrc_t bur = make_rsrc(a.Bu + gbase * N, (uint32_t)(Tc * N * 4));
+  auto bu_off = [&](int q) {
+    return (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad;
+  };
+  float bu[16];
 #pragma unroll
-    for (int m = 0; m < KCH; ++m) {
-      const int ch = m * CB + PER * g;
-      wz[m] = load_frag<IN_BF16, MMA_BF16>(a.W_d, zrow + ch, i < N && ch < d);
-      wsel[m] = load_frag<IN_BF16, MMA_BF16>(a.W_sel, srow + ch, i < K && ch < d);
-    }
-  }
-  const float bdz = i < N ? a.b_d[(size_t)h * N + i] : 0.f;
-  const float cj = act ? Cs[j] : 0.f;
+  for (int q = 0; q < 16; ++q) bu[q] = buf_f32(bur, bu_off(q));
 
   // u rows of tile k for this lane's A operand: group i / 4 of the wave,
   // step 4k + i % 4 of that group's sub-chunk
@@ -956,6 +920,35 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     for (int m = 0; m < KCH; ++m)
       dst[m] = load_frag_buf<IN_BF16, MMA_BF16>(ur, ok ? rb + (uint32_t)(m * CB * ES) : kNoLoad);
   };
+  const int wave_nst = max(min(wave * 4 * S + S, Tc) - wave * 4 * S, 0);
+  const int nblk = (wave_nst + 3) >> 2;            // uniform in the wave
+  FT U[2][KCH];
+  if (nblk > 0) load_tile(U[0], 0);
+  if (nblk > 1) load_tile(U[1], 1);
+
+  // weight fragments: tile 0 = pre-activation columns, tile 1 = score columns
+  FT wz[KCH], wsel[KCH];
+  {
+    const size_t zrow = ((size_t)h * N + (i < N ? i : 0)) * d;
+    const size_t srow = ((size_t)h * K + (i < K ? i : 0)) * d;
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) {
+      const int ch = m * CB + PER * g;
+      wz[m] = load_frag<IN_BF16, MMA_BF16>(a.W_d, zrow + ch, i < N && ch < d);
+      wsel[m] = load_frag<IN_BF16, MMA_BF16>(a.W_sel, srow + ch, i < K && ch < d);
+    }
+  }
+  const float bdz = i < N ? a.b_d[(size_t)h * N + i] : 0.f;
+  const float cj = act ? a.C[(size_t)h * N + j] : 0.f;
+
+  // dictionary inputs for the on-chip tables (K, N <= 16: one entry per lane)
+  const int* dict_h = a.dict + (size_t)h * K * N;
+  const bool dc_on = tid < K * N, src_on = tid < K * 16;
+  const int dq = dc_on ? dict_h[tid] : 0;
+  int drow[16];
+#pragma unroll
+  for (int jq = 0; jq < 16; ++jq) drow[jq] = (src_on && jq < N) ? dict_h[(tid >> 4) * N + jq] : -1;
+
   auto mma_tile = [&](f4v* acc, const FT* src) {
     acc[0] = f4v{0.f, 0.f, 0.f, 0.f};
     acc[1] = f4v{0.f, 0.f, 0.f, 0.f};
@@ -965,21 +958,36 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       mma_step<IN_BF16, MMA_BF16>(acc[1], src[m], wsel[m]);
     }
   };
-
-  __syncthreads();                                 // DC ready
-
-  float hl = 0.f, msc = 1.f;
-  int midx = jj;
-  const int wave_nst = max(min(wave * 4 * S + S, Tc) - wave * 4 * S, 0);
-  const int nblk = (wave_nst + 3) >> 2;            // uniform in the wave
-  FT U[2][KCH];
   f4v A[2][2];
   if (nblk > 0) {
-    load_tile(U[0], 0);
-    if (nblk > 1) load_tile(U[1], 1);
     mma_tile(A[0], U[0]);
     if (nblk > 2) load_tile(U[0], 2);
   }
+
+  // ---- on-chip tables, built while the first tile multiplies
+  // DC[k][m] = (dict[k][m], C[dict[k][m]]): target row and its output weight
+  if (dc_on) DC[(tid / N) * p.DCS + tid % N] = i2v{dq, __float_as_int(a.C[(size_t)h * N + dq])};
+  // SRC[k][i]: the source columns j (ascending) whose one sits in row i under
+  // dictionary entry k: (first eight as nibbles, count); SRC2 holds sources
+  // nine to sixteen
+  if (src_on) {
+    const int iq = tid & 15;
+    unsigned lo = 0, hi = 0;
+    int n = 0;
+#pragma unroll
+    for (int jq = 0; jq < 16; ++jq) {
+      const bool hit = drow[jq] == iq;
+      lo |= (hit && n < 8) ? (unsigned)jq << (4 * (n & 7)) : 0u;
+      hi |= (hit && n >= 8) ? (unsigned)jq << (4 * (n & 7)) : 0u;
+      n += hit ? 1 : 0;
+    }
+    SRC[tid] = i2v{(int)lo, n};
+    SRC2[tid] = (int)hi;
+  }
+  __syncthreads();                                 // tables ready
+
+  float hl = 0.f, msc = 1.f;
+  int midx = jj;
 #pragma unroll
   for (int k = 0; k < SMAX / 4; ++k) {
     if (k >= nblk) break;
@@ -1003,7 +1011,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       for (int r = 0; r < 4 && r < nb; ++r) a.k_out[gbase + tb + 4 * k + r] = ks[r];
     if (a.D_out && act)
       for (int r = 0; r < 4 && r < nb; ++r) a.D_out[(gbase + tb + 4 * k + r) * N + j] = Dr[r];
-    i4v srl[4];
+    i2v srl[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) srl[r] = SRC[(r < nb ? ks[r] : 0) * 16 + j];
     const int lbase = (lane & ~15) << 2;
@@ -1019,19 +1027,20 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       // h'_i = Bu_i + sum over the sources j of row i of D_j h_j, gathered
       // from their lanes in ascending j
       const int vj = __float_as_int(Dr[r] * hl);
-      const int deg = act ? srl[r].z : 0;
+      const int deg = act ? srl[r].y : 0;
       const unsigned lo = (unsigned)srl[r].x;
       float g[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         g[m] = __int_as_float(
             __builtin_amdgcn_ds_bpermute(lbase + (int)(((lo >> (4 * m)) & 15u) << 2), vj));
-      float hn = bu[4 * k + r];
+      float hn = bu[(4 * k + r) & 15];
 #pragma unroll
       for (int m = 0; m < 4; ++m) hn += m < deg ? g[m] : 0.f;
       if (__builtin_amdgcn_ballot_w64(deg > 4)) {
+        const unsigned hi = (unsigned)SRC2[(r < nb ? ks[r] : 0) * 16 + j];
         for (int m = 4; m < 16; ++m) {
-          const unsigned w = m < 8 ? lo >> (4 * m) : (unsigned)srl[r].y >> (4 * (m - 8));
+          const unsigned w = m < 8 ? lo >> (4 * m) : hi >> (4 * (m - 8));
           const float gm = __int_as_float(
               __builtin_amdgcn_ds_bpermute(lbase + (int)((w & 15u) << 2), vj));
           hn += m < deg ? gm : 0.f;
@@ -1046,6 +1055,9 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       if (valid && act) Dbuf[j * TS + t + gam] = __int_as_float(e.y) * msc;
       yp[r] = cj * hl;
     }
+    // refill this block's drive-term slots with the block four ahead
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bu[(4 * k + r) & 15] = buf_f32(bur, bu_off(4 * k + 16 + r));
     // local outputs of the four steps, summed over the group off the scan's
     // critical path
 #pragma unroll
