@@ -3,7 +3,8 @@ MI355X, in state-updates per second, with its HBM roofline fraction and the
 fp64 CPU oracle timed beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload impulse]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--copy-probe]
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload impulse]
 
 Prints one JSON line.  A step is one pdssm_fwd call over the whole workload
 (selection outputs not materialised), with every input already resident in
@@ -65,6 +66,62 @@ def traffic_from_profile(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_PROBE_BYTES = 1 << 30      # the plain copy kernel's source (and destination) size
+
+
+def copy_probe(torch):
+    """A plain streaming kernel of known traffic (read 1 GiB, write 1 GiB):
+    the scale of the HBM byte counters is read off it."""
+    n = COPY_PROBE_BYTES // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"[bench] copy probe: 3 x neg over {COPY_PROBE_BYTES} B", file=sys.stderr, flush=True)
+
+
+def _pmc_rows(d, counter):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir, workload):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of `bench.py --copy-probe` into HBM bytes per launch of the
+    fused kernel, each counter scaled by what it reads for the copy probe."""
+    from statistics import mean
+    out = {}
+    for counter, d, probe_bytes in (("FETCH_SIZE", fetch_dir, COPY_PROBE_BYTES),
+                                    ("WRITE_SIZE", write_dir, COPY_PROBE_BYTES)):
+        rows = _pmc_rows(d, counter)
+        kern = [float(r["Counter_Value"]) for r in rows if "pdssm_" in r["Kernel_Name"]
+                and "clear" not in r["Kernel_Name"]]
+        probe = [float(r["Counter_Value"]) for r in rows if "neg" in r["Kernel_Name"]]
+        if not kern or not probe:
+            raise SystemExit(f"{counter}: no fused-kernel or copy-probe dispatches under {d}")
+        names = sorted({r["Kernel_Name"] for r in rows if "pdssm_" in r["Kernel_Name"]
+                        and "clear" not in r["Kernel_Name"]})
+        scale = probe_bytes / (mean(probe) * 1024.0)
+        out[counter] = {"kernel_kib": mean(kern), "probe_kib": mean(probe),
+                        "scale": scale, "bytes": mean(kern) * 1024.0 * scale,
+                        "dispatches": len(kern), "kernels": names}
+    total = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
+    rec = {"workload": workload, "kernel_hash": kernel_hash(),
+           "hbm_bytes_per_launch": round(total), "counters": out,
+           "copy_probe_bytes": COPY_PROBE_BYTES}
+    path = os.path.join(ROOT, "profiles", f"pdssm_fused_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(inp):
     """The fp64 oracle, as it is, on the host cores: selection plus the dense
     sequential scan over the whole workload (inputs already generated)."""
@@ -105,7 +162,14 @@ def main():
     ap.add_argument("--workload", default="impulse")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain copy kernel of known size (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the forward pass shards over independent sequences with no exchange).",
@@ -195,6 +259,8 @@ def main():
         "roofline": roof,
         "kernel_hash": kernel_hash(),
     }
+    if args.copy_probe:
+        copy_probe(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp)
