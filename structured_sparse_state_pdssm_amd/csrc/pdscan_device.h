@@ -87,6 +87,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ float buf_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+__device__ __forceinline__ int buf_i32(rsrc_t r, uint32_t off) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 
 // DPP lane permutations inside 16-lane rows.
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
@@ -475,6 +478,9 @@ __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, i
 // brings the summary (midx, msc, hl) of its group's sub-chunk; w_t is in the
 // [N][TS] buffer and the local outputs in yloc.
 // ---------------------------------------------------------------------------
+// Words of look-back data one lane requests per batch (64-bit each).
+constexpr int kLookBatchWords = 12;
+
 template <bool ROW16>
 __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, int c, int s, int Tc,
                                            size_t gbase, int NP, int gam, int j, bool act,
@@ -590,36 +596,46 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      // base state: the inclusive state `stop` chunks back, or h0
-      if (stop < c) {
-        uint64_t* pw = inc + ((size_t)(c - 1 - stop) * BH + s) * N;
-        if (on) {
-          uint64_t w = get_tagged(pw + lane);
-          for (int n = 0; !tag_ok(w) && n < kSpinLimit; ++n) w = get_tagged(pw + lane);
-          x = __uint_as_float((uint32_t)w);
+      // The base state (the inclusive state `stop` chunks back, unless the
+      // window reaches chunk 0 and h0 is the base) and the aggregates after
+      // it are loaded in batches: every word of a batch is requested at once
+      // (one round trip), checked, and staged in LDS (the combine's scratch,
+      // free by now); the aggregates are then applied oldest first.
+      uint32_t* stage = (uint32_t*)sIdx;
+      const int wcap = min((p.off_pIdx - p.off_sIdx) / 4, 64 * kLookBatchWords);
+      const int nbmax = (wcap - N) / (3 * N);
+      bool need_base = stop < c;
+      const int base_q = c - 1 - stop;
+      for (int q0 = c - stop; need_base || q0 < c;) {
+        const int nb = min(c - q0, nbmax);
+        const int nbase = need_base ? N : 0;
+        const int W = nbase + nb * 3 * N;
+        auto word_ptr = [&](int w) -> uint64_t* {
+          if (w < nbase) return inc + ((size_t)base_q * BH + s) * N + w;
+          const int r = w - nbase, aq = r / (3 * N);
+          return agg + ((size_t)(q0 + aq) * BH + s) * 3 * N + (r - aq * 3 * N);
+        };
+        uint64_t wv[kLookBatchWords];
+#pragma unroll
+        for (int u = 0; u < kLookBatchWords; ++u) {
+          const int w = lane + 64 * u;
+          wv[u] = w < W ? get_tagged(word_ptr(w)) : kTagValid;
         }
-      }
-      // apply the aggregates after it, oldest first, loading eight at a time
-      for (int r0 = c - stop; r0 < c; r0 += 8) {
-        uint64_t wv[8][3];
 #pragma unroll
-        for (int u8 = 0; u8 < 8; ++u8) {
-          uint64_t* pa = agg + ((size_t)(r0 + u8) * BH + s) * 3 * N;
-#pragma unroll
-          for (int f = 0; f < 3; ++f)
-            wv[u8][f] = (on && r0 + u8 < c) ? get_tagged(pa + f * N + lane) : kTagValid;
+        for (int u = 0; u < kLookBatchWords; ++u) {
+          const int w = lane + 64 * u;
+          if (w < W) {
+            for (int n = 0; !tag_ok(wv[u]) && n < kSpinLimit; ++n) wv[u] = get_tagged(word_ptr(w));
+            stage[w] = (uint32_t)wv[u];
+          }
         }
-#pragma unroll
-        for (int u8 = 0; u8 < 8; ++u8) {
-          if (r0 + u8 >= c) break;
-          uint64_t* pa = agg + ((size_t)(r0 + u8) * BH + s) * 3 * N;
-#pragma unroll
-          for (int f = 0; f < 3; ++f)
-            for (int n = 0; on && !tag_ok(wv[u8][f]) && n < kSpinLimit; ++n)
-              wv[u8][f] = get_tagged(pa + f * N + lane);
-          const float rb = __uint_as_float((uint32_t)wv[u8][2]);
-          const int ri = on ? (int)(uint32_t)wv[u8][0] : -1;
-          const float rv = on ? __uint_as_float((uint32_t)wv[u8][1]) * x : 0.f;
+        WAVE_SYNC();
+        if (need_base && on) x = __uint_as_float(stage[lane]);
+        for (int aq = 0; aq < nb; ++aq) {
+          const uint32_t* e = stage + nbase + aq * 3 * N;
+          const float rb = on ? __uint_as_float(e[2 * N + lane]) : 0.f;
+          const int ri = on ? (int)e[lane] : -1;
+          const float rv = on ? __uint_as_float(e[N + lane]) * x : 0.f;
           if constexpr (ROW16) {
             const float xn = row_gather_add(rb, ri, rv, lane);
             if (on) x = xn;
@@ -632,6 +648,9 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
             WAVE_SYNC();
           }
         }
+        WAVE_SYNC();                               // staging is reused by the next batch
+        q0 += nb;
+        need_base = false;
       }
     }
     // inclusive state of this chunk, with the same arithmetic
@@ -896,16 +915,39 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   i2v* SRC = (i2v*)(smem + p.off_SRC);
   int* SRC2 = (int*)(smem + p.off_SRC + K * 16 * 8);
 
-  // ---- every global load of this chunk is issued before anything waits
-  // drive terms: a ring of four blocks of four steps; each block's slots are
-  // refilled four blocks ahead
-  const rsrc_t bur = make_rsrc(a.Bu + gbase * N, (uint32_t)(Tc * N * 4));
-  auto bu_off = [&](int q) {
-    return (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad;
-  };
-  float bu[16];
+  // ---- every global load of this chunk is issued before anything waits,
+  // the L2-resident ones (dictionary, weights) first: loads retire in order,
+  // so the table build below then waits only for them while the u and Bu
+  // streams are still in flight
+  // (buffer loads: a lane with nothing to load reads zero through an
+  // out-of-range offset instead of branching, so every load is in flight at
+  // once)
+  // dictionary inputs for the on-chip tables (K, N <= 16: one entry per lane)
+  const rsrc_t dr = make_rsrc(a.dict + (size_t)h * K * N, (uint32_t)(K * N * 4));
+  const bool dc_on = tid < K * N, src_on = tid < K * 16;
+  const int dq = buf_i32(dr, dc_on ? (uint32_t)tid * 4u : kNoLoad);
+  int drow[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) bu[q] = buf_f32(bur, bu_off(q));
+  for (int jq = 0; jq < 16; ++jq) {
+    const bool ok = src_on && jq < N;
+    const int v = buf_i32(dr, ok ? (uint32_t)(((tid >> 4) * N + jq) * 4) : kNoLoad);
+    drow[jq] = ok ? v : -1;
+  }
+
+  // weight fragments: tile 0 = pre-activation columns, tile 1 = score columns
+  FT wz[KCH], wsel[KCH];
+  {
+    const rsrc_t wzr = make_rsrc((const unsigned char*)a.W_d + (size_t)h * N * d * ES, (uint32_t)(N * d * ES));
+    const rsrc_t wsr = make_rsrc((const unsigned char*)a.W_sel + (size_t)h * K * d * ES, (uint32_t)(K * d * ES));
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) {
+      const int ch = m * CB + PER * g;
+      wz[m] = load_frag_buf<IN_BF16, MMA_BF16>(wzr, (i < N && ch < d) ? (uint32_t)((i * d + ch) * ES) : kNoLoad);
+      wsel[m] = load_frag_buf<IN_BF16, MMA_BF16>(wsr, (i < K && ch < d) ? (uint32_t)((i * d + ch) * ES) : kNoLoad);
+    }
+  }
+  const float bdz = buf_f32(make_rsrc(a.b_d + (size_t)h * N, (uint32_t)(N * 4)), i < N ? (uint32_t)i * 4u : kNoLoad);
+  const float cj = buf_f32(make_rsrc(a.C + (size_t)h * N, (uint32_t)(N * 4)), act ? (uint32_t)j * 4u : kNoLoad);
 
   // u rows of tile k for this lane's A operand: group i / 4 of the wave,
   // step 4k + i % 4 of that group's sub-chunk
@@ -926,28 +968,15 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   if (nblk > 0) load_tile(U[0], 0);
   if (nblk > 1) load_tile(U[1], 1);
 
-  // weight fragments: tile 0 = pre-activation columns, tile 1 = score columns
-  FT wz[KCH], wsel[KCH];
-  {
-    const size_t zrow = ((size_t)h * N + (i < N ? i : 0)) * d;
-    const size_t srow = ((size_t)h * K + (i < K ? i : 0)) * d;
+  // drive terms: a ring of four blocks of four steps; each block's slots are
+  // refilled four blocks ahead
+  const rsrc_t bur = make_rsrc(a.Bu + gbase * N, (uint32_t)(Tc * N * 4));
+  auto bu_off = [&](int q) {
+    return (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad;
+  };
+  float bu[16];
 #pragma unroll
-    for (int m = 0; m < KCH; ++m) {
-      const int ch = m * CB + PER * g;
-      wz[m] = load_frag<IN_BF16, MMA_BF16>(a.W_d, zrow + ch, i < N && ch < d);
-      wsel[m] = load_frag<IN_BF16, MMA_BF16>(a.W_sel, srow + ch, i < K && ch < d);
-    }
-  }
-  const float bdz = i < N ? a.b_d[(size_t)h * N + i] : 0.f;
-  const float cj = act ? a.C[(size_t)h * N + j] : 0.f;
-
-  // dictionary inputs for the on-chip tables (K, N <= 16: one entry per lane)
-  const int* dict_h = a.dict + (size_t)h * K * N;
-  const bool dc_on = tid < K * N, src_on = tid < K * 16;
-  const int dq = dc_on ? dict_h[tid] : 0;
-  int drow[16];
-#pragma unroll
-  for (int jq = 0; jq < 16; ++jq) drow[jq] = (src_on && jq < N) ? dict_h[(tid >> 4) * N + jq] : -1;
+  for (int q = 0; q < 16; ++q) bu[q] = buf_f32(bur, bu_off(q));
 
   auto mma_tile = [&](f4v* acc, const FT* src) {
     acc[0] = f4v{0.f, 0.f, 0.f, 0.f};
@@ -958,15 +987,13 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       mma_step<IN_BF16, MMA_BF16>(acc[1], src[m], wsel[m]);
     }
   };
-  f4v A[2][2];
-  if (nblk > 0) {
-    mma_tile(A[0], U[0]);
-    if (nblk > 2) load_tile(U[0], 2);
-  }
-
-  // ---- on-chip tables, built while the first tile multiplies
+  // ---- on-chip tables; they need only the dictionary and C
   // DC[k][m] = (dict[k][m], C[dict[k][m]]): target row and its output weight
-  if (dc_on) DC[(tid / N) * p.DCS + tid % N] = i2v{dq, __float_as_int(a.C[(size_t)h * N + dq])};
+  // (C[r] sits in every lane whose row index is r, so a lane permute finds it)
+  {
+    const float cdq = __int_as_float(__builtin_amdgcn_ds_bpermute(dq << 2, __float_as_int(cj)));
+    if (dc_on) DC[(tid / N) * p.DCS + tid % N] = i2v{dq, __float_as_int(cdq)};
+  }
   // SRC[k][i]: the source columns j (ascending) whose one sits in row i under
   // dictionary entry k: (first eight as nibbles, count); SRC2 holds sources
   // nine to sixteen
@@ -985,6 +1012,12 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     SRC2[tid] = (int)hi;
   }
   __syncthreads();                                 // tables ready
+
+  f4v A[2][2];
+  if (nblk > 0) {
+    mma_tile(A[0], U[0]);
+    if (nblk > 2) load_tile(U[0], 2);
+  }
 
   float hl = 0.f, msc = 1.f;
   int midx = jj;
