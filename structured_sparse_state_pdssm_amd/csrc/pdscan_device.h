@@ -260,6 +260,52 @@ __device__ __forceinline__ void mma_step(f4v& acc, typename Frag<IN_BF16, MMA_BF
   }
 }
 
+// fp32 products on the bf16 matrix cores.  Truncation splits an fp32 value
+// exactly into three bf16 pieces, x = x0 + x1 + x2 (each piece holds the next
+// eight significant bits, so each remainder is exact); the six piece products
+// with i + j <= 2 are exact in fp32 and are accumulated in fp32, and the
+// terms left out are below 2^-23 of |x w|.  This is a standard fp32 GEMM
+// emulation; it keeps the scores and pre-activations at fp32 accuracy.
+__device__ __forceinline__ unsigned hi16_pair(float lo, float hi) {
+  // bf16 pair (lo in the low half) from the high halves of two fp32 words
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ __forceinline__ u4v pack_hi8(const f4v& a, const f4v& b) {
+  return u4v{hi16_pair(a.x, a.y), hi16_pair(a.z, a.w), hi16_pair(b.x, b.y), hi16_pair(b.z, b.w)};
+}
+__device__ __forceinline__ f4v trunc_rem(const f4v& a) {
+  // a minus its bf16 truncation (exact)
+  f4v t;
+  t.x = __uint_as_float(__float_as_uint(a.x) & 0xFFFF0000u);
+  t.y = __uint_as_float(__float_as_uint(a.y) & 0xFFFF0000u);
+  t.z = __uint_as_float(__float_as_uint(a.z) & 0xFFFF0000u);
+  t.w = __uint_as_float(__float_as_uint(a.w) & 0xFFFF0000u);
+  return a - t;
+}
+// the three pieces of eight fp32 values (two fragments), as bf16 operands
+__device__ __forceinline__ void split3(f4v a, f4v b, u4v* pc) {
+  pc[0] = pack_hi8(a, b);
+  a = trunc_rem(a);
+  b = trunc_rem(b);
+  pc[1] = pack_hi8(a, b);
+  a = trunc_rem(a);
+  b = trunc_rem(b);
+  pc[2] = pack_hi8(a, b);
+}
+// acc += x w over 32 channels, x and w given as three pieces each
+__device__ __forceinline__ void mma_split3(f4v& acc, const u4v* x, const u4v* w) {
+  auto mm = [&](const u4v& p, const u4v& q) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, p), __builtin_bit_cast(bf8v, q),
+                                                  acc, 0, 0, 0);
+  };
+  mm(x[2], w[0]);                                  // smallest terms first
+  mm(x[1], w[1]);
+  mm(x[0], w[2]);
+  mm(x[1], w[0]);
+  mm(x[0], w[1]);
+  mm(x[0], w[0]);
+}
+
 // channels per fragment block: 16 (fp32 MFMA, 4 per lane group) or 32 (bf16)
 template <int MMA_BF16>
 constexpr int kChanBlock = MMA_BF16 ? 32 : 16;
@@ -877,7 +923,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
 // through LDS, and the next tile's MFMAs are issued before the current
 // tile's scan steps so that the two overlap.
 // ---------------------------------------------------------------------------
-template <int IN_BF16, int MMA_BF16, int KCH>
+template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT>
 __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem) {
   typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
   constexpr int CB = kChanBlock<MMA_BF16>;
@@ -912,8 +958,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   const int jj = act ? j : 0;
 
   const int i = lane & 15, g = lane >> 4;
-  i2v* SRC = (i2v*)(smem + p.off_SRC);
-  int* SRC2 = (int*)(smem + p.off_SRC + K * 16 * 8);
+  i4v* SE = (i4v*)(smem + p.off_SRC);
 
   // ---- every global load of this chunk is issued before anything waits,
   // the L2-resident ones (dictionary, weights) first: loads retire in order,
@@ -935,15 +980,33 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   }
 
   // weight fragments: tile 0 = pre-activation columns, tile 1 = score columns
+  // (split into bf16 pieces once per task when the products are emulated)
+  constexpr int KB = SPLIT ? KCH / 2 : 1;          // 32-channel blocks
   FT wz[KCH], wsel[KCH];
+  u4v wz3[KB][3], ws3[KB][3];
   {
     const rsrc_t wzr = make_rsrc((const unsigned char*)a.W_d + (size_t)h * N * d * ES, (uint32_t)(N * d * ES));
     const rsrc_t wsr = make_rsrc((const unsigned char*)a.W_sel + (size_t)h * K * d * ES, (uint32_t)(K * d * ES));
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int m = 0; m < KCH; ++m) {
-      const int ch = m * CB + PER * g;
-      wz[m] = load_frag_buf<IN_BF16, MMA_BF16>(wzr, (i < N && ch < d) ? (uint32_t)((i * d + ch) * ES) : kNoLoad);
-      wsel[m] = load_frag_buf<IN_BF16, MMA_BF16>(wsr, (i < K && ch < d) ? (uint32_t)((i * d + ch) * ES) : kNoLoad);
+      for (int kb = 0; kb < KB; ++kb) {
+        f4v z[2], q[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int ch = 32 * kb + 8 * g + 4 * hf;
+          z[hf] = load_frag_buf<0, 0>(wzr, i < N ? (uint32_t)((i * d + ch) * 4) : kNoLoad);
+          q[hf] = load_frag_buf<0, 0>(wsr, i < K ? (uint32_t)((i * d + ch) * 4) : kNoLoad);
+        }
+        split3(z[0], z[1], wz3[kb]);
+        split3(q[0], q[1], ws3[kb]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < KCH; ++m) {
+        const int ch = m * CB + PER * g;
+        wz[m] = load_frag_buf<IN_BF16, MMA_BF16>(wzr, (i < N && ch < d) ? (uint32_t)((i * d + ch) * ES) : kNoLoad);
+        wsel[m] = load_frag_buf<IN_BF16, MMA_BF16>(wsr, (i < K && ch < d) ? (uint32_t)((i * d + ch) * ES) : kNoLoad);
+      }
     }
   }
   const float bdz = buf_f32(make_rsrc(a.b_d + (size_t)h * N, (uint32_t)(N * 4)), i < N ? (uint32_t)i * 4u : kNoLoad);
@@ -957,10 +1020,18 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   auto load_tile = [&](FT* dst, int k) {
     const int st = 4 * k + (i & 3);
     const bool ok = st < rg_nst;
-    const uint32_t rb = (uint32_t)(((rg_tb + st) * d + PER * g) * ES);
+    if constexpr (SPLIT) {
+      // fragment m: channels 32 (m / 2) + 8 g + 4 (m % 2) .. +3
+      const uint32_t rb = (uint32_t)(((rg_tb + st) * d + 8 * g) * 4);
 #pragma unroll
-    for (int m = 0; m < KCH; ++m)
-      dst[m] = load_frag_buf<IN_BF16, MMA_BF16>(ur, ok ? rb + (uint32_t)(m * CB * ES) : kNoLoad);
+      for (int m = 0; m < KCH; ++m)
+        dst[m] = load_frag_buf<0, 0>(ur, ok ? rb + (uint32_t)((32 * (m >> 1) + 4 * (m & 1)) * 4) : kNoLoad);
+    } else {
+      const uint32_t rb = (uint32_t)(((rg_tb + st) * d + PER * g) * ES);
+#pragma unroll
+      for (int m = 0; m < KCH; ++m)
+        dst[m] = load_frag_buf<IN_BF16, MMA_BF16>(ur, ok ? rb + (uint32_t)(m * CB * ES) : kNoLoad);
+    }
   };
   const int wave_nst = max(min(wave * 4 * S + S, Tc) - wave * 4 * S, 0);
   const int nblk = (wave_nst + 3) >> 2;            // uniform in the wave
@@ -981,10 +1052,20 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   auto mma_tile = [&](f4v* acc, const FT* src) {
     acc[0] = f4v{0.f, 0.f, 0.f, 0.f};
     acc[1] = f4v{0.f, 0.f, 0.f, 0.f};
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int m = 0; m < KCH; ++m) {
-      mma_step<IN_BF16, MMA_BF16>(acc[0], src[m], wz[m]);
-      mma_step<IN_BF16, MMA_BF16>(acc[1], src[m], wsel[m]);
+      for (int kb = 0; kb < KB; ++kb) {
+        u4v xp[3];
+        split3(src[2 * kb], src[2 * kb + 1], xp);
+        mma_split3(acc[0], xp, wz3[kb]);
+        mma_split3(acc[1], xp, ws3[kb]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < KCH; ++m) {
+        mma_step<IN_BF16, MMA_BF16>(acc[0], src[m], wz[m]);
+        mma_step<IN_BF16, MMA_BF16>(acc[1], src[m], wsel[m]);
+      }
     }
   };
   // ---- on-chip tables; they need only the dictionary and C
@@ -994,22 +1075,25 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     const float cdq = __int_as_float(__builtin_amdgcn_ds_bpermute(dq << 2, __float_as_int(cj)));
     if (dc_on) DC[(tid / N) * p.DCS + tid % N] = i2v{dq, __float_as_int(cdq)};
   }
-  // SRC[k][i]: the source columns j (ascending) whose one sits in row i under
-  // dictionary entry k: (first eight as nibbles, count); SRC2 holds sources
-  // nine to sixteen
+  // SE[k][i]: the source columns j (ascending) whose one sits in row i under
+  // dictionary entry k, packed for the step loop:
+  //   x  byte m (m < 4): 4 * (m-th source), the lane offset of its value
+  //   y  byte m (m < 4): 1 if row i has an m-th source, else 0
+  //   z  nibbles: sources 5 to 12;  w  nibbles: sources 13 to 16, count << 24
   if (src_on) {
     const int iq = tid & 15;
-    unsigned lo = 0, hi = 0;
+    unsigned bx = 0, by = 0, bz = 0, bw = 0;
     int n = 0;
 #pragma unroll
     for (int jq = 0; jq < 16; ++jq) {
       const bool hit = drow[jq] == iq;
-      lo |= (hit && n < 8) ? (unsigned)jq << (4 * (n & 7)) : 0u;
-      hi |= (hit && n >= 8) ? (unsigned)jq << (4 * (n & 7)) : 0u;
+      bx |= (hit && n < 4) ? (unsigned)(4 * jq) << (8 * (n & 3)) : 0u;
+      by |= (hit && n < 4) ? 1u << (8 * (n & 3)) : 0u;
+      bz |= (hit && n >= 4 && n < 12) ? (unsigned)jq << (4 * ((n - 4) & 7)) : 0u;
+      bw |= (hit && n >= 12) ? (unsigned)jq << (4 * ((n - 12) & 3)) : 0u;
       n += hit ? 1 : 0;
     }
-    SRC[tid] = i2v{(int)lo, n};
-    SRC2[tid] = (int)hi;
+    SE[tid] = i4v{(int)bx, (int)by, (int)bz, (int)(bw | ((unsigned)n << 24))};
   }
   __syncthreads();                                 // tables ready
 
@@ -1021,9 +1105,15 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
 
   float hl = 0.f, msc = 1.f;
   int midx = jj;
-#pragma unroll
-  for (int k = 0; k < SMAX / 4; ++k) {
-    if (k >= nblk) break;
+  const int lbase = (lane & ~15) << 2;             // byte offset of this group's lane 0
+  float* wrow = Dbuf + j * TS + tb + gam;          // w_t of this lane's row, step tb
+  float* yrow = yloc + tb + gam;
+  // steps of the last group of this wave: every group of the wave has at
+  // least that many, so a block below it needs no per-step checks
+  const int nst_last = max(min(wave * 4 * S + 4 * S, Tc) - (wave * 4 + 3) * S, 0);
+
+  auto block = [&](auto full_tag, const int k) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int cu = k & 1, nx = cu ^ 1;
     if (k + 1 < nblk) {
       mma_tile(A[nx], U[nx]);                      // next tile, overlaps the scan below
@@ -1039,53 +1129,49 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       const int m = row_max(key);
       ks[r] = row_min(key == m ? i : 0x7fffffff);
     }
-    const int nb = nst - 4 * k;                    // steps left in this group
+    const int nb = FULL ? 4 : nst - 4 * k;         // steps left in this group
     if (a.k_out && j == 0)
       for (int r = 0; r < 4 && r < nb; ++r) a.k_out[gbase + tb + 4 * k + r] = ks[r];
     if (a.D_out && act)
       for (int r = 0; r < 4 && r < nb; ++r) a.D_out[(gbase + tb + 4 * k + r) * N + j] = Dr[r];
-    i2v srl[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) srl[r] = SRC[(r < nb ? ks[r] : 0) * 16 + j];
-    const int lbase = (lane & ~15) << 2;
     float yp[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool valid = r < nb;
-      const int t = tb + 4 * k + r;
-      const int kk = valid ? ks[r] : 0;
-      const i2v e = DC[kk * p.DCS + midx];
+      const bool valid = FULL || r < nb;
+      const int ksel = valid ? ks[r] : 0;
+      const i4v se = SE[ksel * 16 + j];
+      const i2v e = DC[ksel * 16 + midx];
       const float dm = __int_as_float(
           __builtin_amdgcn_ds_bpermute(lbase + (midx << 2), __float_as_int(Dr[r])));
       // h'_i = Bu_i + sum over the sources j of row i of D_j h_j, gathered
-      // from their lanes in ascending j
+      // from their lanes in ascending j; absent sources are weighted by zero
       const int vj = __float_as_int(Dr[r] * hl);
-      const int deg = act ? srl[r].y : 0;
-      const unsigned lo = (unsigned)srl[r].x;
-      float g[4];
+      const unsigned ax = (unsigned)se.x, ay = (unsigned)se.y;
+      float gv[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        g[m] = __int_as_float(
-            __builtin_amdgcn_ds_bpermute(lbase + (int)(((lo >> (4 * m)) & 15u) << 2), vj));
+        gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(lbase | (int)((ax >> (8 * m)) & 0xFFu), vj));
       float hn = bu[(4 * k + r) & 15];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) hn += m < deg ? g[m] : 0.f;
-      if (__builtin_amdgcn_ballot_w64(deg > 4)) {
-        const unsigned hi = (unsigned)SRC2[(r < nb ? ks[r] : 0) * 16 + j];
+      for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(gv[m], (float)((ay >> (8 * m)) & 0xFFu), hn);
+      const unsigned aw = (unsigned)se.w;
+      if (__builtin_amdgcn_ballot_w64(aw >= (5u << 24))) {
+        const int deg = (int)(aw >> 24);
+        const unsigned az = (unsigned)se.z;
         for (int m = 4; m < 16; ++m) {
-          const unsigned w = m < 8 ? lo >> (4 * m) : hi >> (4 * (m - 8));
+          const unsigned nib = m < 12 ? az >> (4 * (m - 4)) : aw >> (4 * (m - 12));
           const float gm = __int_as_float(
-              __builtin_amdgcn_ds_bpermute(lbase + (int)((w & 15u) << 2), vj));
+              __builtin_amdgcn_ds_bpermute(lbase | (int)((nib & 15u) << 2), vj));
           hn += m < deg ? gm : 0.f;
           if (!__builtin_amdgcn_ballot_w64(m + 1 < deg)) break;
         }
       }
-      if (valid) hl = hn;
       if (valid) {
+        hl = hn;
         msc *= dm;
         midx = e.x;
       }
-      if (valid && act) Dbuf[j * TS + t + gam] = __int_as_float(e.y) * msc;
+      if (valid && act) wrow[4 * k + r] = __int_as_float(e.y) * msc;
       yp[r] = cj * hl;
     }
     // refill this block's drive-term slots with the block four ahead
@@ -1096,16 +1182,24 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float yl = group_sum<16>(yp[r]);
-      if (r < nb && j == 0) yloc[tb + 4 * k + r + gam] = yl;
+      if ((FULL || r < nb) && j == 0) yrow[4 * k + r] = yl;
     }
+  };
+#pragma unroll
+  for (int k = 0; k < SMAX / 4; ++k) {
+    if (k >= nblk) break;
+    if (4 * k + 4 <= nst_last)
+      block(std::true_type{}, k);
+    else
+      block(std::false_type{}, k);
   }
   chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
 }
 
-template <int IN_BF16, int MMA_BF16, int KCH>
+template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT>
 __global__ __launch_bounds__(kThreads, 3) void pdssm_fused16_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  fused16_body<IN_BF16, MMA_BF16, KCH>(a, smem);
+  fused16_body<IN_BF16, MMA_BF16, KCH, SPLIT>(a, smem);
 }
 
 // Two entry points over one body: the register-resident fp32 selection paths

@@ -14,13 +14,13 @@ hipError_t launch_fused(const Args& a, hipStream_t st) {
   if (p.fused16) {
     const dim3 grid(p.tasks), block(kThreads);
     if (p.in_bf16)
-      hipLaunchKernelGGL((pdssm_fused16_kernel<1, 1, 4>), grid, block, p.lds_bytes, st, a);
+      hipLaunchKernelGGL((pdssm_fused16_kernel<1, 1, 4, 0>), grid, block, p.lds_bytes, st, a);
     else if (p.d == 64)
-      hipLaunchKernelGGL((pdssm_fused16_kernel<0, 0, 4>), grid, block, p.lds_bytes, st, a);
+      hipLaunchKernelGGL((pdssm_fused16_kernel<0, 0, 4, 1>), grid, block, p.lds_bytes, st, a);
     else if (p.d == 32)
-      hipLaunchKernelGGL((pdssm_fused16_kernel<0, 0, 2>), grid, block, p.lds_bytes, st, a);
+      hipLaunchKernelGGL((pdssm_fused16_kernel<0, 0, 2, 1>), grid, block, p.lds_bytes, st, a);
     else
-      hipLaunchKernelGGL((pdssm_fused16_kernel<0, 0, 1>), grid, block, p.lds_bytes, st, a);
+      hipLaunchKernelGGL((pdssm_fused16_kernel<0, 0, 1, 0>), grid, block, p.lds_bytes, st, a);
     return hipGetLastError();
   }
   if (p.in_bf16 && p.mma_bf16) {

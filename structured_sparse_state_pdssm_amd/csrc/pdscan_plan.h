@@ -84,7 +84,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
     p.TS = align_up(p.chunk, 4);
     if (p.TS % 32 != 4) p.TS += (36 - p.TS % 32) % 32;
   }
-  p.DCS = N + 1;
+  p.DCS = p.fused16 ? 16 : N + 1;   // the step-major kernel indexes with a shift
   p.nC = (L + p.chunk - 1) / p.chunk;
   p.NC = align_up(K + N, 16);
   p.KP = align_up(K, 4);
@@ -100,7 +100,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.off_yl = scan ? take((T + p.G) * 4) : 0;
   p.off_dict = scan ? 0 : take(K * N * 4);   // selection: P_idx gathers
   p.off_DC = scan ? take(K * p.DCS * 8) : 0;  // scan: (row, C[row]) pairs
-  p.off_SRC = p.fused16 ? take(K * 16 * 12) : 0;  // fused16: source columns of each row
+  p.off_SRC = p.fused16 ? take(K * 16 * 16) : 0;  // fused16: source columns of each row
   p.off_C = take(N * 4);
   p.off_bd = take(N * 4);
   p.off_slot = take(kThreads * 4);
