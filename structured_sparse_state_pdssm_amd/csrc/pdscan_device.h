@@ -314,7 +314,11 @@ constexpr int kChanBlock = MMA_BF16 ? 32 : 16;
 // pre-activations, stores.  rows >= rlim are not stored.
 template <int NCT>
 __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, const float* bdr,
-                                              int row0, int rlim, int lane, const SelDst& o) {
+                                              int row0, int rlim, int lane, const SelDst& o,
+                                              int ct0 = 0) {
+  // ct0: the first column tile held in acc; the score columns (K <= 64, at
+  // most four tiles) are always in the pass that starts at 0
+  const bool with_k = ct0 == 0;
   const int i = lane & 15, g = lane >> 4;
   const int K = p.K, N = p.N;
   // argmax per row: the largest score over the row's lanes, then the lowest
@@ -328,8 +332,8 @@ __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, con
   }
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const int col = 16 * ct + i;
-    if (16 * ct < K) {                     // uniform: tile holds score columns
+    const int col = 16 * (ct0 + ct) + i;
+    if (16 * (ct0 + ct) < K) {             // uniform: tile holds score columns
       const bool sc = col < K;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -347,7 +351,7 @@ __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, con
   }
   const int rb = row0 + 4 * g;   // first of this lane's four rows
   const bool full = rb + 4 <= rlim;
-  if (i == 0) {
+  if (with_k && i == 0) {
     if (o.kbuf) {
       if (full) *(i4v*)(o.kbuf + rb) = i4v{bk[0], bk[1], bk[2], bk[3]};
       else
@@ -358,7 +362,7 @@ __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, con
   }
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const int col = 16 * ct + i;
+    const int col = 16 * (ct0 + ct) + i;
     if (col >= K && col < K + N) {
       const int n = col - K;
       f4v dv;
@@ -375,7 +379,7 @@ __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, con
           if (rb + r < rlim) o.D_out[(o.gbase + rb + r) * N + n] = dv[r];
     }
   }
-  if (o.P_out) {
+  if (with_k && o.P_out) {
     for (int r = 0; r < 4; ++r)
       for (int gg = 0; gg < 4; ++gg) {
         const int kr = __shfl(bk[r], 16 * gg, 64);
@@ -499,8 +503,100 @@ __device__ __forceinline__ void select_rows_any(const Args& a, int s_u, int h, i
   }
 }
 
+// bf16 inputs with a wide contraction (d a multiple of 32, too many weights
+// to keep in registers): two 16-row tiles at a time against up to four
+// column tiles per pass, with the u and weight fragments of the next two
+// 32-channel blocks in flight in a three-slot register ring while the current
+// block multiplies.
+template <int NCT>
+__device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, int c0, int rbeg,
+                                                 int rend, int lane, const SelDst& o) {
+  const Plan& p = a.p;
+  const int i = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N, d = p.d;
+  const int KB = d >> 5;                           // 32-channel blocks
+  constexpr int CP = NCT < 4 ? NCT : 4;            // column tiles per pass
+  const rsrc_t rs = make_rsrc((const uint16_t*)a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
+  const rsrc_t rz = make_rsrc((const uint16_t*)a.W_d + (size_t)h * N * d, (uint32_t)(N * d * 2));
+  const int Tc = min(p.chunk, p.L - c0);
+  const rsrc_t ur = make_rsrc((const uint16_t*)a.u + ((size_t)s_u * p.L + c0) * d, (uint32_t)(Tc * d * 2));
+
+  for (int row0 = rbeg; row0 < rend; row0 += 32) {
+    uint32_t uoff[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int row = row0 + 16 * rt + i;
+      uoff[rt] = row < rend ? (uint32_t)((row * d + 8 * g) * 2) : kNoLoad;
+    }
+#pragma unroll
+    for (int ct0 = 0; ct0 < NCT; ct0 += CP) {
+      // weight rows: W_sel for columns < K, W_d for K <= column < K + N.  The
+      // buffer descriptor must be uniform, so a tile reads W_sel, W_d, or
+      // (the one tile that straddles K) both with the other lanes zeroed.
+      float bdr[CP];
+      uint32_t soff[CP], zoff[CP];                 // byte offsets (kNoLoad: none)
+#pragma unroll
+      for (int ct = 0; ct < CP; ++ct) {
+        const int col = 16 * (ct0 + ct) + i;
+        soff[ct] = col < K ? (uint32_t)((col * d + 8 * g) * 2) : kNoLoad;
+        zoff[ct] = (col >= K && col < K + N) ? (uint32_t)(((col - K) * d + 8 * g) * 2) : kNoLoad;
+        bdr[ct] = (col >= K && col < K + N) ? a.b_d[(size_t)h * N + col - K] : 0.f;
+      }
+      constexpr int RING = 3;                      // blocks in flight
+      u4v Ar[RING][2], Br[RING][CP];
+      auto issue = [&](int slot_m, u4v* A2, u4v* Bn) {
+        const bool ok = slot_m < KB;
+        const uint32_t mo = (uint32_t)(slot_m * 64);   // 32 channels of bf16
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          A2[rt] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ur, (ok && uoff[rt] != kNoLoad) ? uoff[rt] + mo : kNoLoad, 0, 0));
+#pragma unroll
+        for (int ct = 0; ct < CP; ++ct) {
+          const int c16 = 16 * (ct0 + ct);         // uniform
+          const uint32_t so = (ok && soff[ct] != kNoLoad) ? soff[ct] + mo : kNoLoad;
+          const uint32_t zo = (ok && zoff[ct] != kNoLoad) ? zoff[ct] + mo : kNoLoad;
+          if (c16 + 16 <= K) {
+            Bn[ct] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0));
+          } else if (c16 >= K) {
+            Bn[ct] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0));
+          } else {
+            Bn[ct] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0)) |
+                     __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0));
+          }
+        }
+      };
+      f4v acc[2][CP];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CP; ++ct) acc[rt][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < RING - 1; ++q) issue(q, Ar[q], Br[q]);
+      for (int mb = 0; mb < KB; mb += RING) {
+#pragma unroll
+        for (int q = 0; q < RING; ++q) {
+          issue(mb + q + RING - 1, Ar[(q + RING - 1) % RING], Br[(q + RING - 1) % RING]);
+          if (mb + q < KB) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+              for (int ct = 0; ct < CP; ++ct)
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf8v, Ar[q][rt]), __builtin_bit_cast(bf8v, Br[q][ct]), acc[rt][ct], 0, 0, 0);
+          }
+        }
+      }
+      tile_epilogue<CP>(p, acc[0], bdr, row0, rend, lane, o, ct0);
+      if (row0 + 16 < rend) tile_epilogue<CP>(p, acc[1], bdr, row0 + 16, rend, lane, o, ct0);
+    }
+  }
+}
+
 // Shapes with a register-resident fast path.
-enum SelPath : int { kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3 };
+// kSelDeep + n: the deep bf16 path with n column tiles (n even; a shape with
+// fewer real column tiles computes zero tiles that are never written).
+enum SelPath : int { kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3, kSelDeep = 16 };
 
 template <int IN_BF16, int MMA_BF16, int PATH>
 __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, int c0, int rbeg,
@@ -511,6 +607,8 @@ __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, i
     select_rows<0, 0, 1, 1>(a, s_u, h, c0, rbeg, rend, lane, o);
   else if constexpr (PATH == kSelBF16D128N3 && IN_BF16 && MMA_BF16)
     select_rows<1, 1, 4, 3>(a, s_u, h, c0, rbeg, rend, lane, o);
+  else if constexpr (PATH > kSelDeep && IN_BF16 && MMA_BF16)
+    select_rows_deep<PATH - kSelDeep>(a, s_u, h, c0, rbeg, rend, lane, o);
   else
     select_rows_any<IN_BF16, MMA_BF16>(a, s_u, h, c0, rbeg, rend, lane, o);
 }
@@ -809,12 +907,15 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   // (selection mode never reads Bu; its pointer may be null there)
   const rsrc_t bur = make_rsrc(MODE == kModeSelect ? (const float*)nullptr : a.Bu + gbase * N,
                                MODE == kModeSelect ? 0u : (uint32_t)(Tc * N * 4));
+  // (the deep selection path needs the registers itself: its first block
+  // follows the selection instead)
   float bu[kBuBlock];
-  if constexpr (MODE != kModeSelect) {
+  auto first_bu = [&]() {
 #pragma unroll
     for (int q = 0; q < kBuBlock; ++q)
       bu[q] = buf_f32(bur, (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad);
-  }
+  };
+  if constexpr (MODE != kModeSelect && PATH < kSelDeep) first_bu();
 
   // ---- per-head constants
   if constexpr (MODE == kModeSelect) {
@@ -854,6 +955,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     select_dispatch<IN_BF16, MMA_BF16, PATH>(a, s_u, h, c0, wr0, wr1, lane, o);
   }
   if constexpr (MODE == kModeSelect) return;
+  if constexpr (PATH >= kSelDeep) first_bu();
   WAVE_SYNC();   // this wave's k* / D rows are read back by its own lane groups
 
   // ---- phase A: each lane group runs its sub-chunk [tb, te) from a zero
@@ -1225,6 +1327,7 @@ static inline int sel_path(const Plan& p) {
   if (!p.in_bf16 && p.d == 64 && nct == 2) return kSelF32D64N2;
   if (!p.in_bf16 && p.d == 16 && nct == 1) return kSelF32D16N1;
   if (p.in_bf16 && p.mma_bf16 && p.d == 128 && nct == 3) return kSelBF16D128N3;
+  if (p.in_bf16 && p.mma_bf16 && p.d % 32 == 0 && p.d >= 256) return kSelDeep + ((nct + 1) & ~1);
   return kSelAny;
 }
 

@@ -7,6 +7,21 @@ namespace pdscan {
 
 void launch_clear(const Args& a, hipStream_t st);
 
+template <int MODE, int NCT>
+static void launch_deep_n(const Args& a, hipStream_t st, int npt) {
+  if (npt == 64) launch_kernel<MODE, 1, 1, kSelDeep + NCT, 64, true>(a, st);
+  else launch_kernel<MODE, 1, 1, kSelDeep + NCT, 0, true>(a, st);
+}
+template <int MODE>
+static void launch_deep(const Args& a, hipStream_t st, int nct, int npt) {
+  switch (nct) {
+    case 2: launch_deep_n<MODE, 2>(a, st, npt); break;
+    case 4: launch_deep_n<MODE, 4>(a, st, npt); break;
+    case 6: launch_deep_n<MODE, 6>(a, st, npt); break;
+    default: launch_deep_n<MODE, 8>(a, st, npt); break;
+  }
+}
+
 hipError_t launch_fused(const Args& a, hipStream_t st) {
   const Plan& p = a.p;
   const int path = sel_path(p), npt = npt_of(p);
@@ -28,6 +43,8 @@ hipError_t launch_fused(const Args& a, hipStream_t st) {
       launch_kernel<kModeFused, 1, 1, kSelBF16D128N3, 32, true>(a, st);
     else if (path == kSelBF16D128N3)
       launch_kernel<kModeFused, 1, 1, kSelBF16D128N3, 0, true>(a, st);
+    else if (path > kSelDeep)
+      launch_deep<kModeFused>(a, st, path - kSelDeep, npt);
     else if (npt == 64)
       launch_kernel<kModeFused, 1, 1, kSelAny, 64, true>(a, st);
     else
