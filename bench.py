@@ -29,15 +29,18 @@ METRIC = "state-updates/sec (B·H·L·N) PD-SSM fwd select+scan; achieved HBM GB
 CSRC = os.path.join(ROOT, "structured_sparse_state_pdssm_amd", "csrc")
 
 
+# the sources the benchmarked forward kernel is built from
+FWD_SOURCES = ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_fused.hip")
+
+
 def kernel_hash() -> str:
-    """Hash of the library sources: ties a stored counter summary to the
-    kernel it was measured on."""
+    """Hash of the forward kernel's sources: ties a stored counter summary to
+    the kernel it was measured on."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    for name in FWD_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
