@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the hard-selection PD-SSM forward pass.
+"""fp64 CPU oracle for the hard-selection PD-SSM forward pass and the
+gradient through its scan for fixed selections.
 
 TEST INFRASTRUCTURE: imported only by the tests, the smoke check and the
 benchmark's CPU-baseline leg; never by the product path."""
@@ -9,6 +10,8 @@ from .pdssm_oracle import (  # noqa: F401
     pd_apply,
     pd_compose,
     scan,
+    scan_states,
+    scan_vjp,
     scores,
     select,
     sigmoid,

@@ -23,6 +23,11 @@ It is the plain definition, written out slowly:
 Everything is upcast exactly to fp64 first.  ``scan`` builds the dense N x N
 transition of every step and multiplies; it never uses the sparse structure.
 
+``scan_vjp`` is the gradient of a scalar loss through that recurrence for
+fixed selections (the adjoint recurrence with the dense transposed
+transitions); ``scan_states`` returns the state after every step, which the
+gradient with respect to the diagonal needs.
+
 ``three_phase`` is a separate fp64 evaluation that follows the pages' kernel
 description (same summary, methodology item 3: phase A runs independent
 sequential recurrences inside chunks, phase B prefix-scans the chunk
@@ -119,6 +124,76 @@ def scan(k_star, dict_idx, D, Bu, C, h0=None):
         x = np.matmul(A, x[..., None])[..., 0] + Bu[:, :, t]
         y[:, :, t] = (C[None] * x).sum(-1)
     return y, x
+
+
+def scan_states(k_star, dict_idx, D, Bu, h0=None):
+    """The state after every step of ``scan``'s recurrence, fp64 [B,H,L,N]
+    (h_t for t = 0..L-1; h_{L-1} is h_L)."""
+    k_star = np.asarray(k_star)
+    dict_idx = np.asarray(dict_idx)
+    D = np.asarray(D, dtype=F64)
+    Bu = np.asarray(Bu, dtype=F64)
+    B, H, L = k_star.shape
+    N = dict_idx.shape[-1]
+    x = np.zeros((B, H, N), dtype=F64) if h0 is None else np.array(h0, dtype=F64)
+    out = np.zeros((B, H, L, N), dtype=F64)
+    heads = np.arange(H)[None, :]
+    bi = np.arange(B)[:, None, None]
+    hi = np.arange(H)[None, :, None]
+    cols = np.arange(N)[None, None, :]
+    for t in range(L):
+        rows = dict_idx[heads, k_star[:, :, t]]
+        A = np.zeros((B, H, N, N), dtype=F64)
+        A[bi, hi, rows, cols] = D[:, :, t]
+        x = np.matmul(A, x[..., None])[..., 0] + Bu[:, :, t]
+        out[:, :, t] = x
+    return out
+
+
+def scan_vjp(k_star, dict_idx, D, Bu, C, h0, g_y, g_hL=None):
+    """Gradient of a scalar loss through ``scan`` for fixed selections.
+
+    Given g_y = dLoss/dy [B,H,L] and g_hL = dLoss/dh_L [B,H,N] (None: zero),
+    returns dLoss/d(Bu, D, h0, C) as fp64 arrays [B,H,L,N], [B,H,L,N],
+    [B,H,N], [H,N].  The selections k* are held fixed: the argmax has no
+    derivative, and the pages' surrogate for it ("Flash PD-SSM" summary,
+    methodology item 2, straight-through estimator) is not part of this.
+
+    The adjoint recurrence of h_t = A_t h_{t-1} + Bu_t, y_t = C h_t, run
+    backwards with the dense transposed transitions:
+        lam_{L-1} = C^T g_y[L-1] + g_hL,
+        lam_t     = C^T g_y[t] + A_{t+1}^T lam_{t+1},
+    and then dBu_t = lam_t, dA_t = lam_t h_{t-1}^T (read at the entries
+    A_t[idx[j], j] = D_t[j]), dh0 = A_0^T lam_0, dC = sum_{b,t} g_y h_t^T."""
+    k_star = np.asarray(k_star)
+    dict_idx = np.asarray(dict_idx)
+    D = np.asarray(D, dtype=F64)
+    C = np.asarray(C, dtype=F64)
+    g_y = np.asarray(g_y, dtype=F64)
+    B, H, L = k_star.shape
+    N = dict_idx.shape[-1]
+    h0f = np.zeros((B, H, N), dtype=F64) if h0 is None else np.array(h0, dtype=F64)
+    states = scan_states(k_star, dict_idx, D, Bu, h0f)
+    lam = np.zeros((B, H, N), dtype=F64) if g_hL is None else np.array(g_hL, dtype=F64)
+    g_Bu = np.zeros((B, H, L, N), dtype=F64)
+    g_D = np.zeros((B, H, L, N), dtype=F64)
+    heads = np.arange(H)[None, :]
+    bi = np.arange(B)[:, None, None]
+    hi = np.arange(H)[None, :, None]
+    cols = np.arange(N)[None, None, :]
+    for t in range(L - 1, -1, -1):
+        lam = lam + C[None] * g_y[:, :, t, None]
+        g_Bu[:, :, t] = lam
+        rows = dict_idx[heads, k_star[:, :, t]]
+        A = np.zeros((B, H, N, N), dtype=F64)
+        A[bi, hi, rows, cols] = D[:, :, t]
+        h_prev = states[:, :, t - 1] if t > 0 else h0f
+        dA = lam[..., :, None] * h_prev[..., None, :]       # [B,H,N,N]
+        g_D[:, :, t] = dA[bi, hi, rows, cols]
+        lam = np.matmul(np.swapaxes(A, -1, -2), lam[..., None])[..., 0]
+    g_h0 = lam
+    g_C = np.einsum("bhl,bhln->hn", g_y, states)
+    return g_Bu, g_D, g_h0, g_C
 
 
 def forward(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0=None, u_shared=False):
