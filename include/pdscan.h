@@ -115,6 +115,41 @@ int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* 
               int32_t* k_star, float* D, float* y, float* h_L,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunked scan that also writes the state after every step.
+ *   Arguments as in pdssm_scan_fwd (same workspace size), plus
+ *   H_all [B,H,L,N] (out): h_t for t = 0..L-1, the states the gradient pass
+ *   below reads.  Each lane group replays its sub-chunk from its true entering
+ *   state, so y here is the sequential recurrence itself. */
+int pdssm_scan_states(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
+                      const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
+                      const float* h0, float* y, float* h_L, float* H_all, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pdssm_scan_bwd needs for these dims and chunk length
+ * (PDSSM_EUNSUPPORTED when its on-chip layout, about chunk * N * 4 bytes
+ * plus the dictionary, exceeds 64 KiB). */
+int pdssm_scan_bwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes);
+
+/* Gradient of a scalar loss through the scan for fixed selections
+ * ("Flash PD-SSM" summary, methodology item 2 covers the selection's own
+ * surrogate gradient, which is not computed here: k* carries no gradient).
+ * Given dLoss/dy and dLoss/dh_L, the adjoint recurrence
+ *   lam_{L-1} = C g_y[L-1] + g_hL,  lam_t = C g_y[t] + A_{t+1}^T lam_{t+1}
+ * gives
+ *   g_Bu [B,H,L,N] = lam_t                              (out, required)
+ *   g_D  [B,H,L,N] = lam_t[dict[h,k*_t,j]] h_{t-1}[j]   (out, required)
+ *   g_h0 [B,H,N]   = A_0^T lam_0                        (out, optional)
+ *   g_C  [H,N]     = sum over b and t of g_y h_t        (out, required)
+ * Inputs: k_star, dict_idx, D, C and h0 (NULL = zero) as in the forward
+ * call; H_all [B,H,L,N] the forward states (pdssm_scan_states); g_y [B,H,L];
+ * g_hL [B,H,N] or NULL (zero).  chunk: as in the forward scan.  g_C is summed
+ * in a fixed order, so results are bit-identical from run to run. */
+int pdssm_scan_bwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
+                   const int32_t* dict_idx, const float* D, const float* C, const float* h0,
+                   const float* H_all, const float* g_y, const float* g_hL, float* g_Bu,
+                   float* g_D, float* g_h0, float* g_C, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* Static text for a status code. */
 const char* pdssm_status_str(int status);
 

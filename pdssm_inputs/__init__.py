@@ -10,6 +10,9 @@ parameters, and both are described where they happen:
   reasonable floating-point precision);
 * the driving term ``Bu = W_b u``, which the forward pass receives as an input.
 
+``upstream_grads`` draws the loss gradients (dLoss/dy, dLoss/dh_L) that the
+gradient pass through the scan takes as inputs.
+
 Workloads follow the pages' experiment descriptions only loosely (they print no
 inputs); the recipes are synthetic stand-ins, see ``configs.py``.
 """
@@ -22,4 +25,5 @@ from .gen import (  # noqa: F401
     bf16_round,
     generate,
     top2_margin,
+    upstream_grads,
 )

@@ -236,3 +236,12 @@ def generate(cfg: Config, *, threads: int | None = None) -> Inputs:
     return Inputs(cfg=cfg, u=u, W_sel=W_sel, W_d=W_d, W_b=W_b, b_d=b_d,
                   dict_idx=dic, C=C, h0=h0, Bu=Bu,
                   rounds=max(r[0] for r in res), redrawn_rows=sum(r[1] for r in res))
+
+
+def upstream_grads(B, H, L, N, seed):
+    """Seeded dLoss/dy [B,H,L] and dLoss/dh_L [B,H,N] (standard normal, fp32)
+    for the gradient pass through the scan."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x6272]))
+    g_y = rng.standard_normal((B, H, L)).astype(np.float32)
+    g_hL = rng.standard_normal((B, H, N)).astype(np.float32)
+    return g_y, g_hL

@@ -205,6 +205,76 @@ def pdssm_fwd(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0=None, chunk=128, want_k=Fa
     return res
 
 
+def scan_bwd_workspace_bytes(dims, chunk):
+    n = ctypes.c_size_t(0)
+    _check(lib.pdssm_scan_bwd_workspace_bytes(ctypes.byref(dims), int(chunk), ctypes.byref(n)))
+    return n.value
+
+
+def _scan_dims(k_star, dict_idx):
+    B, H, L = k_star.shape
+    _, K, N = dict_idx.shape
+    return make_dims(B, H, L, N, K, 8)
+
+
+def pdssm_scan_states(k_star, dict_idx, D, Bu, C, h0=None, chunk=128, workspace=None, out=None):
+    """Chunked scan that also returns the state after every step.  Returns
+    (y [B,H,L], h_L [B,H,N], H_all [B,H,L,N])."""
+    torch = _torch()
+    _need(k_star, "k_star", torch.int32)
+    _need(dict_idx, "dict_idx", torch.int32)
+    for t, n in ((D, "D"), (Bu, "Bu"), (C, "C")):
+        _need(t, n, torch.float32)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    dims = _scan_dims(k_star, dict_idx)
+    B, H, L, N = dims.B, dims.H, dims.L, dims.N
+    dev = k_star.device
+    ws = _workspace(scan_workspace_bytes(dims, chunk), dev, workspace)
+    o = out or {}
+    res = {}
+    for name, shape in (("y", (B, H, L)), ("h_L", (B, H, N)), ("H_all", (B, H, L, N))):
+        t = o.get(name)
+        res[name] = torch.empty(shape, dtype=torch.float32, device=dev) if t is None else _need(t, name)
+    _check(lib.pdssm_scan_states(ctypes.byref(dims), int(chunk), _ptr(k_star), _ptr(dict_idx), _ptr(D),
+                                 _ptr(Bu), _ptr(C), _ptr(h0), _ptr(res["y"]), _ptr(res["h_L"]),
+                                 _ptr(res["H_all"]), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev)))
+    return res["y"], res["h_L"], res["H_all"]
+
+
+def pdssm_scan_bwd(k_star, dict_idx, D, C, H_all, g_y, h0=None, g_hL=None, chunk=128,
+                   want_h0=True, workspace=None, out=None):
+    """Gradient through the scan for fixed selections.  Returns
+    dict(g_Bu [B,H,L,N], g_D [B,H,L,N], g_C [H,N][, g_h0 [B,H,N]])."""
+    torch = _torch()
+    _need(k_star, "k_star", torch.int32)
+    _need(dict_idx, "dict_idx", torch.int32)
+    for t, n in ((D, "D"), (C, "C"), (H_all, "H_all"), (g_y, "g_y")):
+        _need(t, n, torch.float32)
+    for t, n in ((h0, "h0"), (g_hL, "g_hL")):
+        if t is not None:
+            _need(t, n, torch.float32)
+    dims = _scan_dims(k_star, dict_idx)
+    B, H, L, N = dims.B, dims.H, dims.L, dims.N
+    dev = k_star.device
+    ws = _workspace(scan_bwd_workspace_bytes(dims, chunk), dev, workspace)
+    o = out or {}
+    res = {}
+    for name, shape, want in (("g_Bu", (B, H, L, N), True), ("g_D", (B, H, L, N), True),
+                              ("g_h0", (B, H, N), want_h0), ("g_C", (H, N), True)):
+        if want:
+            t = o.get(name)
+            res[name] = torch.empty(shape, dtype=torch.float32, device=dev) if t is None else _need(t, name)
+    _check(lib.pdssm_scan_bwd(ctypes.byref(dims), int(chunk), _ptr(k_star), _ptr(dict_idx), _ptr(D),
+                              _ptr(C), _ptr(h0), _ptr(H_all), _ptr(g_y), _ptr(g_hL), _ptr(res["g_Bu"]),
+                              _ptr(res["g_D"]), _ptr(res.get("g_h0")), _ptr(res["g_C"]), _ptr(ws),
+                              ctypes.c_size_t(ws.numel()), _stream(dev)))
+    return res
+
+
+__all__ += ["scan_bwd_workspace_bytes", "pdssm_scan_states", "pdssm_scan_bwd"]
+
+
 def workspace_error_flag(workspace):
     """Nonzero if a look-back wait in the last call on ``workspace`` gave up
     (read after synchronising).  Header word 1 of the workspace."""

@@ -16,8 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpdscan.so")
 
 SOURCES = ["pdscan_api.cpp", "pdscan_launch_select.hip", "pdscan_launch_scan.hip",
-           "pdscan_launch_fused.hip"]
-HEADERS = ["pdscan_plan.h", "pdscan_device.h"]
+           "pdscan_launch_fused.hip", "pdscan_launch_bwd.hip"]
+HEADERS = ["pdscan_plan.h", "pdscan_device.h", "pdscan_bwd_plan.h", "pdscan_bwd.h"]
 
 COMPILE_FLAGS = [
     "-O3", "-std=c++17", "-fPIC",

@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "pdscan.h"
+#include "pdscan_bwd_plan.h"
 #include "pdscan_plan.h"
 
 namespace pdscan {
@@ -18,6 +19,7 @@ namespace pdscan {
 hipError_t launch_select(const Args& a, hipStream_t st);
 hipError_t launch_scan(const Args& a, hipStream_t st);
 hipError_t launch_fused(const Args& a, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs& a, float* g_C, hipStream_t st);
 }
 
 using pdscan::Plan;
@@ -252,6 +254,84 @@ int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* 
   a.Bu = Bu; a.C = C; a.h0 = h0; a.k_out = k_star; a.D_out = D;
   a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
   return dispatch(pdscan::kModeFused, a, stream);
+}
+
+int pdssm_scan_states(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
+                      const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
+                      const float* h0, float* y, float* h_L, float* H_all, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk))) return rc;
+  if (workspace_bytes < p.ws_bytes)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"k_star", k_star, z.k}, {"dict_idx", dict_idx, z.dict}, {"D", D, z.D},
+                      {"Bu", Bu, z.Bu}, {"C", C, z.C}, {"h0", h0, z.h0}};
+  const Range out[] = {{"y", y, z.y}, {"h_L", h_L, z.hL}, {"H_all", H_all, z.D},
+                       {"workspace", workspace, p.ws_bytes}};
+  static const char* const req[] = {"k_star", "dict_idx", "D", "Bu", "C", "y", "h_L", "H_all",
+                                    "workspace", nullptr};
+  if ((rc = check_ptrs(in, 6, out, 4, req))) return rc;
+  pdscan::Args a = {};
+  a.p = p;
+  a.dict = dict_idx; a.k_in = k_star; a.D_in = D; a.Bu = Bu; a.C = C; a.h0 = h0;
+  a.y = y; a.hL = h_L; a.H_all = H_all; a.ws = (unsigned char*)workspace;
+  return dispatch(pdscan::kModeScan, a, stream);
+}
+
+int pdssm_scan_bwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  if (!bytes) return fail(PDSSM_EINVAL, "bytes is NULL");
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk))) return rc;
+  pdscan::BwdLds l;
+  if (!pdscan::make_bwd_lds(p, l))
+    return fail(PDSSM_EUNSUPPORTED, "chunk=%d with N=%d K=%d needs %d bytes of on-chip memory in the "
+                "gradient pass (limit %d)", p.chunk, dims->N, dims->K, l.bytes, pdscan::kMaxLds);
+  *bytes = pdscan::bwd_ws_bytes(p);
+  return PDSSM_OK;
+}
+
+int pdssm_scan_bwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
+                   const int32_t* dict_idx, const float* D, const float* C, const float* h0,
+                   const float* H_all, const float* g_y, const float* g_hL, float* g_Bu,
+                   float* g_D, float* g_h0, float* g_C, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk))) return rc;
+  pdscan::BwdLds l;
+  if (!pdscan::make_bwd_lds(p, l))
+    return fail(PDSSM_EUNSUPPORTED, "chunk=%d with N=%d K=%d needs %d bytes of on-chip memory in the "
+                "gradient pass (limit %d)", p.chunk, dims->N, dims->K, l.bytes, pdscan::kMaxLds);
+  const size_t need = pdscan::bwd_ws_bytes(p);
+  if (workspace_bytes < need)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"k_star", k_star, z.k}, {"dict_idx", dict_idx, z.dict}, {"D", D, z.D},
+                      {"C", C, z.C},           {"h0", h0, z.h0},           {"H_all", H_all, z.D},
+                      {"g_y", g_y, z.y},       {"g_hL", g_hL, z.hL}};
+  const Range out[] = {{"g_Bu", g_Bu, z.Bu}, {"g_D", g_D, z.D},          {"g_h0", g_h0, z.h0},
+                       {"g_C", g_C, z.C},    {"workspace", workspace, need}};
+  static const char* const req[] = {"k_star", "dict_idx", "D", "C", "H_all", "g_y", "g_Bu",
+                                    "g_D", "g_C", "workspace", nullptr};
+  if ((rc = check_ptrs(in, 8, out, 5, req))) return rc;
+  pdscan::BwdArgs a = {};
+  a.p = p;
+  a.l = l;
+  a.ws_gc = pdscan::bwd_ws_gc(p);
+  a.k_star = k_star; a.dict = dict_idx; a.D = D; a.C = C; a.h0 = h0; a.H_all = H_all;
+  a.g_y = g_y; a.g_hL = g_hL; a.g_Bu = g_Bu; a.g_D = g_D; a.g_h0 = g_h0;
+  a.ws = (unsigned char*)workspace;
+  const hipError_t e = pdscan::launch_bwd(a, g_C, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return PDSSM_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,275 @@
+// Gradient through the chunked scan for fixed selections (device code).
+//
+// With h_t = A_t h_{t-1} + Bu_t and y_t = C h_t, a scalar loss with
+// dLoss/dy_t = g_y[t] and dLoss/dh_L = g_hL has the adjoint recurrence
+//   lam_{L-1} = C g_y[L-1] + g_hL,   lam_t = C g_y[t] + A_{t+1}^T lam_{t+1},
+// and dBu_t = lam_t, dD_t[j] = lam_t[idx_t[j]] h_{t-1}[j],
+// dh0 = A_0^T lam_0, dC = sum over batch and steps of g_y[t] h_t.
+// A_t^T of a column-one-hot-times-diagonal map is a gather,
+// (A_t^T v)_j = D_t[j] v[idx_t[j]], so the adjoint runs backwards in time
+// through maps (src, w, b): v -> w .* v[src] + b, which compose in O(N)
+// (index gather, scale product) like the forward maps.  The three phases of
+// the forward scan ("Flash PD-SSM" summary, methodology item 3) are mirrored:
+// each group of a chunk composes the map of its sub-chunk from its right end,
+// the groups' maps are combined right to left, the chunks' adjoint carries
+// are resolved by a decoupled look-back towards later chunks, and every group
+// then replays its sub-chunk from its true entering adjoint, emitting the
+// gradients.  Forward states h_t are an input (the states variant of the
+// forward scan writes them).
+#pragma once
+
+#include "pdscan_bwd_plan.h"
+#include "pdscan_device.h"
+
+namespace pdscan {
+
+// value of lane `src` of this lane's group (group lanes start at `base`)
+__device__ __forceinline__ float grp_gather(float v, int base, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((base + src) << 2, __float_as_int(v)));
+}
+__device__ __forceinline__ int grp_gather_i(int v, int base, int src) {
+  return __builtin_amdgcn_ds_bpermute((base + src) << 2, v);
+}
+
+// Adjoint map words one lane of the look-back wave loads per batch.
+constexpr int kBwdLookBatch = 4;
+
+__global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Plan& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = p.N, K = p.K, S = p.S, T = p.chunk, G = p.G, NP = p.NP;
+  const int BH = p.B * p.H;
+  int* dic = (int*)(smem + a.l.off_dic);           // [K][N] dictionary of the head
+  float* Dl = (float*)(smem + a.l.off_D);          // [T][N] diagonals of the chunk
+  int* kl = (int*)(smem + a.l.off_k);              // [T] selections
+  float* gyl = (float*)(smem + a.l.off_gy);        // [T] output gradients
+  float* Cs = (float*)(smem + a.l.off_C);
+  int* sSrc = (int*)(smem + a.l.off_s);
+  float* sW = (float*)(sSrc + G * N);
+  float* sB = sW + G * N;
+  int* pSrc = (int*)(smem + a.l.off_p);
+  float* pW = (float*)(pSrc + G * N);
+  float* pB = pW + G * N;
+  float* slots = (float*)(smem + a.l.off_slot);    // [G][NP] entering adjoints
+  float* Hs = (float*)(smem + a.l.off_H);
+  float* gcs = (float*)(smem + a.l.off_gc);        // [G][N] dC partials
+  int* misc = (int*)(smem + a.l.off_misc);
+  uint32_t* hdr = (uint32_t*)a.ws;
+  uint64_t* agg = (uint64_t*)(a.ws + p.ws_agg);
+  uint64_t* inc = (uint64_t*)(a.ws + p.ws_inc);
+
+  // Tickets hand out chunks from the last one down: a chunk waits only for
+  // later chunks, which took their tickets first.
+  if (tid == 0) misc[0] = (int)atomicAdd(&hdr[kWsTicket], 1u);
+  __syncthreads();
+  const int task = misc[0];
+  const int c = p.nC - 1 - task / BH, s = task % BH;
+  const int h = s % p.H;
+  const int c0 = c * T;
+  const int Tc = min(T, p.L - c0);
+  const size_t gbase = (size_t)s * p.L + c0;
+
+  for (int q = tid; q < K * N; q += kThreads) dic[q] = a.dict[(size_t)h * K * N + q];
+  for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
+  for (int q = tid; q < Tc; q += kThreads) {
+    kl[q] = a.k_star[gbase + q];
+    gyl[q] = a.g_y[gbase + q];
+  }
+  for (int q = tid; q < Tc * N; q += kThreads) Dl[q] = a.D[gbase * N + q];
+  __syncthreads();
+
+  const int gpw = 64 / NP;
+  const int gl = lane / NP, j = lane % NP;
+  const int gam = wave * gpw + gl;                 // this lane's group (sub-chunk)
+  const int base = lane - j;                       // first lane of the group
+  const bool act = j < N;
+  const int tb = gam * S, te = min(tb + S, Tc);
+
+  // ---- local pass: from a zero adjoint at the sub-chunk's right end, the
+  // map (src, w, b) from the adjoint entering there to the one leaving on the
+  // left: per step x <- A_t^T (x + C g_y[t]) and (src, w) <- A_t^T o (src, w)
+  float x = 0.f, w = act ? 1.f : 0.f;
+  int src = j;
+  for (int t = te - 1; t >= tb; --t) {
+    const int r = act ? dic[kl[t] * N + j] : j;
+    const float d = act ? Dl[t * N + j] : 0.f;
+    const float lam = act ? x + Cs[j] * gyl[t] : 0.f;
+    const float lr = grp_gather(lam, base, r);
+    const int sr = grp_gather_i(src, base, r);
+    const float wr = grp_gather(w, base, r);
+    x = d * lr;
+    src = sr;
+    w = d * wr;
+  }
+
+  // ---- combine right to left: group g ends up with the map of groups
+  // g..G-1 (the later groups' maps applied first); composing a o b reads b
+  // at a's sources
+  int cs = src;
+  float cw = w, cb = x;
+  for (int o = 1; o < G; o <<= 1) {
+    if (act) {
+      sSrc[gam * N + j] = cs;
+      sW[gam * N + j] = cw;
+      sB[gam * N + j] = cb;
+    }
+    __syncthreads();
+    int ns = cs;
+    float nw = cw, nb = cb;
+    if (act && gam + o < G) {
+      const int q = (gam + o) * N + cs;
+      ns = sSrc[q];
+      nw = cw * sW[q];
+      nb = cw * sB[q] + cb;
+    }
+    __syncthreads();
+    cs = ns;
+    cw = nw;
+    cb = nb;
+  }
+  if (act) {
+    pSrc[gam * N + j] = cs;
+    pW[gam * N + j] = cw;
+    pB[gam * N + j] = cb;
+  }
+  __syncthreads();
+
+  // ---- adjoint carries between chunks (wave 0): publish this chunk's map,
+  // look towards later chunks for the adjoint entering this one, publish the
+  // adjoint it passes on
+  if (wave == 0) {
+    const bool on = lane < N;
+    const int ln = on ? lane : 0;
+    uint64_t* my = agg + ((size_t)c * BH + s) * 3 * N;
+    if (on) {
+      put_tagged(my + lane, (uint32_t)pSrc[ln]);
+      put_tagged(my + N + lane, __float_as_uint(pW[ln]));
+      put_tagged(my + 2 * N + lane, __float_as_uint(pB[ln]));
+    }
+    float nu = (on && a.g_hL) ? a.g_hL[(size_t)s * N + lane] : 0.f;   // entering the last chunk
+    const int later = p.nC - 1 - c;                // chunks after this one
+    if (later > 0) {
+      // lane l polls chunk c+1+l: the nearest one whose passed-on adjoint is
+      // published, with every map between present
+      const int win = min(later, 64);
+      int stop = 0, spins = 0;
+      while (true) {
+        const int q = c + 1 + lane;
+        bool iv = false, av = false;
+        if (lane < win) {
+          iv = tag_ok(get_tagged(inc + ((size_t)q * BH + s) * N));
+          av = tag_ok(get_tagged(agg + ((size_t)q * BH + s) * 3 * N));
+        }
+        const uint64_t mi = __ballot(iv), ma = __ballot(av);
+        const int li = mi ? __builtin_ctzll(mi) : 64;
+        const int need = li < win ? li : win;
+        const uint64_t nm = need >= 64 ? ~0ull : ((1ull << need) - 1ull);
+        if ((ma & nm) == nm && (li < win || later <= 64)) {
+          stop = need;
+          break;
+        }
+        if (++spins > kSpinLimit) {
+          if (lane == 0) atomicOr(&hdr[kWsError], 1u);
+          stop = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (stop < later) {
+        // base: the adjoint passed on by chunk c+1+stop
+        uint64_t* pw = inc + ((size_t)(c + 1 + stop) * BH + s) * N;
+        if (on) {
+          uint64_t wv = get_tagged(pw + lane);
+          for (int n = 0; !tag_ok(wv) && n < kSpinLimit; ++n) wv = get_tagged(pw + lane);
+          nu = __uint_as_float((uint32_t)wv);
+        }
+      }
+      // apply the maps of chunks c+stop .. c+1, farthest first
+      for (int q0 = c + stop; q0 > c; q0 -= kBwdLookBatch) {
+        uint64_t wv[kBwdLookBatch][3];
+#pragma unroll
+        for (int u = 0; u < kBwdLookBatch; ++u) {
+          uint64_t* pa = agg + ((size_t)(q0 - u) * BH + s) * 3 * N;
+#pragma unroll
+          for (int f = 0; f < 3; ++f) wv[u][f] = (on && q0 - u > c) ? get_tagged(pa + f * N + lane) : kTagValid;
+        }
+#pragma unroll
+        for (int u = 0; u < kBwdLookBatch; ++u) {
+          if (q0 - u <= c) break;
+          uint64_t* pa = agg + ((size_t)(q0 - u) * BH + s) * 3 * N;
+#pragma unroll
+          for (int f = 0; f < 3; ++f)
+            for (int n = 0; on && !tag_ok(wv[u][f]) && n < kSpinLimit; ++n) wv[u][f] = get_tagged(pa + f * N + lane);
+          const int rs = on ? (int)(uint32_t)wv[u][0] : lane;
+          const float nv = grp_gather(nu, 0, rs);
+          if (on) nu = __uint_as_float((uint32_t)wv[u][1]) * nv + __uint_as_float((uint32_t)wv[u][2]);
+        }
+      }
+    }
+    // the adjoint this chunk passes on: its whole map applied to nu
+    const float nv = grp_gather(nu, 0, on ? pSrc[ln] : lane);
+    if (on) {
+      put_tagged(inc + ((size_t)c * BH + s) * N + lane, __float_as_uint(pW[ln] * nv + pB[ln]));
+      Hs[lane] = nu;
+    }
+  }
+  __syncthreads();
+
+  // ---- adjoint entering every group: the maps of the groups after it
+  // applied to the chunk's entering adjoint
+  if (act) {
+    float v = Hs[j];
+    if (gam + 1 < G) {
+      const int q = (gam + 1) * N + j;
+      v = pW[q] * Hs[pSrc[q]] + pB[q];
+    }
+    slots[gam * NP + j] = v;
+  }
+  __syncthreads();
+
+  // ---- replay: every group runs its sub-chunk backwards from its true
+  // entering adjoint and writes the gradients
+  float xr = act ? slots[gam * NP + j] : 0.f;
+  float gc = 0.f;
+  float h_cur = (act && te > tb) ? a.H_all[(gbase + te - 1) * N + j] : 0.f;
+  for (int t = te - 1; t >= tb; --t) {
+    const size_t row = (gbase + t) * N;
+    const float lam = act ? xr + Cs[j] * gyl[t] : 0.f;
+    const int r = act ? dic[kl[t] * N + j] : j;
+    const float lr = grp_gather(lam, base, r);
+    float h_prev = 0.f;
+    if (act) {
+      if (c0 + t > 0) h_prev = a.H_all[row - N + j];
+      else if (a.h0) h_prev = a.h0[(size_t)s * N + j];
+      a.g_Bu[row + j] = lam;
+      a.g_D[row + j] = lr * h_prev;
+    }
+    gc += gyl[t] * h_cur;
+    h_cur = h_prev;
+    xr = act ? Dl[t * N + j] * lr : 0.f;
+  }
+  if (c == 0 && gam == 0 && act && a.g_h0) a.g_h0[(size_t)s * N + j] = xr;
+
+  // ---- dC partial of this task, summed over the groups in a fixed order
+  if (act) gcs[gam * N + j] = gc;
+  __syncthreads();
+  if (tid < N) {
+    float acc = 0.f;
+    for (int g = 0; g < G; ++g) acc += gcs[g * N + tid];
+    ((float*)(a.ws + a.ws_gc))[((size_t)c * BH + s) * N + tid] = acc;
+  }
+}
+
+// dC[h][n]: the tasks' partials summed over chunks, then batch, in order.
+__global__ void pdssm_bwd_reduce_c(const float* part, float* g_C, int nC, int B, int H, int N) {
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= H * N) return;
+  const int hh = q / N, n = q % N;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int cc = 0; cc < nC; ++cc) acc += part[((size_t)cc * B * H + (size_t)b * H + hh) * N + n];
+  g_C[q] = acc;
+}
+
+}  // namespace pdscan

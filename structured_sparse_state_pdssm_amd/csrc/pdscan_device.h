@@ -840,6 +840,32 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
       __syncthreads();
     }
   }
+  if constexpr (!ROW16) {
+    if (a.H_all) {
+      // The state after every step is wanted as well: each group replays its
+      // sub-chunk from the state entering it (the step of phase A, now from
+      // the true state), writing the states and the outputs directly.
+      const int* kbuf = (const int*)(smem + p.off_k);
+      const i2v* DC = (const i2v*)(smem + p.off_DC);
+      const float* Cs = (const float*)(smem + p.off_C);
+      float* scr = (float*)sIdx + gam * NP;        // free since phase B
+      float hj = act ? slots[gam * NP + j] : 0.f;
+      const int tb = gam * S, te = min(tb + S, Tc);
+      for (int t = tb; t < te; ++t) {
+        const size_t row = (gbase + t) * N;
+        const int r = act ? DC[kbuf[t] * p.DCS + j].x : j;
+        const float dj = act ? a.D_in[row + j] : 0.f;
+        scr[j] = act ? a.Bu[row + j] : 0.f;
+        // one wave holds the group, so its LDS operations stay in order
+        atomicAdd(&scr[r], dj * hj);
+        hj = scr[j];
+        if (act) a.H_all[row + j] = hj;
+        const float yl = group_sum_rt(act ? Cs[j] * hj : 0.f, NP);
+        if (j == 0) a.y[gbase + t] = yl;
+      }
+      return;
+    }
+  }
   for (int t = tid; t < Tc; t += kThreads) {
     const int gt = t / S;
     const int col = t + (p.skew ? gt : 0);

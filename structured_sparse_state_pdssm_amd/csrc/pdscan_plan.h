@@ -142,6 +142,7 @@ struct Args {
   int32_t* P_out;        // optional (selection mode)
   float* y;
   float* hL;
+  float* H_all;          // optional (scan mode): the state after every step
   unsigned char* ws;     // workspace base
 };
 
