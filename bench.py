@@ -3,8 +3,11 @@ MI355X, in state-updates per second, with its HBM roofline fraction and the
 fp64 CPU oracle timed beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload impulse]
-                    [--no-cpu-baseline] [--copy-probe]
+                    [--no-cpu-baseline] [--copy-probe] [--pass fwd|bwd]
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload impulse]
+
+``--pass bwd`` times the gradient pass through the scan (pdssm_scan_bwd) on
+the same workload instead, with its own roofline and oracle baseline.
 
 Prints one JSON line.  A step is one pdssm_fwd call over the whole workload
 (selection outputs not materialised), with every input already resident in
@@ -54,6 +57,17 @@ def algorithmic(cfg):
     total = u + B * H * L * N * 4 + B * H * L * 4 + 2 * B * H * N * 4 + params
     flops = 2 * (K + N) * d * B * H * L
     return total, flops
+
+
+def algorithmic_bwd(cfg):
+    """Minimum traffic of the gradient pass: k*, D, dLoss/dy and the forward
+    states read once, dBu and dD written once, plus parameters and the small
+    per-sequence vectors."""
+    B, H, L, N, K = cfg.B, cfg.H, cfg.L, cfg.N, cfg.K
+    steps = B * H * L
+    per_step = 4 + 4 * N + 4 + 4 * N + 4 * N + 4 * N
+    small = H * K * N * 4 + 2 * H * N * 4 + 3 * B * H * N * 4
+    return steps * per_step + small
 
 
 def traffic_from_profile(workload):
@@ -157,6 +171,88 @@ def cpu_baseline(inp):
                       "BLAS threads = cores (the step loop itself is single-threaded)"}
 
 
+def bench_bwd(args, torch, np, P):
+    """Time pdssm_scan_bwd; selections and forward states come from the
+    library's own forward calls, outside the timed region."""
+    from pdssm_inputs import generate, get_config, upstream_grads
+    cfg = get_config(args.workload)
+    chunk = args.chunk or cfg.chunk
+    t0 = time.time()
+    inp = generate(cfg)
+    print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    bf = cfg.dtype == "bf16"
+    pdt = torch.bfloat16 if bf else torch.float32
+
+    def dev(x, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+
+    u, W_sel, W_d = dev(inp.u, pdt), dev(inp.W_sel, pdt), dev(inp.W_d, pdt)
+    b_d, dic, Bu, C, h0 = dev(inp.b_d), dev(inp.dict_idx), dev(inp.Bu), dev(inp.C), dev(inp.h0)
+    fw = P.pdssm_fwd(u, W_sel, dic, W_d, b_d, Bu, C, h0, chunk=chunk, want_k=True, want_D=True)
+    k, D = fw["k_star"], fw["D"]
+    del u
+    _, _, Hs = P.pdssm_scan_states(k, dic, D, Bu, C, h0, chunk=chunk)
+    g_y_h, g_hL_h = upstream_grads(cfg.B, cfg.H, cfg.L, cfg.N, cfg.seed)
+    g_y, g_hL = dev(g_y_h), dev(g_hL_h)
+    dims = P.make_dims(cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, 8)
+    ws = torch.zeros(P.scan_bwd_workspace_bytes(dims, chunk), dtype=torch.uint8, device="cuda")
+    out = {"g_Bu": torch.empty_like(D), "g_D": torch.empty_like(D),
+           "g_h0": torch.empty_like(h0), "g_C": torch.empty_like(C)}
+
+    def step():
+        P.pdssm_scan_bwd(k, dic, D, C, Hs, g_y, h0=h0, g_hL=g_hL, chunk=chunk, workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if P.workspace_error_flag(ws):
+        raise RuntimeError("look-back wait gave up during warm-up")
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    ms_step = wall * 1e3 / args.steps
+    alg = algorithmic_bwd(cfg)
+    achieved = alg / launch_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None, "algorithmic_bytes": alg,
+            "launch_us": round(launch_s * 1e6, 2)}
+    rec = {
+        "metric": "state-updates/sec (B·H·L·N) PD-SSM gradient through the scan (fixed selections)",
+        "value": cfg.state_updates / (ms_step / 1e3),
+        "unit": "state-updates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} gradient pass: B={cfg.B} H={cfg.H} L={cfg.L} N={cfg.N} "
+                               f"K={cfg.K} chunk={chunk}",
+                   "B": cfg.B, "H": cfg.H, "L": cfg.L, "N": cfg.N, "K": cfg.K, "chunk": chunk},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        Ls = min(cfg.L, 16384)
+        kh, Dh = k.cpu().numpy()[:, :, :Ls], D.cpu().numpy()[:, :, :Ls].astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.scan_vjp(kh, inp.dict_idx, Dh, inp.Bu[:, :, :Ls], inp.C, inp.h0, g_y_h[:, :, :Ls], g_hL_h)
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": cfg.B * cfg.H * Ls * cfg.N / dt, "unit": "state-updates/s",
+                               "cores": cores, "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": f"first {Ls} steps of every sequence of {cfg.name} "
+                                         "(oracle gradient: states plus the backward recurrence)"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +261,8 @@ def main():
     ap.add_argument("--workload", default="impulse")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="forward pass (default) or the gradient pass through the scan")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain copy kernel of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -186,6 +284,8 @@ def main():
     from pdssm_inputs import generate, get_config
 
     torch.cuda.set_device(0)
+    if args.which == "bwd":
+        return bench_bwd(args, torch, np, P)
     cfg = get_config(args.workload)
     chunk = args.chunk or cfg.chunk
     t0 = time.time()
