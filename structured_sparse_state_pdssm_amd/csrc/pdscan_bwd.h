@@ -33,6 +33,8 @@ __device__ __forceinline__ int grp_gather_i(int v, int base, int src) {
 
 // Adjoint map words one lane of the look-back wave loads per batch.
 constexpr int kBwdLookBatch = 4;
+// Loads one lane keeps in flight when staging the chunk and in the replay.
+constexpr int kBwdLoadBatch = 8;
 
 __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -70,13 +72,63 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   const int Tc = min(T, p.L - c0);
   const size_t gbase = (size_t)s * p.L + c0;
 
+  // chunk inputs to LDS; each lane issues a batch of loads before the first
+  // wait (reads past a buffer's end return zero and are not stored)
   for (int q = tid; q < K * N; q += kThreads) dic[q] = a.dict[(size_t)h * K * N + q];
   for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
-  for (int q = tid; q < Tc; q += kThreads) {
-    kl[q] = a.k_star[gbase + q];
-    gyl[q] = a.g_y[gbase + q];
+  {
+    const rsrc_t kr = make_rsrc(a.k_star + gbase, (uint32_t)(Tc * 4));
+    const rsrc_t gr = make_rsrc(a.g_y + gbase, (uint32_t)(Tc * 4));
+    for (int q0 = 0; q0 < Tc; q0 += kThreads * kBwdLoadBatch) {
+      int kv[kBwdLoadBatch];
+      float gv[kBwdLoadBatch];
+#pragma unroll
+      for (int u = 0; u < kBwdLoadBatch; ++u) {
+        const int q = q0 + u * kThreads + tid;
+        kv[u] = buf_i32(kr, q < Tc ? (uint32_t)q * 4u : kNoLoad);
+        gv[u] = buf_f32(gr, q < Tc ? (uint32_t)q * 4u : kNoLoad);
+      }
+#pragma unroll
+      for (int u = 0; u < kBwdLoadBatch; ++u) {
+        const int q = q0 + u * kThreads + tid;
+        if (q < Tc) {
+          kl[q] = kv[u];
+          gyl[q] = gv[u];
+        }
+      }
+    }
+    const int nD = Tc * N;
+    const rsrc_t dr = make_rsrc(a.D + gbase * N, (uint32_t)(nD * 4));
+    if ((N & 3) == 0) {   // 16-byte rows: the chunk's D is 16-byte aligned
+      for (int q0 = 0; q0 < nD; q0 += kThreads * 4 * kBwdLoadBatch) {
+        f4v v[kBwdLoadBatch];
+#pragma unroll
+        for (int u = 0; u < kBwdLoadBatch; ++u) {
+          const int q = q0 + (u * kThreads + tid) * 4;
+          v[u] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(dr, q < nD ? (uint32_t)q * 4u : kNoLoad, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < kBwdLoadBatch; ++u) {
+          const int q = q0 + (u * kThreads + tid) * 4;
+          if (q < nD) *(f4v*)(Dl + q) = v[u];
+        }
+      }
+    } else {
+      for (int q0 = 0; q0 < nD; q0 += kThreads * kBwdLoadBatch) {
+        float v[kBwdLoadBatch];
+#pragma unroll
+        for (int u = 0; u < kBwdLoadBatch; ++u) {
+          const int q = q0 + u * kThreads + tid;
+          v[u] = buf_f32(dr, q < nD ? (uint32_t)q * 4u : kNoLoad);
+        }
+#pragma unroll
+        for (int u = 0; u < kBwdLoadBatch; ++u) {
+          const int q = q0 + u * kThreads + tid;
+          if (q < nD) Dl[q] = v[u];
+        }
+      }
+    }
   }
-  for (int q = tid; q < Tc * N; q += kThreads) Dl[q] = a.D[gbase * N + q];
   __syncthreads();
 
   const int gpw = 64 / NP;
@@ -88,19 +140,34 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
 
   // ---- local pass: from a zero adjoint at the sub-chunk's right end, the
   // map (src, w, b) from the adjoint entering there to the one leaving on the
-  // left: per step x <- A_t^T (x + C g_y[t]) and (src, w) <- A_t^T o (src, w)
+  // left: per step x <- A_t^T (x + C g_y[t]) and (src, w) <- A_t^T o (src, w).
+  // Operands are read from LDS a block of steps ahead of the chain; steps
+  // past the left end are identity steps (own row, scale 1, no output term).
+  const int nst = te - tb;
+  const float cj = act ? Cs[j] : 0.f;
   float x = 0.f, w = act ? 1.f : 0.f;
   int src = j;
-  for (int t = te - 1; t >= tb; --t) {
-    const int r = act ? dic[kl[t] * N + j] : j;
-    const float d = act ? Dl[t * N + j] : 0.f;
-    const float lam = act ? x + Cs[j] * gyl[t] : 0.f;
-    const float lr = grp_gather(lam, base, r);
-    const int sr = grp_gather_i(src, base, r);
-    const float wr = grp_gather(w, base, r);
-    x = d * lr;
-    src = sr;
-    w = d * wr;
+  for (int i0 = 0; i0 < nst; i0 += kBwdLoadBatch) {
+    int rr[kBwdLoadBatch];
+    float dd[kBwdLoadBatch], gg[kBwdLoadBatch];
+#pragma unroll
+    for (int u = 0; u < kBwdLoadBatch; ++u) {
+      const bool ok = i0 + u < nst;
+      const int t = ok ? te - 1 - i0 - u : tb;
+      rr[u] = (act && ok) ? dic[kl[t] * N + j] : j;
+      dd[u] = act ? (ok ? Dl[t * N + j] : 1.f) : 0.f;
+      gg[u] = ok ? gyl[t] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBwdLoadBatch; ++u) {
+      const float lam = x + cj * gg[u];
+      const float lr = grp_gather(lam, base, rr[u]);
+      const int sr = grp_gather_i(src, base, rr[u]);
+      const float wr = grp_gather(w, base, rr[u]);
+      x = dd[u] * lr;
+      src = sr;
+      w = dd[u] * wr;
+    }
   }
 
   // ---- combine right to left: group g ends up with the map of groups
@@ -230,24 +297,52 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
 
   // ---- replay: every group runs its sub-chunk backwards from its true
   // entering adjoint and writes the gradients
+  // The forward states of the sub-chunk, v_i = h at step te-1-i for
+  // i = 0..te-tb (the last one is the state before step tb: the previous
+  // chunk's last state, or h0), are read kBwdLoadBatch steps ahead of use.
+  // hr covers rows gbase-1 (when the chunk has a predecessor) .. gbase+Tc-1.
+  const int pre = c0 > 0 ? 1 : 0;
+  const rsrc_t hr = make_rsrc(a.H_all + (gbase - pre) * N, (uint32_t)((Tc + pre) * N * 4));
+  const float hinit = (act && c0 == 0 && a.h0) ? a.h0[(size_t)s * N + j] : 0.f;
+  auto h_off = [&](int i) -> uint32_t {   // byte offset of v_i, kNoLoad outside
+    const int x = te - 1 - i + pre;       // row within hr
+    return (act && i <= te - tb && x >= 0) ? (uint32_t)(x * N + j) * 4u : kNoLoad;
+  };
   float xr = act ? slots[gam * NP + j] : 0.f;
   float gc = 0.f;
-  float h_cur = (act && te > tb) ? a.H_all[(gbase + te - 1) * N + j] : 0.f;
-  for (int t = te - 1; t >= tb; --t) {
-    const size_t row = (gbase + t) * N;
-    const float lam = act ? xr + Cs[j] * gyl[t] : 0.f;
-    const int r = act ? dic[kl[t] * N + j] : j;
-    const float lr = grp_gather(lam, base, r);
-    float h_prev = 0.f;
-    if (act) {
-      if (c0 + t > 0) h_prev = a.H_all[row - N + j];
-      else if (a.h0) h_prev = a.h0[(size_t)s * N + j];
-      a.g_Bu[row + j] = lam;
-      a.g_D[row + j] = lr * h_prev;
+  float h_cur = buf_f32(hr, h_off(0));
+  float hn[kBwdLoadBatch];
+#pragma unroll
+  for (int u = 0; u < kBwdLoadBatch; ++u) hn[u] = buf_f32(hr, h_off(1 + u));
+  for (int i0 = 0; i0 < nst; i0 += kBwdLoadBatch) {
+    float hv[kBwdLoadBatch], dd[kBwdLoadBatch], gg[kBwdLoadBatch];
+    int rr[kBwdLoadBatch];
+#pragma unroll
+    for (int u = 0; u < kBwdLoadBatch; ++u) {
+      hv[u] = hn[u];
+      hn[u] = buf_f32(hr, h_off(i0 + kBwdLoadBatch + 1 + u));
+      const bool ok = i0 + u < nst;
+      const int t = ok ? te - 1 - i0 - u : tb;
+      rr[u] = (act && ok) ? dic[kl[t] * N + j] : j;
+      dd[u] = act ? (ok ? Dl[t * N + j] : 1.f) : 0.f;
+      gg[u] = ok ? gyl[t] : 0.f;
     }
-    gc += gyl[t] * h_cur;
-    h_cur = h_prev;
-    xr = act ? Dl[t * N + j] * lr : 0.f;
+#pragma unroll
+    for (int u = 0; u < kBwdLoadBatch; ++u) {
+      const int i = i0 + u;
+      const int t = te - 1 - i;
+      const float lam = xr + cj * gg[u];
+      const float lr = grp_gather(lam, base, rr[u]);
+      const float h_prev = (c0 + t > 0) ? hv[u] : hinit;
+      gc += gg[u] * h_cur;   // gg is zero past the left end
+      if (act && i < nst) {
+        const size_t row = (gbase + t) * N;
+        a.g_Bu[row + j] = lam;
+        a.g_D[row + j] = lr * h_prev;
+      }
+      if (i < nst) h_cur = h_prev;
+      xr = dd[u] * lr;
+    }
   }
   if (c == 0 && gam == 0 && act && a.g_h0) a.g_h0[(size_t)s * N + j] = xr;
 
@@ -261,15 +356,36 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   }
 }
 
-// dC[h][n]: the tasks' partials summed over chunks, then batch, in order.
-__global__ void pdssm_bwd_reduce_c(const float* part, float* g_C, int nC, int B, int H, int N) {
-  const int q = blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= H * N) return;
-  const int hh = q / N, n = q % N;
-  float acc = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int cc = 0; cc < nC; ++cc) acc += part[((size_t)cc * B * H + (size_t)b * H + hh) * N + n];
-  g_C[q] = acc;
+// dC[h][n]: the tasks' partials summed over (batch, chunk) pairs.  One
+// workgroup per head; for each n, P = 256 / N lanes each sum every P-th pair
+// in order, then lane part 0 adds the P part sums in order (a fixed order,
+// so the result does not depend on timing).
+__global__ __launch_bounds__(kThreads) void pdssm_bwd_reduce_c(const float* part, float* g_C, int nC, int B,
+                                                                int H, int N) {
+  __shared__ float acc[kThreads];
+  const int hh = blockIdx.x, tid = threadIdx.x;
+  const int P = N < kThreads ? kThreads / N : 1;
+  const int pairs = B * nC;
+  for (int n0 = 0; n0 < N; n0 += kThreads) {
+    const int n = n0 + tid % N, pp = tid / N;
+    const bool on = pp < P && n < N;
+    float v = 0.f;
+    if (on) {
+#pragma unroll 8
+      for (int q = pp; q < pairs; q += P) {
+        const int b = q / nC, cc = q % nC;
+        v += part[((size_t)cc * B * H + (size_t)b * H + hh) * N + n];
+      }
+    }
+    acc[tid] = v;
+    __syncthreads();
+    if (on && pp == 0) {
+      float t = 0.f;
+      for (int k = 0; k < P; ++k) t += acc[k * N + tid % N];
+      g_C[(size_t)hh * N + n] = t;
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace pdscan

@@ -80,9 +80,17 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;     // 32-bit data format, raw access
 constexpr uint32_t kNoLoad = 0xFFFFFFF0u;
 
+// `base` and `bytes` must be the same in every lane of the wave (every
+// descriptor here is per workgroup).  They are taken through lane 0 so the
+// descriptor stays in scalar registers even where the compiler cannot prove
+// them uniform (values derived from a ticket read back from LDS); a
+// descriptor in vector registers turns each load into a loop over lanes.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kRsrcWord3);
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
 __device__ __forceinline__ float buf_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));

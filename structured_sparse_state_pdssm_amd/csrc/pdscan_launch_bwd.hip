@@ -18,8 +18,7 @@ hipError_t launch_bwd(const BwdArgs& a, float* g_C, hipStream_t st) {
   if (cb < 1) cb = 1;
   hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)cb), dim3(256), 0, st, (uint64_t*)a.ws, words);
   hipLaunchKernelGGL(pdssm_bwd_kernel, dim3((unsigned)p.tasks), dim3(kThreads), (unsigned)a.l.bytes, st, a);
-  const int hn = p.H * p.N;
-  hipLaunchKernelGGL(pdssm_bwd_reduce_c, dim3((unsigned)((hn + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(pdssm_bwd_reduce_c, dim3((unsigned)p.H), dim3(kThreads), 0, st,
                      (const float*)(a.ws + a.ws_gc), g_C, p.nC, p.B, p.H, p.N);
   return hipGetLastError();
 }
