@@ -35,7 +35,13 @@ __device__ __forceinline__ int grp_gather_i(int v, int base, int src) {
 constexpr int kBwdLookBatch = 4;
 // Loads one lane keeps in flight when staging the chunk and in the replay.
 constexpr int kBwdLoadBatch = 8;
+// 16 nibbles mapping every row to itself.
+constexpr uint64_t kIdentityNibbles = 0xFEDCBA9876543210ull;
 
+// PK (N <= 16): dictionary rows are also kept as 64-bit words of 16 nibbles,
+// which lets each lane follow its own index path in the local pass without
+// cross-lane traffic (see there).
+template <bool PK>
 __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Plan& p = a.p;
@@ -43,7 +49,8 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   const int N = p.N, K = p.K, S = p.S, T = p.chunk, G = p.G, NP = p.NP;
   const int BH = p.B * p.H;
   int* dic = (int*)(smem + a.l.off_dic);           // [K][N] dictionary of the head
-  float* Dl = (float*)(smem + a.l.off_D);          // [T][N] diagonals of the chunk
+  uint64_t* dk64 = (uint64_t*)(smem + a.l.off_dk); // PK: [K] rows as nibbles
+  float* Dl = (float*)(smem + a.l.off_D) + 8 * N;  // [G][GS]: group g's S rows of N diagonals
   int* kl = (int*)(smem + a.l.off_k);              // [T] selections
   float* gyl = (float*)(smem + a.l.off_gy);        // [T] output gradients
   float* Cs = (float*)(smem + a.l.off_C);
@@ -72,64 +79,68 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   const int Tc = min(T, p.L - c0);
   const size_t gbase = (size_t)s * p.L + c0;
 
-  // chunk inputs to LDS; each lane issues a batch of loads before the first
-  // wait (reads past a buffer's end return zero and are not stored)
-  for (int q = tid; q < K * N; q += kThreads) dic[q] = a.dict[(size_t)h * K * N + q];
-  for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
+  // Chunk inputs to LDS.  Each pass issues one batch of loads for every
+  // array (reads past a buffer's end return zero and are not stored) before
+  // its first store, so a chunk of up to 2048 steps costs one memory round
+  // trip.
   {
+    const rsrc_t icr = make_rsrc(a.dict + (size_t)h * K * N, (uint32_t)(K * N * 4));
+    const rsrc_t cr = make_rsrc(a.C + (size_t)h * N, (uint32_t)(N * 4));
     const rsrc_t kr = make_rsrc(a.k_star + gbase, (uint32_t)(Tc * 4));
     const rsrc_t gr = make_rsrc(a.g_y + gbase, (uint32_t)(Tc * 4));
-    for (int q0 = 0; q0 < Tc; q0 += kThreads * kBwdLoadBatch) {
+    const int nD = Tc * N, SN = S * N, gpad = a.l.GS - S * N;
+    const rsrc_t dr = make_rsrc(a.D + gbase * N, (uint32_t)(nD * 4));
+    const bool vec = (N & 3) == 0;                 // 16-byte rows: the chunk's D is 16-byte aligned
+    const int per = vec ? 4 : 1;
+    constexpr int span = kThreads * kBwdLoadBatch;
+    const int passes = max(max((Tc + span - 1) / span, (nD + span * per - 1) / (span * per)),
+                           max((K * N + kThreads - 1) / kThreads, (N + kThreads - 1) / kThreads));
+    for (int ps = 0; ps < passes; ++ps) {
+      const int q1 = ps * kThreads + tid;          // dictionary and C: one entry per lane
+      const int dv = buf_i32(icr, q1 < K * N ? (uint32_t)q1 * 4u : kNoLoad);
+      const float cv = buf_f32(cr, q1 < N ? (uint32_t)q1 * 4u : kNoLoad);
       int kv[kBwdLoadBatch];
       float gv[kBwdLoadBatch];
+      f4v v[kBwdLoadBatch];
 #pragma unroll
       for (int u = 0; u < kBwdLoadBatch; ++u) {
-        const int q = q0 + u * kThreads + tid;
+        const int q = ps * span + u * kThreads + tid;
         kv[u] = buf_i32(kr, q < Tc ? (uint32_t)q * 4u : kNoLoad);
         gv[u] = buf_f32(gr, q < Tc ? (uint32_t)q * 4u : kNoLoad);
+        const int qd = q * per;
+        if (vec) {
+          v[u] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(dr, qd < nD ? (uint32_t)qd * 4u : kNoLoad, 0, 0));
+        } else {
+          v[u] = f4v{buf_f32(dr, qd < nD ? (uint32_t)qd * 4u : kNoLoad), 0.f, 0.f, 0.f};
+        }
       }
+      if (q1 < K * N) dic[q1] = dv;
+      if (q1 < N) Cs[q1] = cv;
 #pragma unroll
       for (int u = 0; u < kBwdLoadBatch; ++u) {
-        const int q = q0 + u * kThreads + tid;
+        const int q = ps * span + u * kThreads + tid;
         if (q < Tc) {
           kl[q] = kv[u];
           gyl[q] = gv[u];
         }
-      }
-    }
-    const int nD = Tc * N;
-    const rsrc_t dr = make_rsrc(a.D + gbase * N, (uint32_t)(nD * 4));
-    if ((N & 3) == 0) {   // 16-byte rows: the chunk's D is 16-byte aligned
-      for (int q0 = 0; q0 < nD; q0 += kThreads * 4 * kBwdLoadBatch) {
-        f4v v[kBwdLoadBatch];
-#pragma unroll
-        for (int u = 0; u < kBwdLoadBatch; ++u) {
-          const int q = q0 + (u * kThreads + tid) * 4;
-          v[u] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(dr, q < nD ? (uint32_t)q * 4u : kNoLoad, 0, 0));
-        }
-#pragma unroll
-        for (int u = 0; u < kBwdLoadBatch; ++u) {
-          const int q = q0 + (u * kThreads + tid) * 4;
-          if (q < nD) *(f4v*)(Dl + q) = v[u];
-        }
-      }
-    } else {
-      for (int q0 = 0; q0 < nD; q0 += kThreads * kBwdLoadBatch) {
-        float v[kBwdLoadBatch];
-#pragma unroll
-        for (int u = 0; u < kBwdLoadBatch; ++u) {
-          const int q = q0 + u * kThreads + tid;
-          v[u] = buf_f32(dr, q < nD ? (uint32_t)q * 4u : kNoLoad);
-        }
-#pragma unroll
-        for (int u = 0; u < kBwdLoadBatch; ++u) {
-          const int q = q0 + u * kThreads + tid;
-          if (q < nD) Dl[q] = v[u];
+        const int qd = q * per;
+        if (qd < nD) {
+          float* dst = Dl + qd + (qd / SN) * gpad;
+          if (vec) *(f4v*)dst = v[u];
+          else *dst = v[u].x;
         }
       }
     }
   }
   __syncthreads();
+  if constexpr (PK) {
+    if (tid < K) {
+      uint64_t v = 0;
+      for (int n = 0; n < N; ++n) v |= (uint64_t)(uint32_t)dic[tid * N + n] << (4 * n);
+      dk64[tid] = v;
+    }
+    __syncthreads();
+  }
 
   const int gpw = 64 / NP;
   const int gl = lane / NP, j = lane % NP;
@@ -138,35 +149,83 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   const bool act = j < N;
   const int tb = gam * S, te = min(tb + S, Tc);
 
-  // ---- local pass: from a zero adjoint at the sub-chunk's right end, the
-  // map (src, w, b) from the adjoint entering there to the one leaving on the
-  // left: per step x <- A_t^T (x + C g_y[t]) and (src, w) <- A_t^T o (src, w).
-  // Operands are read from LDS a block of steps ahead of the chain; steps
-  // past the left end are identity steps (own row, scale 1, no output term).
+  // ---- local pass: the map (src, w, b) of the sub-chunk, taking the
+  // adjoint entering at its right end to the one leaving on its left,
+  // (M v)_j = w_j v[src_j] + b_j.
   const int nst = te - tb;
   const float cj = act ? Cs[j] : 0.f;
+  const float* Dg = Dl + gam * a.l.GS - tb * N;    // Dg[t * N + i]: D_t[i] of this group
+  const int jr = act ? j : 0;                      // an in-range row for idle lanes' reads
   float x = 0.f, w = act ? 1.f : 0.f;
   int src = j;
-  for (int i0 = 0; i0 < nst; i0 += kBwdLoadBatch) {
-    int rr[kBwdLoadBatch];
-    float dd[kBwdLoadBatch], gg[kBwdLoadBatch];
+  if constexpr (PK) {
+    // Lane j follows its index path forward in time: p_0 = j,
+    // p_{s+1} = idx_{tb+s}[p_s].  Then src_j = p_S, w_j is the product of
+    // D_{tb+s}[p_s], and b_j sums, over s, that product up to s times
+    // C[p_{s+1}] g_y[tb+s] (expanding the transposed products).  Only this
+    // lane's path is read: one LDS gather of D and C per step, no exchange.
+    int pth = act ? j : 0;                         // idle lanes walk from row 0 with weight 0
+    for (int i0 = 0; i0 < nst; i0 += kBwdLoadBatch) {
+      uint64_t dk[kBwdLoadBatch];
+      float gg[kBwdLoadBatch];
+      int kk[kBwdLoadBatch];
 #pragma unroll
-    for (int u = 0; u < kBwdLoadBatch; ++u) {
-      const bool ok = i0 + u < nst;
-      const int t = ok ? te - 1 - i0 - u : tb;
-      rr[u] = (act && ok) ? dic[kl[t] * N + j] : j;
-      dd[u] = act ? (ok ? Dl[t * N + j] : 1.f) : 0.f;
-      gg[u] = ok ? gyl[t] : 0.f;
+      for (int u = 0; u < kBwdLoadBatch; ++u) {   // unconditional reads at in-range steps
+        const int t = min(tb + i0 + u, te - 1);
+        kk[u] = kl[t];
+        gg[u] = gyl[t];
+      }
+#pragma unroll
+      for (int u = 0; u < kBwdLoadBatch; ++u) {
+        const bool ok = i0 + u < nst;
+        dk[u] = ok ? dk64[kk[u]] : kIdentityNibbles;
+        gg[u] = ok ? gg[u] : 0.f;
+      }
+      const float* drow = Dg + (tb + i0) * N;      // rows past te-1 fall in the slack or the next group
+#pragma unroll
+      for (int u = 0; u < kBwdLoadBatch; ++u) {
+        const float dr = drow[u * N + pth];
+        w *= (i0 + u < nst) ? dr : 1.f;
+        pth = (int)((dk[u] >> (4 * pth)) & 15u);
+        x = __builtin_fmaf(w * Cs[pth], gg[u], x);
+      }
     }
+    src = pth;
+  } else {
+    // Generic N: the sub-chunk runs right to left, per step
+    // x <- A_t^T (x + C g_y[t]) and (src, w) <- A_t^T o (src, w), through
+    // gathers inside the lane group.  Operands are read a block of steps
+    // ahead; steps past the left end are identity steps.
+    for (int i0 = 0; i0 < nst; i0 += kBwdLoadBatch) {
+      int rr[kBwdLoadBatch];
+      float dd[kBwdLoadBatch], gg[kBwdLoadBatch];
+      int kk[kBwdLoadBatch];
+      const float* drow = Dg + (te - 1 - i0) * N + jr;   // rows before tb fall in the slack or the previous group
 #pragma unroll
-    for (int u = 0; u < kBwdLoadBatch; ++u) {
-      const float lam = x + cj * gg[u];
-      const float lr = grp_gather(lam, base, rr[u]);
-      const int sr = grp_gather_i(src, base, rr[u]);
-      const float wr = grp_gather(w, base, rr[u]);
-      x = dd[u] * lr;
-      src = sr;
-      w = dd[u] * wr;
+      for (int u = 0; u < kBwdLoadBatch; ++u) {   // unconditional reads
+        const int t = max(te - 1 - i0 - u, tb);
+        kk[u] = kl[t];
+        dd[u] = drow[-u * N];
+        gg[u] = gyl[t];
+      }
+#pragma unroll
+      for (int u = 0; u < kBwdLoadBatch; ++u) {
+        const bool ok = i0 + u < nst;
+        rr[u] = dic[kk[u] * N + jr];
+        rr[u] = (act && ok) ? rr[u] : j;
+        dd[u] = act ? (ok ? dd[u] : 1.f) : 0.f;
+        gg[u] = ok ? gg[u] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kBwdLoadBatch; ++u) {
+        const float lam = x + cj * gg[u];
+        const float lr = grp_gather(lam, base, rr[u]);
+        const int sr = grp_gather_i(src, base, rr[u]);
+        const float wr = grp_gather(w, base, rr[u]);
+        x = dd[u] * lr;
+        src = sr;
+        w = dd[u] * wr;
+      }
     }
   }
 
@@ -317,15 +376,25 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   for (int i0 = 0; i0 < nst; i0 += kBwdLoadBatch) {
     float hv[kBwdLoadBatch], dd[kBwdLoadBatch], gg[kBwdLoadBatch];
     int rr[kBwdLoadBatch];
+    int kk[kBwdLoadBatch];
+    const float* drow = Dg + (te - 1 - i0) * N + jr;
 #pragma unroll
-    for (int u = 0; u < kBwdLoadBatch; ++u) {
+    for (int u = 0; u < kBwdLoadBatch; ++u) {   // unconditional reads
       hv[u] = hn[u];
       hn[u] = buf_f32(hr, h_off(i0 + kBwdLoadBatch + 1 + u));
+      const int t = max(te - 1 - i0 - u, tb);
+      kk[u] = kl[t];
+      dd[u] = drow[-u * N];
+      gg[u] = gyl[t];
+    }
+#pragma unroll
+    for (int u = 0; u < kBwdLoadBatch; ++u) {
       const bool ok = i0 + u < nst;
-      const int t = ok ? te - 1 - i0 - u : tb;
-      rr[u] = (act && ok) ? dic[kl[t] * N + j] : j;
-      dd[u] = act ? (ok ? Dl[t * N + j] : 1.f) : 0.f;
-      gg[u] = ok ? gyl[t] : 0.f;
+      if constexpr (PK) rr[u] = (int)((dk64[kk[u]] >> (4 * jr)) & 15u);
+      else rr[u] = dic[kk[u] * N + jr];
+      rr[u] = (act && ok) ? rr[u] : j;
+      dd[u] = act ? (ok ? dd[u] : 1.f) : 0.f;
+      gg[u] = ok ? gg[u] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kBwdLoadBatch; ++u) {

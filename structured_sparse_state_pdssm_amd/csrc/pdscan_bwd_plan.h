@@ -8,7 +8,11 @@ namespace pdscan {
 
 // LDS byte offsets of the backward kernel.
 struct BwdLds {
-  int off_dic, off_D, off_k, off_gy, off_C, off_s, off_p, off_slot, off_H, off_gc, off_misc, bytes;
+  int off_dic, off_dk, off_D, off_k, off_gy, off_C, off_s, off_p, off_slot, off_H, off_gc, off_misc, bytes;
+  // word stride between the lane groups' D rows: S*N, plus NP when that is a
+  // multiple of 64, so the groups of one half-wave reading their step i do
+  // not all land on the same banks
+  int GS;
 };
 
 // `p` is the forward scan plan with the same chunk: groups, steps per group,
@@ -19,7 +23,10 @@ inline bool make_bwd_lds(const Plan& p, BwdLds& l) {
   int off = 0;
   auto take = [&](int bytes) { int o = off; off = align_up(off + bytes, 16); return o; };
   l.off_dic = take(K * N * 4);
-  l.off_D = take(T * N * 4);
+  l.off_dk = take(K * 8);        // N <= 16: each dictionary row as 16 nibbles
+  l.GS = p.S * N;
+  if (p.NP < 64 && l.GS % 64 == 0) l.GS += p.NP;
+  l.off_D = take((G * l.GS + 16 * N) * 4);   // 8 rows of slack on each side (block reads past a group's ends)
   l.off_k = take(T * 4);
   l.off_gy = take(T * 4);
   l.off_C = take(N * 4);

@@ -17,7 +17,10 @@ hipError_t launch_bwd(const BwdArgs& a, float* g_C, hipStream_t st) {
   if (cb > 4096) cb = 4096;
   if (cb < 1) cb = 1;
   hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)cb), dim3(256), 0, st, (uint64_t*)a.ws, words);
-  hipLaunchKernelGGL(pdssm_bwd_kernel, dim3((unsigned)p.tasks), dim3(kThreads), (unsigned)a.l.bytes, st, a);
+  if (p.N <= 16)
+    hipLaunchKernelGGL(pdssm_bwd_kernel<true>, dim3((unsigned)p.tasks), dim3(kThreads), (unsigned)a.l.bytes, st, a);
+  else
+    hipLaunchKernelGGL(pdssm_bwd_kernel<false>, dim3((unsigned)p.tasks), dim3(kThreads), (unsigned)a.l.bytes, st, a);
   hipLaunchKernelGGL(pdssm_bwd_reduce_c, dim3((unsigned)p.H), dim3(kThreads), 0, st,
                      (const float*)(a.ws + a.ws_gc), g_C, p.nC, p.B, p.H, p.N);
   return hipGetLastError();

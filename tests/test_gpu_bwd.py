@@ -104,6 +104,23 @@ def test_bwd_chunk_independence(chunk):
     assert_within(host(out["g_C"]), g_C, f"chunk {chunk} g_C")
 
 
+@pytest.mark.parametrize("N,K", [(1, 1), (5, 3), (12, 7), (16, 16), (17, 4), (40, 9)])
+def test_bwd_state_sizes(N, K):
+    """State sizes off the power-of-two grid, on both sides of the 16-row
+    nibble-path limit, with a ragged final chunk."""
+    cs = _case("base", B=1, H=2, L=333, N=N, K=K)
+    d = _dev(cs)
+    g_Bu, g_D, g_h0, g_C = _ref(cs)
+    for chunk in (37, 128):
+        print(f"[gpu] pdssm_scan_bwd N={N} K={K} chunk={chunk}", flush=True)
+        _, _, Hs = _gpu_states(d, chunk)
+        out = _gpu_bwd(d, Hs, chunk)
+        assert_within(host(out["g_Bu"]), g_Bu, f"N={N} chunk {chunk} g_Bu")
+        assert_within(host(out["g_D"]), g_D, f"N={N} chunk {chunk} g_D")
+        assert_within(host(out["g_h0"]), g_h0, f"N={N} chunk {chunk} g_h0")
+        assert_within(host(out["g_C"]), g_C, f"N={N} chunk {chunk} g_C")
+
+
 def test_bwd_deterministic():
     cs = _case("impulse", H=4, L=1500)
     d = _dev(cs)
