@@ -261,21 +261,68 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- adjoint carries between chunks (wave 0): publish this chunk's map,
-  // look towards later chunks for the adjoint entering this one, publish the
-  // adjoint it passes on
+  // ---- adjoint carries between chunks.  All lanes (NP per chunk) read the
+  // carries and maps of the next kBwdLookWin later chunks in one batch; the
+  // nearest published carry with every map before it present settles the
+  // adjoint entering this chunk in one memory round trip.  Otherwise wave 0
+  // polls as below.
+  if (wave == 0 && lane < N) {                     // this chunk's map, for earlier chunks
+    uint64_t* my = agg + ((size_t)c * BH + s) * 3 * N;
+    put_tagged(my + lane, (uint32_t)pSrc[lane]);
+    put_tagged(my + N + lane, __float_as_uint(pW[lane]));
+    put_tagged(my + 2 * N + lane, __float_as_uint(pB[lane]));
+  }
+  const int later = p.nC - 1 - c;                  // chunks after this one
+  const int wq = min(min(kThreads / NP, kBwdLookWin), later);
+  int* wSrc = (int*)(smem + a.l.off_win);          // [kBwdLookWin][N] window maps and carries
+  float* wW = (float*)(wSrc + kBwdLookWin * N);
+  float* wB = wW + kBwdLookWin * N;
+  float* wI = wB + kBwdLookWin * N;
+  int* wFlag = (int*)(wI + kBwdLookWin * N);       // bit 0: carry complete, bit 1: map complete
+  if (later > 0) {
+    const int qq = tid / NP, jj = tid % NP;
+    const bool in = qq < wq, on = in && jj < N;
+    uint64_t iv = kTagValid, m0 = kTagValid, m1 = kTagValid, m2 = kTagValid;
+    if (on) {
+      const size_t cq = (size_t)(c + 1 + qq) * BH + s;
+      iv = get_tagged(inc + cq * N + jj);
+      m0 = get_tagged(agg + cq * 3 * N + jj);
+      m1 = get_tagged(agg + cq * 3 * N + N + jj);
+      m2 = get_tagged(agg + cq * 3 * N + 2 * N + jj);
+      wI[qq * N + jj] = __uint_as_float((uint32_t)iv);
+      wSrc[qq * N + jj] = (int)(uint32_t)m0;
+      wW[qq * N + jj] = __uint_as_float((uint32_t)m1);
+      wB[qq * N + jj] = __uint_as_float((uint32_t)m2);
+    }
+    const uint64_t bi = __ballot(tag_ok(iv));
+    const uint64_t ba = __ballot(tag_ok(m0) && tag_ok(m1) && tag_ok(m2));
+    if (in && jj == 0) {                           // NP <= 64: a chunk's lanes share a wave
+      const uint64_t gm = NP >= 64 ? ~0ull : (((1ull << NP) - 1ull) << lane);
+      wFlag[qq] = ((bi & gm) == gm ? 1 : 0) | ((ba & gm) == gm ? 2 : 0);
+    }
+  }
+  __syncthreads();
+
+  // find the adjoint entering this chunk, publish the adjoint it passes on
+  // (wave 0)
   if (wave == 0) {
     const bool on = lane < N;
     const int ln = on ? lane : 0;
-    uint64_t* my = agg + ((size_t)c * BH + s) * 3 * N;
-    if (on) {
-      put_tagged(my + lane, (uint32_t)pSrc[ln]);
-      put_tagged(my + N + lane, __float_as_uint(pW[ln]));
-      put_tagged(my + 2 * N + lane, __float_as_uint(pB[ln]));
-    }
     float nu = (on && a.g_hL) ? a.g_hL[(size_t)s * N + lane] : 0.f;   // entering the last chunk
-    const int later = p.nC - 1 - c;                // chunks after this one
-    if (later > 0) {
+    int hit = -1;
+    for (int q = 0; q < wq; ++q) {
+      const int f = wFlag[q];
+      if (f & 1) { hit = q; break; }
+      if (!(f & 2)) break;
+    }
+    if (hit >= 0) {
+      // the carry of chunk c+1+hit, then the maps of chunks c+hit .. c+1
+      if (on) nu = wI[hit * N + lane];
+      for (int q = hit - 1; q >= 0; --q) {
+        const float nv = grp_gather(nu, 0, on ? wSrc[q * N + lane] : lane);
+        if (on) nu = wW[q * N + lane] * nv + wB[q * N + lane];
+      }
+    } else if (later > 0) {
       // lane l polls chunk c+1+l: the nearest one whose passed-on adjoint is
       // published, with every map between present
       const int win = min(later, 64);
@@ -363,10 +410,17 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   const int pre = c0 > 0 ? 1 : 0;
   const rsrc_t hr = make_rsrc(a.H_all + (gbase - pre) * N, (uint32_t)((Tc + pre) * N * 4));
   const float hinit = (act && c0 == 0 && a.h0) ? a.h0[(size_t)s * N + j] : 0.f;
-  auto h_off = [&](int i) -> uint32_t {   // byte offset of v_i, kNoLoad outside
-    const int x = te - 1 - i + pre;       // row within hr
-    return (act && i <= te - tb && x >= 0) ? (uint32_t)(x * N + j) * 4u : kNoLoad;
+  // byte offset of v_i in hr: row te-1-i+pre, kNoLoad outside
+  const int h_top = ((te - 1 + pre) * N + j) * 4;
+  auto h_off = [&](int i) -> uint32_t {
+    return (act && i <= nst && te - 1 - i + pre >= 0) ? (uint32_t)(h_top - i * N * 4) : kNoLoad;
   };
+  // gradients of the chunk through buffer stores: byte offset of (t, j) is
+  // (t N + j) 4, walking down from t = te-1; idle lanes and steps past the
+  // left end store to kNoLoad, which the hardware drops
+  const rsrc_t bur = make_rsrc(a.g_Bu + gbase * N, (uint32_t)(Tc * N * 4));
+  const rsrc_t gdr = make_rsrc(a.g_D + gbase * N, (uint32_t)(Tc * N * 4));
+  const int s_top = ((te - 1) * N + j) * 4;
   float xr = act ? slots[gam * NP + j] : 0.f;
   float gc = 0.f;
   float h_cur = buf_f32(hr, h_off(0));
@@ -396,20 +450,19 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
       dd[u] = act ? (ok ? dd[u] : 1.f) : 0.f;
       gg[u] = ok ? gg[u] : 0.f;
     }
+    const int s_blk = s_top - i0 * N * 4;
 #pragma unroll
     for (int u = 0; u < kBwdLoadBatch; ++u) {
       const int i = i0 + u;
-      const int t = te - 1 - i;
+      const bool ok = i < nst;
       const float lam = xr + cj * gg[u];
       const float lr = grp_gather(lam, base, rr[u]);
-      const float h_prev = (c0 + t > 0) ? hv[u] : hinit;
+      const float h_prev = (c0 + te - 1 - i > 0) ? hv[u] : hinit;
       gc += gg[u] * h_cur;   // gg is zero past the left end
-      if (act && i < nst) {
-        const size_t row = (gbase + t) * N;
-        a.g_Bu[row + j] = lam;
-        a.g_D[row + j] = lr * h_prev;
-      }
-      if (i < nst) h_cur = h_prev;
+      const uint32_t so = (act && ok) ? (uint32_t)(s_blk - u * N * 4) : kNoLoad;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lam), bur, so, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lr * h_prev), gdr, so, 0, 0);
+      h_cur = ok ? h_prev : h_cur;
       xr = dd[u] * lr;
     }
   }

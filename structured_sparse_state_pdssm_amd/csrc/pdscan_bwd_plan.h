@@ -6,9 +6,12 @@
 
 namespace pdscan {
 
+// Later chunks whose carries and maps the look-back reads in one batch.
+constexpr int kBwdLookWin = 8;
+
 // LDS byte offsets of the backward kernel.
 struct BwdLds {
-  int off_dic, off_dk, off_D, off_k, off_gy, off_C, off_s, off_p, off_slot, off_H, off_gc, off_misc, bytes;
+  int off_dic, off_dk, off_D, off_k, off_gy, off_C, off_s, off_p, off_slot, off_H, off_gc, off_win, off_misc, bytes;
   // word stride between the lane groups' D rows: S*N, plus NP when that is a
   // multiple of 64, so the groups of one half-wave reading their step i do
   // not all land on the same banks
@@ -35,6 +38,7 @@ inline bool make_bwd_lds(const Plan& p, BwdLds& l) {
   l.off_slot = take(kThreads * 4);
   l.off_H = take(64 * 4);
   l.off_gc = take(G * N * 4);
+  l.off_win = take(kBwdLookWin * (4 * N + 1) * 4);   // look-back window: maps, carries, flags
   l.off_misc = take(16);
   l.bytes = off;
   return l.bytes <= kMaxLds;
