@@ -31,8 +31,6 @@ __device__ __forceinline__ int grp_gather_i(int v, int base, int src) {
   return __builtin_amdgcn_ds_bpermute((base + src) << 2, v);
 }
 
-// Adjoint map words one lane of the look-back wave loads per batch.
-constexpr int kBwdLookBatch = 4;
 // Loads one lane keeps in flight when staging the chunk and in the replay.
 constexpr int kBwdLoadBatch = 8;
 // 16 nibbles mapping every row to itself.
@@ -261,12 +259,13 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- adjoint carries between chunks.  All lanes (NP per chunk) read the
-  // carries and maps of the next kBwdLookWin later chunks in one batch; the
-  // nearest published carry with every map before it present settles the
-  // adjoint entering this chunk in one memory round trip.  Otherwise wave 0
-  // polls as below.
-  if (wave == 0 && lane < N) {                     // this chunk's map, for earlier chunks
+  // ---- adjoint carries between chunks.  This chunk's map is published
+  // first; then all lanes (NP per chunk) read the carries and maps of the
+  // next later chunks in one batch.  The nearest published carry with every
+  // map before it present settles the adjoint entering this chunk; without
+  // one the window is read again (chunk c+1 publishes its carry without
+  // waiting for this chunk, so the loop ends).
+  if (wave == 0 && lane < N) {
     uint64_t* my = agg + ((size_t)c * BH + s) * 3 * N;
     put_tagged(my + lane, (uint32_t)pSrc[lane]);
     put_tagged(my + N + lane, __float_as_uint(pW[lane]));
@@ -279,7 +278,8 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
   float* wB = wW + kBwdLookWin * N;
   float* wI = wB + kBwdLookWin * N;
   int* wFlag = (int*)(wI + kBwdLookWin * N);       // bit 0: carry complete, bit 1: map complete
-  if (later > 0) {
+  int hit = -1;
+  for (int spins = 0; wq > 0; ++spins) {
     const int qq = tid / NP, jj = tid % NP;
     const bool in = qq < wq, on = in && jj < N;
     uint64_t iv = kTagValid, m0 = kTagValid, m1 = kTagValid, m2 = kTagValid;
@@ -300,84 +300,32 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
       const uint64_t gm = NP >= 64 ? ~0ull : (((1ull << NP) - 1ull) << lane);
       wFlag[qq] = ((bi & gm) == gm ? 1 : 0) | ((ba & gm) == gm ? 2 : 0);
     }
-  }
-  __syncthreads();
-
-  // find the adjoint entering this chunk, publish the adjoint it passes on
-  // (wave 0)
-  if (wave == 0) {
-    const bool on = lane < N;
-    const int ln = on ? lane : 0;
-    float nu = (on && a.g_hL) ? a.g_hL[(size_t)s * N + lane] : 0.f;   // entering the last chunk
-    int hit = -1;
-    for (int q = 0; q < wq; ++q) {
+    __syncthreads();
+    for (int q = 0; q < wq; ++q) {                 // the same answer in every lane
       const int f = wFlag[q];
       if (f & 1) { hit = q; break; }
       if (!(f & 2)) break;
     }
+    if (hit >= 0) break;
+    if (spins >= kSpinLimit) {
+      if (tid == 0) atomicOr(&hdr[kWsError], 1u);
+      break;
+    }
+    __syncthreads();                               // the window is rewritten
+    __builtin_amdgcn_s_sleep(1);
+  }
+
+  // the adjoint entering this chunk, then the one it passes on (wave 0)
+  if (wave == 0) {
+    const bool on = lane < N;
+    const int ln = on ? lane : 0;
+    float nu = (on && a.g_hL) ? a.g_hL[(size_t)s * N + lane] : 0.f;   // entering the last chunk
     if (hit >= 0) {
       // the carry of chunk c+1+hit, then the maps of chunks c+hit .. c+1
       if (on) nu = wI[hit * N + lane];
       for (int q = hit - 1; q >= 0; --q) {
         const float nv = grp_gather(nu, 0, on ? wSrc[q * N + lane] : lane);
         if (on) nu = wW[q * N + lane] * nv + wB[q * N + lane];
-      }
-    } else if (later > 0) {
-      // lane l polls chunk c+1+l: the nearest one whose passed-on adjoint is
-      // published, with every map between present
-      const int win = min(later, 64);
-      int stop = 0, spins = 0;
-      while (true) {
-        const int q = c + 1 + lane;
-        bool iv = false, av = false;
-        if (lane < win) {
-          iv = tag_ok(get_tagged(inc + ((size_t)q * BH + s) * N));
-          av = tag_ok(get_tagged(agg + ((size_t)q * BH + s) * 3 * N));
-        }
-        const uint64_t mi = __ballot(iv), ma = __ballot(av);
-        const int li = mi ? __builtin_ctzll(mi) : 64;
-        const int need = li < win ? li : win;
-        const uint64_t nm = need >= 64 ? ~0ull : ((1ull << need) - 1ull);
-        if ((ma & nm) == nm && (li < win || later <= 64)) {
-          stop = need;
-          break;
-        }
-        if (++spins > kSpinLimit) {
-          if (lane == 0) atomicOr(&hdr[kWsError], 1u);
-          stop = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (stop < later) {
-        // base: the adjoint passed on by chunk c+1+stop
-        uint64_t* pw = inc + ((size_t)(c + 1 + stop) * BH + s) * N;
-        if (on) {
-          uint64_t wv = get_tagged(pw + lane);
-          for (int n = 0; !tag_ok(wv) && n < kSpinLimit; ++n) wv = get_tagged(pw + lane);
-          nu = __uint_as_float((uint32_t)wv);
-        }
-      }
-      // apply the maps of chunks c+stop .. c+1, farthest first
-      for (int q0 = c + stop; q0 > c; q0 -= kBwdLookBatch) {
-        uint64_t wv[kBwdLookBatch][3];
-#pragma unroll
-        for (int u = 0; u < kBwdLookBatch; ++u) {
-          uint64_t* pa = agg + ((size_t)(q0 - u) * BH + s) * 3 * N;
-#pragma unroll
-          for (int f = 0; f < 3; ++f) wv[u][f] = (on && q0 - u > c) ? get_tagged(pa + f * N + lane) : kTagValid;
-        }
-#pragma unroll
-        for (int u = 0; u < kBwdLookBatch; ++u) {
-          if (q0 - u <= c) break;
-          uint64_t* pa = agg + ((size_t)(q0 - u) * BH + s) * 3 * N;
-#pragma unroll
-          for (int f = 0; f < 3; ++f)
-            for (int n = 0; on && !tag_ok(wv[u][f]) && n < kSpinLimit; ++n) wv[u][f] = get_tagged(pa + f * N + lane);
-          const int rs = on ? (int)(uint32_t)wv[u][0] : lane;
-          const float nv = grp_gather(nu, 0, rs);
-          if (on) nu = __uint_as_float((uint32_t)wv[u][1]) * nv + __uint_as_float((uint32_t)wv[u][2]);
-        }
       }
     }
     // the adjoint this chunk passes on: its whole map applied to nu

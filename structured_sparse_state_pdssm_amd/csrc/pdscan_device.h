@@ -630,8 +630,8 @@ __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, i
 // brings the summary (midx, msc, hl) of its group's sub-chunk; w_t is in the
 // [N][TS] buffer and the local outputs in yloc.
 // ---------------------------------------------------------------------------
-// Words of look-back data one lane requests per batch (64-bit each).
-constexpr int kLookBatchWords = 12;
+// Previous chunks whose states and aggregates phase B reads in one batch.
+constexpr int kLookWin = 8;
 
 template <bool ROW16>
 __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, int c, int s, int Tc,
@@ -706,104 +706,92 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
   }
   __syncthreads();
 
-  // ---- phase B (wave 0): publish the chunk aggregate, look back for the
-  // carry into this chunk, publish the inclusive state
+  // ---- phase B: publish the chunk aggregate (wave 0); all lanes (NP per
+  // chunk) read the inclusive states and aggregates of the previous chunks
+  // in one batch into the combine's scratch (free by now).  The nearest
+  // inclusive state with every aggregate after it present gives the carry;
+  // without one the window is read again (chunk c-1 publishes its state
+  // without waiting for this chunk, so the loop ends).
+  const int lq = (G - 1) * N + (lane < N ? lane : 0);
+  if (wave == 0 && lane < N) {
+    uint64_t* my = agg + ((size_t)c * BH + s) * 3 * N;
+    put_tagged(my + lane, (uint32_t)pIdx[lq]);
+    put_tagged(my + N + lane, __float_as_uint(pSc[lq]));
+    put_tagged(my + 2 * N + lane, __float_as_uint(pB[lq]));
+  }
+  // window rows that fit the scratch (four [wst][N] arrays, then the flags;
+  // at least one row for every supported N)
+  const int wst = min(kLookWin, ((p.off_pIdx - p.off_sIdx) - 4 * kLookWin) / (16 * N));
+  const int wq = min(min(kThreads / NP, wst), c);
+  int* wIdx = sIdx;                                // [wst][N] window aggregates and states
+  float* wSc = (float*)(wIdx + wst * N);
+  float* wB = wSc + wst * N;
+  float* wI = wB + wst * N;
+  int* wFlag = (int*)(wI + wst * N);               // bit 0: state complete, bit 1: aggregate complete
+  int hit = -1;
+  for (int spins = 0; wq > 0; ++spins) {
+    const int qq = tid / NP, jj = tid % NP;
+    const bool in = qq < wq, on = in && jj < N;
+    uint64_t iv = kTagValid, m0 = kTagValid, m1 = kTagValid, m2 = kTagValid;
+    if (on) {
+      const size_t cq = (size_t)(c - 1 - qq) * BH + s;
+      iv = get_tagged(inc + cq * N + jj);
+      m0 = get_tagged(agg + cq * 3 * N + jj);
+      m1 = get_tagged(agg + cq * 3 * N + N + jj);
+      m2 = get_tagged(agg + cq * 3 * N + 2 * N + jj);
+      wI[qq * N + jj] = __uint_as_float((uint32_t)iv);
+      wIdx[qq * N + jj] = (int)(uint32_t)m0;
+      wSc[qq * N + jj] = __uint_as_float((uint32_t)m1);
+      wB[qq * N + jj] = __uint_as_float((uint32_t)m2);
+    }
+    const uint64_t bi = __ballot(tag_ok(iv));
+    const uint64_t ba = __ballot(tag_ok(m0) && tag_ok(m1) && tag_ok(m2));
+    if (in && jj == 0) {                           // NP <= 64: a chunk's lanes share a wave
+      const uint64_t gm = NP >= 64 ? ~0ull : (((1ull << NP) - 1ull) << lane);
+      wFlag[qq] = ((bi & gm) == gm ? 1 : 0) | ((ba & gm) == gm ? 2 : 0);
+    }
+    __syncthreads();
+    for (int q = 0; q < wq; ++q) {                 // the same answer in every lane
+      const int f = wFlag[q];
+      if (f & 1) { hit = q; break; }
+      if (!(f & 2)) break;
+    }
+    if (hit >= 0) break;
+    if (spins >= kSpinLimit) {
+      if (tid == 0) atomicOr(&hdr[kWsError], 1u);
+      break;
+    }
+    __syncthreads();                               // the window is rewritten
+    __builtin_amdgcn_s_sleep(1);
+  }
+
+  // the carry into this chunk, then the inclusive state (wave 0)
   if (wave == 0) {
     const bool on = lane < N;
-    const int lq = (G - 1) * N + (on ? lane : 0);
     const int ai = pIdx[lq];
     const float as = pSc[lq], ab = pB[lq];
-    uint64_t* my = agg + ((size_t)c * BH + s) * 3 * N;
-    if (on) {
-      put_tagged(my + lane, (uint32_t)ai);
-      put_tagged(my + N + lane, __float_as_uint(as));
-      put_tagged(my + 2 * N + lane, __float_as_uint(ab));
-    }
-
-    float x = (on && a.h0) ? a.h0[(size_t)s * N + lane] : 0.f;
-    if (c > 0) {
-      // Poll up to 64 predecessors at once (lane l looks at chunk c-1-l) for
-      // the nearest inclusive state with every aggregate after it present.
-      const int win = min(c, 64);
-      int stop = 0, spins = 0;
-      while (true) {
-        const int q = c - 1 - lane;
-        bool iv = false, av = false;
-        if (lane < win) {
-          iv = tag_ok(get_tagged(inc + ((size_t)q * BH + s) * N));
-          av = tag_ok(get_tagged(agg + ((size_t)q * BH + s) * 3 * N));
-        }
-        const uint64_t mi = __ballot(iv), ma = __ballot(av);
-        const int li = mi ? __builtin_ctzll(mi) : 64;
-        const int need = li < win ? li : win;
-        const uint64_t nm = need >= 64 ? ~0ull : ((1ull << need) - 1ull);
-        if ((ma & nm) == nm && (li < win || c <= 64)) {
-          stop = need;
-          break;
-        }
-        if (++spins > kSpinLimit) {
-          if (lane == 0) atomicOr(&hdr[kWsError], 1u);
-          stop = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      // The base state (the inclusive state `stop` chunks back, unless the
-      // window reaches chunk 0 and h0 is the base) and the aggregates after
-      // it are loaded in batches: every word of a batch is requested at once
-      // (one round trip), checked, and staged in LDS (the combine's scratch,
-      // free by now); the aggregates are then applied oldest first.
-      uint32_t* stage = (uint32_t*)sIdx;
-      const int wcap = min((p.off_pIdx - p.off_sIdx) / 4, 64 * kLookBatchWords);
-      const int nbmax = (wcap - N) / (3 * N);
-      bool need_base = stop < c;
-      const int base_q = c - 1 - stop;
-      for (int q0 = c - stop; need_base || q0 < c;) {
-        const int nb = min(c - q0, nbmax);
-        const int nbase = need_base ? N : 0;
-        const int W = nbase + nb * 3 * N;
-        auto word_ptr = [&](int w) -> uint64_t* {
-          if (w < nbase) return inc + ((size_t)base_q * BH + s) * N + w;
-          const int r = w - nbase, aq = r / (3 * N);
-          return agg + ((size_t)(q0 + aq) * BH + s) * 3 * N + (r - aq * 3 * N);
-        };
-        uint64_t wv[kLookBatchWords];
-#pragma unroll
-        for (int u = 0; u < kLookBatchWords; ++u) {
-          const int w = lane + 64 * u;
-          wv[u] = w < W ? get_tagged(word_ptr(w)) : kTagValid;
-        }
-#pragma unroll
-        for (int u = 0; u < kLookBatchWords; ++u) {
-          const int w = lane + 64 * u;
-          if (w < W) {
-            for (int n = 0; !tag_ok(wv[u]) && n < kSpinLimit; ++n) wv[u] = get_tagged(word_ptr(w));
-            stage[w] = (uint32_t)wv[u];
-          }
-        }
+    // x <- scatter of (scale .* x) by idx, plus b: one aggregate applied
+    auto apply = [&](float& x, int ri, float rsc, float rb) {
+      const float rv = on ? rsc * x : 0.f;
+      if constexpr (ROW16) {
+        const float xn = row_gather_add(on ? rb : 0.f, on ? ri : -1, rv, lane);
+        if (on) x = xn;
+      } else {
+        if (on) tmp[lane] = rb;
         WAVE_SYNC();
-        if (need_base && on) x = __uint_as_float(stage[lane]);
-        for (int aq = 0; aq < nb; ++aq) {
-          const uint32_t* e = stage + nbase + aq * 3 * N;
-          const float rb = on ? __uint_as_float(e[2 * N + lane]) : 0.f;
-          const int ri = on ? (int)e[lane] : -1;
-          const float rv = on ? __uint_as_float(e[N + lane]) * x : 0.f;
-          if constexpr (ROW16) {
-            const float xn = row_gather_add(rb, ri, rv, lane);
-            if (on) x = xn;
-          } else {
-            if (on) tmp[lane] = rb;
-            WAVE_SYNC();
-            if (on) atomicAdd(&tmp[ri], rv);
-            WAVE_SYNC();
-            if (on) x = tmp[lane];
-            WAVE_SYNC();
-          }
-        }
-        WAVE_SYNC();                               // staging is reused by the next batch
-        q0 += nb;
-        need_base = false;
+        if (on) atomicAdd(&tmp[ri], rv);
+        WAVE_SYNC();
+        if (on) x = tmp[lane];
+        WAVE_SYNC();
       }
+    };
+    float x = (on && a.h0) ? a.h0[(size_t)s * N + lane] : 0.f;
+    if (hit >= 0) {
+      // the inclusive state of chunk c-1-hit, then the aggregates of chunks
+      // c-hit .. c-1, oldest first
+      if (on) x = wI[hit * N + lane];
+      for (int q = hit - 1; q >= 0; --q)
+        apply(x, on ? wIdx[q * N + lane] : 0, on ? wSc[q * N + lane] : 0.f, on ? wB[q * N + lane] : 0.f);
     }
     // inclusive state of this chunk, with the same arithmetic
     float xo;
