@@ -8,6 +8,9 @@ fp64 CPU oracle timed beside it.
 
 ``--pass bwd`` times the gradient pass through the scan (pdssm_scan_bwd) on
 the same workload instead, with its own roofline and oracle baseline.
+``timing`` in the JSON line gives the median, p10 and p90 of the per-call
+event durations with warm caches ("hot") and with a 1 GiB fill before each
+call ("cold").
 
 Prints one JSON line.  A step is one pdssm_fwd call over the whole workload
 (selection outputs not materialised), with every input already resident in
@@ -32,15 +35,22 @@ METRIC = "state-updates/sec (B·H·L·N) PD-SSM fwd select+scan; achieved HBM GB
 CSRC = os.path.join(ROOT, "structured_sparse_state_pdssm_amd", "csrc")
 
 
-# the sources the benchmarked forward kernel is built from
-FWD_SOURCES = ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_fused.hip")
+# the sources each benchmarked kernel is built from
+SOURCES = {
+    "fwd": ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_fused.hip"),
+    "bwd": ("pdscan_device.h", "pdscan_plan.h", "pdscan_bwd_plan.h", "pdscan_bwd.h",
+            "pdscan_launch_bwd.hip"),
+}
+# stem of the committed counter summary of each pass
+TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd"}
+COLD_FILL_BYTES = 1 << 30       # written before each cold-cache rep (beyond L2 and MALL)
 
 
-def kernel_hash() -> str:
-    """Hash of the forward kernel's sources: ties a stored counter summary to
-    the kernel it was measured on."""
+def kernel_hash(which="fwd") -> str:
+    """Hash of a kernel's sources: ties a stored counter summary to the kernel
+    it was measured on."""
     h = hashlib.sha256()
-    for name in FWD_SOURCES:
+    for name in SOURCES[which]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -70,17 +80,48 @@ def algorithmic_bwd(cfg):
     return steps * per_step + small
 
 
-def traffic_from_profile(workload):
+def traffic_from_profile(workload, which="fwd"):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"pdssm_fused_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{TRAFFIC_STEM[which]}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_hash") != kernel_hash():
+    if rec.get("kernel_hash") != kernel_hash(which):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def time_calls(torch, np, step, reps, stream):
+    """Per-call durations (µs) from HIP events on the launch stream: `reps`
+    back-to-back calls with warm caches, then `reps` calls each preceded
+    (outside its events) by a 1 GiB fill that evicts L2 and MALL."""
+    def pct(v):
+        return {"median_us": round(float(np.median(v)), 2), "p10_us": round(float(np.percentile(v, 10)), 2),
+                "p90_us": round(float(np.percentile(v, 90)), 2), "mean_us": round(float(np.mean(v)), 2)}
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    hot = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    fill = torch.empty(COLD_FILL_BYTES // 4, device="cuda")
+    cold = []
+    for _ in range(reps):
+        fill.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        cold.append(a.elapsed_time(b) * 1e3)
+    del fill
+    return wall, hot, {"reps": reps, "hot": pct(hot), "cold": pct(cold)}
 
 
 COPY_PROBE_BYTES = 1 << 30      # the plain copy kernel's source (and destination) size
@@ -109,31 +150,36 @@ def _pmc_rows(d, counter):
     return rows
 
 
-def pmc_summary(fetch_dir, write_dir, workload):
+def _is_kernel(name, which):
+    if which == "bwd":
+        return "pdssm_bwd_kernel" in name
+    return "pdssm_" in name and "clear" not in name and "bwd" not in name
+
+
+def pmc_summary(fetch_dir, write_dir, workload, which="fwd"):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
     dispatch) of `bench.py --copy-probe` into HBM bytes per launch of the
-    fused kernel, each counter scaled by what it reads for the copy probe."""
+    benchmarked kernel, each counter scaled by what it reads for the copy
+    probe."""
     from statistics import mean
     out = {}
     for counter, d, probe_bytes in (("FETCH_SIZE", fetch_dir, COPY_PROBE_BYTES),
                                     ("WRITE_SIZE", write_dir, COPY_PROBE_BYTES)):
         rows = _pmc_rows(d, counter)
-        kern = [float(r["Counter_Value"]) for r in rows if "pdssm_" in r["Kernel_Name"]
-                and "clear" not in r["Kernel_Name"]]
+        kern = [float(r["Counter_Value"]) for r in rows if _is_kernel(r["Kernel_Name"], which)]
         probe = [float(r["Counter_Value"]) for r in rows if "neg" in r["Kernel_Name"]]
         if not kern or not probe:
-            raise SystemExit(f"{counter}: no fused-kernel or copy-probe dispatches under {d}")
-        names = sorted({r["Kernel_Name"] for r in rows if "pdssm_" in r["Kernel_Name"]
-                        and "clear" not in r["Kernel_Name"]})
+            raise SystemExit(f"{counter}: no {which} kernel or copy-probe dispatches under {d}")
+        names = sorted({r["Kernel_Name"] for r in rows if _is_kernel(r["Kernel_Name"], which)})
         scale = probe_bytes / (mean(probe) * 1024.0)
         out[counter] = {"kernel_kib": mean(kern), "probe_kib": mean(probe),
                         "scale": scale, "bytes": mean(kern) * 1024.0 * scale,
                         "dispatches": len(kern), "kernels": names}
     total = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
-    rec = {"workload": workload, "kernel_hash": kernel_hash(),
+    rec = {"workload": workload, "pass": which, "kernel_hash": kernel_hash(which),
            "hbm_bytes_per_launch": round(total), "counters": out,
            "copy_probe_bytes": COPY_PROBE_BYTES}
-    path = os.path.join(ROOT, "profiles", f"pdssm_fused_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{TRAFFIC_STEM[which]}_{workload}_traffic.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
@@ -208,23 +254,16 @@ def bench_bwd(args, torch, np, P):
     if P.workspace_error_flag(ws):
         raise RuntimeError("look-back wait gave up during warm-up")
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    wall, hot, timing = time_calls(torch, np, step, args.steps, stream)
+    if P.workspace_error_flag(ws):
+        raise RuntimeError("look-back wait gave up during timing")
+    launch_s = float(np.mean(hot)) / 1e6
     ms_step = wall * 1e3 / args.steps
     alg = algorithmic_bwd(cfg)
     achieved = alg / launch_s / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None, "algorithmic_bytes": alg,
-            "launch_us": round(launch_s * 1e6, 2)}
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_from_profile(cfg.name, "bwd"),
+            "algorithmic_bytes": alg, "launch_us": round(launch_s * 1e6, 2)}
     rec = {
         "metric": "state-updates/sec (B·H·L·N) PD-SSM gradient through the scan (fixed selections)",
         "value": cfg.state_updates / (ms_step / 1e3),
@@ -237,7 +276,11 @@ def bench_bwd(args, torch, np, P):
                                f"K={cfg.K} chunk={chunk}",
                    "B": cfg.B, "H": cfg.H, "L": cfg.L, "N": cfg.N, "K": cfg.K, "chunk": chunk},
         "roofline": roof,
+        "timing": timing,
+        "kernel_hash": kernel_hash("bwd"),
     }
+    if args.copy_probe:
+        copy_probe(torch)
     if not args.no_cpu_baseline:
         import oracle
         cores = len(os.sched_getaffinity(0))
@@ -256,7 +299,7 @@ def bench_bwd(args, torch, np, P):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="impulse")
     ap.add_argument("--chunk", type=int, default=None)
@@ -269,7 +312,7 @@ def main():
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary, args.workload)
+        pmc_summary(*args.pmc_summary, args.workload, args.which)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -314,19 +357,11 @@ def main():
         raise RuntimeError("look-back wait gave up during warm-up")
     # per-launch durations with events on the stream the kernels run on
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    wall, hot, timing = time_calls(torch, np, step, args.steps, stream)
+    if P.workspace_error_flag(ws):
+        raise RuntimeError("look-back wait gave up during timing")
     ms_step = wall * 1e3 / args.steps
-    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    avg_launch_s = float(np.mean(hot)) / 1e6
 
     alg_bytes, flops = algorithmic(cfg)
     # the dominant cost: HBM traffic, except where the score GEMM outweighs it
@@ -341,7 +376,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = traffic_from_profile(cfg.name)
+    roof["traffic"] = traffic_from_profile(cfg.name, "fwd")
     roof["algorithmic_bytes"] = alg_bytes
     roof["launch_us"] = round(avg_launch_s * 1e6, 2)
 
@@ -360,7 +395,8 @@ def main():
                    "chunk": chunk, "u_dtype": cfg.dtype, "state_dtype": "f32"},
         "hbm_GBps": round(alg_bytes / avg_launch_s / 1e9, 1),
         "roofline": roof,
-        "kernel_hash": kernel_hash(),
+        "timing": timing,
+        "kernel_hash": kernel_hash("fwd"),
     }
     if args.copy_probe:
         copy_probe(torch)
