@@ -5,7 +5,9 @@ TEST INFRASTRUCTURE: imported only by the tests, the smoke check and the
 benchmark's CPU-baseline leg; never by the product path."""
 
 from .pdssm_oracle import (  # noqa: F401
+    drive,
     forward,
+    forward_wb,
     forward_inputs,
     pd_apply,
     pd_compose,

@@ -23,6 +23,9 @@ It is the plain definition, written out slowly:
 Everything is upcast exactly to fp64 first.  ``scan`` builds the dense N x N
 transition of every step and multiplies; it never uses the sparse structure.
 
+``forward_wb`` is the same forward pass with the drive terms Bu_t = W_b u_t
+formed from the input (``drive``) instead of being given.
+
 ``scan_vjp`` is the gradient of a scalar loss through that recurrence for
 fixed selections (the adjoint recurrence with the dense transposed
 transitions); ``scan_states`` returns the state after every step, which the
@@ -203,6 +206,24 @@ def forward(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0=None, u_shared=False):
     k_star, D, s = select(u, W_sel, W_d, b_d, u_shared)
     y, hL = scan(k_star, dict_idx, D, Bu, C, h0)
     return {"k_star": k_star, "D": D, "scores": s, "y": y, "h_L": hL}
+
+
+def drive(u, W_b, u_shared=False):
+    """Drive terms of the recurrence, Bu_t = W_b u_t for every head, in fp64:
+    out[b,h,t,n] = sum_c W_b[h,n,c] u[b,(h),t,c] (the input map B of the
+    linear SSM in the problem statement of the same summary).  It is the same
+    linear form as the scores, with W_b's rows as the outputs."""
+    return scores(u, W_b, u_shared)
+
+
+def forward_wb(u, W_sel, dict_idx, W_d, b_d, W_b, C, h0=None, u_shared=False):
+    """``forward`` with the drive terms formed from u and W_b instead of given.
+
+    Returns dict(k_star, D, scores, Bu, y, h_L)."""
+    Bu = drive(u, W_b, u_shared)
+    out = forward(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0, u_shared)
+    out["Bu"] = Bu
+    return out
 
 
 def forward_inputs(inp, L=None):
