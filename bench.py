@@ -7,7 +7,9 @@ fp64 CPU oracle timed beside it.
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload impulse]
 
 ``--pass bwd`` times the gradient pass through the scan (pdssm_scan_bwd) on
-the same workload instead, with its own roofline and oracle baseline.
+the same workload instead, with its own roofline and oracle baseline;
+``--pass fold`` times pdssm_fwd_wb (the drive term formed from u and W_b in
+the same pass, so Bu is never read).
 ``timing`` in the JSON line gives the median, p10 and p90 of the per-call
 event durations with warm caches ("hot") and with a 1 GiB fill before each
 call ("cold").
@@ -32,6 +34,8 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (matrix / packed vector)
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 METRIC = "state-updates/sec (B·H·L·N) PD-SSM fwd select+scan; achieved HBM GB/s vs peak"
+METRIC_FOLD = ("state-updates/sec (B·H·L·N) PD-SSM fwd select+scan with Bu = W_b u folded into the "
+               "selection GEMM; achieved HBM GB/s vs peak")
 CSRC = os.path.join(ROOT, "structured_sparse_state_pdssm_amd", "csrc")
 
 
@@ -41,8 +45,9 @@ SOURCES = {
     "bwd": ("pdscan_device.h", "pdscan_plan.h", "pdscan_bwd_plan.h", "pdscan_bwd.h",
             "pdscan_launch_bwd.hip"),
 }
+SOURCES["fold"] = SOURCES["fwd"]
 # stem of the committed counter summary of each pass
-TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd"}
+TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd", "fold": "pdssm_fold"}
 COLD_FILL_BYTES = 1 << 30       # written before each cold-cache rep (beyond L2 and MALL)
 
 
@@ -57,15 +62,19 @@ def kernel_hash(which="fwd") -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(cfg):
+def algorithmic(cfg, fold=False):
     """Minimum traffic: every input read once, outputs written once; and the
-    score-GEMM flops 2 (K + N) d per (b, h, t)."""
+    selection-GEMM flops 2 (K + N) d per (b, h, t).  fold: the drive term is
+    formed from u and W_b (no Bu read; W_b read; 2 N d more flops)."""
     es = 2 if cfg.dtype == "bf16" else 4
     B, H, L, N, K, d = cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, cfg.d
     u = B * (1 if cfg.u_shared else H) * L * d * es
     params = H * K * d * es + H * N * d * es + H * N * 4 + H * K * N * 4 + H * N * 4
-    total = u + B * H * L * N * 4 + B * H * L * 4 + 2 * B * H * N * 4 + params
-    flops = 2 * (K + N) * d * B * H * L
+    if fold:
+        params += H * N * d * es
+    drive = 0 if fold else B * H * L * N * 4
+    total = u + drive + B * H * L * 4 + 2 * B * H * N * 4 + params
+    flops = 2 * (K + (2 * N if fold else N)) * d * B * H * L
     return total, flops
 
 
@@ -153,7 +162,7 @@ def _pmc_rows(d, counter):
 def _is_kernel(name, which):
     if which == "bwd":
         return "pdssm_bwd_kernel" in name
-    return "pdssm_" in name and "clear" not in name and "bwd" not in name
+    return "pdssm_" in name and "clear" not in name and "bwd" not in name and "fill" not in name.lower()
 
 
 def pmc_summary(fetch_dir, write_dir, workload, which="fwd"):
@@ -185,9 +194,10 @@ def pmc_summary(fetch_dir, write_dir, workload, which="fwd"):
     print(json.dumps(rec, indent=1))
 
 
-def cpu_baseline(inp):
-    """The fp64 oracle, as it is, on the host cores: selection plus the dense
-    sequential scan over the whole workload (inputs already generated)."""
+def cpu_baseline(inp, fold=False):
+    """The fp64 oracle, as it is, on the host cores: selection (and, with
+    fold, the drive terms) plus the dense sequential scan over the whole
+    workload (inputs already generated)."""
     import numpy as np  # noqa: F401
     import oracle
     cores = len(os.sched_getaffinity(0))
@@ -200,7 +210,11 @@ def cpu_baseline(inp):
     c = inp.cfg
     with ctx:
         t0 = time.perf_counter()
-        oracle.forward_inputs(inp)
+        if fold:
+            oracle.forward_wb(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, inp.C,
+                              inp.h0, c.u_shared)
+        else:
+            oracle.forward_inputs(inp)
         dt = time.perf_counter() - t0
     model = ""
     try:
@@ -304,8 +318,9 @@ def main():
     ap.add_argument("--workload", default="impulse")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="forward pass (default) or the gradient pass through the scan")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fold"), default="fwd",
+                    help="forward pass (default), the gradient pass through the scan, or the "
+                         "forward pass with the drive Bu = W_b u folded into the selection GEMM")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain copy kernel of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -340,15 +355,21 @@ def main():
     def dev(x, dt=None):
         return torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
 
+    fold = args.which == "fold"
     u, W_sel, W_d = dev(inp.u, pdt), dev(inp.W_sel, pdt), dev(inp.W_d, pdt)
-    b_d, dic, Bu, C, h0 = dev(inp.b_d), dev(inp.dict_idx), dev(inp.Bu), dev(inp.C), dev(inp.h0)
+    b_d, dic, C, h0 = dev(inp.b_d), dev(inp.dict_idx), dev(inp.C), dev(inp.h0)
+    Bu = None if fold else dev(inp.Bu)
+    W_b = dev(inp.W_b, pdt) if fold else None
     dims = P.make_dims(cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, cfg.d, cfg.u_shared, bf)
     ws = torch.empty(P.fwd_workspace_bytes(dims, chunk), dtype=torch.uint8, device="cuda")
     out = {"y": torch.empty((cfg.B, cfg.H, cfg.L), device="cuda"),
            "h_L": torch.empty((cfg.B, cfg.H, cfg.N), device="cuda")}
 
     def step():
-        P.pdssm_fwd(u, W_sel, dic, W_d, b_d, Bu, C, h0, chunk=chunk, workspace=ws, out=out)
+        if fold:
+            P.pdssm_fwd_wb(u, W_sel, dic, W_d, b_d, W_b, C, h0, chunk=chunk, workspace=ws, out=out)
+        else:
+            P.pdssm_fwd(u, W_sel, dic, W_d, b_d, Bu, C, h0, chunk=chunk, workspace=ws, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -363,7 +384,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     avg_launch_s = float(np.mean(hot)) / 1e6
 
-    alg_bytes, flops = algorithmic(cfg)
+    alg_bytes, flops = algorithmic(cfg, fold)
     # the dominant cost: HBM traffic, except where the score GEMM outweighs it
     t_hbm = alg_bytes / (PEAK_HBM_GBPS * 1e9)
     t_mma = flops / ((PEAK_BF16_TFLOPS if (bf and cfg.d >= 128) else PEAK_FP32_TFLOPS) * 1e12)
@@ -376,12 +397,12 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = traffic_from_profile(cfg.name, "fwd")
+    roof["traffic"] = traffic_from_profile(cfg.name, args.which)
     roof["algorithmic_bytes"] = alg_bytes
     roof["launch_us"] = round(avg_launch_s * 1e6, 2)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC_FOLD if fold else METRIC,
         "value": cfg.state_updates / (ms_step / 1e3),
         "unit": "state-updates/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -389,20 +410,21 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} L={cfg.L} N={cfg.N} K={cfg.K} "
-                               f"d={cfg.d} chunk={chunk} u={'shared' if cfg.u_shared else 'per-head'}",
+        "config": {"workload": f"{cfg.name}{' (drive folded)' if fold else ''}: B={cfg.B} H={cfg.H} "
+                               f"L={cfg.L} N={cfg.N} K={cfg.K} d={cfg.d} chunk={chunk} "
+                               f"u={'shared' if cfg.u_shared else 'per-head'}",
                    "B": cfg.B, "H": cfg.H, "L": cfg.L, "N": cfg.N, "K": cfg.K, "d_in": cfg.d,
                    "chunk": chunk, "u_dtype": cfg.dtype, "state_dtype": "f32"},
         "hbm_GBps": round(alg_bytes / avg_launch_s / 1e9, 1),
         "roofline": roof,
         "timing": timing,
-        "kernel_hash": kernel_hash("fwd"),
+        "kernel_hash": kernel_hash(args.which),
     }
     if args.copy_probe:
         copy_probe(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(inp)
+        rec["cpu_baseline"] = cpu_baseline(inp, fold)
     print(json.dumps(rec), flush=True)
 
 

@@ -115,6 +115,23 @@ int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* 
               int32_t* k_star, float* D, float* y, float* h_L,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* pdssm_fwd with the drive term computed in the same pass: Bu_t = W_b u_t
+ * (the input map B of the state-space recurrence, "Flash PD-SSM" summary,
+ * methodology item 1) is a third column tile of the selection GEMM, so Bu is
+ * never read from or written to memory.
+ *   W_b [H,N,d_in] (in, u's dtype): row n holds the weights of state row n.
+ *   All other arguments, the workspace (pdssm_fwd_workspace_bytes) and the
+ *   outputs as in pdssm_fwd.  The products are formed like the scores (fp32
+ *   for fp32 inputs, bf16 x bf16 with fp32 accumulation for bf16 inputs).
+ * Shapes: the step-major kernel only (per-head u, N <= 16, K <= 16,
+ * chunk <= 512, fp32 d_in in {16, 32, 64} or bf16 d_in = 128); anything else
+ * returns PDSSM_EUNSUPPORTED. */
+int pdssm_fwd_wb(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
+                 const int32_t* dict_idx, const void* W_d, const float* b_d,
+                 const void* W_b, const float* C, const float* h0,
+                 int32_t* k_star, float* D, float* y, float* h_L,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunked scan that also writes the state after every step.
  *   Arguments as in pdssm_scan_fwd (same workspace size), plus
  *   H_all [B,H,L,N] (out): h_t for t = 0..L-1, the states the gradient pass

@@ -38,7 +38,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "pdssm_select", "pdssm_scan_fwd", "pdssm_fwd", "scan_workspace_bytes",
+    "pdssm_select", "pdssm_scan_fwd", "pdssm_fwd", "pdssm_fwd_wb", "scan_workspace_bytes",
     "fwd_workspace_bytes", "make_dims", "PdssmError", "lib", "LIB_PATH",
 ]
 
@@ -202,6 +202,40 @@ def pdssm_fwd(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0=None, chunk=128, want_k=Fa
                          _ptr(W_d), _ptr(b_d), _ptr(Bu), _ptr(C), _ptr(h0),
                          _ptr(res.get("k_star")), _ptr(res.get("D")), _ptr(res["y"]),
                          _ptr(res["h_L"]), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev)))
+    return res
+
+
+def pdssm_fwd_wb(u, W_sel, dict_idx, W_d, b_d, W_b, C, h0=None, chunk=128, want_k=False,
+                 want_D=False, workspace=None, out=None):
+    """Fused selection + chunked scan with the drive term Bu = W_b u formed in
+    the same pass (W_b [H,N,d] in u's dtype).  Returns dict(y, h_L[, k_star][, D])."""
+    torch = _torch()
+    for t, n in ((u, "u"), (W_sel, "W_sel"), (W_d, "W_d"), (W_b, "W_b")):
+        _need(t, n)
+    if W_b.dtype != W_d.dtype or tuple(W_b.shape) != tuple(W_d.shape):
+        raise ValueError("W_b must have W_d's shape [H,N,d] and dtype")
+    _need(dict_idx, "dict_idx", torch.int32)
+    for t, n in ((b_d, "b_d"), (C, "C")):
+        _need(t, n, torch.float32)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    dims = _dims_from(u, W_sel, W_d)
+    dev = u.device
+    B, H, L, N = dims.B, dims.H, dims.L, dims.N
+    ws = _workspace(fwd_workspace_bytes(dims, chunk), dev, workspace)
+    o = out or {}
+    res = {}
+    for name, shape, dt, want in (("y", (B, H, L), torch.float32, True),
+                                  ("h_L", (B, H, N), torch.float32, True),
+                                  ("k_star", (B, H, L), torch.int32, want_k),
+                                  ("D", (B, H, L, N), torch.float32, want_D)):
+        if want:
+            t = o.get(name)
+            res[name] = torch.empty(shape, dtype=dt, device=dev) if t is None else _need(t, name)
+    _check(lib.pdssm_fwd_wb(ctypes.byref(dims), int(chunk), _ptr(u), _ptr(W_sel), _ptr(dict_idx),
+                            _ptr(W_d), _ptr(b_d), _ptr(W_b), _ptr(C), _ptr(h0),
+                            _ptr(res.get("k_star")), _ptr(res.get("D")), _ptr(res["y"]),
+                            _ptr(res["h_L"]), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev)))
     return res
 
 

@@ -44,6 +44,7 @@ def _load():
         "pdssm_scan_fwd": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "pdssm_fwd_workspace_bytes": [dp, i32, ctypes.POINTER(sz)],
         "pdssm_fwd": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "pdssm_fwd_wb": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "pdssm_scan_states": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "pdssm_scan_bwd_workspace_bytes": [dp, i32, ctypes.POINTER(sz)],
         "pdssm_scan_bwd": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],

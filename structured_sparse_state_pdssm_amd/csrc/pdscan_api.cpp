@@ -70,10 +70,10 @@ int check_dims(const pdssm_dims* d, int32_t chunk) {
   return PDSSM_OK;
 }
 
-int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk) {
+int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_bu = 0) {
   const int c = (mode == pdscan::kModeSelect) ? pdscan::kSelectRows : chunk;
   if (!pdscan::make_plan(p, mode, d->B, d->H, d->L, d->N, d->K, d->d_in, d->u_shared,
-                         d->in_dtype == PDSSM_BF16, c))
+                         d->in_dtype == PDSSM_BF16, c, fold_bu))
     return fail(PDSSM_EUNSUPPORTED,
                 "chunk=%d with N=%d needs %d bytes of on-chip memory per workgroup (limit %d)", c,
                 d->N, p.lds_bytes, pdscan::kMaxLds);
@@ -252,6 +252,40 @@ int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* 
   a.p = p;
   a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx;
   a.Bu = Bu; a.C = C; a.h0 = h0; a.k_out = k_star; a.D_out = D;
+  a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
+  return dispatch(pdscan::kModeFused, a, stream);
+}
+
+int pdssm_fwd_wb(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
+                 const int32_t* dict_idx, const void* W_d, const float* b_d, const void* W_b,
+                 const float* C, const float* h0, int32_t* k_star, float* D, float* y, float* h_L,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk, 1))) return rc;
+  if (!p.fold_bu)
+    return fail(PDSSM_EUNSUPPORTED,
+                "the drive term is folded into the step-major kernel only: per-head u, N <= 16, "
+                "K <= 16, chunk <= 512, fp32 d in {16, 32, 64} or bf16 d = 128 (got u_shared=%d "
+                "N=%d K=%d d=%d %s)", dims->u_shared, dims->N, dims->K, dims->d_in,
+                dims->in_dtype == PDSSM_BF16 ? "bf16" : "fp32");
+  if (workspace_bytes < p.ws_bytes)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"u", u, z.u},         {"W_sel", W_sel, z.Wsel}, {"dict_idx", dict_idx, z.dict},
+                      {"W_d", W_d, z.Wd},    {"b_d", b_d, z.bd},       {"W_b", W_b, z.Wd},
+                      {"C", C, z.C},         {"h0", h0, z.h0}};
+  const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y},
+                       {"h_L", h_L, z.hL},      {"workspace", workspace, p.ws_bytes}};
+  static const char* const req[] = {"u",  "W_sel", "dict_idx", "W_d", "b_d",      "W_b",
+                                    "C",  "y",     "h_L",      "workspace", nullptr};
+  if ((rc = check_ptrs(in, 8, out, 5, req))) return rc;
+  pdscan::Args a = {};
+  a.p = p;
+  a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx; a.W_b = W_b;
+  a.C = C; a.h0 = h0; a.k_out = k_star; a.D_out = D;
   a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
   return dispatch(pdscan::kModeFused, a, stream);
 }

@@ -1047,7 +1047,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
 // through LDS, and the next tile's MFMAs are issued before the current
 // tile's scan steps so that the two overlap.
 // ---------------------------------------------------------------------------
-template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT>
+template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT, int FOLD>
 __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem) {
   typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
   constexpr int CB = kChanBlock<MMA_BF16>;
@@ -1133,6 +1133,38 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       }
     }
   }
+  // FOLD: the drive term is a third tile, Bu = W_b u (rows of W_b as its
+  // columns).  Its fragments are built like the others and parked in LDS,
+  // one 16-byte slot per lane and fragment (the same for every wave), so the
+  // register budget stays at three waves per SIMD; each block reads them
+  // back for its MFMAs.
+  constexpr int WBF = SPLIT ? 3 * KB : KCH;        // fragments per lane
+  static_assert(!FOLD || WBF * (int)sizeof(FT) <= kWbFrags * 16, "W_b fragments exceed their LDS slots");
+  unsigned char* wbl = smem + p.off_WB + lane * 16;
+  if constexpr (FOLD) {
+    const rsrc_t wbr = make_rsrc((const unsigned char*)a.W_b + (size_t)h * N * d * ES, (uint32_t)(N * d * ES));
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        f4v z[2];
+        u4v w3[3];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          z[hf] = load_frag_buf<0, 0>(wbr, i < N ? (uint32_t)((i * d + 32 * kb + 8 * g + 4 * hf) * 4) : kNoLoad);
+        split3(z[0], z[1], w3);
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          if (wave == 0) *(u4v*)(wbl + (3 * kb + q) * 1024) = w3[q];
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < KCH; ++m) {
+        const int ch = m * CB + PER * g;
+        const FT w = load_frag_buf<IN_BF16, MMA_BF16>(wbr, (i < N && ch < d) ? (uint32_t)((i * d + ch) * ES) : kNoLoad);
+        if (wave == 0) *(FT*)(wbl + m * 1024) = w;
+      }
+    }
+  }
   const float bdz = buf_f32(make_rsrc(a.b_d + (size_t)h * N, (uint32_t)(N * 4)), i < N ? (uint32_t)i * 4u : kNoLoad);
   const float cj = buf_f32(make_rsrc(a.C + (size_t)h * N, (uint32_t)(N * 4)), act ? (uint32_t)j * 4u : kNoLoad);
 
@@ -1169,13 +1201,17 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   auto bu_off = [&](int q) {
     return (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad;
   };
-  float bu[16];
+  float bu[FOLD ? 1 : 16];
+  if constexpr (!FOLD) {
 #pragma unroll
-  for (int q = 0; q < 16; ++q) bu[q] = buf_f32(bur, bu_off(q));
+    for (int q = 0; q < 16; ++q) bu[q] = buf_f32(bur, bu_off(q));
+  }
 
+  // acc[0]: pre-activations, acc[1]: scores, acc[2] (FOLD): drive terms
   auto mma_tile = [&](f4v* acc, const FT* src) {
     acc[0] = f4v{0.f, 0.f, 0.f, 0.f};
     acc[1] = f4v{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FOLD) acc[2] = f4v{0.f, 0.f, 0.f, 0.f};
     if constexpr (SPLIT) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -1183,12 +1219,19 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
         split3(src[2 * kb], src[2 * kb + 1], xp);
         mma_split3(acc[0], xp, wz3[kb]);
         mma_split3(acc[1], xp, ws3[kb]);
+        if constexpr (FOLD) {
+          u4v w3[3];
+#pragma unroll
+          for (int q = 0; q < 3; ++q) w3[q] = *(const u4v*)(wbl + (3 * kb + q) * 1024);
+          mma_split3(acc[2], xp, w3);
+        }
       }
     } else {
 #pragma unroll
       for (int m = 0; m < KCH; ++m) {
         mma_step<IN_BF16, MMA_BF16>(acc[0], src[m], wz[m]);
         mma_step<IN_BF16, MMA_BF16>(acc[1], src[m], wsel[m]);
+        if constexpr (FOLD) mma_step<IN_BF16, MMA_BF16>(acc[2], src[m], *(const FT*)(wbl + m * 1024));
       }
     }
   };
@@ -1221,7 +1264,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   }
   __syncthreads();                                 // tables ready
 
-  f4v A[2][2];
+  f4v A[2][FOLD ? 3 : 2];
   if (nblk > 0) {
     mma_tile(A[0], U[0]);
     if (nblk > 2) load_tile(U[0], 2);
@@ -1275,7 +1318,9 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(lbase | (int)((ax >> (8 * m)) & 0xFFu), vj));
-      float hn = bu[(4 * k + r) & 15];
+      float hn;
+      if constexpr (FOLD) hn = A[cu][2][r];
+      else hn = bu[(4 * k + r) & 15];
 #pragma unroll
       for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(gv[m], (float)((ay >> (8 * m)) & 0xFFu), hn);
       const unsigned aw = (unsigned)se.w;
@@ -1299,8 +1344,10 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       yp[r] = cj * hl;
     }
     // refill this block's drive-term slots with the block four ahead
+    if constexpr (!FOLD) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bu[(4 * k + r) & 15] = buf_f32(bur, bu_off(4 * k + 16 + r));
+      for (int r = 0; r < 4; ++r) bu[(4 * k + r) & 15] = buf_f32(bur, bu_off(4 * k + 16 + r));
+    }
     // local outputs of the four steps, summed over the group off the scan's
     // critical path
 #pragma unroll
@@ -1320,10 +1367,10 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
 }
 
-template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT>
+template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT, int FOLD = 0>
 __global__ __launch_bounds__(kThreads, 3) void pdssm_fused16_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  fused16_body<IN_BF16, MMA_BF16, KCH, SPLIT>(a, smem);
+  fused16_body<IN_BF16, MMA_BF16, KCH, SPLIT, FOLD>(a, smem);
 }
 
 // Two entry points over one body: the register-resident fp32 selection paths

@@ -18,6 +18,7 @@ constexpr int kThreads = 256;          // lanes per workgroup
 constexpr int kWaves = kThreads / 64;  // wave64
 constexpr int kSelectRows = 256;       // rows per workgroup for selection alone
 constexpr int kMaxLds = 64 * 1024;     // bytes of LDS one workgroup may use
+constexpr int kWbFrags = 6;            // W_b fragments per lane at most (fp32 d = 64: 2 blocks x 3 pieces)
 
 enum Mode : int { kModeSelect = 0, kModeScan = 1, kModeFused = 2 };
 
@@ -36,10 +37,11 @@ struct Plan {
   int KP;    // score staging width
   int mma_bf16;  // score GEMM on bf16 MFMA (else fp32 MFMA)
   int fused16;   // fused pass with step-major MFMA tiles (N, K <= 16; see below)
+  int fold_bu;   // fused16: Bu = W_b u from a third MFMA tile instead of an input
   int tasks;     // workgroups
   // LDS byte offsets
   int off_D, off_k, off_yl, off_dict, off_DC, off_SRC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
-      off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_misc, lds_bytes;
+      off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_WB, off_misc, lds_bytes;
   // workspace byte offsets (scan / fused)
   size_t ws_agg, ws_inc, ws_bytes;
 };
@@ -55,7 +57,7 @@ inline int align_up(int x, int a) { return (x + a - 1) / a * a; }
 // Fills `p` for one call.  `mode` selects which parts exist.  Returns false
 // when the plan needs more than kMaxLds bytes of LDS.
 inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int d, int u_shared,
-                      int in_bf16, int chunk) {
+                      int in_bf16, int chunk, int fold_bu = 0) {
   p.B = B; p.H = H; p.L = L; p.N = N; p.K = K; p.d = d;
   p.u_shared = u_shared; p.in_bf16 = in_bf16;
   // a chunk longer than the sequence behaves exactly like chunk = L
@@ -67,6 +69,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   const int kch = in_bf16 ? (d >= 128 ? (d == 128 ? 4 : 0) : 0) : (d == 16 || d == 32 || d == 64 ? d / 16 : 0);
   p.fused16 = (mode == kModeFused && !u_shared && N <= 16 && K <= 16 && kch > 0 &&
                (chunk < L ? chunk : L) <= 512) ? 1 : 0;
+  p.fold_bu = (p.fused16 && fold_bu) ? 1 : 0;
   p.NP = p.fused16 ? 16 : next_pow2(N);
   p.G = kThreads / p.NP;
   p.S = align_up((p.chunk + p.G - 1) / p.G, 4);
@@ -112,6 +115,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.off_pB = scan ? take(p.G * N * 4) : 0;
   p.off_H = take(64 * 4);
   p.off_tmp = take(64 * 4);
+  p.off_WB = p.fold_bu ? take(kWbFrags * 64 * 16) : 0;   // W_b MFMA fragments, one 16-byte slot per lane
   p.off_misc = take(16);
   p.lds_bytes = off;
 
@@ -133,6 +137,7 @@ struct Args {
   const float* b_d;
   const int32_t* dict;
   const float* Bu;
+  const void* W_b;       // fold_bu: [H,N,d] in u's dtype
   const float* C;
   const float* h0;
   const int32_t* k_in;   // scan mode

@@ -1,0 +1,123 @@
+"""Parity of the forward pass with the drive term folded into the selection
+GEMM (``pdssm_fwd_wb``, HIP through the C ABI) with the fp64 oracle
+(``forward_wb``: Bu = W_b u in fp64, then the sequential scan).
+
+Bar: k* bit-exact; y and h_L within 1e-4 (1 + |ref|) elementwise; D within
+2e-6 absolute."""
+
+import numpy as np
+import pytest
+
+import oracle
+from pdssm_inputs import generate, get_config
+from tests._gpu import assert_within, host, lib, proj_dev, to_dev, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+# shapes of the step-major kernel: fp32 d = 64 (split products), fp32 d = 32,
+# fp32 d = 16 (fp32 MFMA), bf16 d = 128 (bf16 MFMA); ragged last chunks
+CASES = {
+    "impulse": ("impulse", dict(H=3, L=1300)),
+    "base": ("base", dict(B=2, H=3, L=700)),
+    "base_d32": ("base", dict(B=1, H=2, L=450, d=32)),
+    "tiny": ("tiny", dict(L=250)),
+    "bf16_d128": ("timeseries", dict(B=1, H=2, L=600, N=16, K=8)),
+}
+
+_cache = {}
+
+
+def _case(key):
+    if key not in _cache:
+        name, kw = CASES[key]
+        inp = generate(get_config(name, **kw))
+        ref = oracle.forward_wb(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, inp.C,
+                                inp.h0, inp.cfg.u_shared)
+        _cache[key] = (inp, ref)
+    return _cache[key]
+
+
+def _dev(inp):
+    bf = inp.cfg.dtype == "bf16"
+    return dict(u=proj_dev(inp.u, bf), W_sel=proj_dev(inp.W_sel, bf), W_d=proj_dev(inp.W_d, bf),
+                W_b=proj_dev(inp.W_b, bf), b_d=to_dev(inp.b_d), dict_idx=to_dev(inp.dict_idx),
+                C=to_dev(inp.C), h0=to_dev(inp.h0))
+
+
+def _run(d, chunk, h0=True, want=True):
+    P = lib()
+    return P.pdssm_fwd_wb(d["u"], d["W_sel"], d["dict_idx"], d["W_d"], d["b_d"], d["W_b"], d["C"],
+                          d["h0"] if h0 else None, chunk=chunk, want_k=want, want_D=want)
+
+
+def _check(out, ref, what):
+    assert np.array_equal(host(out["k_star"]), ref["k_star"]), f"{what}: k* differs"
+    assert np.max(np.abs(host(out["D"]) - ref["D"])) <= 2e-6, f"{what}: D"
+    assert_within(host(out["y"]), ref["y"], f"{what} y")
+    assert_within(host(out["h_L"]), ref["h_L"], f"{what} h_L")
+
+
+@pytest.mark.parametrize("key", list(CASES))
+def test_fold_parity(key):
+    inp, ref = _case(key)
+    print(f"[gpu] pdssm_fwd_wb {key} chunk={inp.cfg.chunk}", flush=True)
+    _check(_run(_dev(inp), inp.cfg.chunk), ref, key)
+
+
+@pytest.mark.parametrize("chunk", [1, 4, 16, 100, 128, 512])
+def test_fold_chunk_independence(chunk):
+    inp, ref = _case("impulse")
+    print(f"[gpu] pdssm_fwd_wb impulse chunk={chunk}", flush=True)
+    _check(_run(_dev(inp), chunk), ref, f"chunk {chunk}")
+
+
+def test_fold_without_selection_outputs_or_h0():
+    inp, _ = _case("base")
+    ref = oracle.forward_wb(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, inp.C, None)
+    out = _run(_dev(inp), inp.cfg.chunk, h0=False, want=False)
+    assert "k_star" not in out and "D" not in out
+    assert_within(host(out["y"]), ref["y"], "y")
+    assert_within(host(out["h_L"]), ref["h_L"], "h_L")
+
+
+def test_fold_matches_the_unfolded_pass_on_the_same_drive():
+    """Same u, W_b: pdssm_fwd fed the fp64 drive rounded to fp32 agrees with
+    pdssm_fwd_wb within the tolerance (and exactly on k*)."""
+    inp, ref = _case("impulse")
+    P = lib()
+    d = _dev(inp)
+    a = _run(d, 512)
+    b = P.pdssm_fwd(d["u"], d["W_sel"], d["dict_idx"], d["W_d"], d["b_d"],
+                    to_dev(ref["Bu"].astype(np.float32)), d["C"], d["h0"], chunk=512, want_k=True)
+    assert np.array_equal(host(a["k_star"]), host(b["k_star"]))
+    assert_within(host(a["y"]), host(b["y"]), "y vs unfolded")
+
+
+def test_fold_deterministic():
+    inp, _ = _case("base")
+    d = _dev(inp)
+    a, b = _run(d, 128), _run(d, 128)
+    for n in ("y", "h_L", "k_star", "D"):
+        assert np.array_equal(host(a[n]), host(b[n])), n
+
+
+@pytest.mark.parametrize("name,kw", [("lm_layer", dict(B=1, H=2, L=64)),
+                                     ("timeseries", dict(B=1, H=2, L=64)),
+                                     ("base", dict(B=1, H=2, L=64, N=17))])
+def test_fold_rejects_shapes_outside_the_step_major_kernel(name, kw):
+    P = lib()
+    inp = generate(get_config(name, **kw))
+    with pytest.raises(P.PdssmError) as e:
+        _run(_dev(inp), inp.cfg.chunk)
+    assert e.value.status == P.PDSSM_EUNSUPPORTED
+
+
+@pytest.mark.slow
+def test_fold_full_impulse():
+    torch = torch_mod()
+    inp = generate(get_config("impulse"))
+    ref = oracle.forward_wb(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, inp.C, inp.h0)
+    print("[gpu] pdssm_fwd_wb impulse full size", flush=True)
+    out = _run(_dev(inp), inp.cfg.chunk)
+    torch.cuda.synchronize()
+    _check(out, ref, "impulse full")
