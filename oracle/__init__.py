@@ -9,6 +9,7 @@ from .pdssm_oracle import (  # noqa: F401
     forward,
     forward_wb,
     forward_inputs,
+    impulse_sensitivity,
     pd_apply,
     pd_compose,
     scan,

@@ -26,6 +26,9 @@ transition of every step and multiplies; it never uses the sparse structure.
 ``forward_wb`` is the same forward pass with the drive terms Bu_t = W_b u_t
 formed from the input (``drive``) instead of being given.
 
+``impulse_sensitivity`` is dy_t / du_0 for fixed selections, carried forward
+from step 0 by the same dense transitions (forward mode).
+
 ``scan_vjp`` is the gradient of a scalar loss through that recurrence for
 fixed selections (the adjoint recurrence with the dense transposed
 transitions); ``scan_states`` returns the state after every step, which the
@@ -197,6 +200,45 @@ def scan_vjp(k_star, dict_idx, D, Bu, C, h0, g_y, g_hL=None):
     g_h0 = lam
     g_C = np.einsum("bhl,bhln->hn", g_y, states)
     return g_Bu, g_D, g_h0, g_C
+
+
+def impulse_sensitivity(k_star, dict_idx, D, W_d, W_b, C, h0=None):
+    """Sensitivity of every output to the first input, dy_t / du_0, for fixed
+    selections (the impulse-response derivative of "Breaking the Memory Wall:
+    Exact Analytical Differentiation via Tiled Operator-Space Evolution",
+    abstract: exact derivatives of an SSM over a long sequence).
+
+    u_0 enters only step 0: through the diagonal D_0 = sigmoid(W_d u_0 + b_d),
+    whose derivative is D_0 (1 - D_0) W_d, and through the drive W_b u_0 (k*_0
+    is piecewise constant and carries no derivative).  So the tangent of the
+    state after step 0 is
+        J[i, c] = W_b[i, c] + sum over j with idx_0[j] = i of
+                  D_0[j] (1 - D_0[j]) h0[j] W_d[j, c],
+    later steps carry it forward with the same transitions, V_t = A_t V_{t-1},
+    and dy_t / du_0 = C V_t.  Dense, forward-mode, fp64.
+
+    k_star [B,H,L]; dict_idx [H,K,N]; D [B,H,L,N]; W_d, W_b [H,N,d]; C [H,N];
+    h0 [B,H,N] or None (zeros).  Returns fp64 [B,H,L,d]."""
+    k_star = np.asarray(k_star)
+    dict_idx = np.asarray(dict_idx)
+    D = np.asarray(D, dtype=F64)
+    W_d = np.asarray(W_d, dtype=F64)
+    W_b = np.asarray(W_b, dtype=F64)
+    C = np.asarray(C, dtype=F64)
+    B, H, L = k_star.shape
+    N, d = W_d.shape[1], W_d.shape[2]
+    h0 = np.zeros((B, H, N), dtype=F64) if h0 is None else np.asarray(h0, dtype=F64)
+    out = np.zeros((B, H, L, d), dtype=F64)
+    for b in range(B):
+        for h in range(H):
+            idx0 = dict_idx[h, k_star[b, h, 0]]
+            coef = D[b, h, 0] * (1.0 - D[b, h, 0]) * h0[b, h]          # [N]
+            V = W_b[h] + transition_matrix(idx0, coef) @ W_d[h]          # [N, d]
+            out[b, h, 0] = C[h] @ V
+            for t in range(1, L):
+                V = transition_matrix(dict_idx[h, k_star[b, h, t]], D[b, h, t]) @ V
+                out[b, h, t] = C[h] @ V
+    return out
 
 
 def forward(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0=None, u_shared=False):
