@@ -9,7 +9,8 @@ fp64 CPU oracle timed beside it.
 ``--pass bwd`` times the gradient pass through the scan (pdssm_scan_bwd) on
 the same workload instead, with its own roofline and oracle baseline;
 ``--pass fold`` times pdssm_fwd_wb (the drive term formed from u and W_b in
-the same pass, so Bu is never read).
+the same pass, so Bu is never read); ``--pass sens`` times the impulse
+sensitivity dy_t/du_0 (pdssm_impulse_sens).
 ``timing`` in the JSON line gives the median, p10 and p90 of the per-call
 event durations with warm caches ("hot") and with a 1 GiB fill before each
 call ("cold").
@@ -46,8 +47,10 @@ SOURCES = {
             "pdscan_launch_bwd.hip"),
 }
 SOURCES["fold"] = SOURCES["fwd"]
+SOURCES["sens"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_sens_plan.h", "pdscan_sens.h",
+                   "pdscan_launch_sens.hip")
 # stem of the committed counter summary of each pass
-TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd", "fold": "pdssm_fold"}
+TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd", "fold": "pdssm_fold", "sens": "pdssm_sens"}
 COLD_FILL_BYTES = 1 << 30       # written before each cold-cache rep (beyond L2 and MALL)
 
 
@@ -162,6 +165,8 @@ def _pmc_rows(d, counter):
 def _is_kernel(name, which):
     if which == "bwd":
         return "pdssm_bwd_kernel" in name
+    if which == "sens":
+        return "pdssm_sens_kernel" in name
     return "pdssm_" in name and "clear" not in name and "bwd" not in name and "fill" not in name.lower()
 
 
@@ -310,6 +315,92 @@ def bench_bwd(args, torch, np, P):
     print(json.dumps(rec), flush=True)
 
 
+def algorithmic_sens(cfg):
+    """Minimum traffic of the impulse sensitivity: k* and D read once, dY
+    written once, plus the dictionary, C, W_d, W_b and h0."""
+    B, H, L, N, K, d = cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, cfg.d
+    es = 2 if cfg.dtype == "bf16" else 4
+    steps = B * H * L
+    return steps * (4 + 4 * N + 4 * d) + H * K * N * 4 + H * N * 4 + 2 * H * N * d * es + B * H * N * 4
+
+
+def bench_sens(args, torch, np, P):
+    """Time pdssm_impulse_sens; the selections come from the library's own
+    forward pass, outside the timed region."""
+    from pdssm_inputs import generate, get_config
+    cfg = get_config(args.workload)
+    chunk = args.chunk or cfg.chunk
+    t0 = time.time()
+    inp = generate(cfg)
+    print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    bf = cfg.dtype == "bf16"
+    pdt = torch.bfloat16 if bf else torch.float32
+
+    def dev(x, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+
+    u, W_sel, W_d, W_b = dev(inp.u, pdt), dev(inp.W_sel, pdt), dev(inp.W_d, pdt), dev(inp.W_b, pdt)
+    b_d, dic, Bu, C, h0 = dev(inp.b_d), dev(inp.dict_idx), dev(inp.Bu), dev(inp.C), dev(inp.h0)
+    fw = P.pdssm_fwd(u, W_sel, dic, W_d, b_d, Bu, C, h0, chunk=chunk, want_k=True, want_D=True)
+    k, D = fw["k_star"], fw["D"]
+    del u, Bu
+    dims = P.make_dims(cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, cfg.d, 0, bf)
+    ws = torch.zeros(P.impulse_sens_workspace_bytes(dims, chunk), dtype=torch.uint8, device="cuda")
+    dY = torch.empty((cfg.B, cfg.H, cfg.L, cfg.d), device="cuda")
+
+    def step():
+        P.pdssm_impulse_sens(k, dic, D, W_d, W_b, C, h0, chunk=chunk, workspace=ws, out=dY)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if P.workspace_error_flag(ws):
+        raise RuntimeError("look-back wait gave up during warm-up")
+    stream = torch.cuda.current_stream()
+    wall, hot, timing = time_calls(torch, np, step, args.steps, stream)
+    if P.workspace_error_flag(ws):
+        raise RuntimeError("look-back wait gave up during timing")
+    launch_s = float(np.mean(hot)) / 1e6
+    ms_step = wall * 1e3 / args.steps
+    alg = algorithmic_sens(cfg)
+    achieved = alg / launch_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_from_profile(cfg.name, "sens"),
+            "algorithmic_bytes": alg, "launch_us": round(launch_s * 1e6, 2)}
+    rec = {
+        "metric": "state-updates/sec (B·H·L·N) PD-SSM impulse sensitivity dy_t/du_0 (fixed selections)",
+        "value": cfg.state_updates / (ms_step / 1e3),
+        "unit": "state-updates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} impulse sensitivity: B={cfg.B} H={cfg.H} L={cfg.L} N={cfg.N} "
+                               f"K={cfg.K} d={cfg.d} chunk={chunk}",
+                   "B": cfg.B, "H": cfg.H, "L": cfg.L, "N": cfg.N, "K": cfg.K, "d_in": cfg.d, "chunk": chunk},
+        "roofline": roof,
+        "timing": timing,
+        "kernel_hash": kernel_hash("sens"),
+    }
+    if args.copy_probe:
+        copy_probe(torch)
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        Hs, Ls = min(cfg.H, 2), min(cfg.L, 16384)
+        kh = k.cpu().numpy()[:, :Hs, :Ls]
+        Dh = D.cpu().numpy()[:, :Hs, :Ls].astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.impulse_sensitivity(kh, inp.dict_idx[:Hs], Dh, inp.W_d[:Hs], inp.W_b[:Hs], inp.C[:Hs],
+                                   inp.h0[:, :Hs])
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": cfg.B * Hs * Ls * cfg.N / dt, "unit": "state-updates/s",
+                               "cores": cores, "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": f"first {Ls} steps of {Hs} heads of {cfg.name} "
+                                         "(dense forward-mode tangent, single-threaded step loop)"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,9 +409,10 @@ def main():
     ap.add_argument("--workload", default="impulse")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fold"), default="fwd",
-                    help="forward pass (default), the gradient pass through the scan, or the "
-                         "forward pass with the drive Bu = W_b u folded into the selection GEMM")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fold", "sens"), default="fwd",
+                    help="forward pass (default), the gradient pass through the scan, the "
+                         "forward pass with the drive Bu = W_b u folded into the selection GEMM, "
+                         "or the impulse sensitivity dy_t/du_0")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain copy kernel of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -344,6 +436,8 @@ def main():
     torch.cuda.set_device(0)
     if args.which == "bwd":
         return bench_bwd(args, torch, np, P)
+    if args.which == "sens":
+        return bench_sens(args, torch, np, P)
     cfg = get_config(args.workload)
     chunk = args.chunk or cfg.chunk
     t0 = time.time()

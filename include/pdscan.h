@@ -167,6 +167,29 @@ int pdssm_scan_bwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
                    float* g_D, float* g_h0, float* g_C, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Bytes of workspace pdssm_impulse_sens needs for these dims and chunk length
+ * (about nC * B * H * N * (d_in + 2) * 8 bytes: one tangent state per chunk). */
+int pdssm_impulse_sens_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes);
+
+/* Sensitivity of every output to the first input, dY[b,h,t,:] = dy_t / du_0,
+ * for fixed selections ("Breaking the Memory Wall: Exact Analytical
+ * Differentiation via Tiled Operator-Space Evolution" summary: exact
+ * derivatives over long sequences without storing the graph; here the
+ * 128k-step impulse-response derivative of this layer).  u_0 enters step 0
+ * through D_0 = sigmoid(W_d u_0 + b_d) and the drive W_b u_0, so the state
+ * tangent after step 0 is J = W_b + P_0 diag(D_0 (1 - D_0) h0) W_d, and
+ * dY_t = C A_t ... A_1 J (k*_0 carries no derivative).
+ *   k_star [B,H,L], dict_idx [H,K,N], D [B,H,L,N] (in): the selections of a
+ *     forward pass (pdssm_select, or pdssm_fwd's optional outputs).
+ *   W_d, W_b [H,N,d_in] (in, dtype in_dtype); C [H,N]; h0 [B,H,N] or NULL.
+ *   dY [B,H,L,d_in] fp32 (out).
+ * Shapes: per-head layout, N <= 16, d_in a multiple of 16 and at most 128,
+ * on-chip layout within 64 KiB (chunk <= 512); else PDSSM_EUNSUPPORTED. */
+int pdssm_impulse_sens(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
+                       const int32_t* dict_idx, const float* D, const void* W_d, const void* W_b,
+                       const float* C, const float* h0, float* dY, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* pdssm_status_str(int status);
 

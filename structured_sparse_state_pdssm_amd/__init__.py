@@ -38,7 +38,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "pdssm_select", "pdssm_scan_fwd", "pdssm_fwd", "pdssm_fwd_wb", "scan_workspace_bytes",
+    "pdssm_select", "pdssm_scan_fwd", "pdssm_fwd", "pdssm_fwd_wb", "pdssm_impulse_sens",
+    "scan_workspace_bytes",
     "fwd_workspace_bytes", "make_dims", "PdssmError", "lib", "LIB_PATH",
 ]
 
@@ -237,6 +238,41 @@ def pdssm_fwd_wb(u, W_sel, dict_idx, W_d, b_d, W_b, C, h0=None, chunk=128, want_
                             _ptr(res.get("k_star")), _ptr(res.get("D")), _ptr(res["y"]),
                             _ptr(res["h_L"]), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev)))
     return res
+
+
+def impulse_sens_workspace_bytes(dims, chunk):
+    n = ctypes.c_size_t(0)
+    _check(lib.pdssm_impulse_sens_workspace_bytes(ctypes.byref(dims), int(chunk), ctypes.byref(n)))
+    return n.value
+
+
+def pdssm_impulse_sens(k_star, dict_idx, D, W_d, W_b, C, h0=None, chunk=128, workspace=None, out=None):
+    """dy_t / du_0 for fixed selections: returns dY [B,H,L,d] fp32.  W_d and W_b
+    [H,N,d] share a dtype (fp32 or bf16)."""
+    torch = _torch()
+    _need(k_star, "k_star", torch.int32)
+    _need(dict_idx, "dict_idx", torch.int32)
+    _need(D, "D", torch.float32)
+    _need(C, "C", torch.float32)
+    _need(W_d, "W_d")
+    _need(W_b, "W_b")
+    if W_b.dtype != W_d.dtype or tuple(W_b.shape) != tuple(W_d.shape):
+        raise ValueError("W_b must have W_d's shape [H,N,d] and dtype")
+    if W_d.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("W_d and W_b must be float32 or bfloat16")
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    B, H, L = k_star.shape
+    K, N = dict_idx.shape[1], dict_idx.shape[2]
+    d = W_d.shape[2]
+    dims = make_dims(B, H, L, N, K, d, 0, W_d.dtype == torch.bfloat16)
+    dev = k_star.device
+    ws = _workspace(impulse_sens_workspace_bytes(dims, chunk), dev, workspace)
+    dY = torch.empty((B, H, L, d), dtype=torch.float32, device=dev) if out is None else _need(out, "dY")
+    _check(lib.pdssm_impulse_sens(ctypes.byref(dims), int(chunk), _ptr(k_star), _ptr(dict_idx), _ptr(D),
+                                  _ptr(W_d), _ptr(W_b), _ptr(C), _ptr(h0), _ptr(dY), _ptr(ws),
+                                  ctypes.c_size_t(ws.numel()), _stream(dev)))
+    return dY
 
 
 def scan_bwd_workspace_bytes(dims, chunk):

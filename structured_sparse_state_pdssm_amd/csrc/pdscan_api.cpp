@@ -12,6 +12,7 @@
 #include "pdscan.h"
 #include "pdscan_bwd_plan.h"
 #include "pdscan_plan.h"
+#include "pdscan_sens_plan.h"
 
 namespace pdscan {
 // One launcher per mode, each in its own translation unit.  They enqueue on
@@ -20,6 +21,7 @@ hipError_t launch_select(const Args& a, hipStream_t st);
 hipError_t launch_scan(const Args& a, hipStream_t st);
 hipError_t launch_fused(const Args& a, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, float* g_C, hipStream_t st);
+hipError_t launch_sens(const SensArgs& a, hipStream_t st);
 }
 
 using pdscan::Plan;
@@ -140,6 +142,25 @@ int dispatch(int mode, const pdscan::Args& a, void* stream) {
                                                    : pdscan::launch_fused(a, st);
   if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_err[0] = 0;
+  return PDSSM_OK;
+}
+
+int sens_plan(pdscan::SensPlan& q, const pdssm_dims* dims, int32_t chunk) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  if (dims->u_shared)
+    return fail(PDSSM_EUNSUPPORTED, "impulse sensitivity: u shared by the heads is not supported");
+  if (dims->N > 16)
+    return fail(PDSSM_EUNSUPPORTED, "impulse sensitivity: N=%d > 16", dims->N);
+  if (dims->d_in % 16 || dims->d_in > pdscan::kSensMaxD)
+    return fail(PDSSM_EUNSUPPORTED, "impulse sensitivity: d_in=%d must be a multiple of 16, at most %d",
+                dims->d_in, pdscan::kSensMaxD);
+  if (!pdscan::make_sens_plan(q, dims->B, dims->H, dims->L, dims->N, dims->K, dims->d_in,
+                              dims->in_dtype == PDSSM_BF16, chunk))
+    return fail(PDSSM_EUNSUPPORTED, "impulse sensitivity: chunk=%d with d_in=%d needs %d bytes of "
+                "on-chip memory (limit %d)", chunk, dims->d_in, q.bytes, pdscan::kMaxLds);
+  if ((uint64_t)q.nC * dims->B * dims->H > 0x7fffffffull)
+    return fail(PDSSM_EUNSUPPORTED, "too many chunks");
   return PDSSM_OK;
 }
 
@@ -363,6 +384,43 @@ int pdssm_scan_bwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
   a.g_y = g_y; a.g_hL = g_hL; a.g_Bu = g_Bu; a.g_D = g_D; a.g_h0 = g_h0;
   a.ws = (unsigned char*)workspace;
   const hipError_t e = pdscan::launch_bwd(a, g_C, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return PDSSM_OK;
+}
+
+int pdssm_impulse_sens_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes) {
+  pdscan::SensPlan q;
+  int rc = sens_plan(q, dims, chunk);
+  if (rc) return rc;
+  if (!bytes) return fail(PDSSM_EINVAL, "bytes is NULL");
+  *bytes = q.ws_bytes;
+  return PDSSM_OK;
+}
+
+int pdssm_impulse_sens(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
+                       const int32_t* dict_idx, const float* D, const void* W_d, const void* W_b,
+                       const float* C, const float* h0, float* dY, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  pdscan::SensPlan q;
+  int rc = sens_plan(q, dims, chunk);
+  if (rc) return rc;
+  if (workspace_bytes < q.ws_bytes)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, q.ws_bytes);
+  const Sizes z = sizes(dims);
+  const size_t ydz = (size_t)dims->B * dims->H * dims->L * dims->d_in * 4;
+  const Range in[] = {{"k_star", k_star, z.k}, {"dict_idx", dict_idx, z.dict}, {"D", D, z.D},
+                      {"W_d", W_d, z.Wd},      {"W_b", W_b, z.Wd},           {"C", C, z.C},
+                      {"h0", h0, z.h0}};
+  const Range out[] = {{"dY", dY, ydz}, {"workspace", workspace, q.ws_bytes}};
+  static const char* const req[] = {"k_star", "dict_idx", "D", "W_d", "W_b", "C", "dY", "workspace",
+                                    nullptr};
+  if ((rc = check_ptrs(in, 7, out, 2, req))) return rc;
+  pdscan::SensArgs a = {};
+  a.q = q;
+  a.k_star = k_star; a.dict = dict_idx; a.D = D; a.W_d = W_d; a.W_b = W_b; a.C = C; a.h0 = h0;
+  a.dY = dY; a.ws = (unsigned char*)workspace;
+  const hipError_t e = pdscan::launch_sens(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_err[0] = 0;
   return PDSSM_OK;

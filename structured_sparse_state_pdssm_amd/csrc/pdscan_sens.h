@@ -1,0 +1,306 @@
+// Sensitivity of every output to the first input, dy_t / du_0, for fixed
+// selections (device code).
+//
+// u_0 enters only step 0, so the tangent of the state after step 0 is the
+// N x d matrix J_0 = W_b + P_0 diag(D_0 (1 - D_0) h0) W_d, later steps carry it
+// with the same transitions, V_t = A_t V_{t-1}, and dy_t/du_0 = C V_t.  With
+// Phi_t = A_t ... A_1 this is w_t J_0 where w_t = C Phi_t, the row of output
+// weights the forward scan also forms.  The three phases of the chunked scan
+// ("Flash PD-SSM" summary, methodology item 3) become: per lane group, the
+// weight rows of its sub-chunk by lane-local index paths; per chunk, the
+// composed map and a look-back for the tangent state V (N x d) entering it;
+// the outputs as one K = N product per chunk, [T x N] x [N x d], on the fp32
+// matrix cores.  Nothing of the sequence is stored besides the outputs and
+// one N x d state per chunk ("Breaking the Memory Wall" summary: exact
+// derivatives without materialising the graph).
+#pragma once
+
+#include "pdscan_device.h"
+#include "pdscan_sens_plan.h"
+
+namespace pdscan {
+
+__device__ __forceinline__ float sens_w(const void* base, size_t i, int bf16) {
+  return bf16 ? __uint_as_float((uint32_t)((const uint16_t*)base)[i] << 16) : ((const float*)base)[i];
+}
+
+__global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const SensPlan& q = a.q;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = q.N, K = q.K, S = q.S, G = q.G, GS = q.GS, d = q.d, T = q.chunk;
+  const int BH = q.B * q.H;
+  uint64_t* dk64 = (uint64_t*)(smem + q.off_dk);   // [K] dictionary rows as nibbles
+  float* Cs = (float*)(smem + q.off_C);
+  int* kl = (int*)(smem + q.off_k);                // [S*G] selections of the chunk
+  float* Wt = (float*)(smem + q.off_W);            // group g, step i: row g*GS + i*16: D_t, then w_t
+  float* cb = (float*)(smem + q.off_cb);           // [16] step-0 coefficients, [16] step-0 rows
+  int* sP = (int*)(smem + q.off_P);                // [G][16] combine scratch (rows)
+  float* sS = (float*)(sP + G * kSensRow);         // [G][16] combine scratch (scales)
+  int* pP = (int*)(sS + G * kSensRow);             // [G][16] inclusive prefix maps
+  float* pS = (float*)(pP + G * kSensRow);
+  float* Vt = (float*)(smem + q.off_V);            // [16][d] tangent state entering the chunk
+  float* V2 = (float*)(smem + q.off_V2);           // [16][d] scratch
+  int* wIdx = (int*)(smem + q.off_win);            // [kSensWin][16] window maps
+  float* wSc = (float*)(wIdx + kSensWin * kSensRow);
+  int* wFlag = (int*)(wSc + kSensWin * kSensRow);  // bit 0: state ready, bit 1: map complete
+  int* misc = (int*)(smem + q.off_misc);
+  uint32_t* hdr = (uint32_t*)a.ws;
+  uint64_t* agg = (uint64_t*)(a.ws + q.ws_agg);
+  uint64_t* inc = (uint64_t*)(a.ws + q.ws_inc);
+
+  // tickets in chunk-major order: a chunk waits only for earlier chunks
+  if (tid == 0) misc[0] = (int)atomicAdd(&hdr[kWsTicket], 1u);
+  __syncthreads();
+  const int task = misc[0];
+  const int c = task / BH, s = task % BH;
+  const int h = s % q.H;
+  const int c0 = c * T;
+  const int Tc = min(T, q.L - c0);
+  const size_t gbase = (size_t)s * q.L + c0;
+  const int ND = N * d;
+
+  // ---- staging: dictionary rows, C, k*, and the chunk's D rows (reads
+  // past a buffer's end return zero)
+  {
+    const rsrc_t dr = make_rsrc(a.dict + (size_t)h * K * N, (uint32_t)(K * N * 4));
+    if (tid < K) {
+      uint64_t v = 0;
+#pragma unroll
+      for (int n = 0; n < 16; ++n)
+        v |= (uint64_t)(uint32_t)buf_i32(dr, n < N ? (uint32_t)(tid * N + n) * 4u : kNoLoad) << (4 * n);
+      dk64[tid] = v;
+    }
+    if (tid < kSensRow) Cs[tid] = tid < N ? a.C[(size_t)h * N + tid] : 0.f;
+  }
+  // each lane group stages its own sub-chunk: row i of group g holds D at
+  // step g S + i (16-wide rows, lanes j >= N write zero)
+  const int gl = lane >> 4, j = lane & 15;
+  const int gam = wave * 4 + gl;
+  const int tb = gam * S;
+  const int nst = max(min(tb + S, Tc) - tb, 0);
+  const bool act = j < N;
+  float* Wg = Wt + gam * GS;
+  {
+    const rsrc_t kr = make_rsrc(a.k_star + gbase, (uint32_t)(Tc * 4));
+    const rsrc_t Dr = make_rsrc(a.D + gbase * N, (uint32_t)(Tc * N * 4));
+    for (int i0 = 0; i0 < nst; i0 += 8) {
+      float dv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        dv[u] = buf_f32(Dr, (act && i0 + u < nst) ? (uint32_t)((tb + i0 + u) * N + j) * 4u : kNoLoad);
+      const int kv = buf_i32(kr, (j < 8 && i0 + j < nst) ? (uint32_t)(tb + i0 + j) * 4u : kNoLoad);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u < nst) Wg[(i0 + u) * kSensRow + j] = dv[u];
+      if (j < 8 && i0 + j < nst) kl[tb + i0 + j] = kv;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase A: lane j of group gam follows the path of row j through its
+  // sub-chunk: p <- idx_t[p], scale <- D_t[p] scale, and replaces row t with
+  // w_t[j] = C[p] scale (the row is read by every lane of the group before
+  // any lane writes it: one wave, LDS in order).  Global step 0 is the
+  // identity (the tangent starts after it).
+  int pth = act ? j : 0;
+  float sc = act ? 1.f : 0.f;
+  for (int i0 = 0; i0 < nst; i0 += 8) {
+    uint64_t dk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dk[u] = dk64[kl[tb + min(i0 + u, nst - 1)]];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u;
+      const bool ok = i < nst;
+      const bool adv = ok && (c0 + tb + i > 0);
+      const float dv = Wg[i * kSensRow + pth];    // rows past nst: slack or the next group, unused
+      const int pn = (int)((dk[u] >> (4 * pth)) & 15u);
+      sc = adv ? sc * dv : sc;
+      pth = adv ? pn : pth;
+      if (ok) Wg[i * kSensRow + j] = act ? Cs[pth] * sc : 0.f;
+    }
+  }
+
+  // ---- combine: inclusive prefix of the group maps in time order (group g
+  // ends with the map from the chunk start to its own end)
+  int cp = pth;
+  float cs = sc;
+  for (int o = 1; o < G; o <<= 1) {
+    sP[gam * kSensRow + j] = cp;
+    sS[gam * kSensRow + j] = cs;
+    __syncthreads();
+    int np_ = cp;
+    float ns_ = cs;
+    if (act && gam >= o) {
+      const int pp = sP[(gam - o) * kSensRow + j];
+      const float ps = sS[(gam - o) * kSensRow + j];
+      np_ = sP[gam * kSensRow + pp];
+      ns_ = sS[gam * kSensRow + pp] * ps;
+    }
+    __syncthreads();
+    cp = np_;
+    cs = ns_;
+  }
+  pP[gam * kSensRow + j] = cp;
+  pS[gam * kSensRow + j] = cs;
+  __syncthreads();
+
+  // ---- publish this chunk's map (rows and scales of the last group)
+  if (wave == 0 && lane < N) {
+    uint64_t* my = agg + ((size_t)c * BH + s) * 2 * N;
+    put_tagged(my + lane, (uint32_t)pP[(G - 1) * kSensRow + lane]);
+    put_tagged(my + N + lane, __float_as_uint(pS[(G - 1) * kSensRow + lane]));
+  }
+
+  // dst = M src for an N x d state, M = (rows, scales) in LDS: row i of dst
+  // sums scale[j] src[j, :] over the j with rows[j] = i, in ascending j, so
+  // the result does not depend on timing
+  auto map_apply = [&](const int* mr, const float* ms, const float* src, float* dst) {
+    for (int e = tid; e < ND; e += kThreads) {
+      const int i = e / d, cc = e - i * d;
+      float acc = 0.f;
+      for (int jj = 0; jj < N; ++jj)
+        if (mr[jj] == i) acc += ms[jj] * src[jj * d + cc];
+      dst[e] = acc;
+    }
+  };
+  // x <- M x for the state in Vt
+  auto apply_map = [&](const int* mr, const float* ms) {
+    map_apply(mr, ms, Vt, V2);
+    __syncthreads();
+    for (int e = tid; e < ND; e += kThreads) Vt[e] = V2[e];
+    __syncthreads();
+  };
+
+  // ---- the tangent state entering this chunk
+  if (c == 0) {
+    // J_0[i, cc] = W_b[i, cc] + sum over j with idx_0[j] = i of
+    //              D_0[j] (1 - D_0[j]) h0[j] W_d[j, cc]
+    if (tid < kSensRow) {
+      float coef = 0.f;
+      int row = 0;
+      if (tid < N) {
+        const float d0 = a.D[gbase * N + tid];
+        coef = d0 * (1.f - d0) * (a.h0 ? a.h0[(size_t)s * N + tid] : 0.f);
+        row = (int)((dk64[kl[0]] >> (4 * tid)) & 15u);
+      }
+      cb[tid] = coef;
+      ((int*)cb)[kSensRow + tid] = row;
+    }
+    __syncthreads();
+    const size_t wb = (size_t)h * N * d;
+    for (int e = tid; e < ND; e += kThreads) {
+      const int i = e / d, cc = e - i * d;
+      float v = sens_w(a.W_b, wb + e, q.in_bf16);
+      for (int jj = 0; jj < N; ++jj)
+        if (((const int*)cb)[kSensRow + jj] == i) v += cb[jj] * sens_w(a.W_d, wb + (size_t)jj * d + cc, q.in_bf16);
+      Vt[e] = v;
+    }
+    __syncthreads();
+  } else {
+    // window over the previous chunks: the nearest published state with
+    // every map after it present; read again until one is (chunk c-1
+    // publishes without waiting for this chunk)
+    const int wq = min(kSensWin, c);
+    int hit = -1;
+    for (int spins = 0;; ++spins) {
+      const int qq = tid / kSensRow, jj = tid % kSensRow;
+      const bool in = qq < wq, on = in && jj < N;
+      uint64_t m0 = kTagValid, m1 = kTagValid, iv = kTagValid;
+      if (on) {
+        const size_t cq = (size_t)(c - 1 - qq) * BH + s;
+        m0 = get_tagged(agg + cq * 2 * N + jj);
+        m1 = get_tagged(agg + cq * 2 * N + N + jj);
+        if (jj == 0) iv = get_tagged(inc + cq * ND);
+        wIdx[qq * kSensRow + jj] = (int)(uint32_t)m0;
+        wSc[qq * kSensRow + jj] = __uint_as_float((uint32_t)m1);
+      }
+      const uint64_t bi = __ballot(tag_ok(iv)), ba = __ballot(tag_ok(m0) && tag_ok(m1));
+      if (in && jj == 0) {
+        const uint64_t gm = 0xFFFFull << lane;
+        wFlag[qq] = ((bi & gm) == gm ? 1 : 0) | ((ba & gm) == gm ? 2 : 0);
+      }
+      __syncthreads();
+      for (int qx = 0; qx < wq; ++qx) {
+        const int f = wFlag[qx];
+        if (f & 1) { hit = qx; break; }
+        if (!(f & 2)) break;
+      }
+      if (hit >= 0) break;
+      if (spins >= kSpinLimit) {
+        if (tid == 0) atomicOr(&hdr[kWsError], 1u);
+        hit = 0;
+        break;
+      }
+      __syncthreads();
+      __builtin_amdgcn_s_sleep(1);
+    }
+    // the published state of chunk c-1-hit (every word checked)
+    {
+      const uint64_t* src = inc + ((size_t)(c - 1 - hit) * BH + s) * ND;
+      for (int e = tid; e < ND; e += kThreads) {
+        uint64_t w = get_tagged((uint64_t*)src + e);
+        for (int n = 0; !tag_ok(w) && n < kSpinLimit; ++n) w = get_tagged((uint64_t*)src + e);
+        Vt[e] = __uint_as_float((uint32_t)w);
+      }
+    }
+    __syncthreads();
+    // then the maps of chunks c-hit .. c-1, oldest first
+    for (int qx = hit - 1; qx >= 0; --qx) apply_map(wIdx + qx * kSensRow, wSc + qx * kSensRow);
+  }
+
+  // ---- publish the state this chunk passes on: its map applied to Vt
+  {
+    map_apply(pP + (G - 1) * kSensRow, pS + (G - 1) * kSensRow, Vt, V2);
+    uint64_t* dst = inc + ((size_t)c * BH + s) * ND;
+    for (int e = tid; e < ND; e += kThreads) put_tagged(dst + e, __float_as_uint(V2[e]));
+  }
+
+  // ---- phase C: dY[t, :] = w_t V for the chunk's steps, where the weight
+  // row of step t (group g) is re-based to the chunk start through the
+  // groups before it: w_t[j] = W[t][P(j)] S(j).  One 16 (channels) x 16
+  // (steps) tile per v_mfma_f32_16x16x4_f32 chain over K = 16 rows; each
+  // lane stores four consecutive channels of one step.
+  {
+    const int i16 = lane & 15, kq = lane >> 4;
+    const int nct = d / 16, nst16 = (Tc + 15) / 16;
+    const rsrc_t yr = make_rsrc(a.dY + gbase * d, (uint32_t)(Tc * d * 4));
+    float av[kSensMaxD / 16][4];                   // A operands: V^T, channels x rows
+#pragma unroll
+    for (int ct = 0; ct < kSensMaxD / 16; ++ct)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int jj = kb * 4 + kq;
+        av[ct][kb] = (ct < nct && jj < N) ? Vt[jj * d + ct * 16 + i16] : 0.f;
+      }
+    for (int st = wave; st < nst16; st += kWaves) {
+      const int t = min(st * 16 + i16, Tc - 1);
+      const int g = t / S, ti = t - g * S;
+      const float* wrow = Wt + g * GS + ti * kSensRow;
+      float bw[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int jj = kb * 4 + kq;
+        float v = 0.f;
+        if (jj < N) {
+          if (g == 0) v = wrow[jj];
+          else v = wrow[pP[(g - 1) * kSensRow + jj]] * pS[(g - 1) * kSensRow + jj];
+        }
+        bw[kb] = v;
+      }
+      const int ts = st * 16 + i16;
+#pragma unroll
+      for (int ct = 0; ct < kSensMaxD / 16; ++ct) {
+        if (ct >= nct) break;
+        f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ct][kb], bw[kb], acc, 0, 0, 0);
+        const uint32_t off = ts < Tc ? (uint32_t)((ts * d + ct * 16 + 4 * kq) * 4) : kNoLoad;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, acc), yr, off, 0, 0);
+      }
+    }
+  }
+}
+
+}  // namespace pdscan
