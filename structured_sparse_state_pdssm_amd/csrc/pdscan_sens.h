@@ -8,11 +8,12 @@
 // weights the forward scan also forms.  The three phases of the chunked scan
 // ("Flash PD-SSM" summary, methodology item 3) become: per lane group, the
 // weight rows of its sub-chunk by lane-local index paths; per chunk, the
-// composed map and a look-back for the tangent state V (N x d) entering it;
+// composed map and a look-back for the map entering it;
 // the outputs as one K = N product per chunk, [T x N] x [N x d], on the fp32
-// matrix cores.  Nothing of the sequence is stored besides the outputs and
-// one N x d state per chunk ("Breaking the Memory Wall" summary: exact
-// derivatives without materialising the graph).
+// matrix cores.  Between chunks only PD maps travel (2N words each): the
+// state entering a chunk is rebuilt as E J_0 from the composed map E, so
+// nothing of the sequence is stored besides the outputs ("Breaking the
+// Memory Wall" summary: exact derivatives without materialising the graph).
 #pragma once
 
 #include "pdscan_device.h"
@@ -34,16 +35,23 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
   float* Cs = (float*)(smem + q.off_C);
   int* kl = (int*)(smem + q.off_k);                // [S*G] selections of the chunk
   float* Wt = (float*)(smem + q.off_W);            // group g, step i: row g*GS + i*16: D_t, then w_t
-  float* cb = (float*)(smem + q.off_cb);           // [16] step-0 coefficients, [16] step-0 rows
+  float* cb = (float*)(smem + q.off_cb);           // [16] step-0 coefficients D_0 (1 - D_0) h0
   int* sP = (int*)(smem + q.off_P);                // [G][16] combine scratch (rows)
   float* sS = (float*)(sP + G * kSensRow);         // [G][16] combine scratch (scales)
   int* pP = (int*)(sS + G * kSensRow);             // [G][16] inclusive prefix maps
   float* pS = (float*)(pP + G * kSensRow);
   float* Vt = (float*)(smem + q.off_V);            // [16][d] tangent state entering the chunk
-  float* V2 = (float*)(smem + q.off_V2);           // [16][d] scratch
-  int* wIdx = (int*)(smem + q.off_win);            // [kSensWin][16] window maps
+  float* Wbt = (float*)(smem + q.off_Wb);          // [N][d] W_b of the head
+  float* Wdt = (float*)(smem + q.off_Wd);          // [N][d] W_d of the head
+  int* wIdx = (int*)(smem + q.off_win);            // [kSensWin][16] window: chunk maps
   float* wSc = (float*)(wIdx + kSensWin * kSensRow);
-  int* wFlag = (int*)(wSc + kSensWin * kSensRow);  // bit 0: state ready, bit 1: map complete
+  int* wIi = (int*)(wSc + kSensWin * kSensRow);    // [kSensWin][16] window: inclusive maps
+  float* wIs = (float*)(wIi + kSensWin * kSensRow);
+  int* wFlag = (int*)(wIs + kSensWin * kSensRow);  // bit 0: inclusive map complete, bit 1: chunk map complete
+  int* eP = wFlag + kSensWin;                      // [16] map entering the chunk (E)
+  float* eS = (float*)(eP + kSensRow);
+  int* fP = (int*)(eS + kSensRow);                 // [16] E composed with step 0's coefficient map (F)
+  float* fS = (float*)(fP + kSensRow);
   int* misc = (int*)(smem + q.off_misc);
   uint32_t* hdr = (uint32_t*)a.ws;
   uint64_t* agg = (uint64_t*)(a.ws + q.ws_agg);
@@ -72,6 +80,22 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
       dk64[tid] = v;
     }
     if (tid < kSensRow) Cs[tid] = tid < N ? a.C[(size_t)h * N + tid] : 0.f;
+    // the head's W_b and W_d (fp32 in LDS) and step 0 of the sequence: k*_0
+    // and the coefficients D_0 (1 - D_0) h0 of the state tangent after it
+    const size_t wb = (size_t)h * N * d;
+    for (int e = tid; e < ND; e += kThreads) {
+      Wbt[e] = sens_w(a.W_b, wb + e, q.in_bf16);
+      Wdt[e] = sens_w(a.W_d, wb + e, q.in_bf16);
+    }
+    if (tid < kSensRow) {
+      float coef = 0.f;
+      if (tid < N) {
+        const float d0 = a.D[(size_t)s * q.L * N + tid];
+        coef = d0 * (1.f - d0) * (a.h0 ? a.h0[(size_t)s * N + tid] : 0.f);
+      }
+      cb[tid] = coef;
+    }
+    if (tid == 0) misc[1] = a.k_star[(size_t)s * q.L];
   }
   // each lane group stages its own sub-chunk: row i of group g holds D at
   // step g S + i (16-wide rows, lanes j >= N write zero)
@@ -153,109 +177,94 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
     put_tagged(my + N + lane, __float_as_uint(pS[(G - 1) * kSensRow + lane]));
   }
 
-  // dst = M src for an N x d state, M = (rows, scales) in LDS: row i of dst
-  // sums scale[j] src[j, :] over the j with rows[j] = i, in ascending j, so
-  // the result does not depend on timing
-  auto map_apply = [&](const int* mr, const float* ms, const float* src, float* dst) {
-    for (int e = tid; e < ND; e += kThreads) {
-      const int i = e / d, cc = e - i * d;
-      float acc = 0.f;
-      for (int jj = 0; jj < N; ++jj)
-        if (mr[jj] == i) acc += ms[jj] * src[jj * d + cc];
-      dst[e] = acc;
+  // ---- the map entering this chunk, E = M_{c-1} o ... o M_0 (from step 1
+  // to the chunk start; identity for chunk 0), composed like the forward
+  // scan's carries: all lanes read the inclusive maps and chunk maps of the
+  // previous chunks in one batch; the nearest complete inclusive map with
+  // every chunk map after it present gives E, read again until one is
+  // (chunk c-1 publishes without waiting for this chunk)
+  int hit = -1;
+  const int wq = min(kSensWin, c);
+  for (int spins = 0; wq > 0; ++spins) {
+    const int qq = tid / kSensRow, jj = tid % kSensRow;
+    const bool in = qq < wq, on = in && jj < N;
+    uint64_t m0 = kTagValid, m1 = kTagValid, i0 = kTagValid, i1 = kTagValid;
+    if (on) {
+      const size_t cq = (size_t)(c - 1 - qq) * BH + s;
+      m0 = get_tagged(agg + cq * 2 * N + jj);
+      m1 = get_tagged(agg + cq * 2 * N + N + jj);
+      i0 = get_tagged(inc + cq * 2 * N + jj);
+      i1 = get_tagged(inc + cq * 2 * N + N + jj);
+      wIdx[qq * kSensRow + jj] = (int)(uint32_t)m0;
+      wSc[qq * kSensRow + jj] = __uint_as_float((uint32_t)m1);
+      wIi[qq * kSensRow + jj] = (int)(uint32_t)i0;
+      wIs[qq * kSensRow + jj] = __uint_as_float((uint32_t)i1);
     }
-  };
-  // x <- M x for the state in Vt
-  auto apply_map = [&](const int* mr, const float* ms) {
-    map_apply(mr, ms, Vt, V2);
-    __syncthreads();
-    for (int e = tid; e < ND; e += kThreads) Vt[e] = V2[e];
-    __syncthreads();
-  };
-
-  // ---- the tangent state entering this chunk
-  if (c == 0) {
-    // J_0[i, cc] = W_b[i, cc] + sum over j with idx_0[j] = i of
-    //              D_0[j] (1 - D_0[j]) h0[j] W_d[j, cc]
-    if (tid < kSensRow) {
-      float coef = 0.f;
-      int row = 0;
-      if (tid < N) {
-        const float d0 = a.D[gbase * N + tid];
-        coef = d0 * (1.f - d0) * (a.h0 ? a.h0[(size_t)s * N + tid] : 0.f);
-        row = (int)((dk64[kl[0]] >> (4 * tid)) & 15u);
-      }
-      cb[tid] = coef;
-      ((int*)cb)[kSensRow + tid] = row;
+    const uint64_t bi = __ballot(tag_ok(i0) && tag_ok(i1)), ba = __ballot(tag_ok(m0) && tag_ok(m1));
+    if (in && jj == 0) {
+      const uint64_t gm = 0xFFFFull << lane;
+      wFlag[qq] = ((bi & gm) == gm ? 1 : 0) | ((ba & gm) == gm ? 2 : 0);
     }
     __syncthreads();
-    const size_t wb = (size_t)h * N * d;
-    for (int e = tid; e < ND; e += kThreads) {
-      const int i = e / d, cc = e - i * d;
-      float v = sens_w(a.W_b, wb + e, q.in_bf16);
-      for (int jj = 0; jj < N; ++jj)
-        if (((const int*)cb)[kSensRow + jj] == i) v += cb[jj] * sens_w(a.W_d, wb + (size_t)jj * d + cc, q.in_bf16);
-      Vt[e] = v;
+    for (int qx = 0; qx < wq; ++qx) {
+      const int f = wFlag[qx];
+      if (f & 1) { hit = qx; break; }
+      if (!(f & 2)) break;
+    }
+    if (hit >= 0) break;
+    if (spins >= kSpinLimit) {
+      if (tid == 0) atomicOr(&hdr[kWsError], 1u);
+      hit = 0;
+      break;
     }
     __syncthreads();
-  } else {
-    // window over the previous chunks: the nearest published state with
-    // every map after it present; read again until one is (chunk c-1
-    // publishes without waiting for this chunk)
-    const int wq = min(kSensWin, c);
-    int hit = -1;
-    for (int spins = 0;; ++spins) {
-      const int qq = tid / kSensRow, jj = tid % kSensRow;
-      const bool in = qq < wq, on = in && jj < N;
-      uint64_t m0 = kTagValid, m1 = kTagValid, iv = kTagValid;
-      if (on) {
-        const size_t cq = (size_t)(c - 1 - qq) * BH + s;
-        m0 = get_tagged(agg + cq * 2 * N + jj);
-        m1 = get_tagged(agg + cq * 2 * N + N + jj);
-        if (jj == 0) iv = get_tagged(inc + cq * ND);
-        wIdx[qq * kSensRow + jj] = (int)(uint32_t)m0;
-        wSc[qq * kSensRow + jj] = __uint_as_float((uint32_t)m1);
-      }
-      const uint64_t bi = __ballot(tag_ok(iv)), ba = __ballot(tag_ok(m0) && tag_ok(m1));
-      if (in && jj == 0) {
-        const uint64_t gm = 0xFFFFull << lane;
-        wFlag[qq] = ((bi & gm) == gm ? 1 : 0) | ((ba & gm) == gm ? 2 : 0);
-      }
-      __syncthreads();
-      for (int qx = 0; qx < wq; ++qx) {
-        const int f = wFlag[qx];
-        if (f & 1) { hit = qx; break; }
-        if (!(f & 2)) break;
-      }
-      if (hit >= 0) break;
-      if (spins >= kSpinLimit) {
-        if (tid == 0) atomicOr(&hdr[kWsError], 1u);
-        hit = 0;
-        break;
-      }
-      __syncthreads();
-      __builtin_amdgcn_s_sleep(1);
-    }
-    // the published state of chunk c-1-hit (every word checked)
-    {
-      const uint64_t* src = inc + ((size_t)(c - 1 - hit) * BH + s) * ND;
-      for (int e = tid; e < ND; e += kThreads) {
-        uint64_t w = get_tagged((uint64_t*)src + e);
-        for (int n = 0; !tag_ok(w) && n < kSpinLimit; ++n) w = get_tagged((uint64_t*)src + e);
-        Vt[e] = __uint_as_float((uint32_t)w);
-      }
-    }
-    __syncthreads();
-    // then the maps of chunks c-hit .. c-1, oldest first
-    for (int qx = hit - 1; qx >= 0; --qx) apply_map(wIdx + qx * kSensRow, wSc + qx * kSensRow);
+    __builtin_amdgcn_s_sleep(1);
   }
-
-  // ---- publish the state this chunk passes on: its map applied to Vt
-  {
-    map_apply(pP + (G - 1) * kSensRow, pS + (G - 1) * kSensRow, Vt, V2);
-    uint64_t* dst = inc + ((size_t)c * BH + s) * ND;
-    for (int e = tid; e < ND; e += kThreads) put_tagged(dst + e, __float_as_uint(V2[e]));
+  // E, the inclusive map this chunk publishes (M_c o E), and F = E o F0 with
+  // F0 = (idx_0, D_0 (1 - D_0) h0), step 0's coefficient map: lane-local
+  // path compositions (lanes j < N of wave 0)
+  if (wave == 0 && lane < kSensRow) {
+    const int jj = lane;
+    int ep = jj;
+    float es = jj < N ? 1.f : 0.f;
+    if (hit >= 0 && jj < N) {
+      ep = wIi[hit * kSensRow + jj];
+      es = wIs[hit * kSensRow + jj];
+      for (int qx = hit - 1; qx >= 0; --qx) {   // chunks c-hit .. c-1, oldest first
+        es = wSc[qx * kSensRow + ep] * es;
+        ep = wIdx[qx * kSensRow + ep];
+      }
+    }
+    eP[jj] = ep;
+    eS[jj] = es;
+    const int r0 = jj < N ? (int)((dk64[misc[1]] >> (4 * jj)) & 15u) : 0;
+    if (jj < N) {
+      // publish M_c o E
+      const int* mr = pP + (G - 1) * kSensRow;
+      const float* ms = pS + (G - 1) * kSensRow;
+      uint64_t* my = inc + ((size_t)c * BH + s) * 2 * N;
+      put_tagged(my + jj, (uint32_t)mr[ep]);
+      put_tagged(my + N + jj, __float_as_uint(ms[ep] * es));
+    }
+    WAVE_SYNC();
+    fP[jj] = jj < N ? eP[r0] : 0;
+    fS[jj] = jj < N ? eS[r0] * cb[jj] : 0.f;
   }
+  __syncthreads();
+
+  // ---- the tangent state entering this chunk: V = E J_0 with
+  // J_0 = W_b + F0 W_d, i.e. V = E W_b + F W_d; row i sums the rows j mapped
+  // to it in ascending j, so the result does not depend on timing
+  for (int e = tid; e < ND; e += kThreads) {
+    const int i = e / d, cc = e - i * d;
+    float acc = 0.f;
+    for (int jj = 0; jj < N; ++jj) {
+      if (eP[jj] == i) acc += eS[jj] * Wbt[jj * d + cc];
+      if (fP[jj] == i) acc += fS[jj] * Wdt[jj * d + cc];
+    }
+    Vt[e] = acc;
+  }
+  __syncthreads();
 
   // ---- phase C: dY[t, :] = w_t V for the chunk's steps, where the weight
   // row of step t (group g) is re-based to the chunk start through the

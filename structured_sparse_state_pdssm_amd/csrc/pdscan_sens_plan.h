@@ -15,7 +15,7 @@ constexpr int kSensRow = 16;     // LDS row width of the weight rows (N <= 16)
 struct SensPlan {
   int B, H, L, N, K, d, in_bf16, chunk;
   int S, G, GS, nC, tasks;
-  int off_dk, off_C, off_k, off_W, off_cb, off_P, off_V, off_V2, off_win, off_misc, bytes;
+  int off_dk, off_C, off_k, off_W, off_cb, off_P, off_V, off_Wb, off_Wd, off_win, off_misc, bytes;
   size_t ws_agg, ws_inc, ws_bytes;
 };
 
@@ -34,17 +34,18 @@ inline bool make_sens_plan(SensPlan& q, int B, int H, int L, int N, int K, int d
   q.off_C = take(kSensRow * 4);
   q.off_k = take(q.S * q.G * 4);
   q.off_W = take((q.G * q.GS + 8 * kSensRow) * 4);   // + 8 rows of slack for block reads
-  q.off_cb = take(2 * kSensRow * 4);                 // step-0 coefficients and rows (chunk 0)
+  q.off_cb = take(kSensRow * 4);                     // step-0 coefficients
   q.off_P = take(4 * q.G * kSensRow * 4);            // combine: sP, sS, pP, pS
-  q.off_V = take(kSensRow * d * 4);
-  q.off_V2 = take(kSensRow * d * 4);
-  q.off_win = take(kSensWin * (2 * kSensRow + 1) * 4);
+  q.off_V = take(kSensRow * d * 4);                  // tangent state entering the chunk
+  q.off_Wb = take(kSensRow * d * 4);                 // W_b of the head (fp32)
+  q.off_Wd = take(kSensRow * d * 4);                 // W_d of the head (fp32)
+  q.off_win = take((kSensWin * (4 * kSensRow + 1) + 4 * kSensRow) * 4);   // window, E and F maps
   q.off_misc = take(16);
   q.bytes = off;
   const size_t seqchunks = (size_t)q.nC * B * H;
   q.ws_agg = 256;
   q.ws_inc = q.ws_agg + seqchunks * 2 * N * sizeof(uint64_t);
-  q.ws_bytes = q.ws_inc + seqchunks * (size_t)N * d * sizeof(uint64_t);
+  q.ws_bytes = q.ws_inc + seqchunks * 2 * N * sizeof(uint64_t);
   return q.bytes <= kMaxLds;
 }
 
