@@ -157,8 +157,9 @@ int sens_plan(pdscan::SensPlan& q, const pdssm_dims* dims, int32_t chunk) {
                 dims->d_in, pdscan::kSensMaxD);
   if (!pdscan::make_sens_plan(q, dims->B, dims->H, dims->L, dims->N, dims->K, dims->d_in,
                               dims->in_dtype == PDSSM_BF16, chunk))
-    return fail(PDSSM_EUNSUPPORTED, "impulse sensitivity: chunk=%d with d_in=%d needs %d bytes of "
-                "on-chip memory (limit %d)", chunk, dims->d_in, q.bytes, pdscan::kMaxLds);
+    return fail(PDSSM_EUNSUPPORTED, "impulse sensitivity: chunk=%d with d_in=%d needs %d steps per lane "
+                "group (at most %d: chunk <= 512) and %d bytes of on-chip memory (at most %d)", chunk,
+                dims->d_in, q.S, pdscan::kSensMaxS, q.bytes, pdscan::kMaxLds);
   if ((uint64_t)q.nC * dims->B * dims->H > 0x7fffffffull)
     return fail(PDSSM_EUNSUPPORTED, "too many chunks");
   return PDSSM_OK;

@@ -17,7 +17,17 @@ hipError_t launch_sens(const SensArgs& a, hipStream_t st) {
   if (cb > 8192) cb = 8192;
   if (cb < 1) cb = 1;
   hipLaunchKernelGGL(sens_clear_kernel, dim3((unsigned)cb), dim3(256), 0, st, (uint64_t*)a.ws, words);
-  hipLaunchKernelGGL(pdssm_sens_kernel, dim3((unsigned)q.tasks), dim3(kThreads), (unsigned)q.bytes, st, a);
+  const dim3 grid((unsigned)q.tasks), block(kThreads);
+  switch (q.d / 16) {
+    case 1: hipLaunchKernelGGL(pdssm_sens_kernel<1>, grid, block, (unsigned)q.bytes, st, a); break;
+    case 2: hipLaunchKernelGGL(pdssm_sens_kernel<2>, grid, block, (unsigned)q.bytes, st, a); break;
+    case 3: hipLaunchKernelGGL(pdssm_sens_kernel<3>, grid, block, (unsigned)q.bytes, st, a); break;
+    case 4: hipLaunchKernelGGL(pdssm_sens_kernel<4>, grid, block, (unsigned)q.bytes, st, a); break;
+    case 5: hipLaunchKernelGGL(pdssm_sens_kernel<5>, grid, block, (unsigned)q.bytes, st, a); break;
+    case 6: hipLaunchKernelGGL(pdssm_sens_kernel<6>, grid, block, (unsigned)q.bytes, st, a); break;
+    case 7: hipLaunchKernelGGL(pdssm_sens_kernel<7>, grid, block, (unsigned)q.bytes, st, a); break;
+    default: hipLaunchKernelGGL(pdssm_sens_kernel<8>, grid, block, (unsigned)q.bytes, st, a); break;
+  }
   return hipGetLastError();
 }
 

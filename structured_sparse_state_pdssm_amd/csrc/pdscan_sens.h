@@ -21,10 +21,8 @@
 
 namespace pdscan {
 
-__device__ __forceinline__ float sens_w(const void* base, size_t i, int bf16) {
-  return bf16 ? __uint_as_float((uint32_t)((const uint16_t*)base)[i] << 16) : ((const float*)base)[i];
-}
-
+// NCT = d / 16 channel tiles (1..8)
+template <int NCT>
 __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const SensPlan& q = a.q;
@@ -40,9 +38,10 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
   float* sS = (float*)(sP + G * kSensRow);         // [G][16] combine scratch (scales)
   int* pP = (int*)(sS + G * kSensRow);             // [G][16] inclusive prefix maps
   float* pS = (float*)(pP + G * kSensRow);
-  float* Vt = (float*)(smem + q.off_V);            // [16][d] tangent state entering the chunk
-  float* Wbt = (float*)(smem + q.off_Wb);          // [N][d] W_b of the head
-  float* Wdt = (float*)(smem + q.off_Wd);          // [N][d] W_d of the head
+  int* gEp = (int*)(smem + q.off_V);               // [G][16] per-group maps GE and GF (phase C)
+  float* gEs = (float*)(gEp + G * kSensRow);
+  int* gFp = (int*)(gEs + G * kSensRow);
+  float* gFs = (float*)(gFp + G * kSensRow);
   int* wIdx = (int*)(smem + q.off_win);            // [kSensWin][16] window: chunk maps
   float* wSc = (float*)(wIdx + kSensWin * kSensRow);
   int* wIi = (int*)(wSc + kSensWin * kSensRow);    // [kSensWin][16] window: inclusive maps
@@ -68,56 +67,107 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
   const size_t gbase = (size_t)s * q.L + c0;
   const int ND = N * d;
 
-  // ---- staging: dictionary rows, C, k*, and the chunk's D rows (reads
-  // past a buffer's end return zero)
-  {
-    const rsrc_t dr = make_rsrc(a.dict + (size_t)h * K * N, (uint32_t)(K * N * 4));
-    if (tid < K) {
-      uint64_t v = 0;
-#pragma unroll
-      for (int n = 0; n < 16; ++n)
-        v |= (uint64_t)(uint32_t)buf_i32(dr, n < N ? (uint32_t)(tid * N + n) * 4u : kNoLoad) << (4 * n);
-      dk64[tid] = v;
-    }
-    if (tid < kSensRow) Cs[tid] = tid < N ? a.C[(size_t)h * N + tid] : 0.f;
-    // the head's W_b and W_d (fp32 in LDS) and step 0 of the sequence: k*_0
-    // and the coefficients D_0 (1 - D_0) h0 of the state tangent after it
-    const size_t wb = (size_t)h * N * d;
-    for (int e = tid; e < ND; e += kThreads) {
-      Wbt[e] = sens_w(a.W_b, wb + e, q.in_bf16);
-      Wdt[e] = sens_w(a.W_d, wb + e, q.in_bf16);
-    }
-    if (tid < kSensRow) {
-      float coef = 0.f;
-      if (tid < N) {
-        const float d0 = a.D[(size_t)s * q.L * N + tid];
-        coef = d0 * (1.f - d0) * (a.h0 ? a.h0[(size_t)s * N + tid] : 0.f);
-      }
-      cb[tid] = coef;
-    }
-    if (tid == 0) misc[1] = a.k_star[(size_t)s * q.L];
-  }
-  // each lane group stages its own sub-chunk: row i of group g holds D at
-  // step g S + i (16-wide rows, lanes j >= N write zero)
+  // ---- staging: every load of the task is issued before the first wait
+  // (buffer loads; a lane with nothing to load reads zero through an
+  // out-of-range offset): dictionary rows, C, step 0 of the sequence (k*_0
+  // and D_0, h0 for the coefficients D_0 (1 - D_0) h0 of the state tangent
+  // after it), this group's k* and D rows, and phase C's operands W_b, W_d
   const int gl = lane >> 4, j = lane & 15;
   const int gam = wave * 4 + gl;
   const int tb = gam * S;
   const int nst = max(min(tb + S, Tc) - tb, 0);
   const bool act = j < N;
   float* Wg = Wt + gam * GS;
+  const int i16 = lane & 15, kq = lane >> 4;
+  float av[NCT][8];                                // phase C A operands: [W_b; W_d]^T
+  int kv[kSensMaxS / 16];
+  f4v v4[kSensMaxS * 16 / 64];                     // this group's D rows, four values per slot
+  const bool vec = (N & 3) == 0;                   // 16-byte pieces never straddle a row
+  const int nD = nst * N, eb = tb * N;
   {
+    const rsrc_t dr = make_rsrc(a.dict + (size_t)h * K * N, (uint32_t)(K * N * 4));
+    const rsrc_t cr = make_rsrc(a.C + (size_t)h * N, (uint32_t)(N * 4));
+    const rsrc_t sd = make_rsrc(a.D + (size_t)s * q.L * N, (uint32_t)(N * 4));
+    const rsrc_t hr = make_rsrc(a.h0 ? a.h0 + (size_t)s * N : a.C, a.h0 ? (uint32_t)(N * 4) : 0u);
     const rsrc_t kr = make_rsrc(a.k_star + gbase, (uint32_t)(Tc * 4));
+    const rsrc_t k0r = make_rsrc(a.k_star + (size_t)s * q.L, 4u);
     const rsrc_t Dr = make_rsrc(a.D + gbase * N, (uint32_t)(Tc * N * 4));
-    for (int i0 = 0; i0 < nst; i0 += 8) {
-      float dv[8];
+    const int es = q.in_bf16 ? 2 : 4;
+    const rsrc_t wbr = make_rsrc((const unsigned char*)a.W_b + (size_t)h * N * d * es, (uint32_t)(N * d * es));
+    const rsrc_t wdr = make_rsrc((const unsigned char*)a.W_d + (size_t)h * N * d * es, (uint32_t)(N * d * es));
+    int dn[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        dv[u] = buf_f32(Dr, (act && i0 + u < nst) ? (uint32_t)((tb + i0 + u) * N + j) * 4u : kNoLoad);
-      const int kv = buf_i32(kr, (j < 8 && i0 + j < nst) ? (uint32_t)(tb + i0 + j) * 4u : kNoLoad);
+    for (int n = 0; n < 16; ++n) dn[n] = buf_i32(dr, (tid < K && n < N) ? (uint32_t)(tid * N + n) * 4u : kNoLoad);
+    const float cv = buf_f32(cr, tid < N ? (uint32_t)tid * 4u : kNoLoad);
+    const float d0 = buf_f32(sd, tid < N ? (uint32_t)tid * 4u : kNoLoad);
+    const float hv = buf_f32(hr, tid < N ? (uint32_t)tid * 4u : kNoLoad);
+    const int k0 = buf_i32(k0r, tid == 0 ? 0u : kNoLoad);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (i0 + u < nst) Wg[(i0 + u) * kSensRow + j] = dv[u];
-      if (j < 8 && i0 + j < nst) kl[tb + i0 + j] = kv;
+    for (int m = 0; m < kSensMaxS / 16; ++m)
+      kv[m] = buf_i32(kr, j + 16 * m < nst ? (uint32_t)(tb + j + 16 * m) * 4u : kNoLoad);
+    if (vec) {
+#pragma unroll
+      for (int m = 0; m < kSensMaxS * 16 / 64; ++m) {
+        const int e = 4 * (j + 16 * m);
+        v4[m] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(Dr, e < nD ? (uint32_t)(eb + e) * 4u : kNoLoad, 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < kSensMaxS * 16 / 64; ++m)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int e = j + 16 * (4 * m + q4);
+          v4[m][q4] = buf_f32(Dr, e < nD ? (uint32_t)(eb + e) * 4u : kNoLoad);
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const int kk = kb * 4 + kq, jj = kk & 15;
+        const bool ok = jj < N;
+        const uint32_t e = (uint32_t)(jj * d + ct * 16 + i16);
+        const rsrc_t wr = kk < 16 ? wbr : wdr;
+        if (q.in_bf16)
+          av[ct][kb] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, ok ? e * 2u : kNoLoad, 0, 0) << 16);
+        else
+          av[ct][kb] = buf_f32(wr, ok ? e * 4u : kNoLoad);
+      }
+    // stores
+    if (tid < K) {
+      uint64_t v = 0;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) v |= (uint64_t)(uint32_t)dn[n] << (4 * n);
+      dk64[tid] = v;
+    }
+    if (tid < kSensRow) {
+      Cs[tid] = cv;
+      cb[tid] = d0 * (1.f - d0) * hv;              // zero past N (and without h0)
+    }
+    if (tid == 0) misc[1] = k0;
+#pragma unroll
+    for (int m = 0; m < kSensMaxS / 16; ++m)
+      if (j + 16 * m < nst) kl[tb + j + 16 * m] = kv[m];
+    if (vec) {
+#pragma unroll
+      for (int m = 0; m < kSensMaxS * 16 / 64; ++m) {
+        const int e = 4 * (j + 16 * m);
+        if (e < nD) {
+          const int r = e / N;
+          *(f4v*)(Wg + r * kSensRow + (e - r * N)) = v4[m];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < kSensMaxS * 16 / 64; ++m)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int e = j + 16 * (4 * m + q4);
+          if (e < nD) {
+            const int r = e / N;
+            Wg[r * kSensRow + (e - r * N)] = v4[m][q4];
+          }
+        }
     }
   }
   __syncthreads();
@@ -130,20 +180,35 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
   int pth = act ? j : 0;
   float sc = act ? 1.f : 0.f;
   for (int i0 = 0; i0 < nst; i0 += 8) {
+    // per block of eight steps: the path (registers only), then every read
+    // of the block, then the scales, then the block's rows are replaced
     uint64_t dk[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) dk[u] = dk64[kl[tb + min(i0 + u, nst - 1)]];
+    int pp[9];
+    pp[0] = pth;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u;
-      const bool ok = i < nst;
-      const bool adv = ok && (c0 + tb + i > 0);
-      const float dv = Wg[i * kSensRow + pth];    // rows past nst: slack or the next group, unused
-      const int pn = (int)((dk[u] >> (4 * pth)) & 15u);
-      sc = adv ? sc * dv : sc;
-      pth = adv ? pn : pth;
-      if (ok) Wg[i * kSensRow + j] = act ? Cs[pth] * sc : 0.f;
+      const bool adv = i0 + u < nst && c0 + tb + i0 + u > 0;
+      pp[u + 1] = adv ? (int)((dk[u] >> (4 * pp[u])) & 15u) : pp[u];
     }
+    float dv[8], cv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      dv[u] = Wg[(i0 + u) * kSensRow + pp[u]];     // rows past nst: slack or the next group, unused
+      cv[u] = Cs[pp[u + 1]];
+    }
+    float wv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool adv = i0 + u < nst && c0 + tb + i0 + u > 0;
+      sc = adv ? sc * dv[u] : sc;
+      wv[u] = act ? cv[u] * sc : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u < nst) Wg[(i0 + u) * kSensRow + j] = wv[u];
+    pth = pp[8];
   }
 
   // ---- combine: inclusive prefix of the group maps in time order (group g
@@ -252,59 +317,54 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
   }
   __syncthreads();
 
-  // ---- the tangent state entering this chunk: V = E J_0 with
-  // J_0 = W_b + F0 W_d, i.e. V = E W_b + F W_d; row i sums the rows j mapped
-  // to it in ascending j, so the result does not depend on timing
-  for (int e = tid; e < ND; e += kThreads) {
-    const int i = e / d, cc = e - i * d;
-    float acc = 0.f;
-    for (int jj = 0; jj < N; ++jj) {
-      if (eP[jj] == i) acc += eS[jj] * Wbt[jj * d + cc];
-      if (fP[jj] == i) acc += fS[jj] * Wdt[jj * d + cc];
+  // ---- the per-group maps Phase C reads: with Pg the map from the chunk
+  // start to group g's start (identity for g = 0), GE = Pg o E and
+  // GF = Pg o F.  Then dy_t/du_0 = (w_t GE) W_b + (w_t GF) W_d for a step t
+  // of group g, where w_t is the group-local weight row of phase A.
+  {
+    const int g = tid / kSensRow, jj = tid % kSensRow;
+    int ep = eP[jj], fp = fP[jj];
+    float es = eS[jj], fs = fS[jj];
+    if (g > 0) {
+      const int* gp = pP + (g - 1) * kSensRow;
+      const float* gs = pS + (g - 1) * kSensRow;
+      es *= gs[ep];
+      ep = gp[ep];
+      fs *= gs[fp];
+      fp = gp[fp];
     }
-    Vt[e] = acc;
+    gEp[g * kSensRow + jj] = ep;
+    gEs[g * kSensRow + jj] = jj < N ? es : 0.f;
+    gFp[g * kSensRow + jj] = fp;
+    gFs[g * kSensRow + jj] = jj < N ? fs : 0.f;
   }
   __syncthreads();
 
-  // ---- phase C: dY[t, :] = w_t V for the chunk's steps, where the weight
-  // row of step t (group g) is re-based to the chunk start through the
-  // groups before it: w_t[j] = W[t][P(j)] S(j).  One 16 (channels) x 16
-  // (steps) tile per v_mfma_f32_16x16x4_f32 chain over K = 16 rows; each
-  // lane stores four consecutive channels of one step.
+  // ---- phase C: dY[t, :] = (w_t GE) W_b + (w_t GF) W_d for the chunk's
+  // steps: one 16 (channels) x 16 (steps) tile per chain of eight
+  // v_mfma_f32_16x16x4_f32 over K = 32 (the rows of W_b, then of W_d); each
+  // lane stores four consecutive channels of one step
   {
-    const int i16 = lane & 15, kq = lane >> 4;
-    const int nct = d / 16, nst16 = (Tc + 15) / 16;
+    const int nst16 = (Tc + 15) / 16;
     const rsrc_t yr = make_rsrc(a.dY + gbase * d, (uint32_t)(Tc * d * 4));
-    float av[kSensMaxD / 16][4];                   // A operands: V^T, channels x rows
-#pragma unroll
-    for (int ct = 0; ct < kSensMaxD / 16; ++ct)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int jj = kb * 4 + kq;
-        av[ct][kb] = (ct < nct && jj < N) ? Vt[jj * d + ct * 16 + i16] : 0.f;
-      }
     for (int st = wave; st < nst16; st += kWaves) {
       const int t = min(st * 16 + i16, Tc - 1);
       const int g = t / S, ti = t - g * S;
       const float* wrow = Wt + g * GS + ti * kSensRow;
-      float bw[4];
+      float bw[8];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int jj = kb * 4 + kq;
-        float v = 0.f;
-        if (jj < N) {
-          if (g == 0) v = wrow[jj];
-          else v = wrow[pP[(g - 1) * kSensRow + jj]] * pS[(g - 1) * kSensRow + jj];
-        }
-        bw[kb] = v;
+      for (int kb = 0; kb < 8; ++kb) {
+        const int kk = kb * 4 + kq, jj = kk & 15;
+        const int mp = kk < 16 ? gEp[g * kSensRow + jj] : gFp[g * kSensRow + jj];
+        const float ms = kk < 16 ? gEs[g * kSensRow + jj] : gFs[g * kSensRow + jj];
+        bw[kb] = wrow[mp] * ms;                    // ms is zero for rows jj >= N
       }
       const int ts = st * 16 + i16;
 #pragma unroll
-      for (int ct = 0; ct < kSensMaxD / 16; ++ct) {
-        if (ct >= nct) break;
+      for (int ct = 0; ct < NCT; ++ct) {
         f4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ct][kb], bw[kb], acc, 0, 0, 0);
+        for (int kb = 0; kb < 8; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ct][kb], bw[kb], acc, 0, 0, 0);
         const uint32_t off = ts < Tc ? (uint32_t)((ts * d + ct * 16 + 4 * kq) * 4) : kNoLoad;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, acc), yr, off, 0, 0);
       }

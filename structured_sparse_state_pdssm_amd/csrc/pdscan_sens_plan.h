@@ -11,11 +11,12 @@ namespace pdscan {
 constexpr int kSensMaxD = 128;   // input channels (multiple of 16)
 constexpr int kSensWin = 8;      // later-published chunks one window read covers
 constexpr int kSensRow = 16;     // LDS row width of the weight rows (N <= 16)
+constexpr int kSensMaxS = 32;    // steps per lane group at most (chunk <= 512)
 
 struct SensPlan {
   int B, H, L, N, K, d, in_bf16, chunk;
   int S, G, GS, nC, tasks;
-  int off_dk, off_C, off_k, off_W, off_cb, off_P, off_V, off_Wb, off_Wd, off_win, off_misc, bytes;
+  int off_dk, off_C, off_k, off_W, off_cb, off_P, off_V, off_win, off_misc, bytes;
   size_t ws_agg, ws_inc, ws_bytes;
 };
 
@@ -36,9 +37,7 @@ inline bool make_sens_plan(SensPlan& q, int B, int H, int L, int N, int K, int d
   q.off_W = take((q.G * q.GS + 8 * kSensRow) * 4);   // + 8 rows of slack for block reads
   q.off_cb = take(kSensRow * 4);                     // step-0 coefficients
   q.off_P = take(4 * q.G * kSensRow * 4);            // combine: sP, sS, pP, pS
-  q.off_V = take(kSensRow * d * 4);                  // tangent state entering the chunk
-  q.off_Wb = take(kSensRow * d * 4);                 // W_b of the head (fp32)
-  q.off_Wd = take(kSensRow * d * 4);                 // W_d of the head (fp32)
+  q.off_V = take(4 * q.G * kSensRow * 4);            // per-group maps of phase C
   q.off_win = take((kSensWin * (4 * kSensRow + 1) + 4 * kSensRow) * 4);   // window, E and F maps
   q.off_misc = take(16);
   q.bytes = off;
@@ -46,7 +45,7 @@ inline bool make_sens_plan(SensPlan& q, int B, int H, int L, int N, int K, int d
   q.ws_agg = 256;
   q.ws_inc = q.ws_agg + seqchunks * 2 * N * sizeof(uint64_t);
   q.ws_bytes = q.ws_inc + seqchunks * 2 * N * sizeof(uint64_t);
-  return q.bytes <= kMaxLds;
+  return q.S <= kSensMaxS && q.bytes <= kMaxLds;
 }
 
 struct SensArgs {
