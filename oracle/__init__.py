@@ -5,6 +5,7 @@ TEST INFRASTRUCTURE: imported only by the tests, the smoke check and the
 benchmark's CPU-baseline leg; never by the product path."""
 
 from .pdssm_oracle import (  # noqa: F401
+    dict_hardmax,
     drive,
     forward,
     forward_wb,
@@ -13,11 +14,13 @@ from .pdssm_oracle import (  # noqa: F401
     pd_apply,
     pd_compose,
     scan,
+    scan_pidx,
     scan_states,
     scan_vjp,
     scores,
     select,
     sigmoid,
+    soft_select,
     three_phase,
     transition_matrix,
 )

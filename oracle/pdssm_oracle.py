@@ -26,6 +26,11 @@ transition of every step and multiplies; it never uses the sparse structure.
 ``forward_wb`` is the same forward pass with the drive terms Bu_t = W_b u_t
 formed from the input (``drive``) instead of being given.
 
+``soft_select`` / ``scan_pidx`` are the original soft-selection model, kept
+as a comparison path: a softmax-weighted mixture of dense dictionary
+matrices, its column hardmax per step, and the recurrence on those per-step
+maps; ``dict_hardmax`` builds the sparse dictionary from dense matrices.
+
 ``impulse_sensitivity`` is dy_t / du_0 for fixed selections, carried forward
 from step 0 by the same dense transitions (forward mode).
 
@@ -200,6 +205,55 @@ def scan_vjp(k_star, dict_idx, D, Bu, C, h0, g_y, g_hL=None):
     g_h0 = lam
     g_C = np.einsum("bhl,bhln->hn", g_y, states)
     return g_Bu, g_D, g_h0, g_C
+
+
+def dict_hardmax(M):
+    """Column hardmax of every dense dictionary matrix: out[h,k,j] = the
+    lowest row i with M[h,k,i,j] maximal (numpy's argmax returns the first
+    maximum).  M [H,K,N,N] (row i, column j) -> int [H,K,N]."""
+    return np.argmax(np.asarray(M, dtype=F64), axis=-2)
+
+
+def soft_select(u, W_sel, M, W_d, b_d, u_shared=False):
+    """Selection of the original soft-selection PD-SSM ("Flash PD-SSM"
+    summary, background): alpha_t = softmax(W_sel u_t) over the K dense
+    dictionary matrices, the convex combination M_t = sum_k alpha_t[k] M[h,k],
+    its column hardmax P_idx_t[j] = lowest row i with M_t[i, j] maximal, and
+    D_t = sigmoid(W_d u_t + b_d).  fp64.
+
+    Returns dict(alpha [B,H,L,K], M_t [B,H,L,N,N], P_idx [B,H,L,N],
+    gap [B,H,L,N] (top minus runner-up of every column), D [B,H,L,N])."""
+    s = scores(u, W_sel, u_shared)
+    s = s - s.max(axis=-1, keepdims=True)
+    e = np.exp(s)
+    alpha = e / e.sum(axis=-1, keepdims=True)
+    Mt = np.einsum("bhlk,hkij->bhlij", alpha, np.asarray(M, dtype=F64))
+    P_idx = np.argmax(Mt, axis=-2)
+    srt = np.sort(Mt, axis=-2)
+    gap = srt[..., -1, :] - srt[..., -2, :] if Mt.shape[-2] > 1 else np.full(P_idx.shape, np.inf)
+    D = sigmoid(scores(u, W_d, u_shared) + np.asarray(b_d, dtype=F64)[None, :, None, :])
+    return {"alpha": alpha, "M_t": Mt, "P_idx": P_idx, "gap": gap, "D": D}
+
+
+def scan_pidx(P_idx, D, Bu, C, h0=None):
+    """The sequential recurrence on per-step column maps: A_t[P_idx_t[j], j] =
+    D_t[j], dense, fp64.  P_idx [B,H,L,N].  Returns (y [B,H,L], h_L [B,H,N])."""
+    P_idx = np.asarray(P_idx)
+    D = np.asarray(D, dtype=F64)
+    Bu = np.asarray(Bu, dtype=F64)
+    C = np.asarray(C, dtype=F64)
+    B, H, L, N = P_idx.shape
+    x = np.zeros((B, H, N), dtype=F64) if h0 is None else np.array(h0, dtype=F64)
+    y = np.zeros((B, H, L), dtype=F64)
+    bi = np.arange(B)[:, None, None]
+    hi = np.arange(H)[None, :, None]
+    cols = np.arange(N)[None, None, :]
+    for t in range(L):
+        A = np.zeros((B, H, N, N), dtype=F64)
+        A[bi, hi, P_idx[:, :, t], cols] = D[:, :, t]
+        x = np.matmul(A, x[..., None])[..., 0] + Bu[:, :, t]
+        y[:, :, t] = (C[None] * x).sum(-1)
+    return y, x
 
 
 def impulse_sensitivity(k_star, dict_idx, D, W_d, W_b, C, h0=None):
