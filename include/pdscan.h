@@ -190,6 +190,38 @@ int pdssm_impulse_sens(const pdssm_dims* dims, int32_t chunk, const int32_t* k_s
                        const float* C, const float* h0, float* dY, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* The scan of pdssm_scan_fwd on per-step column maps instead of a
+ * dictionary and selections: P_idx [B,H,L,N] (in) holds, for every step, the
+ * row of column j's one (as pdssm_soft_select or pdssm_select's P_idx write
+ * it; values in [0, N)).  dims->K is ignored.  Workspace as
+ * pdssm_scan_workspace_bytes.  The on-chip table holds one map per step of a
+ * chunk (chunk * (N + 1) * 8 bytes), so chunks longer than about 256 steps
+ * return PDSSM_EUNSUPPORTED for N = 16. */
+int pdssm_scan_fwd_pidx(const pdssm_dims* dims, int32_t chunk, const int32_t* P_idx, const float* D,
+                        const float* Bu, const float* C, const float* h0, float* y, float* h_L,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Selection of the original (soft-selection) PD-SSM, kept as a comparison
+ * path ("Flash PD-SSM" summary, background: the original model mixes dense
+ * dictionary matrices and sparsifies the mixture column by column, at
+ * O(L N^2) memory).  Per step t of sequence (b, h):
+ *   alpha_t = softmax(W_sel u_t), M_t = sum_k alpha_t[k] M[h,k]  (written to M_t),
+ *   P_idx_t[j] = lowest row i with M_t[i, j] maximal (column hardmax),
+ *   D_t = sigmoid(W_d u_t + b_d).
+ *   u, W_sel, W_d, b_d as in pdssm_select (fp32 or bf16); M [H,K,N,N] fp32,
+ *   M[h,k,i,j] = row i, column j.  Outputs: M_t [B,H,L,N,N], P_idx [B,H,L,N],
+ *   D [B,H,L,N] (all required).  fp32 arithmetic.
+ * Shapes: N <= 16, K <= 16, d_in <= 128; else PDSSM_EUNSUPPORTED. */
+int pdssm_soft_select(const pdssm_dims* dims, const void* u, const void* W_sel, const float* M,
+                      const void* W_d, const float* b_d, float* M_t, int32_t* P_idx, float* D,
+                      void* stream);
+
+/* The sparse dictionary of the hard-selection path from dense parameters:
+ * dict_idx[h,k,j] = lowest row i with M[h,k,i,j] maximal (column hardmax of
+ * every dictionary matrix; "Flash PD-SSM" summary, methodology item 1).
+ *   M [H,K,N,N] fp32 (in); dict_idx [H,K,N] int32 (out). */
+int pdssm_dict_hardmax(int32_t H, int32_t K, int32_t N, const float* M, int32_t* dict_idx, void* stream);
+
 /* Static text for a status code. */
 const char* pdssm_status_str(int status);
 

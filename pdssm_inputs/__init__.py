@@ -11,7 +11,8 @@ parameters, and both are described where they happen:
 * the driving term ``Bu = W_b u``, which the forward pass receives as an input.
 
 ``upstream_grads`` draws the loss gradients (dLoss/dy, dLoss/dh_L) that the
-gradient pass through the scan takes as inputs.
+gradient pass through the scan takes as inputs; ``dense_dictionary`` draws
+the dense dictionary matrices of the soft-selection comparison path.
 
 Workloads follow the pages' experiment descriptions only loosely (they print no
 inputs); the recipes are synthetic stand-ins, see ``configs.py``.
@@ -23,6 +24,7 @@ from .gen import (  # noqa: F401
     Inputs,
     bf16_bits,
     bf16_round,
+    dense_dictionary,
     generate,
     top2_margin,
     upstream_grads,

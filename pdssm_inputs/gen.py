@@ -245,3 +245,10 @@ def upstream_grads(B, H, L, N, seed):
     g_y = rng.standard_normal((B, H, L)).astype(np.float32)
     g_hL = rng.standard_normal((B, H, N)).astype(np.float32)
     return g_y, g_hL
+
+
+def dense_dictionary(H, K, N, seed):
+    """Seeded dense dictionary matrices M [H,K,N,N] (standard normal, fp32;
+    M[h,k,i,j] is row i, column j) for the soft-selection comparison path."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x736F6674]))
+    return rng.standard_normal((H, K, N, N)).astype(np.float32)

@@ -39,6 +39,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "pdssm_select", "pdssm_scan_fwd", "pdssm_fwd", "pdssm_fwd_wb", "pdssm_impulse_sens",
+    "pdssm_soft_select", "pdssm_scan_fwd_pidx", "pdssm_dict_hardmax",
     "scan_workspace_bytes",
     "fwd_workspace_bytes", "make_dims", "PdssmError", "lib", "LIB_PATH",
 ]
@@ -273,6 +274,63 @@ def pdssm_impulse_sens(k_star, dict_idx, D, W_d, W_b, C, h0=None, chunk=128, wor
                                   _ptr(W_d), _ptr(W_b), _ptr(C), _ptr(h0), _ptr(dY), _ptr(ws),
                                   ctypes.c_size_t(ws.numel()), _stream(dev)))
     return dY
+
+
+def pdssm_soft_select(u, W_sel, M, W_d, b_d, out=None):
+    """Soft-selection comparison path: returns dict(M_t, P_idx, D).  M is
+    [H,K,N,N] fp32 (row i, column j)."""
+    torch = _torch()
+    for t, n in ((u, "u"), (W_sel, "W_sel"), (W_d, "W_d")):
+        _need(t, n)
+    for t, n in ((M, "M"), (b_d, "b_d")):
+        _need(t, n, torch.float32)
+    dims = _dims_from(u, W_sel, W_d)
+    dev = u.device
+    B, H, L, N = dims.B, dims.H, dims.L, dims.N
+    o = out or {}
+    res = {}
+    for name, shape, dt in (("M_t", (B, H, L, N, N), torch.float32), ("P_idx", (B, H, L, N), torch.int32),
+                            ("D", (B, H, L, N), torch.float32)):
+        t = o.get(name)
+        res[name] = torch.empty(shape, dtype=dt, device=dev) if t is None else _need(t, name)
+    _check(lib.pdssm_soft_select(ctypes.byref(dims), _ptr(u), _ptr(W_sel), _ptr(M), _ptr(W_d), _ptr(b_d),
+                                 _ptr(res["M_t"]), _ptr(res["P_idx"]), _ptr(res["D"]), _stream(dev)))
+    return res
+
+
+def pdssm_scan_fwd_pidx(P_idx, D, Bu, C, h0=None, chunk=128, workspace=None, out=None):
+    """The scan on per-step column maps P_idx [B,H,L,N].  Returns (y, h_L)."""
+    torch = _torch()
+    _need(P_idx, "P_idx", torch.int32)
+    for t, n in ((D, "D"), (Bu, "Bu"), (C, "C")):
+        _need(t, n, torch.float32)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    B, H, L, N = P_idx.shape
+    dims = make_dims(B, H, L, N, 1, 8, 0, False)
+    dev = P_idx.device
+    ws = _workspace(scan_workspace_bytes(dims, chunk), dev, workspace)
+    o = out or {}
+    y = o.get("y")
+    y = torch.empty((B, H, L), dtype=torch.float32, device=dev) if y is None else _need(y, "y")
+    hL = o.get("h_L")
+    hL = torch.empty((B, H, N), dtype=torch.float32, device=dev) if hL is None else _need(hL, "h_L")
+    _check(lib.pdssm_scan_fwd_pidx(ctypes.byref(dims), int(chunk), _ptr(P_idx), _ptr(D), _ptr(Bu), _ptr(C),
+                                   _ptr(h0), _ptr(y), _ptr(hL), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                   _stream(dev)))
+    return y, hL
+
+
+def pdssm_dict_hardmax(M):
+    """dict_idx[h,k,j] = lowest row i with M[h,k,i,j] maximal; M [H,K,N,N] fp32."""
+    torch = _torch()
+    _need(M, "M", torch.float32)
+    H, K, N, N2 = M.shape
+    if N != N2:
+        raise ValueError("M must be [H,K,N,N]")
+    out = torch.empty((H, K, N), dtype=torch.int32, device=M.device)
+    _check(lib.pdssm_dict_hardmax(int(H), int(K), int(N), _ptr(M), _ptr(out), _stream(M.device)))
+    return out
 
 
 def scan_bwd_workspace_bytes(dims, chunk):

@@ -47,6 +47,9 @@ def _load():
         "pdssm_fwd_wb": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "pdssm_impulse_sens_workspace_bytes": [dp, i32, ctypes.POINTER(sz)],
         "pdssm_impulse_sens": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "pdssm_scan_fwd_pidx": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "pdssm_soft_select": [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "pdssm_dict_hardmax": [i32, i32, i32, vp, vp, vp],
         "pdssm_scan_states": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "pdssm_scan_bwd_workspace_bytes": [dp, i32, ctypes.POINTER(sz)],
         "pdssm_scan_bwd": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],

@@ -16,9 +16,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpdscan.so")
 
 SOURCES = ["pdscan_api.cpp", "pdscan_launch_select.hip", "pdscan_launch_scan.hip",
-           "pdscan_launch_fused.hip", "pdscan_launch_bwd.hip", "pdscan_launch_sens.hip"]
+           "pdscan_launch_fused.hip", "pdscan_launch_bwd.hip", "pdscan_launch_sens.hip", "pdscan_launch_soft.hip"]
 HEADERS = ["pdscan_plan.h", "pdscan_device.h", "pdscan_bwd_plan.h", "pdscan_bwd.h",
-           "pdscan_sens_plan.h", "pdscan_sens.h"]
+           "pdscan_sens_plan.h", "pdscan_sens.h", "pdscan_soft_plan.h", "pdscan_soft.h"]
 
 COMPILE_FLAGS = [
     "-O3", "-std=c++17", "-fPIC",

@@ -13,6 +13,7 @@
 #include "pdscan_bwd_plan.h"
 #include "pdscan_plan.h"
 #include "pdscan_sens_plan.h"
+#include "pdscan_soft_plan.h"
 
 namespace pdscan {
 // One launcher per mode, each in its own translation unit.  They enqueue on
@@ -22,6 +23,8 @@ hipError_t launch_scan(const Args& a, hipStream_t st);
 hipError_t launch_fused(const Args& a, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, float* g_C, hipStream_t st);
 hipError_t launch_sens(const SensArgs& a, hipStream_t st);
+hipError_t launch_soft(const SoftArgs& a, hipStream_t st);
+hipError_t launch_dict_hardmax(const float* M, int32_t* dict, int HK, int N, hipStream_t st);
 }
 
 using pdscan::Plan;
@@ -312,6 +315,37 @@ int pdssm_fwd_wb(const pdssm_dims* dims, int32_t chunk, const void* u, const voi
   return dispatch(pdscan::kModeFused, a, stream);
 }
 
+int pdssm_scan_fwd_pidx(const pdssm_dims* dims, int32_t chunk, const int32_t* P_idx, const float* D,
+                        const float* Bu, const float* C, const float* h0, float* y, float* h_L,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dims) return fail(PDSSM_EINVAL, "dims is NULL");
+  pdssm_dims dd = *dims;
+  dd.K = 1;                                        // no dictionary: one map per step
+  int rc = check_dims(&dd, chunk);
+  if (rc) return rc;
+  Plan p;
+  const int T = chunk < dd.L ? chunk : dd.L;
+  dd.K = T;                                        // the step maps of a chunk are its table
+  if (!pdscan::make_plan(p, pdscan::kModeScan, dd.B, dd.H, dd.L, dd.N, T, dd.d_in, dd.u_shared,
+                         dd.in_dtype == PDSSM_BF16, chunk))
+    return fail(PDSSM_EUNSUPPORTED, "chunk=%d with N=%d needs %d bytes of on-chip memory with per-step "
+                "maps (limit %d); use a shorter chunk", chunk, dd.N, p.lds_bytes, pdscan::kMaxLds);
+  if (workspace_bytes < p.ws_bytes)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"P_idx", P_idx, z.D}, {"D", D, z.D}, {"Bu", Bu, z.Bu}, {"C", C, z.C},
+                      {"h0", h0, z.h0}};
+  const Range out[] = {{"y", y, z.y}, {"h_L", h_L, z.hL}, {"workspace", workspace, p.ws_bytes}};
+  static const char* const req[] = {"P_idx", "D", "Bu", "C", "y", "h_L", "workspace", nullptr};
+  if ((rc = check_ptrs(in, 5, out, 3, req))) return rc;
+  pdscan::Args a = {};
+  a.p = p;
+  a.P_in = P_idx; a.D_in = D; a.Bu = Bu; a.C = C; a.h0 = h0;
+  a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
+  return dispatch(pdscan::kModeScan, a, stream);
+}
+
 int pdssm_scan_states(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
                       const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
                       const float* h0, float* y, float* h_L, float* H_all, void* workspace,
@@ -422,6 +456,48 @@ int pdssm_impulse_sens(const pdssm_dims* dims, int32_t chunk, const int32_t* k_s
   a.k_star = k_star; a.dict = dict_idx; a.D = D; a.W_d = W_d; a.W_b = W_b; a.C = C; a.h0 = h0;
   a.dY = dY; a.ws = (unsigned char*)workspace;
   const hipError_t e = pdscan::launch_sens(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return PDSSM_OK;
+}
+
+int pdssm_soft_select(const pdssm_dims* dims, const void* u, const void* W_sel, const float* M,
+                      const void* W_d, const float* b_d, float* M_t, int32_t* P_idx, float* D,
+                      void* stream) {
+  int rc = check_dims(dims, -1);
+  if (rc) return rc;
+  pdscan::SoftPlan q;
+  if (!pdscan::make_soft_plan(q, dims->B, dims->H, dims->L, dims->N, dims->K, dims->d_in, dims->u_shared,
+                              dims->in_dtype == PDSSM_BF16))
+    return fail(PDSSM_EUNSUPPORTED, "soft selection: N=%d K=%d d_in=%d (at most %d, %d, %d)", dims->N, dims->K,
+                dims->d_in, pdscan::kSoftMaxN, pdscan::kSoftMaxK, pdscan::kSoftMaxD);
+  const Sizes z = sizes(dims);
+  const size_t mz = (size_t)dims->H * dims->K * dims->N * dims->N * 4;
+  const size_t mtz = (size_t)dims->B * dims->H * dims->L * dims->N * dims->N * 4;
+  const Range in[] = {{"u", u, z.u}, {"W_sel", W_sel, z.Wsel}, {"M", M, mz}, {"W_d", W_d, z.Wd},
+                      {"b_d", b_d, z.bd}};
+  const Range out[] = {{"M_t", M_t, mtz}, {"P_idx", P_idx, z.D}, {"D", D, z.D}};
+  static const char* const req[] = {"u", "W_sel", "M", "W_d", "b_d", "M_t", "P_idx", "D", nullptr};
+  if ((rc = check_ptrs(in, 5, out, 3, req))) return rc;
+  pdscan::SoftArgs a = {};
+  a.q = q;
+  a.u = u; a.W_sel = W_sel; a.M = M; a.W_d = W_d; a.b_d = b_d; a.M_t = M_t; a.P_idx = P_idx; a.D = D;
+  const hipError_t e = pdscan::launch_soft(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return PDSSM_OK;
+}
+
+int pdssm_dict_hardmax(int32_t H, int32_t K, int32_t N, const float* M, int32_t* dict_idx, void* stream) {
+  if (H < 1 || K < 1 || N < 1) return fail(PDSSM_EINVAL, "H, K, N must be >= 1 (got %d %d %d)", H, K, N);
+  if (N > 64) return fail(PDSSM_EUNSUPPORTED, "N=%d > 64", N);
+  const size_t mz = (size_t)H * K * N * N * 4, dz = (size_t)H * K * N * 4;
+  const Range in[] = {{"M", M, mz}};
+  const Range out[] = {{"dict_idx", dict_idx, dz}};
+  static const char* const req[] = {"M", "dict_idx", nullptr};
+  int rc = check_ptrs(in, 1, out, 1, req);
+  if (rc) return rc;
+  const hipError_t e = pdscan::launch_dict_hardmax(M, dict_idx, H * K, N, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_err[0] = 0;
   return PDSSM_OK;

@@ -946,14 +946,22 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   } else {
     for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
     __syncthreads();
-    // DC[k][m] = (dict[k][m], C[dict[k][m]]): target row and its output weight
-    for (int q = tid; q < K * N; q += kThreads) {
-      const int r = a.dict[(size_t)h * K * N + q];
-      DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
+    // DC[k][m] = (dict[k][m], C[dict[k][m]]): target row and its output weight;
+    // with per-step maps, entry t is step t's map and k*_t = t
+    if (MODE == kModeScan && a.P_in) {
+      for (int q = tid; q < Tc * N; q += kThreads) {
+        const int r = a.P_in[gbase * N + q];
+        DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
+      }
+    } else {
+      for (int q = tid; q < K * N; q += kThreads) {
+        const int r = a.dict[(size_t)h * K * N + q];
+        DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
+      }
     }
   }
   if constexpr (MODE == kModeScan) {
-    for (int q = tid; q < Tc; q += kThreads) kbuf[q] = a.k_in[gbase + q];
+    for (int q = tid; q < Tc; q += kThreads) kbuf[q] = a.P_in ? q : a.k_in[gbase + q];
     for (int q = tid; q < Tc * N; q += kThreads) {
       const int t = q / N, n = q - t * N;
       Dbuf[n * TS + t] = a.D_in[gbase * N + q];

@@ -141,6 +141,8 @@ struct Args {
   const float* C;
   const float* h0;
   const int32_t* k_in;   // scan mode
+  const int32_t* P_in;   // scan mode, per-step column maps [B,H,L,N] instead of k_in and dict
+                         // (the plan's K is then the chunk length: one table entry per step)
   const float* D_in;     // scan mode
   int32_t* k_out;        // optional
   float* D_out;          // optional
