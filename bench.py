@@ -10,7 +10,9 @@ fp64 CPU oracle timed beside it.
 the same workload instead, with its own roofline and oracle baseline;
 ``--pass fold`` times pdssm_fwd_wb (the drive term formed from u and W_b in
 the same pass, so Bu is never read); ``--pass sens`` times the impulse
-sensitivity dy_t/du_0 (pdssm_impulse_sens).
+sensitivity dy_t/du_0 (pdssm_impulse_sens); ``--pass soft`` times the
+soft-selection comparison path (pdssm_soft_select + pdssm_scan_fwd_pidx) with
+the hard-selection forward pass beside it.
 ``timing`` in the JSON line gives the median, p10 and p90 of the per-call
 event durations with warm caches ("hot") and with a 1 GiB fill before each
 call ("cold").
@@ -47,10 +49,13 @@ SOURCES = {
             "pdscan_launch_bwd.hip"),
 }
 SOURCES["fold"] = SOURCES["fwd"]
+SOURCES["soft"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_soft_plan.h", "pdscan_soft.h",
+                   "pdscan_launch_soft.hip", "pdscan_launch_scan.hip")
 SOURCES["sens"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_sens_plan.h", "pdscan_sens.h",
                    "pdscan_launch_sens.hip")
 # stem of the committed counter summary of each pass
-TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd", "fold": "pdssm_fold", "sens": "pdssm_sens"}
+TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd", "fold": "pdssm_fold", "sens": "pdssm_sens",
+                "soft": "pdssm_soft"}
 COLD_FILL_BYTES = 1 << 30       # written before each cold-cache rep (beyond L2 and MALL)
 
 
@@ -167,6 +172,8 @@ def _is_kernel(name, which):
         return "pdssm_bwd_kernel" in name
     if which == "sens":
         return "pdssm_sens_kernel" in name
+    if which == "soft":
+        return "pdssm_soft_kernel" in name
     return "pdssm_" in name and "clear" not in name and "bwd" not in name and "fill" not in name.lower()
 
 
@@ -401,6 +408,111 @@ def bench_sens(args, torch, np, P):
     print(json.dumps(rec), flush=True)
 
 
+def algorithmic_soft(cfg):
+    """Minimum traffic of the soft-selection pipeline as the original model
+    runs it: u read, every dense mixture M_t written (the O(L N^2)
+    materialisation), the per-step maps and diagonals written and read back
+    by the scan together with Bu, y written, plus parameters."""
+    B, H, L, N, K, d = cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, cfg.d
+    es = 2 if cfg.dtype == "bf16" else 4
+    steps = B * H * L
+    u = B * (1 if cfg.u_shared else H) * L * d * es
+    per_step = 4 * N * N + 2 * (4 * N + 4 * N) + 4 * N + 4
+    params = H * K * d * es + H * N * d * es + H * N * 4 + H * K * N * N * 4 + H * N * 4 + 2 * B * H * N * 4
+    return u + steps * per_step + params
+
+
+def bench_soft(args, torch, np, P):
+    """Time the soft-selection comparison path (pdssm_soft_select, then
+    pdssm_scan_fwd_pidx) and, in the same run, the hard-selection forward pass
+    on the same inputs, for the ratio of the two."""
+    from pdssm_inputs import dense_dictionary, generate, get_config
+    cfg = get_config(args.workload)
+    chunk = args.chunk or 128                      # the per-step table holds one map per step
+    t0 = time.time()
+    inp = generate(cfg)
+    print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    bf = cfg.dtype == "bf16"
+    pdt = torch.bfloat16 if bf else torch.float32
+
+    def dev(x, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+
+    u, W_sel, W_d = dev(inp.u, pdt), dev(inp.W_sel, pdt), dev(inp.W_d, pdt)
+    b_d, dic, Bu, C, h0 = dev(inp.b_d), dev(inp.dict_idx), dev(inp.Bu), dev(inp.C), dev(inp.h0)
+    Mh = dense_dictionary(cfg.H, cfg.K, cfg.N, cfg.seed)
+    M = dev(Mh)
+    B, H, L, N = cfg.B, cfg.H, cfg.L, cfg.N
+    sel = {"M_t": torch.empty((B, H, L, N, N), device="cuda"),
+           "P_idx": torch.empty((B, H, L, N), dtype=torch.int32, device="cuda"),
+           "D": torch.empty((B, H, L, N), device="cuda")}
+    dims = P.make_dims(B, H, L, N, 1, 8, 0, False)
+    ws = torch.zeros(P.scan_workspace_bytes(dims, chunk), dtype=torch.uint8, device="cuda")
+    so = {"y": torch.empty((B, H, L), device="cuda"), "h_L": torch.empty((B, H, N), device="cuda")}
+
+    def step():
+        P.pdssm_soft_select(u, W_sel, M, W_d, b_d, out=sel)
+        P.pdssm_scan_fwd_pidx(sel["P_idx"], sel["D"], Bu, C, h0, chunk=chunk, workspace=ws, out=so)
+
+    dimsf = P.make_dims(B, H, L, N, cfg.K, cfg.d, cfg.u_shared, bf)
+    wsf = torch.empty(P.fwd_workspace_bytes(dimsf, cfg.chunk), dtype=torch.uint8, device="cuda")
+    fo = {"y": torch.empty((B, H, L), device="cuda"), "h_L": torch.empty((B, H, N), device="cuda")}
+
+    def hard():
+        P.pdssm_fwd(u, W_sel, dic, W_d, b_d, Bu, C, h0, chunk=cfg.chunk, workspace=wsf, out=fo)
+
+    for _ in range(args.warmup):
+        step()
+        hard()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    wall, hot, timing = time_calls(torch, np, step, args.steps, stream)
+    if P.workspace_error_flag(ws):
+        raise RuntimeError("look-back wait gave up during timing")
+    _, hot_h, _ = time_calls(torch, np, hard, args.steps, stream)
+    launch_s = float(np.mean(hot)) / 1e6
+    ms_step = wall * 1e3 / args.steps
+    alg = algorithmic_soft(cfg)
+    achieved = alg / launch_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_from_profile(cfg.name, "soft"),
+            "algorithmic_bytes": alg, "launch_us": round(launch_s * 1e6, 2)}
+    hard_us = float(np.mean(hot_h))
+    rec = {
+        "metric": "state-updates/sec (B·H·L·N) original soft-selection PD-SSM forward (dense mixture "
+                  "materialised, column hardmax, scan)",
+        "value": cfg.state_updates / (ms_step / 1e3),
+        "unit": "state-updates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} soft selection: B={B} H={H} L={L} N={N} K={cfg.K} d={cfg.d} "
+                               f"scan chunk={chunk}",
+                   "B": B, "H": H, "L": L, "N": N, "K": cfg.K, "d_in": cfg.d, "chunk": chunk},
+        "roofline": roof,
+        "timing": timing,
+        "hard_selection_us": round(hard_us, 2),
+        "soft_over_hard_time": round(launch_s * 1e6 / hard_us, 3),
+        "kernel_hash": kernel_hash("soft"),
+    }
+    if args.copy_probe:
+        copy_probe(torch)
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        Hs, Ls = min(H, 2), min(L, 16384)
+        t0 = time.perf_counter()
+        r = oracle.soft_select(inp.u[:, :Hs, :Ls], inp.W_sel[:Hs], Mh[:Hs], inp.W_d[:Hs], inp.b_d[:Hs])
+        oracle.scan_pidx(r["P_idx"], r["D"], inp.Bu[:, :Hs, :Ls], inp.C[:Hs], inp.h0[:, :Hs])
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": B * Hs * Ls * N / dt, "unit": "state-updates/s", "cores": cores,
+                               "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": f"first {Ls} steps of {Hs} heads of {cfg.name} "
+                                         "(soft selection plus the dense sequential scan)"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,10 +521,10 @@ def main():
     ap.add_argument("--workload", default="impulse")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fold", "sens"), default="fwd",
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fold", "sens", "soft"), default="fwd",
                     help="forward pass (default), the gradient pass through the scan, the "
                          "forward pass with the drive Bu = W_b u folded into the selection GEMM, "
-                         "or the impulse sensitivity dy_t/du_0")
+                         "the impulse sensitivity dy_t/du_0, or the soft-selection comparison path")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain copy kernel of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -438,6 +550,8 @@ def main():
         return bench_bwd(args, torch, np, P)
     if args.which == "sens":
         return bench_sens(args, torch, np, P)
+    if args.which == "soft":
+        return bench_soft(args, torch, np, P)
     cfg = get_config(args.workload)
     chunk = args.chunk or cfg.chunk
     t0 = time.time()

@@ -211,7 +211,7 @@ int pdssm_scan_fwd_pidx(const pdssm_dims* dims, int32_t chunk, const int32_t* P_
  *   u, W_sel, W_d, b_d as in pdssm_select (fp32 or bf16); M [H,K,N,N] fp32,
  *   M[h,k,i,j] = row i, column j.  Outputs: M_t [B,H,L,N,N], P_idx [B,H,L,N],
  *   D [B,H,L,N] (all required).  fp32 arithmetic.
- * Shapes: N <= 16, K <= 16, d_in <= 128; else PDSSM_EUNSUPPORTED. */
+ * Shapes: N <= 16, K <= 16, d_in in {16, 32, 64, 128}; else PDSSM_EUNSUPPORTED. */
 int pdssm_soft_select(const pdssm_dims* dims, const void* u, const void* W_sel, const float* M,
                       const void* W_d, const float* b_d, float* M_t, int32_t* P_idx, float* D,
                       void* stream);

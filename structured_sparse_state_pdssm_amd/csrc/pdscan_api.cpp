@@ -469,8 +469,8 @@ int pdssm_soft_select(const pdssm_dims* dims, const void* u, const void* W_sel, 
   pdscan::SoftPlan q;
   if (!pdscan::make_soft_plan(q, dims->B, dims->H, dims->L, dims->N, dims->K, dims->d_in, dims->u_shared,
                               dims->in_dtype == PDSSM_BF16))
-    return fail(PDSSM_EUNSUPPORTED, "soft selection: N=%d K=%d d_in=%d (at most %d, %d, %d)", dims->N, dims->K,
-                dims->d_in, pdscan::kSoftMaxN, pdscan::kSoftMaxK, pdscan::kSoftMaxD);
+    return fail(PDSSM_EUNSUPPORTED, "soft selection: N=%d K=%d d_in=%d (N, K at most %d, %d; d_in one of "
+                "16, 32, 64, 128)", dims->N, dims->K, dims->d_in, pdscan::kSoftMaxN, pdscan::kSoftMaxK);
   const Sizes z = sizes(dims);
   const size_t mz = (size_t)dims->H * dims->K * dims->N * dims->N * 4;
   const size_t mtz = (size_t)dims->B * dims->H * dims->L * dims->N * dims->N * 4;

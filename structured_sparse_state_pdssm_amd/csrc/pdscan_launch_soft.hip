@@ -4,7 +4,15 @@
 namespace pdscan {
 
 hipError_t launch_soft(const SoftArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(pdssm_soft_kernel, dim3((unsigned)a.q.tasks), dim3(kThreads), (unsigned)a.q.bytes, st, a);
+  const dim3 grid((unsigned)a.q.tasks), block(kThreads);
+  const unsigned lds = (unsigned)a.q.bytes;
+  switch (a.q.d) {
+    case 16: hipLaunchKernelGGL(pdssm_soft_kernel<4>, grid, block, lds, st, a); break;
+    case 32: hipLaunchKernelGGL(pdssm_soft_kernel<8>, grid, block, lds, st, a); break;
+    case 64: hipLaunchKernelGGL(pdssm_soft_kernel<16>, grid, block, lds, st, a); break;
+    case 128: hipLaunchKernelGGL(pdssm_soft_kernel<32>, grid, block, lds, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -15,28 +15,6 @@
 
 namespace pdscan {
 
-// Stage n values (fp32, or bf16 widened) into LDS: each lane issues a batch
-// of buffer loads before storing (base uniform in the workgroup).
-__device__ __forceinline__ void soft_stage(float* dst, const void* src, size_t base, int n, int bf16) {
-  const int es = bf16 ? 2 : 4;
-  const rsrc_t r = make_rsrc((const unsigned char*)src + base * es, (uint32_t)(n * es));
-  for (int e0 = 0; e0 < n; e0 += kThreads * 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * kThreads + (int)threadIdx.x;
-      const uint32_t off = e < n ? (uint32_t)(e * es) : kNoLoad;
-      v[u] = bf16 ? __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16)
-                  : buf_f32(r, off);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * kThreads + (int)threadIdx.x;
-      if (e < n) dst[e] = v[u];
-    }
-  }
-}
-
 // Column hardmax of every dense dictionary matrix: dict[h,k,j] = the lowest
 // row i with M[h,k,i,j] maximal (the sparse dictionary of the hard-selection
 // path built from dense parameters; same summary, methodology item 1).
@@ -55,88 +33,176 @@ __global__ void pdssm_dict_hardmax_kernel(const float* M, int32_t* dict, int HK,
   dict[e] = best;
 }
 
-// One workgroup: kSoftSteps consecutive steps of one sequence, 16 at a time;
-// lane group r (16 lanes) owns step t0 + r, lane j of it owns column j.
+// Four consecutive channels of row `row` of a [rows x d] operand (fp32 or
+// bf16 widened), as one 16-byte or 8-byte buffer load; `off` is the element
+// offset of the first, kNoLoad for zeros.
+__device__ __forceinline__ f4v soft_load4(rsrc_t r, uint32_t off, int bf16) {
+  if (bf16) {
+    const u2v w = __builtin_bit_cast(
+        u2v, __builtin_amdgcn_raw_buffer_load_b64(r, off == kNoLoad ? kNoLoad : off * 2, 0, 0));
+    return f4v{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xFFFF0000u)};
+  }
+  return __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(r, off == kNoLoad ? kNoLoad : off * 4, 0, 0));
+}
+
+// One workgroup: kSoftSteps consecutive steps of one sequence; each wave takes
+// 16 of them at a time, all in registers.  Every contraction runs on the fp32
+// matrix cores (v_mfma_f32_16x16x4_f32, fp32 products and accumulation) with
+// the weights as the row operand and the 16 steps as the columns, so lane
+// (g, c) of the 64 ends with rows 4g..4g+3 of step c:
+//   scores:          [K rows x d] x [d x 16 steps]  (row x holds matrix
+//                    (x / 4) + 4 (x % 4), so register r of lane group g is
+//                    matrix g + 4 r: the mixture's contraction slot),
+//   pre-activations: [N rows x d] x [d x 16 steps],
+//   mixture, per row i of M_t:  [N columns j x K] x [K x 16 steps],
+// the softmax is a 4-register, 4-lane-group reduction, the column hardmax is a
+// running maximum over i in each lane, and a lane writes four consecutive
+// columns j of a step with one 16-byte store.  The contraction over channels
+// takes slot (g, kb) as channel 16 (kb / 4) + 4 g + kb % 4 on both operands,
+// so each lane reads four consecutive channels per load.
+template <int NKB>   // NKB = d / 4 channel slots
 __global__ __launch_bounds__(kThreads) void pdssm_soft_kernel(SoftArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
   const SoftPlan& q = a.q;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = q.N, K = q.K, d = q.d, L = q.L;
   const int task = blockIdx.x;
   const int s = task / q.blocks_per_seq;
   const int tblk = (task - s * q.blocks_per_seq) * kSoftSteps;
   const int b = s / q.H, h = s % q.H;
-  float* ul = (float*)(smem + q.off_u);            // [16][d]
-  float* Ml = (float*)(smem + q.off_M);            // [K][N][N]
-  float* Wl = (float*)(smem + q.off_W);            // [K + N][d]
-  float* al = (float*)(smem + q.off_a);            // [16][16]
+  const int c16 = lane & 15, g = lane >> 4;
+  const int bf = q.in_bf16;
+  const int es = bf ? 2 : 4;
+  constexpr int NM = NKB / 4;                      // four-channel loads per operand row
 
-  // ---- the head's parameters, once per workgroup
-  soft_stage(Ml, a.M, (size_t)h * K * N * N, K * N * N, 0);
-  soft_stage(Wl, a.W_sel, (size_t)h * K * d, K * d, q.in_bf16);
-  soft_stage(Wl + K * d, a.W_d, (size_t)h * N * d, N * d, q.in_bf16);
-  const int r = tid >> 4, j = tid & 15;
-  const float bdj = j < N ? a.b_d[(size_t)h * N + j] : 0.f;
+  // ---- row operands, once per workgroup: W_sel rows (permuted as above),
+  // W_d rows, dictionary fragments (matrix g + 4 kb, row i, column c16)
+  f4v wsel[NM], wd[NM];
+  {
+    const int ks = (c16 >> 2) + 4 * (c16 & 3);
+    const rsrc_t sr = make_rsrc((const unsigned char*)a.W_sel + (size_t)h * K * d * es, (uint32_t)(K * d * es));
+    const rsrc_t zr = make_rsrc((const unsigned char*)a.W_d + (size_t)h * N * d * es, (uint32_t)(N * d * es));
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      wsel[m] = soft_load4(sr, ks < K ? (uint32_t)(ks * d + 16 * m + 4 * g) : kNoLoad, bf);
+      wd[m] = soft_load4(zr, c16 < N ? (uint32_t)(c16 * d + 16 * m + 4 * g) : kNoLoad, bf);
+    }
+  }
+  float mb[kSoftMaxN][kSoftMaxK / 4];
+  {
+    const rsrc_t mr = make_rsrc(a.M + (size_t)h * K * N * N, (uint32_t)(K * N * N * 4));
+#pragma unroll
+    for (int i = 0; i < kSoftMaxN; ++i)
+#pragma unroll
+      for (int kb = 0; kb < kSoftMaxK / 4; ++kb) {
+        const int k = g + 4 * kb;
+        mb[i][kb] = buf_f32(mr, (i < N && k < K && c16 < N) ? (uint32_t)(((k * N + i) * N + c16) * 4) : kNoLoad);
+      }
+  }
+  float bd[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) bd[r] = 4 * g + r < N ? a.b_d[(size_t)h * N + 4 * g + r] : 0.f;
 
-  for (int t0 = tblk; t0 < min(tblk + kSoftSteps, L); t0 += kSoftRows) {
-    const int nrow = min(kSoftRows, L - t0);
-    __syncthreads();                               // previous rows done with ul and al
-    const size_t urow = (size_t)(q.u_shared ? b : s) * L + t0;
-    soft_stage(ul, a.u, urow * d, nrow * d, q.in_bf16);
-    __syncthreads();
+  // per-sequence descriptors: steps past L fall outside them (reads give
+  // zeros, writes are dropped)
+  const size_t useq = (size_t)(q.u_shared ? b : s) * L;
+  const rsrc_t ur = make_rsrc((const unsigned char*)a.u + useq * d * es, (uint32_t)(L * d * es));
+  const rsrc_t mtr = make_rsrc(a.M_t + (size_t)s * L * N * N, (uint32_t)(L * N * N * 4));
+  const rsrc_t pr = make_rsrc(a.P_idx + (size_t)s * L * N, (uint32_t)(L * N * 4));
+  const rsrc_t dr = make_rsrc(a.D + (size_t)s * L * N, (uint32_t)(L * N * 4));
+  const bool vec = (N & 3) == 0;                   // whole four-column groups
 
-    const bool row_ok = r < nrow;
-    const float* ur = ul + r * d;
-    // scores (lanes j < K) and pre-activations (lanes j < N), fp32 FMA in
-    // channel order
-    float sc = 0.f, z = 0.f;
-    if (row_ok) {
-      const float* ws = Wl + (j < K ? j : 0) * d;
-      const float* wz = Wl + (K + (j < N ? j : 0)) * d;
-      for (int c = 0; c < d; ++c) {
-        sc = __builtin_fmaf(ws[c], ur[c], sc);
-        z = __builtin_fmaf(wz[c], ur[c], z);
+  const int tend = min(tblk + kSoftSteps, L);
+  int t0 = tblk + 16 * wave;
+  f4v ub[NM];                                      // column operand: step t0 + c16
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+    ub[m] = soft_load4(ur, t0 + c16 < tend ? (uint32_t)((t0 + c16) * d + 16 * m + 4 * g) : kNoLoad, bf);
+
+  for (; t0 < tend; t0 += 16 * kWaves) {
+    f4v sc = {0.f, 0.f, 0.f, 0.f}, zc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc = __builtin_amdgcn_mfma_f32_16x16x4f32(wsel[m][e], ub[m][e], sc, 0, 0, 0);
+        zc = __builtin_amdgcn_mfma_f32_16x16x4f32(wd[m][e], ub[m][e], zc, 0, 0, 0);
+      }
+    // the next 16 steps' inputs, in flight during the rest of this pass
+    const int tn = t0 + 16 * kWaves;
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      ub[m] = soft_load4(ur, tn + c16 < tend ? (uint32_t)((tn + c16) * d + 16 * m + 4 * g) : kNoLoad, bf);
+
+    // softmax over the K matrices of step t0 + c16: register r of lane group
+    // g is matrix g + 4 r
+    float al[4];
+    {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (g + 4 * r < K) mx = fmaxf(mx, sc[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        al[r] = g + 4 * r < K ? expf(sc[r] - mx) : 0.f;
+        sum += al[r];
+      }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) al[r] = al[r] / sum;
+    }
+
+    // mixture, row by row: lane (g, c16) gets M_t[t0 + c16][i][4 g + r]; the
+    // running column maximum (strictly greater: the lowest row on ties)
+    const int t = t0 + c16;
+    const uint32_t rowo = (uint32_t)t * N;         // element offset of step t's first row/entry
+    f4v best = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    int bi[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kSoftMaxN; ++i) {
+      if (i < N) {                                 // a guard, not an exit: every index stays constant
+        f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < kSoftMaxK / 4; ++kb)
+          if (4 * kb < K) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mb[i][kb], al[kb], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (acc[r] > best[r]) {
+            best[r] = acc[r];
+            bi[r] = i;
+          }
+        const uint32_t o = (rowo + i) * N + 4 * g;  // M_t element [t][i][4 g]
+        if (vec) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, acc), mtr,
+                                                 4 * g < N ? o * 4 : kNoLoad, 0, 0);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), mtr,
+                                                  4 * g + r < N ? (o + r) * 4 : kNoLoad, 0, 0);
+        }
       }
     }
-    // softmax over the K scores of the row (16-lane reductions)
-    float m = j < K ? sc : -INFINITY;
+    f4v dv;
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
-    const float ex = j < K ? expf(sc - m) : 0.f;
-    float sum = ex;
+    for (int r = 0; r < 4; ++r) dv[r] = 1.f / (1.f + expf(-(zc[r] + bd[r])));
+    const uint32_t o = rowo + 4 * g;               // P_idx / D element [t][4 g]
+    if (vec) {
+      const uint32_t ob = 4 * g < N ? o * 4 : kNoLoad;
+      __builtin_amdgcn_raw_buffer_store_b128(u4v{(uint32_t)bi[0], (uint32_t)bi[1], (uint32_t)bi[2], (uint32_t)bi[3]},
+                                             pr, ob, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, dv), dr, ob, 0, 0);
+    } else {
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 16);
-    al[r * kSoftMaxK + j] = ex / sum;
-    __syncthreads();
-
-    if (row_ok && j < N) {
-      const size_t row = (size_t)s * L + t0 + r;
-      // column j of M_t (mixture in dictionary order), then its hardmax
-      // (strictly greater: the lowest row on ties)
-      float col[kSoftMaxN];
-#pragma unroll
-      for (int i = 0; i < kSoftMaxN; ++i) col[i] = 0.f;
-      for (int k = 0; k < K; ++k) {
-        const float ak = al[r * kSoftMaxK + k];
-        const float* mk = Ml + k * N * N + j;
-#pragma unroll
-        for (int i = 0; i < kSoftMaxN; ++i)
-          if (i < N) col[i] = __builtin_fmaf(ak, mk[i * N], col[i]);
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t ob = 4 * g + r < N ? (o + r) * 4 : kNoLoad;
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)bi[r], pr, ob, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dv[r]), dr, ob, 0, 0);
       }
-      int best = 0;
-      float bv = col[0];
-#pragma unroll
-      for (int i = 1; i < kSoftMaxN; ++i)
-        if (i < N && col[i] > bv) {
-          bv = col[i];
-          best = i;
-        }
-      float* mt = a.M_t + row * N * N + j;
-#pragma unroll
-      for (int i = 0; i < kSoftMaxN; ++i)
-        if (i < N) mt[i * N] = col[i];
-      a.P_idx[row * N + j] = best;
-      a.D[row * N + j] = 1.f / (1.f + expf(-(z + bdj)));
     }
   }
 }

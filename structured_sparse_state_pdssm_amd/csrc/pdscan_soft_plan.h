@@ -7,8 +7,7 @@
 
 namespace pdscan {
 
-constexpr int kSoftRows = 16;      // steps per pass of a workgroup (one 16-lane group each)
-constexpr int kSoftSteps = 64;     // steps per workgroup
+constexpr int kSoftSteps = 1024;   // steps per workgroup (16 per wave and pass)
 constexpr int kSoftMaxK = 16;      // dictionary matrices
 constexpr int kSoftMaxN = 16;      // state size
 constexpr int kSoftMaxD = 128;     // input channels
@@ -16,7 +15,7 @@ constexpr int kSoftMaxD = 128;     // input channels
 struct SoftPlan {
   int B, H, L, N, K, d, u_shared, in_bf16;
   int blocks_per_seq, tasks;
-  int off_u, off_M, off_W, off_a, bytes;
+  int bytes;
 };
 
 inline bool make_soft_plan(SoftPlan& q, int B, int H, int L, int N, int K, int d, int u_shared,
@@ -24,14 +23,10 @@ inline bool make_soft_plan(SoftPlan& q, int B, int H, int L, int N, int K, int d
   q.B = B; q.H = H; q.L = L; q.N = N; q.K = K; q.d = d; q.u_shared = u_shared; q.in_bf16 = in_bf16;
   q.blocks_per_seq = (L + kSoftSteps - 1) / kSoftSteps;
   q.tasks = q.blocks_per_seq * B * H;
-  int off = 0;
-  auto take = [&](int bytes) { int o = off; off = align_up(off + bytes, 16); return o; };
-  q.off_u = take(kSoftRows * d * 4);               // the block's input rows (fp32)
-  q.off_M = take(K * N * N * 4);                   // the head's dense dictionary matrices
-  q.off_W = take((K + N) * d * 4);                 // W_sel then W_d rows of the head (fp32)
-  q.off_a = take(kSoftRows * kSoftMaxK * 4);       // mixture weights per row
-  q.bytes = off;
-  return N <= kSoftMaxN && K <= kSoftMaxK && d <= kSoftMaxD && q.bytes <= kMaxLds;
+  q.bytes = 0;                                     // registers only, no LDS
+  // per-sequence byte ranges addressed with 32-bit offsets
+  const bool fits = (size_t)L * N * N * 4 < (size_t)0x80000000u && (size_t)L * d * 4 < (size_t)0x80000000u;
+  return N <= kSoftMaxN && K <= kSoftMaxK && (d == 16 || d == 32 || d == 64 || d == 128) && fits;
 }
 
 struct SoftArgs {
