@@ -12,7 +12,9 @@ the same workload instead, with its own roofline and oracle baseline;
 the same pass, so Bu is never read); ``--pass sens`` times the impulse
 sensitivity dy_t/du_0 (pdssm_impulse_sens); ``--pass soft`` times the
 soft-selection comparison path (pdssm_soft_select + pdssm_scan_fwd_pidx) with
-the hard-selection forward pass beside it.
+the hard-selection forward pass beside it; ``--pass scan`` and ``--pass
+select`` time the two stages of the forward pass alone (pdssm_scan_fwd given
+the selections, pdssm_select).
 ``timing`` in the JSON line gives the median, p10 and p90 of the per-call
 event durations with warm caches ("hot") and with a 1 GiB fill before each
 call ("cold").
@@ -53,9 +55,11 @@ SOURCES["soft"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_soft_plan.h", "pd
                    "pdscan_launch_soft.hip", "pdscan_launch_scan.hip")
 SOURCES["sens"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_sens_plan.h", "pdscan_sens.h",
                    "pdscan_launch_sens.hip")
+SOURCES["scan"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_scan.hip")
+SOURCES["select"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_select.hip")
 # stem of the committed counter summary of each pass
 TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd", "fold": "pdssm_fold", "sens": "pdssm_sens",
-                "soft": "pdssm_soft"}
+                "soft": "pdssm_soft", "scan": "pdssm_scan", "select": "pdssm_select"}
 COLD_FILL_BYTES = 1 << 30       # written before each cold-cache rep (beyond L2 and MALL)
 
 
@@ -174,6 +178,10 @@ def _is_kernel(name, which):
         return "pdssm_sens_kernel" in name
     if which == "soft":
         return "pdssm_soft_kernel" in name
+    if which == "scan":
+        return "pdssm_step16_kernel" in name or ("pdssm_kernel<1," in name)
+    if which == "select":
+        return "pdssm_kernel<0," in name or "pdssm_kernel_wide<0," in name
     return "pdssm_" in name and "clear" not in name and "bwd" not in name and "fill" not in name.lower()
 
 
@@ -428,7 +436,7 @@ def bench_soft(args, torch, np, P):
     on the same inputs, for the ratio of the two."""
     from pdssm_inputs import dense_dictionary, generate, get_config
     cfg = get_config(args.workload)
-    chunk = args.chunk or 128                      # the per-step table holds one map per step
+    chunk = args.chunk or cfg.chunk
     t0 = time.time()
     inp = generate(cfg)
     print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -513,6 +521,105 @@ def bench_soft(args, torch, np, P):
     print(json.dumps(rec), flush=True)
 
 
+def bench_part(args, torch, np, P):
+    """Time one stage of the forward pass alone: ``select`` (pdssm_select:
+    scores, argmax, diagonal; k* and D written) or ``scan`` (pdssm_scan_fwd
+    given k* and D, which come from the library's own selection call outside
+    the timed region)."""
+    from pdssm_inputs import generate, get_config
+    cfg = get_config(args.workload)
+    chunk = args.chunk or cfg.chunk
+    t0 = time.time()
+    inp = generate(cfg)
+    print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    bf = cfg.dtype == "bf16"
+    pdt = torch.bfloat16 if bf else torch.float32
+
+    def dev(x, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+
+    B, H, L, N, K, d = cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, cfg.d
+    u, W_sel, W_d = dev(inp.u, pdt), dev(inp.W_sel, pdt), dev(inp.W_d, pdt)
+    b_d, dic, Bu, C, h0 = dev(inp.b_d), dev(inp.dict_idx), dev(inp.Bu), dev(inp.C), dev(inp.h0)
+    so = {"k_star": torch.empty((B, H, L), dtype=torch.int32, device="cuda"),
+          "D": torch.empty((B, H, L, N), device="cuda")}
+    P.pdssm_select(u, W_sel, W_d, b_d, out=so)
+    es = 2 if bf else 4
+    steps = B * H * L
+    if args.which == "select":
+        def step():
+            P.pdssm_select(u, W_sel, W_d, b_d, out=so)
+        alg = (B * (1 if cfg.u_shared else H) * L * d * es + steps * (4 + 4 * N)
+               + H * K * d * es + H * N * d * es + H * N * 4)
+        flops = 2 * (K + N) * d * steps
+        what = "selection alone (scores, argmax, diagonal; k* and D written)"
+    else:
+        dims = P.make_dims(B, H, L, N, K, 8, 0, False)
+        ws = torch.zeros(P.scan_workspace_bytes(dims, chunk), dtype=torch.uint8, device="cuda")
+        oo = {"y": torch.empty((B, H, L), device="cuda"), "h_L": torch.empty((B, H, N), device="cuda")}
+
+        def step():
+            P.pdssm_scan_fwd(so["k_star"], dic, so["D"], Bu, C, h0, chunk=chunk, workspace=ws, out=oo)
+        alg = steps * (4 + 4 * N + 4 * N + 4) + H * K * N * 4 + H * N * 4 + 2 * B * H * N * 4
+        flops = 0
+        what = "scan alone given k* and D (chunked, look-back)"
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    wall, hot, timing = time_calls(torch, np, step, args.steps, stream)
+    if args.which == "scan" and P.workspace_error_flag(ws):
+        raise RuntimeError("look-back wait gave up during timing")
+    launch_s = float(np.mean(hot)) / 1e6
+    ms_step = wall * 1e3 / args.steps
+    t_hbm = alg / (PEAK_HBM_GBPS * 1e9)
+    peak_mma = PEAK_BF16_TFLOPS if (bf and d >= 128) else PEAK_FP32_TFLOPS
+    if flops and flops / (peak_mma * 1e12) > t_hbm:
+        roof = {"bound": "mfma", "achieved": round(flops / launch_s / 1e12, 2), "peak": peak_mma,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(alg / launch_s / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic_from_profile(cfg.name, args.which)
+    roof["algorithmic_bytes"] = alg
+    roof["launch_us"] = round(launch_s * 1e6, 2)
+    rec = {
+        "metric": f"state-updates/sec (B·H·L·N) PD-SSM {what}",
+        "value": cfg.state_updates / (ms_step / 1e3),
+        "unit": "state-updates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} {args.which}: B={B} H={H} L={L} N={N} K={K} d={d} chunk={chunk}",
+                   "B": B, "H": H, "L": L, "N": N, "K": K, "d_in": d, "chunk": chunk},
+        "roofline": roof,
+        "timing": timing,
+        "kernel_hash": kernel_hash(args.which),
+    }
+    if args.copy_probe:
+        copy_probe(torch)
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        Hs = H
+        t0 = time.perf_counter()
+        if args.which == "select":
+            oracle.select(inp.u[:, :Hs] if not cfg.u_shared else inp.u, inp.W_sel[:Hs], inp.W_d[:Hs],
+                          inp.b_d[:Hs], cfg.u_shared)
+        else:
+            k_h = so["k_star"][:, :Hs].cpu().numpy()
+            D_h = so["D"][:, :Hs].cpu().numpy().astype(np.float64)
+            t0 = time.perf_counter()
+            oracle.scan(k_h, inp.dict_idx[:Hs], D_h, inp.Bu[:, :Hs], inp.C[:Hs], inp.h0[:, :Hs])
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": B * Hs * L * N / dt, "unit": "state-updates/s", "cores": cores,
+                               "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": f"whole {cfg.name} workload ({B}x{H}x{L} steps, N={N}), one run"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,10 +628,12 @@ def main():
     ap.add_argument("--workload", default="impulse")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fold", "sens", "soft"), default="fwd",
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fold", "sens", "soft", "scan", "select"),
+                    default="fwd",
                     help="forward pass (default), the gradient pass through the scan, the "
                          "forward pass with the drive Bu = W_b u folded into the selection GEMM, "
-                         "the impulse sensitivity dy_t/du_0, or the soft-selection comparison path")
+                         "the impulse sensitivity dy_t/du_0, the soft-selection comparison path, "
+                         "or one stage of the forward pass alone (scan, select)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain copy kernel of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -552,6 +661,8 @@ def main():
         return bench_sens(args, torch, np, P)
     if args.which == "soft":
         return bench_soft(args, torch, np, P)
+    if args.which in ("scan", "select"):
+        return bench_part(args, torch, np, P)
     cfg = get_config(args.workload)
     chunk = args.chunk or cfg.chunk
     t0 = time.time()

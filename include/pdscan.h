@@ -194,9 +194,10 @@ int pdssm_impulse_sens(const pdssm_dims* dims, int32_t chunk, const int32_t* k_s
  * dictionary and selections: P_idx [B,H,L,N] (in) holds, for every step, the
  * row of column j's one (as pdssm_soft_select or pdssm_select's P_idx write
  * it; values in [0, N)).  dims->K is ignored.  Workspace as
- * pdssm_scan_workspace_bytes.  The on-chip table holds one map per step of a
- * chunk (chunk * (N + 1) * 8 bytes), so chunks longer than about 256 steps
- * return PDSSM_EUNSUPPORTED for N = 16. */
+ * pdssm_scan_workspace_bytes.  With N <= 16 and chunk <= 512 the maps stream
+ * through registers; otherwise an on-chip table holds one map per step of a
+ * chunk (chunk * (N + 1) * 8 bytes), and a chunk whose table does not fit
+ * (N = 16: above 512; N = 20: above 192) returns PDSSM_EUNSUPPORTED. */
 int pdssm_scan_fwd_pidx(const pdssm_dims* dims, int32_t chunk, const int32_t* P_idx, const float* D,
                         const float* Bu, const float* C, const float* h0, float* y, float* h_L,
                         void* workspace, size_t workspace_bytes, void* stream);

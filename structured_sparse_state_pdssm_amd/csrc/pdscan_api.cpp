@@ -75,10 +75,10 @@ int check_dims(const pdssm_dims* d, int32_t chunk) {
   return PDSSM_OK;
 }
 
-int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_bu = 0) {
+int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_bu = 0, int step16 = 0) {
   const int c = (mode == pdscan::kModeSelect) ? pdscan::kSelectRows : chunk;
   if (!pdscan::make_plan(p, mode, d->B, d->H, d->L, d->N, d->K, d->d_in, d->u_shared,
-                         d->in_dtype == PDSSM_BF16, c, fold_bu))
+                         d->in_dtype == PDSSM_BF16, c, fold_bu, step16))
     return fail(PDSSM_EUNSUPPORTED,
                 "chunk=%d with N=%d needs %d bytes of on-chip memory per workgroup (limit %d)", c,
                 d->N, p.lds_bytes, pdscan::kMaxLds);
@@ -235,7 +235,7 @@ int pdssm_scan_fwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
   int rc = check_dims(dims, chunk);
   if (rc) return rc;
   Plan p;
-  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk))) return rc;
+  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk, 0, 1))) return rc;
   if (workspace_bytes < p.ws_bytes)
     return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 p.ws_bytes);
@@ -325,9 +325,12 @@ int pdssm_scan_fwd_pidx(const pdssm_dims* dims, int32_t chunk, const int32_t* P_
   if (rc) return rc;
   Plan p;
   const int T = chunk < dd.L ? chunk : dd.L;
-  dd.K = T;                                        // the step maps of a chunk are its table
-  if (!pdscan::make_plan(p, pdscan::kModeScan, dd.B, dd.H, dd.L, dd.N, T, dd.d_in, dd.u_shared,
-                         dd.in_dtype == PDSSM_BF16, chunk))
+  // N <= 16 and chunks up to 512: the maps stream through registers (the
+  // step-major scan); otherwise the step maps of a chunk are its table
+  const bool sm = dd.N <= 16 && T <= 512;
+  dd.K = sm ? 1 : T;
+  if (!pdscan::make_plan(p, pdscan::kModeScan, dd.B, dd.H, dd.L, dd.N, dd.K, dd.d_in, dd.u_shared,
+                         dd.in_dtype == PDSSM_BF16, chunk, 0, sm ? 1 : 0))
     return fail(PDSSM_EUNSUPPORTED, "chunk=%d with N=%d needs %d bytes of on-chip memory with per-step "
                 "maps (limit %d); use a shorter chunk", chunk, dd.N, p.lds_bytes, pdscan::kMaxLds);
   if (workspace_bytes < p.ws_bytes)

@@ -1043,6 +1043,58 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
 }
 
 // ---------------------------------------------------------------------------
+// Inverse dictionary rows for the step-major kernels (N, K <= 16).
+// SE[k][i]: the source columns j (ascending) whose one sits in row i under
+// dictionary entry k, packed for the step loop:
+//   x  byte m (m < 4): 4 * (m-th source), the lane offset of its value
+//   y  byte m (m < 4): 1 if row i has an m-th source, else 0
+//   z  nibbles: sources 5 to 12;  w  nibbles: sources 13 to 16, count << 24
+// Thread tid < 16 K builds entry (k, i) = (tid / 16, tid % 16) from its
+// dictionary row drow (-1 past N).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void write_se(i4v* SE, int tid, const int (&drow)[16]) {
+  const int iq = tid & 15;
+  unsigned bx = 0, by = 0, bz = 0, bw = 0;
+  int n = 0;
+#pragma unroll
+  for (int jq = 0; jq < 16; ++jq) {
+    const bool hit = drow[jq] == iq;
+    bx |= (hit && n < 4) ? (unsigned)(4 * jq) << (8 * (n & 3)) : 0u;
+    by |= (hit && n < 4) ? 1u << (8 * (n & 3)) : 0u;
+    bz |= (hit && n >= 4 && n < 12) ? (unsigned)jq << (4 * ((n - 4) & 7)) : 0u;
+    bw |= (hit && n >= 12) ? (unsigned)jq << (4 * ((n - 12) & 3)) : 0u;
+    n += hit ? 1 : 0;
+  }
+  SE[tid] = i4v{(int)bx, (int)by, (int)bz, (int)(bw | ((unsigned)n << 24))};
+}
+
+// h'_i = hn + sum over the sources j of row i (entry se) of the value vj of
+// lane j of this 16-lane group (byte offset lbase), gathered in ascending j;
+// absent sources are weighted by zero.  Rows with more than four sources take
+// a loop that the whole wave enters only when some lane needs it.
+__device__ __forceinline__ float se_gather(const i4v se, int vj, int lbase, float hn) {
+  const unsigned ax = (unsigned)se.x, ay = (unsigned)se.y;
+  float gv[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(lbase | (int)((ax >> (8 * m)) & 0xFFu), vj));
+#pragma unroll
+  for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(gv[m], (float)((ay >> (8 * m)) & 0xFFu), hn);
+  const unsigned aw = (unsigned)se.w;
+  if (__builtin_amdgcn_ballot_w64(aw >= (5u << 24))) {
+    const int deg = (int)(aw >> 24);
+    const unsigned az = (unsigned)se.z;
+    for (int m = 4; m < 16; ++m) {
+      const unsigned nib = m < 12 ? az >> (4 * (m - 4)) : aw >> (4 * (m - 12));
+      const float gm = __int_as_float(__builtin_amdgcn_ds_bpermute(lbase | (int)((nib & 15u) << 2), vj));
+      hn += m < deg ? gm : 0.f;
+      if (!__builtin_amdgcn_ballot_w64(m + 1 < deg)) break;
+    }
+  }
+  return hn;
+}
+
+// ---------------------------------------------------------------------------
 // Fused pass with step-major tiles (N <= 16, K <= 16, per-head u).
 //
 // A wave holds four lane groups of 16 (group = lane / 16, state row j =
@@ -1250,26 +1302,8 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     const float cdq = __int_as_float(__builtin_amdgcn_ds_bpermute(dq << 2, __float_as_int(cj)));
     if (dc_on) DC[(tid / N) * p.DCS + tid % N] = i2v{dq, __float_as_int(cdq)};
   }
-  // SE[k][i]: the source columns j (ascending) whose one sits in row i under
-  // dictionary entry k, packed for the step loop:
-  //   x  byte m (m < 4): 4 * (m-th source), the lane offset of its value
-  //   y  byte m (m < 4): 1 if row i has an m-th source, else 0
-  //   z  nibbles: sources 5 to 12;  w  nibbles: sources 13 to 16, count << 24
-  if (src_on) {
-    const int iq = tid & 15;
-    unsigned bx = 0, by = 0, bz = 0, bw = 0;
-    int n = 0;
-#pragma unroll
-    for (int jq = 0; jq < 16; ++jq) {
-      const bool hit = drow[jq] == iq;
-      bx |= (hit && n < 4) ? (unsigned)(4 * jq) << (8 * (n & 3)) : 0u;
-      by |= (hit && n < 4) ? 1u << (8 * (n & 3)) : 0u;
-      bz |= (hit && n >= 4 && n < 12) ? (unsigned)jq << (4 * ((n - 4) & 7)) : 0u;
-      bw |= (hit && n >= 12) ? (unsigned)jq << (4 * ((n - 12) & 3)) : 0u;
-      n += hit ? 1 : 0;
-    }
-    SE[tid] = i4v{(int)bx, (int)by, (int)bz, (int)(bw | ((unsigned)n << 24))};
-  }
+  // SE: the inverse dictionary rows (sources of each row)
+  if (src_on) write_se(SE, tid, drow);
   __syncthreads();                                 // tables ready
 
   f4v A[2][FOLD ? 3 : 2];
@@ -1318,31 +1352,11 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       const i2v e = DC[ksel * 16 + midx];
       const float dm = __int_as_float(
           __builtin_amdgcn_ds_bpermute(lbase + (midx << 2), __float_as_int(Dr[r])));
-      // h'_i = Bu_i + sum over the sources j of row i of D_j h_j, gathered
-      // from their lanes in ascending j; absent sources are weighted by zero
-      const int vj = __float_as_int(Dr[r] * hl);
-      const unsigned ax = (unsigned)se.x, ay = (unsigned)se.y;
-      float gv[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(lbase | (int)((ax >> (8 * m)) & 0xFFu), vj));
+      // h'_i = Bu_i + sum over the sources j of row i of D_j h_j
       float hn;
       if constexpr (FOLD) hn = A[cu][2][r];
       else hn = bu[(4 * k + r) & 15];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(gv[m], (float)((ay >> (8 * m)) & 0xFFu), hn);
-      const unsigned aw = (unsigned)se.w;
-      if (__builtin_amdgcn_ballot_w64(aw >= (5u << 24))) {
-        const int deg = (int)(aw >> 24);
-        const unsigned az = (unsigned)se.z;
-        for (int m = 4; m < 16; ++m) {
-          const unsigned nib = m < 12 ? az >> (4 * (m - 4)) : aw >> (4 * (m - 12));
-          const float gm = __int_as_float(
-              __builtin_amdgcn_ds_bpermute(lbase | (int)((nib & 15u) << 2), vj));
-          hn += m < deg ? gm : 0.f;
-          if (!__builtin_amdgcn_ballot_w64(m + 1 < deg)) break;
-        }
-      }
+      hn = se_gather(se, __float_as_int(Dr[r] * hl), lbase, hn);
       if (valid) {
         hl = hn;
         msc *= dm;
@@ -1373,6 +1387,168 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       block(std::false_type{}, k);
   }
   chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
+}
+
+// ---------------------------------------------------------------------------
+// Scan alone with the step-major layout (N <= 16): 16-lane groups, lane j of
+// a group owns state row j, and the maps of the group's steps stream through
+// registers instead of an on-chip table.  PMAP = 1: step t's map is read
+// whole from P_in (row of column j's one, per step); PMAP = 0: it is
+// dictionary entry k*_t (K <= 16), looked up in the (row, C[row]) table.  The
+// step
+//   h'_i = Bu_i + sum over the columns j with idx_t[j] = i of D_t[j] h_j
+// is, with a dictionary, a gather over the inverse rows (as in the fused
+// pass); with per-step maps, whose inverses are not tabulated, a scatter-add
+// done with DPP row rotations (no LDS, no atomics, a fixed summation order).
+// Each lane also follows its column's
+// path through the maps (p <- idx_t[p], scale <- D_t[p] scale) for the chunk
+// summary and the output weights w_t = C Phi_t, exactly as the fused
+// step-major pass does.  Everything after phase A is chunk_tail.
+// ---------------------------------------------------------------------------
+template <int PMAP>
+__device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) {
+  constexpr int SMAX = 32;                         // steps per group
+  const Plan& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = p.N, K = p.K, S = p.S, T = p.chunk, TS = p.TS;
+  const int BH = p.B * p.H;
+
+  float* Dbuf = (float*)(smem + p.off_D);          // holds w_t
+  float* yloc = (float*)(smem + p.off_yl);
+  float* Cs = (float*)(smem + p.off_C);
+  i2v* DC = (i2v*)(smem + p.off_DC);
+  int* misc = (int*)(smem + p.off_misc);
+  uint32_t* hdr = (uint32_t*)a.ws;
+
+  if (tid == 0) misc[0] = (int)atomicAdd(&hdr[kWsTicket], 1u);
+  __syncthreads();
+  const int task = misc[0];
+  const int c = task / BH, s = task % BH;
+  const int h = s % p.H;
+  const int c0 = c * T;
+  const int Tc = min(T, p.L - c0);
+  const size_t gbase = (size_t)s * p.L + c0;
+
+  const int gl = lane >> 4, j = lane & 15;
+  const int gam = wave * 4 + gl;
+  const int tb = gam * S;
+  const int nst = max(min(tb + S, Tc) - tb, 0);
+  const bool act = j < N;
+  const int jj = act ? j : 0;
+
+  // ---- every stream of the group's first 16 steps is in flight before
+  // anything waits (out-of-range offsets read zero: no branches)
+  const uint32_t rows = (uint32_t)(Tc * N * 4);
+  const rsrc_t mr = PMAP ? make_rsrc(a.P_in + gbase * N, rows) : make_rsrc(a.k_in + gbase, (uint32_t)(Tc * 4));
+  const rsrc_t dr = make_rsrc(a.D_in + gbase * N, rows);
+  const rsrc_t bur = make_rsrc(a.Bu + gbase * N, rows);
+  auto row_off = [&](int q) { return (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad; };
+  auto map_off = [&](int q) {
+    if constexpr (PMAP) return row_off(q);
+    else return q < nst ? (uint32_t)(tb + q) * 4u : kNoLoad;
+  };
+  int mi[16];                                      // P_in entry, or k*_t
+  float dv[16], bu[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    mi[q] = buf_i32(mr, map_off(q));
+    dv[q] = buf_f32(dr, row_off(q));
+    bu[q] = buf_f32(bur, row_off(q));
+  }
+  const float cj = buf_f32(make_rsrc(a.C + (size_t)h * N, (uint32_t)(N * 4)), act ? (uint32_t)j * 4u : kNoLoad);
+  if (tid < 16 && act) Cs[j] = cj;
+  if constexpr (!PMAP) {
+    // DC[k][m] = (dict[k][m], C[dict[k][m]]) and the inverse rows SE
+    // (K <= 16: one entry per thread)
+    const rsrc_t dr = make_rsrc(a.dict + (size_t)h * K * N, (uint32_t)(K * N * 4));
+    const bool dc_on = tid < K * N, src_on = tid < K * 16;
+    const int dq = buf_i32(dr, dc_on ? (uint32_t)tid * 4u : kNoLoad);
+    int drow[16];
+#pragma unroll
+    for (int jq = 0; jq < 16; ++jq) {
+      const bool ok = src_on && jq < N;
+      const int v = buf_i32(dr, ok ? (uint32_t)(((tid >> 4) * N + jq) * 4) : kNoLoad);
+      drow[jq] = ok ? v : -1;
+    }
+    __syncthreads();                               // Cs ready
+    if (dc_on) DC[(tid / N) * 16 + tid % N] = i2v{dq, __float_as_int(Cs[dq])};
+    if (src_on) write_se((i4v*)(smem + p.off_SRC), tid, drow);
+  }
+  __syncthreads();
+  const i4v* SE = (const i4v*)(smem + p.off_SRC);
+
+  float hl = 0.f, msc = 1.f;
+  int midx = jj;
+  const int lbase = (lane & ~15) << 2;             // byte offset of this group's lane 0
+  float* wrow = Dbuf + j * TS + tb + gam;          // w_t of this lane's row, step tb
+  float* yrow = yloc + tb + gam;
+  const int wave_nst = max(min(wave * 4 * S + S, Tc) - wave * 4 * S, 0);
+  const int nblk = (wave_nst + 3) >> 2;            // uniform in the wave
+  const int nst_last = max(min(wave * 4 * S + 4 * S, Tc) - (wave * 4 + 3) * S, 0);
+
+  auto block = [&](auto full_tag, const int k) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int nb = FULL ? 4 : nst - 4 * k;         // steps left in this group
+    float yp[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool valid = FULL || r < nb;
+      const int q = (4 * k + r) & 15;
+      const float dt = dv[q];
+      int nidx;
+      float cw, hn;
+      if constexpr (PMAP) {
+        // scatter-add of D_t h onto the drive term, inside the 16-lane row
+        const int it = mi[q] & 15;
+        nidx = __builtin_amdgcn_ds_bpermute(lbase + (midx << 2), it);
+        hn = row_gather_add(bu[q], act ? it : -1, dt * hl, j);
+      } else {
+        // the same as a gather over the inverse dictionary row
+        const int kt = mi[q];
+        const i2v e = DC[kt * 16 + midx];
+        nidx = e.x;
+        cw = __int_as_float(e.y);
+        hn = se_gather(SE[kt * 16 + j], __float_as_int(dt * hl), lbase, bu[q]);
+      }
+      const float dm = __int_as_float(__builtin_amdgcn_ds_bpermute(lbase + (midx << 2), __float_as_int(dt)));
+      if (valid) {
+        hl = hn;
+        msc *= dm;
+        midx = nidx;
+      }
+      if constexpr (PMAP) cw = Cs[midx];
+      if (valid && act) wrow[4 * k + r] = cw * msc;
+      yp[r] = cj * hl;
+    }
+    // refill this block's slots with the block four ahead
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = 4 * k + 16 + r;
+      mi[(4 * k + r) & 15] = buf_i32(mr, map_off(q));
+      dv[(4 * k + r) & 15] = buf_f32(dr, row_off(q));
+      bu[(4 * k + r) & 15] = buf_f32(bur, row_off(q));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float yl = group_sum<16>(yp[r]);
+      if ((FULL || r < nb) && j == 0) yrow[4 * k + r] = yl;
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < SMAX / 4; ++k) {
+    if (k >= nblk) break;
+    if (4 * k + 4 <= nst_last)
+      block(std::true_type{}, k);
+    else
+      block(std::false_type{}, k);
+  }
+  chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
+}
+
+template <int PMAP>
+__global__ __launch_bounds__(kThreads, 3) void pdssm_step16_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  step16_body<PMAP>(a, smem);
 }
 
 template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT, int FOLD = 0>

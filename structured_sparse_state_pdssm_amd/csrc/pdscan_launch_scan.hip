@@ -22,6 +22,13 @@ void launch_clear(const Args& a, hipStream_t st) {
 
 hipError_t launch_scan(const Args& a, hipStream_t st) {
   launch_clear(a, st);
+  if (a.p.step16) {
+    if (a.P_in)
+      hipLaunchKernelGGL(pdssm_step16_kernel<1>, dim3(a.p.tasks), dim3(kThreads), a.p.lds_bytes, st, a);
+    else
+      hipLaunchKernelGGL(pdssm_step16_kernel<0>, dim3(a.p.tasks), dim3(kThreads), a.p.lds_bytes, st, a);
+    return hipGetLastError();
+  }
   switch (npt_of(a.p)) {
     case 8: launch_kernel<kModeScan, 0, 0, kSelAny, 8, false>(a, st); break;
     case 16: launch_kernel<kModeScan, 0, 0, kSelAny, 16, false>(a, st); break;

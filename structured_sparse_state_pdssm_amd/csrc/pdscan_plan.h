@@ -38,6 +38,7 @@ struct Plan {
   int mma_bf16;  // score GEMM on bf16 MFMA (else fp32 MFMA)
   int fused16;   // fused pass with step-major MFMA tiles (N, K <= 16; see below)
   int fold_bu;   // fused16: Bu = W_b u from a third MFMA tile instead of an input
+  int step16;    // scan alone with the step-major layout (N <= 16, no per-step states)
   int tasks;     // workgroups
   // LDS byte offsets
   int off_D, off_k, off_yl, off_dict, off_DC, off_SRC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
@@ -57,7 +58,7 @@ inline int align_up(int x, int a) { return (x + a - 1) / a * a; }
 // Fills `p` for one call.  `mode` selects which parts exist.  Returns false
 // when the plan needs more than kMaxLds bytes of LDS.
 inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int d, int u_shared,
-                      int in_bf16, int chunk, int fold_bu = 0) {
+                      int in_bf16, int chunk, int fold_bu = 0, int step16 = 0) {
   p.B = B; p.H = H; p.L = L; p.N = N; p.K = K; p.d = d;
   p.u_shared = u_shared; p.in_bf16 = in_bf16;
   // a chunk longer than the sequence behaves exactly like chunk = L
@@ -70,7 +71,11 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.fused16 = (mode == kModeFused && !u_shared && N <= 16 && K <= 16 && kch > 0 &&
                (chunk < L ? chunk : L) <= 512) ? 1 : 0;
   p.fold_bu = (p.fused16 && fold_bu) ? 1 : 0;
-  p.NP = p.fused16 ? 16 : next_pow2(N);
+  // the scan alone on the same layout: maps streamed per step (at most 32
+  // steps per group, as above)
+  p.step16 = (mode == kModeScan && step16 && N <= 16 && K <= 16 && (chunk < L ? chunk : L) <= 512) ? 1 : 0;
+  const bool sm = p.fused16 || p.step16;
+  p.NP = sm ? 16 : next_pow2(N);
   p.G = kThreads / p.NP;
   p.S = align_up((p.chunk + p.G - 1) / p.G, 4);
   // t-contiguous rows; a stride of 4 (mod 32) words spreads the rows of one
@@ -79,7 +84,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   // row stride is 2 (mod 32), so the 64 lanes of a wave writing one step of
   // four groups hit 64 distinct banks in every 32-lane half.  Otherwise
   // t-contiguous rows with a stride of 4 (mod 32) for 16-byte accesses.
-  p.skew = p.fused16;
+  p.skew = sm ? 1 : 0;
   if (p.skew) {
     p.TS = p.chunk + p.G;
     p.TS += ((2 - p.TS % 32) + 32) % 32;
@@ -87,7 +92,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
     p.TS = align_up(p.chunk, 4);
     if (p.TS % 32 != 4) p.TS += (36 - p.TS % 32) % 32;
   }
-  p.DCS = p.fused16 ? 16 : N + 1;   // the step-major kernel indexes with a shift
+  p.DCS = sm ? 16 : N + 1;   // the step-major kernels index with a shift
   p.nC = (L + p.chunk - 1) / p.chunk;
   p.NC = align_up(K + N, 16);
   p.KP = align_up(K, 4);
@@ -103,7 +108,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.off_yl = scan ? take((T + p.G) * 4) : 0;
   p.off_dict = scan ? 0 : take(K * N * 4);   // selection: P_idx gathers
   p.off_DC = scan ? take(K * p.DCS * 8) : 0;  // scan: (row, C[row]) pairs
-  p.off_SRC = p.fused16 ? take(K * 16 * 16) : 0;  // fused16: source columns of each row
+  p.off_SRC = sm ? take(K * 16 * 16) : 0;  // step-major: source columns of each row
   p.off_C = take(N * 4);
   p.off_bd = take(N * 4);
   p.off_slot = take(kThreads * 4);

@@ -89,6 +89,33 @@ def test_scan_standalone(name):
     assert_within(host(hL), h_ref, f"{name} h_L")
 
 
+@pytest.mark.parametrize("chunk", [1, 3, 16, 100, 512, 700])
+@pytest.mark.parametrize("name,kw", [("impulse", dict(H=3, L=1300)), ("base", dict(B=1, H=2, L=333, N=5, K=3))])
+def test_scan_chunk_independence(name, kw, chunk):
+    """Chunks up to 512 with N <= 16 run the step-major scan (maps streamed
+    through registers), longer ones the table-driven scan: both agree with
+    the sequential oracle."""
+    inp, ref = _case(name, **kw)
+    P = lib()
+    D32 = ref["D"].astype(np.float32)
+    y_ref, h_ref = oracle.scan(ref["k_star"], inp.dict_idx, D32, inp.Bu, inp.C, inp.h0)
+    print(f"[gpu] pdssm_scan_fwd {name} N={inp.cfg.N} chunk={chunk}", flush=True)
+    y, hL = P.pdssm_scan_fwd(to_dev(ref["k_star"]), to_dev(inp.dict_idx), to_dev(D32),
+                             to_dev(inp.Bu), to_dev(inp.C), to_dev(inp.h0), chunk=chunk)
+    assert_within(host(y), y_ref, f"{name} chunk {chunk} y")
+    assert_within(host(hL), h_ref, f"{name} chunk {chunk} h_L")
+
+
+def test_scan_deterministic():
+    inp, ref = _case("impulse", **REDUCED["impulse"])
+    P = lib()
+    args = (to_dev(ref["k_star"]), to_dev(inp.dict_idx), to_dev(ref["D"].astype(np.float32)),
+            to_dev(inp.Bu), to_dev(inp.C), to_dev(inp.h0))
+    a = P.pdssm_scan_fwd(*args, chunk=512)
+    b = P.pdssm_scan_fwd(*args, chunk=512)
+    assert np.array_equal(host(a[0]), host(b[0])) and np.array_equal(host(a[1]), host(b[1]))
+
+
 @pytest.mark.parametrize("chunk", [1, 3, 4, 16, 64, 100, 128, 512, 700, 4096])
 def test_chunk_size_independence(chunk):
     inp, ref = _case("base", **REDUCED["base"])

@@ -86,17 +86,22 @@ def test_soft_forward_parity(key):
     assert_within(host(hL), hr, f"{key} h_L")
 
 
-@pytest.mark.parametrize("chunk", [1, 3, 16, 100, 128, 256])
-def test_scan_pidx_chunk_independence(chunk):
-    rng = np.random.default_rng(chunk)
-    B, H, L, N = 2, 3, 600, 16
+@pytest.mark.parametrize("chunk", [1, 3, 16, 100, 128, 256, 512])
+@pytest.mark.parametrize("N", [16, 5, 20])
+def test_scan_pidx_chunk_independence(chunk, N):
+    """N <= 16 with chunks up to 512: maps streamed through registers (the
+    step-major scan); N = 20: one on-chip table entry per step."""
+    if N == 20 and chunk > 192:
+        pytest.skip("the per-step table of N = 20 exceeds on-chip memory past 192 steps")
+    rng = np.random.default_rng(chunk + 1000 * N)
+    B, H, L = 2, 3, 600
     pidx = rng.integers(0, N, (B, H, L, N)).astype(np.int32)
     D = rng.uniform(0.2, 1.0, (B, H, L, N)).astype(np.float32)
     Bu = rng.standard_normal((B, H, L, N)).astype(np.float32)
     C = rng.standard_normal((H, N)).astype(np.float32)
     h0 = rng.standard_normal((B, H, N)).astype(np.float32)
     P = lib()
-    print(f"[gpu] pdssm_scan_fwd_pidx chunk={chunk}", flush=True)
+    print(f"[gpu] pdssm_scan_fwd_pidx N={N} chunk={chunk}", flush=True)
     y, hL = P.pdssm_scan_fwd_pidx(to_dev(pidx), to_dev(D), to_dev(Bu), to_dev(C), to_dev(h0), chunk=chunk)
     yr, hr = oracle.scan_pidx(pidx, D.astype(np.float64), Bu, C, h0)
     assert_within(host(y), yr, f"chunk {chunk} y")
@@ -110,6 +115,19 @@ def test_scan_pidx_rejects_a_chunk_too_long_for_its_table():
         P.pdssm_scan_fwd_pidx(to_dev(z.astype(np.int32)), to_dev(z), to_dev(z), to_dev(np.zeros((1, 16), np.float32)),
                               chunk=1024)
     assert e.value.status == P.PDSSM_EUNSUPPORTED
+
+
+def test_scan_pidx_deterministic():
+    rng = np.random.default_rng(3)
+    B, H, L, N = 1, 4, 2000, 16
+    args = (to_dev(rng.integers(0, N, (B, H, L, N)).astype(np.int32)),
+            to_dev(rng.uniform(0.2, 1.0, (B, H, L, N)).astype(np.float32)),
+            to_dev(rng.standard_normal((B, H, L, N)).astype(np.float32)),
+            to_dev(rng.standard_normal((H, N)).astype(np.float32)))
+    P = lib()
+    a = P.pdssm_scan_fwd_pidx(*args, chunk=512)
+    b = P.pdssm_scan_fwd_pidx(*args, chunk=512)
+    assert np.array_equal(host(a[0]), host(b[0])) and np.array_equal(host(a[1]), host(b[1]))
 
 
 def test_dict_hardmax_parity():
