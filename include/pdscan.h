@@ -167,6 +167,31 @@ int pdssm_scan_bwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
                    float* g_D, float* g_h0, float* g_C, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Several outputs per head: y_t = C h_t ("Flash PD-SSM" summary, methodology
+ * item 1) with C holding n_out rows per head, the output channels of a layer
+ * that reads u and writes y.  The pass of pdssm_fwd_wb with
+ *   n_out  1 <= n_out <= 4 (else PDSSM_EINVAL);
+ *   C      [H,n_out,N] fp32 (in): row o of head h is C[h,o,:];
+ *   y      [B,H,L,n_out] fp32 (out): y[b,h,t,o] = C[h,o,:] . h_t.
+ * Everything else, the workspace (pdssm_fwd_workspace_bytes) and the shape
+ * limits as in pdssm_fwd_wb.  The on-chip output weights grow with n_out, so
+ * the chunk shrinks with it (N = 16: n_out = 2 up to chunk 256, n_out = 3 or 4
+ * up to chunk 128); a chunk that does not fit returns PDSSM_EUNSUPPORTED. */
+int pdssm_fwd_wb_multi(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const void* u,
+                       const void* W_sel, const int32_t* dict_idx, const void* W_d, const float* b_d,
+                       const void* W_b, const float* C, const float* h0, int32_t* k_star, float* D,
+                       float* y, float* h_L, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pdssm_scan_fwd with several outputs per head: C [H,n_out,N] and
+ * y [B,H,L,n_out] as in pdssm_fwd_wb_multi; 1 <= n_out <= 4.  Runs on the
+ * step-major scan only (N <= 16, K <= 16, chunk <= 512 and fitting on chip as
+ * above); otherwise PDSSM_EUNSUPPORTED.  Workspace as
+ * pdssm_scan_workspace_bytes. */
+int pdssm_scan_fwd_multi(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const int32_t* k_star,
+                         const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
+                         const float* h0, float* y, float* h_L, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Bytes of workspace pdssm_impulse_sens needs for these dims and chunk length
  * (about nC * B * H * N * (d_in + 2) * 8 bytes: one tangent state per chunk). */
 int pdssm_impulse_sens_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes);

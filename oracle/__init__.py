@@ -9,11 +9,13 @@ from .pdssm_oracle import (  # noqa: F401
     drive,
     forward,
     forward_wb,
+    forward_wb_multi,
     forward_inputs,
     impulse_sensitivity,
     pd_apply,
     pd_compose,
     scan,
+    scan_multi,
     scan_pidx,
     scan_states,
     scan_vjp,

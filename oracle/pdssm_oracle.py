@@ -24,7 +24,9 @@ Everything is upcast exactly to fp64 first.  ``scan`` builds the dense N x N
 transition of every step and multiplies; it never uses the sparse structure.
 
 ``forward_wb`` is the same forward pass with the drive terms Bu_t = W_b u_t
-formed from the input (``drive``) instead of being given.
+formed from the input (``drive``) instead of being given; ``scan_multi`` /
+``forward_wb_multi`` read several outputs per head, y_t = C h_t with C
+holding n_out rows, from the states of ``scan_states``.
 
 ``soft_select`` / ``scan_pidx`` are the original soft-selection model, kept
 as a comparison path: a softmax-weighted mixture of dense dictionary
@@ -320,6 +322,26 @@ def forward_wb(u, W_sel, dict_idx, W_d, b_d, W_b, C, h0=None, u_shared=False):
     out = forward(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0, u_shared)
     out["Bu"] = Bu
     return out
+
+
+def scan_multi(k_star, dict_idx, D, Bu, C, h0=None):
+    """``scan`` with several outputs per head ("Flash PD-SSM" summary,
+    methodology item 1, y_t = C h_t with C holding n_out rows per head):
+    C [H,n_out,N] gives y[b,h,t,o] = sum_n C[h,o,n] h_t[n], fp64 [B,H,L,n_out];
+    returns (y, h_L) with h_L the state after the last step."""
+    states = scan_states(k_star, dict_idx, D, Bu, h0)
+    C = np.asarray(C, dtype=F64)
+    y = np.einsum("bhln,hon->bhlo", states, C)
+    return y, states[:, :, -1].copy()
+
+
+def forward_wb_multi(u, W_sel, dict_idx, W_d, b_d, W_b, C, h0=None, u_shared=False):
+    """``forward_wb`` with C [H,n_out,N]: selections, the drive W_b u, then
+    ``scan_multi``.  Returns dict(k_star, D, Bu, y [B,H,L,n_out], h_L)."""
+    k_star, D, _ = select(u, W_sel, W_d, b_d, u_shared)
+    Bu = drive(u, W_b, u_shared)
+    y, h_L = scan_multi(k_star, dict_idx, D, Bu, C, h0)
+    return {"k_star": k_star, "D": D, "Bu": Bu, "y": y, "h_L": h_L}
 
 
 def forward_inputs(inp, L=None):

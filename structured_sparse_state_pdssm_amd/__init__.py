@@ -40,6 +40,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "pdssm_select", "pdssm_scan_fwd", "pdssm_fwd", "pdssm_fwd_wb", "pdssm_impulse_sens",
     "pdssm_soft_select", "pdssm_scan_fwd_pidx", "pdssm_dict_hardmax",
+    "pdssm_fwd_wb_multi", "pdssm_scan_fwd_multi",
     "scan_workspace_bytes",
     "fwd_workspace_bytes", "make_dims", "PdssmError", "lib", "LIB_PATH",
 ]
@@ -239,6 +240,72 @@ def pdssm_fwd_wb(u, W_sel, dict_idx, W_d, b_d, W_b, C, h0=None, chunk=128, want_
                             _ptr(res.get("k_star")), _ptr(res.get("D")), _ptr(res["y"]),
                             _ptr(res["h_L"]), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev)))
     return res
+
+
+def pdssm_fwd_wb_multi(u, W_sel, dict_idx, W_d, b_d, W_b, C, h0=None, chunk=128, want_k=False,
+                       want_D=False, workspace=None, out=None):
+    """pdssm_fwd_wb with several outputs per head: C [H,n_out,N] (n_out <= 4)
+    gives y [B,H,L,n_out].  Returns dict(y, h_L[, k_star][, D])."""
+    torch = _torch()
+    for t, n in ((u, "u"), (W_sel, "W_sel"), (W_d, "W_d"), (W_b, "W_b")):
+        _need(t, n)
+    if W_b.dtype != W_d.dtype or tuple(W_b.shape) != tuple(W_d.shape):
+        raise ValueError("W_b must have W_d's shape [H,N,d] and dtype")
+    _need(dict_idx, "dict_idx", torch.int32)
+    for t, n in ((b_d, "b_d"), (C, "C")):
+        _need(t, n, torch.float32)
+    if C.dim() != 3:
+        raise ValueError("C must be [H, n_out, N]")
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    dims = _dims_from(u, W_sel, W_d)
+    dev = u.device
+    B, H, L, N = dims.B, dims.H, dims.L, dims.N
+    P = int(C.shape[1])
+    ws = _workspace(fwd_workspace_bytes(dims, chunk), dev, workspace)
+    o = out or {}
+    res = {}
+    for name, shape, dt, want in (("y", (B, H, L, P), torch.float32, True),
+                                  ("h_L", (B, H, N), torch.float32, True),
+                                  ("k_star", (B, H, L), torch.int32, want_k),
+                                  ("D", (B, H, L, N), torch.float32, want_D)):
+        if want:
+            t = o.get(name)
+            res[name] = torch.empty(shape, dtype=dt, device=dev) if t is None else _need(t, name)
+    _check(lib.pdssm_fwd_wb_multi(ctypes.byref(dims), int(chunk), P, _ptr(u), _ptr(W_sel), _ptr(dict_idx),
+                                  _ptr(W_d), _ptr(b_d), _ptr(W_b), _ptr(C), _ptr(h0),
+                                  _ptr(res.get("k_star")), _ptr(res.get("D")), _ptr(res["y"]),
+                                  _ptr(res["h_L"]), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev)))
+    return res
+
+
+def pdssm_scan_fwd_multi(k_star, dict_idx, D, Bu, C, h0=None, chunk=128, workspace=None, out=None):
+    """pdssm_scan_fwd with several outputs per head: C [H,n_out,N] (n_out <= 4).
+    Returns (y [B,H,L,n_out], h_L [B,H,N])."""
+    torch = _torch()
+    _need(k_star, "k_star", torch.int32)
+    _need(dict_idx, "dict_idx", torch.int32)
+    for t, n in ((D, "D"), (Bu, "Bu"), (C, "C")):
+        _need(t, n, torch.float32)
+    if C.dim() != 3:
+        raise ValueError("C must be [H, n_out, N]")
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+    B, H, L = k_star.shape
+    _, K, N = dict_idx.shape
+    P = int(C.shape[1])
+    dims = make_dims(B, H, L, N, K, 8)
+    dev = k_star.device
+    ws = _workspace(scan_workspace_bytes(dims, chunk), dev, workspace)
+    o = out or {}
+    y = o.get("y")
+    y = torch.empty((B, H, L, P), dtype=torch.float32, device=dev) if y is None else _need(y, "y")
+    hL = o.get("h_L")
+    hL = torch.empty((B, H, N), dtype=torch.float32, device=dev) if hL is None else _need(hL, "h_L")
+    _check(lib.pdssm_scan_fwd_multi(ctypes.byref(dims), int(chunk), P, _ptr(k_star), _ptr(dict_idx), _ptr(D),
+                                    _ptr(Bu), _ptr(C), _ptr(h0), _ptr(y), _ptr(hL), _ptr(ws),
+                                    ctypes.c_size_t(ws.numel()), _stream(dev)))
+    return y, hL
 
 
 def impulse_sens_workspace_bytes(dims, chunk):

@@ -45,6 +45,8 @@ def _load():
         "pdssm_fwd_workspace_bytes": [dp, i32, ctypes.POINTER(sz)],
         "pdssm_fwd": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "pdssm_fwd_wb": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "pdssm_fwd_wb_multi": [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "pdssm_scan_fwd_multi": [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "pdssm_impulse_sens_workspace_bytes": [dp, i32, ctypes.POINTER(sz)],
         "pdssm_impulse_sens": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "pdssm_scan_fwd_pidx": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],

@@ -75,10 +75,11 @@ int check_dims(const pdssm_dims* d, int32_t chunk) {
   return PDSSM_OK;
 }
 
-int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_bu = 0, int step16 = 0) {
+int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_bu = 0, int step16 = 0,
+               int n_out = 1) {
   const int c = (mode == pdscan::kModeSelect) ? pdscan::kSelectRows : chunk;
   if (!pdscan::make_plan(p, mode, d->B, d->H, d->L, d->N, d->K, d->d_in, d->u_shared,
-                         d->in_dtype == PDSSM_BF16, c, fold_bu, step16))
+                         d->in_dtype == PDSSM_BF16, c, fold_bu, step16, n_out))
     return fail(PDSSM_EUNSUPPORTED,
                 "chunk=%d with N=%d needs %d bytes of on-chip memory per workgroup (limit %d)", c,
                 d->N, p.lds_bytes, pdscan::kMaxLds);
@@ -170,6 +171,78 @@ int sens_plan(pdscan::SensPlan& q, const pdssm_dims* dims, int32_t chunk) {
 
 }  // namespace
 
+namespace {
+
+int scan_fwd_impl(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const int32_t* k_star,
+                  const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
+                  const float* h0, float* y, float* h_L, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk, 0, 1, n_out))) return rc;
+  if (n_out > 1 && !p.step16)
+    return fail(PDSSM_EUNSUPPORTED, "several outputs per head need the step-major scan: N <= 16, K <= 16, "
+                "chunk <= 512 (got N=%d K=%d chunk=%d)", dims->N, dims->K, chunk);
+  if (workspace_bytes < p.ws_bytes)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"k_star", k_star, z.k}, {"dict_idx", dict_idx, z.dict}, {"D", D, z.D},
+                      {"Bu", Bu, z.Bu}, {"C", C, z.C * n_out}, {"h0", h0, z.h0}};
+  const Range out[] = {{"y", y, z.y * n_out}, {"h_L", h_L, z.hL}, {"workspace", workspace, p.ws_bytes}};
+  static const char* const req[] = {"k_star", "dict_idx", "D", "Bu", "C", "y", "h_L", "workspace",
+                                    nullptr};
+  if ((rc = check_ptrs(in, 6, out, 3, req))) return rc;
+  pdscan::Args a = {};
+  a.p = p;
+  a.dict = dict_idx; a.k_in = k_star; a.D_in = D; a.Bu = Bu; a.C = C; a.h0 = h0;
+  a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
+  return dispatch(pdscan::kModeScan, a, stream);
+}
+
+int fwd_wb_impl(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const void* u, const void* W_sel,
+                const int32_t* dict_idx, const void* W_d, const float* b_d, const void* W_b,
+                const float* C, const float* h0, int32_t* k_star, float* D, float* y, float* h_L,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk, 1, 0, n_out))) return rc;
+  if (!p.fold_bu)
+    return fail(PDSSM_EUNSUPPORTED,
+                "the drive term is folded into the step-major kernel only: per-head u, N <= 16, "
+                "K <= 16, chunk <= 512, fp32 d in {16, 32, 64} or bf16 d = 128 (got u_shared=%d "
+                "N=%d K=%d d=%d %s)", dims->u_shared, dims->N, dims->K, dims->d_in,
+                dims->in_dtype == PDSSM_BF16 ? "bf16" : "fp32");
+  if (workspace_bytes < p.ws_bytes)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"u", u, z.u},         {"W_sel", W_sel, z.Wsel}, {"dict_idx", dict_idx, z.dict},
+                      {"W_d", W_d, z.Wd},    {"b_d", b_d, z.bd},       {"W_b", W_b, z.Wd},
+                      {"C", C, z.C * n_out}, {"h0", h0, z.h0}};
+  const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y * n_out},
+                       {"h_L", h_L, z.hL},      {"workspace", workspace, p.ws_bytes}};
+  static const char* const req[] = {"u",  "W_sel", "dict_idx", "W_d", "b_d",      "W_b",
+                                    "C",  "y",     "h_L",      "workspace", nullptr};
+  if ((rc = check_ptrs(in, 8, out, 5, req))) return rc;
+  pdscan::Args a = {};
+  a.p = p;
+  a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx; a.W_b = W_b;
+  a.C = C; a.h0 = h0; a.k_out = k_star; a.D_out = D;
+  a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
+  return dispatch(pdscan::kModeFused, a, stream);
+}
+
+int check_n_out(int32_t n_out) {
+  if (n_out < 1 || n_out > pdscan::kMaxOut)
+    return fail(PDSSM_EINVAL, "n_out=%d outside [1, %d]", n_out, pdscan::kMaxOut);
+  return PDSSM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int pdssm_abi_version(void) { return PDSSM_ABI_VERSION; }
@@ -228,29 +301,23 @@ int pdssm_fwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* byt
   return PDSSM_OK;
 }
 
+
 int pdssm_scan_fwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
                    const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
                    const float* h0, float* y, float* h_L, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  int rc = check_dims(dims, chunk);
+  return scan_fwd_impl(dims, chunk, 1, k_star, dict_idx, D, Bu, C, h0, y, h_L, workspace, workspace_bytes,
+                       stream);
+}
+
+int pdssm_scan_fwd_multi(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const int32_t* k_star,
+                         const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
+                         const float* h0, float* y, float* h_L, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int rc = check_n_out(n_out);
   if (rc) return rc;
-  Plan p;
-  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk, 0, 1))) return rc;
-  if (workspace_bytes < p.ws_bytes)
-    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
-                p.ws_bytes);
-  const Sizes z = sizes(dims);
-  const Range in[] = {{"k_star", k_star, z.k}, {"dict_idx", dict_idx, z.dict}, {"D", D, z.D},
-                      {"Bu", Bu, z.Bu}, {"C", C, z.C}, {"h0", h0, z.h0}};
-  const Range out[] = {{"y", y, z.y}, {"h_L", h_L, z.hL}, {"workspace", workspace, p.ws_bytes}};
-  static const char* const req[] = {"k_star", "dict_idx", "D", "Bu", "C", "y", "h_L", "workspace",
-                                    nullptr};
-  if ((rc = check_ptrs(in, 6, out, 3, req))) return rc;
-  pdscan::Args a = {};
-  a.p = p;
-  a.dict = dict_idx; a.k_in = k_star; a.D_in = D; a.Bu = Bu; a.C = C; a.h0 = h0;
-  a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
-  return dispatch(pdscan::kModeScan, a, stream);
+  return scan_fwd_impl(dims, chunk, n_out, k_star, dict_idx, D, Bu, C, h0, y, h_L, workspace,
+                       workspace_bytes, stream);
 }
 
 int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
@@ -285,34 +352,18 @@ int pdssm_fwd_wb(const pdssm_dims* dims, int32_t chunk, const void* u, const voi
                  const int32_t* dict_idx, const void* W_d, const float* b_d, const void* W_b,
                  const float* C, const float* h0, int32_t* k_star, float* D, float* y, float* h_L,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_dims(dims, chunk);
+  return fwd_wb_impl(dims, chunk, 1, u, W_sel, dict_idx, W_d, b_d, W_b, C, h0, k_star, D, y, h_L, workspace,
+                     workspace_bytes, stream);
+}
+
+int pdssm_fwd_wb_multi(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const void* u,
+                       const void* W_sel, const int32_t* dict_idx, const void* W_d, const float* b_d,
+                       const void* W_b, const float* C, const float* h0, int32_t* k_star, float* D,
+                       float* y, float* h_L, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_n_out(n_out);
   if (rc) return rc;
-  Plan p;
-  if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk, 1))) return rc;
-  if (!p.fold_bu)
-    return fail(PDSSM_EUNSUPPORTED,
-                "the drive term is folded into the step-major kernel only: per-head u, N <= 16, "
-                "K <= 16, chunk <= 512, fp32 d in {16, 32, 64} or bf16 d = 128 (got u_shared=%d "
-                "N=%d K=%d d=%d %s)", dims->u_shared, dims->N, dims->K, dims->d_in,
-                dims->in_dtype == PDSSM_BF16 ? "bf16" : "fp32");
-  if (workspace_bytes < p.ws_bytes)
-    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
-                p.ws_bytes);
-  const Sizes z = sizes(dims);
-  const Range in[] = {{"u", u, z.u},         {"W_sel", W_sel, z.Wsel}, {"dict_idx", dict_idx, z.dict},
-                      {"W_d", W_d, z.Wd},    {"b_d", b_d, z.bd},       {"W_b", W_b, z.Wd},
-                      {"C", C, z.C},         {"h0", h0, z.h0}};
-  const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y},
-                       {"h_L", h_L, z.hL},      {"workspace", workspace, p.ws_bytes}};
-  static const char* const req[] = {"u",  "W_sel", "dict_idx", "W_d", "b_d",      "W_b",
-                                    "C",  "y",     "h_L",      "workspace", nullptr};
-  if ((rc = check_ptrs(in, 8, out, 5, req))) return rc;
-  pdscan::Args a = {};
-  a.p = p;
-  a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx; a.W_b = W_b;
-  a.C = C; a.h0 = h0; a.k_out = k_star; a.D_out = D;
-  a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
-  return dispatch(pdscan::kModeFused, a, stream);
+  return fwd_wb_impl(dims, chunk, n_out, u, W_sel, dict_idx, W_d, b_d, W_b, C, h0, k_star, D, y, h_L,
+                     workspace, workspace_bytes, stream);
 }
 
 int pdssm_scan_fwd_pidx(const pdssm_dims* dims, int32_t chunk, const int32_t* P_idx, const float* D,

@@ -862,13 +862,28 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
       return;
     }
   }
-  for (int t = tid; t < Tc; t += kThreads) {
-    const int gt = t / S;
-    const int col = t + (p.skew ? gt : 0);
-    const float* cr = slots + gt * NP;
-    float acc = yloc[col];
-    for (int n = 0; n < N; ++n) acc += Dbuf[n * TS + col] * cr[n];
-    a.y[gbase + t] = acc;
+  const int P = p.n_out;
+  if (P == 1) {
+    for (int t = tid; t < Tc; t += kThreads) {
+      const int gt = t / S;
+      const int col = t + (p.skew ? gt : 0);
+      const float* cr = slots + gt * NP;
+      float acc = yloc[col];
+      for (int n = 0; n < N; ++n) acc += Dbuf[n * TS + col] * cr[n];
+      a.y[gbase + t] = acc;
+    }
+  } else {
+    // several rows of C: output o of step t at y[(gbase + t) P + o]
+    for (int e = tid; e < Tc * P; e += kThreads) {
+      const int t = e / P, o = e - t * P;
+      const int gt = t / S;
+      const int col = t + (p.skew ? gt : 0);
+      const float* cr = slots + gt * NP;
+      const float* wo = Dbuf + o * N * TS;
+      float acc = yloc[o * p.YS + col];
+      for (int n = 0; n < N; ++n) acc += wo[n * TS + col] * cr[n];
+      a.y[(gbase + t) * P + o] = acc;
+    }
   }
 }
 
@@ -1107,7 +1122,7 @@ __device__ __forceinline__ float se_gather(const i4v se, int vj, int lbase, floa
 // through LDS, and the next tile's MFMAs are issued before the current
 // tile's scan steps so that the two overlap.
 // ---------------------------------------------------------------------------
-template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT, int FOLD>
+template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT, int FOLD, int NOUT>
 __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem) {
   typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
   constexpr int CB = kChanBlock<MMA_BF16>;
@@ -1226,7 +1241,15 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     }
   }
   const float bdz = buf_f32(make_rsrc(a.b_d + (size_t)h * N, (uint32_t)(N * 4)), i < N ? (uint32_t)i * 4u : kNoLoad);
-  const float cj = buf_f32(make_rsrc(a.C + (size_t)h * N, (uint32_t)(N * 4)), act ? (uint32_t)j * 4u : kNoLoad);
+  // rows of C (NOUT > 1: p.n_out of them, C[h][o][j]); row 0 also feeds DC
+  const int P = NOUT > 1 ? p.n_out : 1;
+  float cjo[NOUT];
+  {
+    const rsrc_t cr = make_rsrc(a.C + (size_t)h * P * N, (uint32_t)(P * N * 4));
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) cjo[o] = buf_f32(cr, (act && o < P) ? (uint32_t)(o * N + j) * 4u : kNoLoad);
+  }
+  const float cj = cjo[0];
 
   // u rows of tile k for this lane's A operand: group i / 4 of the wave,
   // step 4k + i % 4 of that group's sub-chunk
@@ -1304,6 +1327,11 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   }
   // SE: the inverse dictionary rows (sources of each row)
   if (src_on) write_se(SE, tid, drow);
+  float* Cs = (float*)(smem + p.off_C);            // NOUT > 1: row o of C at 16 o
+  if (NOUT > 1 && tid < 16) {
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) Cs[o * 16 + j] = cjo[o];
+  }
   __syncthreads();                                 // tables ready
 
   f4v A[2][FOLD ? 3 : 2];
@@ -1343,7 +1371,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       for (int r = 0; r < 4 && r < nb; ++r) a.k_out[gbase + tb + 4 * k + r] = ks[r];
     if (a.D_out && act)
       for (int r = 0; r < 4 && r < nb; ++r) a.D_out[(gbase + tb + 4 * k + r) * N + j] = Dr[r];
-    float yp[4];
+    float yp[NOUT][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool valid = FULL || r < nb;
@@ -1362,8 +1390,14 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
         msc *= dm;
         midx = e.x;
       }
-      if (valid && act) wrow[4 * k + r] = __int_as_float(e.y) * msc;
-      yp[r] = cj * hl;
+      if (valid && act) {
+        wrow[4 * k + r] = __int_as_float(e.y) * msc;
+#pragma unroll
+        for (int o = 1; o < NOUT; ++o)
+          if (o < P) wrow[o * N * TS + 4 * k + r] = Cs[o * 16 + midx] * msc;
+      }
+#pragma unroll
+      for (int o = 0; o < NOUT; ++o) yp[o][r] = cjo[o] * hl;
     }
     // refill this block's drive-term slots with the block four ahead
     if constexpr (!FOLD) {
@@ -1373,10 +1407,12 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     // local outputs of the four steps, summed over the group off the scan's
     // critical path
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float yl = group_sum<16>(yp[r]);
-      if ((FULL || r < nb) && j == 0) yrow[4 * k + r] = yl;
-    }
+    for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float yl = group_sum<16>(yp[o][r]);
+        if ((FULL || r < nb) && j == 0 && o < P) yrow[o * p.YS + 4 * k + r] = yl;
+      }
   };
 #pragma unroll
   for (int k = 0; k < SMAX / 4; ++k) {
@@ -1405,7 +1441,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
 // summary and the output weights w_t = C Phi_t, exactly as the fused
 // step-major pass does.  Everything after phase A is chunk_tail.
 // ---------------------------------------------------------------------------
-template <int PMAP>
+template <int PMAP, int NOUT>
 __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) {
   constexpr int SMAX = 32;                         // steps per group
   const Plan& p = a.p;
@@ -1455,8 +1491,19 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
     dv[q] = buf_f32(dr, row_off(q));
     bu[q] = buf_f32(bur, row_off(q));
   }
-  const float cj = buf_f32(make_rsrc(a.C + (size_t)h * N, (uint32_t)(N * 4)), act ? (uint32_t)j * 4u : kNoLoad);
-  if (tid < 16 && act) Cs[j] = cj;
+  // rows of C (NOUT > 1: p.n_out of them, C[h][o][j]), row o at Cs[16 o]
+  const int P = NOUT > 1 ? p.n_out : 1;
+  float cjo[NOUT];
+  {
+    const rsrc_t cr = make_rsrc(a.C + (size_t)h * P * N, (uint32_t)(P * N * 4));
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) cjo[o] = buf_f32(cr, (act && o < P) ? (uint32_t)(o * N + j) * 4u : kNoLoad);
+  }
+  const float cj = cjo[0];
+  if (tid < 16) {
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) Cs[o * 16 + j] = cjo[o];
+  }
   if constexpr (!PMAP) {
     // DC[k][m] = (dict[k][m], C[dict[k][m]]) and the inverse rows SE
     // (K <= 16: one entry per thread)
@@ -1489,7 +1536,7 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
   auto block = [&](auto full_tag, const int k) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int nb = FULL ? 4 : nst - 4 * k;         // steps left in this group
-    float yp[4];
+    float yp[NOUT][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool valid = FULL || r < nb;
@@ -1517,8 +1564,14 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
         midx = nidx;
       }
       if constexpr (PMAP) cw = Cs[midx];
-      if (valid && act) wrow[4 * k + r] = cw * msc;
-      yp[r] = cj * hl;
+      if (valid && act) {
+        wrow[4 * k + r] = cw * msc;
+#pragma unroll
+        for (int o = 1; o < NOUT; ++o)
+          if (o < P) wrow[o * N * TS + 4 * k + r] = Cs[o * 16 + midx] * msc;
+      }
+#pragma unroll
+      for (int o = 0; o < NOUT; ++o) yp[o][r] = cjo[o] * hl;
     }
     // refill this block's slots with the block four ahead
 #pragma unroll
@@ -1529,10 +1582,12 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
       bu[(4 * k + r) & 15] = buf_f32(bur, row_off(q));
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float yl = group_sum<16>(yp[r]);
-      if ((FULL || r < nb) && j == 0) yrow[4 * k + r] = yl;
-    }
+    for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float yl = group_sum<16>(yp[o][r]);
+        if ((FULL || r < nb) && j == 0 && o < P) yrow[o * p.YS + 4 * k + r] = yl;
+      }
   };
 #pragma unroll
   for (int k = 0; k < SMAX / 4; ++k) {
@@ -1545,16 +1600,17 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
   chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
 }
 
-template <int PMAP>
+template <int PMAP, int NOUT = 1>
 __global__ __launch_bounds__(kThreads, 3) void pdssm_step16_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  step16_body<PMAP>(a, smem);
+  step16_body<PMAP, NOUT>(a, smem);
 }
 
-template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT, int FOLD = 0>
-__global__ __launch_bounds__(kThreads, 3) void pdssm_fused16_kernel(Args a) {
+// (several rows of C need more registers: two waves per SIMD then)
+template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT, int FOLD = 0, int NOUT = 1>
+__global__ __launch_bounds__(kThreads, NOUT > 1 ? 2 : 3) void pdssm_fused16_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  fused16_body<IN_BF16, MMA_BF16, KCH, SPLIT, FOLD>(a, smem);
+  fused16_body<IN_BF16, MMA_BF16, KCH, SPLIT, FOLD, NOUT>(a, smem);
 }
 
 // Two entry points over one body: the register-resident fp32 selection paths

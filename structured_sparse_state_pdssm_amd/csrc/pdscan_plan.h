@@ -19,6 +19,7 @@ constexpr int kWaves = kThreads / 64;  // wave64
 constexpr int kSelectRows = 256;       // rows per workgroup for selection alone
 constexpr int kMaxLds = 64 * 1024;     // bytes of LDS one workgroup may use
 constexpr int kWbFrags = 6;            // W_b fragments per lane at most (fp32 d = 64: 2 blocks x 3 pieces)
+constexpr int kMaxOut = 4;             // outputs per head (rows of C) on the multi-output paths
 
 enum Mode : int { kModeSelect = 0, kModeScan = 1, kModeFused = 2 };
 
@@ -39,6 +40,8 @@ struct Plan {
   int fused16;   // fused pass with step-major MFMA tiles (N, K <= 16; see below)
   int fold_bu;   // fused16: Bu = W_b u from a third MFMA tile instead of an input
   int step16;    // scan alone with the step-major layout (N <= 16, no per-step states)
+  int n_out;     // outputs per head, rows of C (> 1: step-major paths only)
+  int YS;        // stride of the per-output local-output rows
   int tasks;     // workgroups
   // LDS byte offsets
   int off_D, off_k, off_yl, off_dict, off_DC, off_SRC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
@@ -58,7 +61,7 @@ inline int align_up(int x, int a) { return (x + a - 1) / a * a; }
 // Fills `p` for one call.  `mode` selects which parts exist.  Returns false
 // when the plan needs more than kMaxLds bytes of LDS.
 inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int d, int u_shared,
-                      int in_bf16, int chunk, int fold_bu = 0, int step16 = 0) {
+                      int in_bf16, int chunk, int fold_bu = 0, int step16 = 0, int n_out = 1) {
   p.B = B; p.H = H; p.L = L; p.N = N; p.K = K; p.d = d;
   p.u_shared = u_shared; p.in_bf16 = in_bf16;
   // a chunk longer than the sequence behaves exactly like chunk = L
@@ -103,13 +106,16 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   int off = 0;
   auto take = [&](int bytes) { int o = off; off = align_up(off + bytes, 16); return o; };
   const bool scan = mode != kModeSelect;
-  p.off_D = scan ? take(N * p.TS * 4) : 0;
+  // multi-output: w_t and the local outputs once per row of C
+  p.n_out = n_out;
+  p.YS = align_up(T + p.G, 4);
+  p.off_D = scan ? take(n_out * N * p.TS * 4) : 0;
   p.off_k = scan ? take(align_up(T, 4) * 4) : 0;
-  p.off_yl = scan ? take((T + p.G) * 4) : 0;
+  p.off_yl = scan ? take(n_out * p.YS * 4) : 0;
   p.off_dict = scan ? 0 : take(K * N * 4);   // selection: P_idx gathers
   p.off_DC = scan ? take(K * p.DCS * 8) : 0;  // scan: (row, C[row]) pairs
   p.off_SRC = sm ? take(K * 16 * 16) : 0;  // step-major: source columns of each row
-  p.off_C = take(N * 4);
+  p.off_C = take((N > 16 * n_out ? N : 16 * n_out) * 4);   // step-major: row o of C at 16 o
   p.off_bd = take(N * 4);
   p.off_slot = take(kThreads * 4);
   p.off_sIdx = scan ? take(p.G * N * 4) : 0;
@@ -130,6 +136,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.ws_agg = 256;
   p.ws_inc = p.ws_agg + seqchunks * 3 * N * sizeof(uint64_t);
   p.ws_bytes = (mode == kModeSelect) ? 0 : p.ws_inc + seqchunks * N * sizeof(uint64_t);
+  if (n_out < 1 || n_out > kMaxOut || (n_out > 1 && !sm)) return false;
   return p.lds_bytes <= kMaxLds;
 }
 

@@ -166,3 +166,27 @@ def test_binding_rejects_host_tensors(P):
     with pytest.raises(ValueError):
         P.pdssm_scan_fwd(torch.zeros((1, 1, 4), dtype=torch.int32), torch.zeros((1, 1, 2), dtype=torch.int32),
                          x, x, x)
+
+
+def test_multi_output_validation(P):
+    """n_out outside [1, 4]: invalid; a chunk whose per-output on-chip rows do
+    not fit, or a shape off the step-major paths: unsupported; a fitting call
+    then fails only on its (empty) workspace."""
+    big = 1 << 30
+    d = _dims(P, L=4096)
+    args = lambda ws: (A, A + big, A + 2 * big, A + 3 * big, A + 4 * big, None,  # noqa: E731
+                       A + 5 * big, A + 6 * big, A + 7 * big, ws, None)
+    for n_out, chunk, want in ((0, 128, -1), (5, 128, -1), (2, 512, -2), (4, 256, -2), (4, 128, -3),
+                               (2, 256, -3)):
+        rc = P.lib.pdssm_scan_fwd_multi(ctypes.byref(d), chunk, n_out, *args(0))
+        assert rc == want, (n_out, chunk, rc, P.lib.pdssm_last_error())
+    d17 = _dims(P, L=4096, N=17)
+    assert P.lib.pdssm_scan_fwd_multi(ctypes.byref(d17), 128, 2, *args(1 << 20)) == -2
+    rc = P.lib.pdssm_fwd_wb_multi(ctypes.byref(d), 512, 2, A, A + big, A + 2 * big, A + 3 * big,
+                                  A + 4 * big, A + 5 * big, A + 6 * big, None, None, None, A + 7 * big,
+                                  A + 8 * big, A + 9 * big, 0, None)
+    assert rc == -2
+    rc = P.lib.pdssm_fwd_wb_multi(ctypes.byref(d), 128, 4, A, A + big, A + 2 * big, A + 3 * big,
+                                  A + 4 * big, A + 5 * big, A + 6 * big, None, None, None, A + 7 * big,
+                                  A + 8 * big, A + 9 * big, 0, None)
+    assert rc == -3
