@@ -1062,41 +1062,46 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
 // SE[k][i]: the source columns j (ascending) whose one sits in row i under
 // dictionary entry k, packed for the step loop:
 //   x  byte m (m < 4): 4 * (m-th source), the lane offset of its value
-//   y  byte m (m < 4): 1 if row i has an m-th source, else 0
 //   z  nibbles: sources 5 to 12;  w  nibbles: sources 13 to 16, count << 24
+// SW[k][i]: the weight of each of the first four slots as a float, 1 where
+// row i has an m-th source and 0 past its count (so a missing source costs a
+// multiply by zero instead of a branch or a conversion).
 // Thread tid < 16 K builds entry (k, i) = (tid / 16, tid % 16) from its
 // dictionary row drow (-1 past N).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void write_se(i4v* SE, int tid, const int (&drow)[16]) {
+__device__ __forceinline__ void write_se(i4v* SE, f4v* SW, int tid, const int (&drow)[16]) {
   const int iq = tid & 15;
-  unsigned bx = 0, by = 0, bz = 0, bw = 0;
+  unsigned bx = 0, bz = 0, bw = 0;
   int n = 0;
 #pragma unroll
   for (int jq = 0; jq < 16; ++jq) {
     const bool hit = drow[jq] == iq;
     bx |= (hit && n < 4) ? (unsigned)(4 * jq) << (8 * (n & 3)) : 0u;
-    by |= (hit && n < 4) ? 1u << (8 * (n & 3)) : 0u;
     bz |= (hit && n >= 4 && n < 12) ? (unsigned)jq << (4 * ((n - 4) & 7)) : 0u;
     bw |= (hit && n >= 12) ? (unsigned)jq << (4 * ((n - 12) & 3)) : 0u;
     n += hit ? 1 : 0;
   }
-  SE[tid] = i4v{(int)bx, (int)by, (int)bz, (int)(bw | ((unsigned)n << 24))};
+  SE[tid] = i4v{(int)bx, 0, (int)bz, (int)(bw | ((unsigned)n << 24))};
+  SW[tid] = f4v{n > 0 ? 1.f : 0.f, n > 1 ? 1.f : 0.f, n > 2 ? 1.f : 0.f, n > 3 ? 1.f : 0.f};
 }
 
-// h'_i = hn + sum over the sources j of row i (entry se) of the value vj of
-// lane j of this 16-lane group (byte offset lbase), gathered in ascending j;
-// absent sources are weighted by zero.  Rows with more than four sources take
-// a loop that the whole wave enters only when some lane needs it.
-__device__ __forceinline__ float se_gather(const i4v se, int vj, int lbase, float hn) {
-  const unsigned ax = (unsigned)se.x, ay = (unsigned)se.y;
+// h'_i = hn + sum over the sources j of row i (entries se, wt) of the value
+// vj of lane j of this 16-lane group, gathered in ascending j.  lb4 holds the
+// group's lane-0 byte offset in each of its four bytes (a multiple of 64, and
+// a slot offset is below 64, so one OR places all four addresses).  Rows
+// with more than four sources take a loop that the whole wave enters only
+// when some lane needs it.
+__device__ __forceinline__ float se_gather(const i4v se, const f4v wt, int vj, unsigned lb4, float hn) {
+  const unsigned ax = (unsigned)se.x | lb4;
   float gv[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
-    gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(lbase | (int)((ax >> (8 * m)) & 0xFFu), vj));
+    gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)__builtin_amdgcn_ubfe(ax, 8 * m, 8), vj));
 #pragma unroll
-  for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(gv[m], (float)((ay >> (8 * m)) & 0xFFu), hn);
+  for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(gv[m], wt[m], hn);
   const unsigned aw = (unsigned)se.w;
   if (__builtin_amdgcn_ballot_w64(aw >= (5u << 24))) {
+    const int lbase = (int)(lb4 & 0xFFu);
     const int deg = (int)(aw >> 24);
     const unsigned az = (unsigned)se.z;
     for (int m = 4; m < 16; ++m) {
@@ -1107,6 +1112,32 @@ __device__ __forceinline__ float se_gather(const i4v se, int vj, int lbase, floa
     }
   }
   return hn;
+}
+
+// k* of four steps at once (key r of each lane = score column i of step r;
+// keys past K hold the minimum): the row maximum, then the lowest column that
+// reaches it, each level applied to all four steps before the next so that
+// the DPP reads never wait on the instruction just before them.
+__device__ __forceinline__ void row_argmax4(const int (&key)[4], int i, int (&ks)[4]) {
+  int m[4], c[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = max(key[r], dpp_i<kDppXor1>(key[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = max(m[r], dpp_i<kDppXor2>(m[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = max(m[r], dpp_i<kDppHalfMirror>(m[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = max(m[r], dpp_i<kDppMirror>(m[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = key[r] == m[r] ? i : 0x7fffffff;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = min(c[r], dpp_i<kDppXor1>(c[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = min(c[r], dpp_i<kDppXor2>(c[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = min(c[r], dpp_i<kDppHalfMirror>(c[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ks[r] = min(c[r], dpp_i<kDppMirror>(c[r]));
 }
 
 // ---------------------------------------------------------------------------
@@ -1158,6 +1189,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
 
   const int i = lane & 15, g = lane >> 4;
   i4v* SE = (i4v*)(smem + p.off_SRC);
+  f4v* SW = (f4v*)(smem + p.off_SRC + K * 16 * 16);
 
   // ---- every global load of this chunk is issued before anything waits,
   // the L2-resident ones (dictionary, weights) first: loads retire in order,
@@ -1326,7 +1358,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     if (dc_on) DC[(tid / N) * p.DCS + tid % N] = i2v{dq, __float_as_int(cdq)};
   }
   // SE: the inverse dictionary rows (sources of each row)
-  if (src_on) write_se(SE, tid, drow);
+  if (src_on) write_se(SE, SW, tid, drow);
   float* Cs = (float*)(smem + p.off_C);            // NOUT > 1: row o of C at 16 o
   if (NOUT > 1 && tid < 16) {
 #pragma unroll
@@ -1343,6 +1375,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   float hl = 0.f, msc = 1.f;
   int midx = jj;
   const int lbase = (lane & ~15) << 2;             // byte offset of this group's lane 0
+  const unsigned lb4 = (unsigned)lbase * 0x01010101u;
   float* wrow = Dbuf + j * TS + tb + gam;          // w_t of this lane's row, step tb
   float* yrow = yloc + tb + gam;
   // steps of the last group of this wave: every group of the wave has at
@@ -1358,14 +1391,13 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     }
     // selections of this tile: D for this lane's row, k* for its group
     float Dr[4];
-    int ks[4];
+    int key[4], ks[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       Dr[r] = logistic(A[cu][0][r] + bdz);
-      const int key = i < K ? order_key(A[cu][1][r]) : (int)0x80000000;
-      const int m = row_max(key);
-      ks[r] = row_min(key == m ? i : 0x7fffffff);
+      key[r] = i < K ? order_key(A[cu][1][r]) : (int)0x80000000;
     }
+    row_argmax4(key, i, ks);
     const int nb = FULL ? 4 : nst - 4 * k;         // steps left in this group
     if (a.k_out && j == 0)
       for (int r = 0; r < 4 && r < nb; ++r) a.k_out[gbase + tb + 4 * k + r] = ks[r];
@@ -1377,6 +1409,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       const bool valid = FULL || r < nb;
       const int ksel = valid ? ks[r] : 0;
       const i4v se = SE[ksel * 16 + j];
+      const f4v wt = SW[ksel * 16 + j];
       const i2v e = DC[ksel * 16 + midx];
       const float dm = __int_as_float(
           __builtin_amdgcn_ds_bpermute(lbase + (midx << 2), __float_as_int(Dr[r])));
@@ -1384,7 +1417,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       float hn;
       if constexpr (FOLD) hn = A[cu][2][r];
       else hn = bu[(4 * k + r) & 15];
-      hn = se_gather(se, __float_as_int(Dr[r] * hl), lbase, hn);
+      hn = se_gather(se, wt, __float_as_int(Dr[r] * hl), lb4, hn);
       if (valid) {
         hl = hn;
         msc *= dm;
@@ -1519,14 +1552,16 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
     }
     __syncthreads();                               // Cs ready
     if (dc_on) DC[(tid / N) * 16 + tid % N] = i2v{dq, __float_as_int(Cs[dq])};
-    if (src_on) write_se((i4v*)(smem + p.off_SRC), tid, drow);
+    if (src_on) write_se((i4v*)(smem + p.off_SRC), (f4v*)(smem + p.off_SRC + K * 16 * 16), tid, drow);
   }
   __syncthreads();
   const i4v* SE = (const i4v*)(smem + p.off_SRC);
+  const f4v* SW = (const f4v*)(smem + p.off_SRC + K * 16 * 16);
 
   float hl = 0.f, msc = 1.f;
   int midx = jj;
   const int lbase = (lane & ~15) << 2;             // byte offset of this group's lane 0
+  const unsigned lb4 = (unsigned)lbase * 0x01010101u;
   float* wrow = Dbuf + j * TS + tb + gam;          // w_t of this lane's row, step tb
   float* yrow = yloc + tb + gam;
   const int wave_nst = max(min(wave * 4 * S + S, Tc) - wave * 4 * S, 0);
@@ -1555,7 +1590,7 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
         const i2v e = DC[kt * 16 + midx];
         nidx = e.x;
         cw = __int_as_float(e.y);
-        hn = se_gather(SE[kt * 16 + j], __float_as_int(dt * hl), lbase, bu[q]);
+        hn = se_gather(SE[kt * 16 + j], SW[kt * 16 + j], __float_as_int(dt * hl), lb4, bu[q]);
       }
       const float dm = __int_as_float(__builtin_amdgcn_ds_bpermute(lbase + (midx << 2), __float_as_int(dt)));
       if (valid) {

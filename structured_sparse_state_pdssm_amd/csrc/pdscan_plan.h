@@ -114,7 +114,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.off_yl = scan ? take(n_out * p.YS * 4) : 0;
   p.off_dict = scan ? 0 : take(K * N * 4);   // selection: P_idx gathers
   p.off_DC = scan ? take(K * p.DCS * 8) : 0;  // scan: (row, C[row]) pairs
-  p.off_SRC = sm ? take(K * 16 * 16) : 0;  // step-major: source columns of each row
+  p.off_SRC = sm ? take(K * 16 * 32) : 0;  // step-major: source columns of each row and their weights
   p.off_C = take((N > 16 * n_out ? N : 16 * n_out) * 4);   // step-major: row o of C at 16 o
   p.off_bd = take(N * 4);
   p.off_slot = take(kThreads * 4);
