@@ -1316,6 +1316,9 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   auto bu_off = [&](int q) {
     return (act && q < nst) ? (uint32_t)((tb + q) * N + j) * 4u : kNoLoad;
   };
+  // refills take no checks: a step past the group's own (another group's, or
+  // zero past the chunk) is never committed, and inactive rows are never read
+  const uint32_t bu_lane = (uint32_t)(tb * N + j) * 4u;
   float bu[FOLD ? 1 : 16];
   if constexpr (!FOLD) {
 #pragma unroll
@@ -1435,7 +1438,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     // refill this block's drive-term slots with the block four ahead
     if constexpr (!FOLD) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bu[(4 * k + r) & 15] = buf_f32(bur, bu_off(4 * k + 16 + r));
+      for (int r = 0; r < 4; ++r) bu[(4 * k + r) & 15] = buf_f32(bur, bu_lane + (uint32_t)((4 * k + 16 + r) * N * 4));
     }
     // local outputs of the four steps, summed over the group off the scan's
     // critical path
@@ -1455,6 +1458,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     else
       block(std::false_type{}, k);
   }
+  __syncthreads();                                 // the tables' bytes become the scratch of the steps below
   chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
 }
 
@@ -1516,6 +1520,9 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
     if constexpr (PMAP) return row_off(q);
     else return q < nst ? (uint32_t)(tb + q) * 4u : kNoLoad;
   };
+  // refills take no checks: a step past the group's own (another group's, or
+  // zero past the chunk) is never committed, and inactive rows are never read
+  const uint32_t row_lane = (uint32_t)(tb * N + j) * 4u, map_lane = PMAP ? row_lane : (uint32_t)tb * 4u;
   int mi[16];                                      // P_in entry, or k*_t
   float dv[16], bu[16];
 #pragma unroll
@@ -1611,10 +1618,10 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
     // refill this block's slots with the block four ahead
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int q = 4 * k + 16 + r;
-      mi[(4 * k + r) & 15] = buf_i32(mr, map_off(q));
-      dv[(4 * k + r) & 15] = buf_f32(dr, row_off(q));
-      bu[(4 * k + r) & 15] = buf_f32(bur, row_off(q));
+      const uint32_t q = 4 * k + 16 + r;
+      mi[(4 * k + r) & 15] = buf_i32(mr, map_lane + q * (PMAP ? N * 4 : 4));
+      dv[(4 * k + r) & 15] = buf_f32(dr, row_lane + q * N * 4);
+      bu[(4 * k + r) & 15] = buf_f32(bur, row_lane + q * N * 4);
     }
 #pragma unroll
     for (int o = 0; o < NOUT; ++o)
@@ -1632,6 +1639,7 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
     else
       block(std::false_type{}, k);
   }
+  __syncthreads();                                 // the tables' bytes become the scratch of the steps below
   chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
 }
 

@@ -110,23 +110,41 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.n_out = n_out;
   p.YS = align_up(T + p.G, 4);
   p.off_D = scan ? take(n_out * N * p.TS * 4) : 0;
-  p.off_k = scan ? take(align_up(T, 4) * 4) : 0;
+  p.off_k = (scan && !sm) ? take(align_up(T, 4) * 4) : 0;   // the step-major kernels keep k* in registers
   p.off_yl = scan ? take(n_out * p.YS * 4) : 0;
   p.off_dict = scan ? 0 : take(K * N * 4);   // selection: P_idx gathers
-  p.off_DC = scan ? take(K * p.DCS * 8) : 0;  // scan: (row, C[row]) pairs
-  p.off_SRC = sm ? take(K * 16 * 32) : 0;  // step-major: source columns of each row and their weights
   p.off_C = take((N > 16 * n_out ? N : 16 * n_out) * 4);   // step-major: row o of C at 16 o
   p.off_bd = take(N * 4);
   p.off_slot = take(kThreads * 4);
-  p.off_sIdx = scan ? take(p.G * N * 4) : 0;
-  p.off_sSc = scan ? take(p.G * N * 4) : 0;
-  p.off_sB = scan ? take(p.G * N * 4) : 0;
-  p.off_pIdx = scan ? take(p.G * N * 4) : 0;
-  p.off_pSc = scan ? take(p.G * N * 4) : 0;
-  p.off_pB = scan ? take(p.G * N * 4) : 0;
+  const int gn = p.G * N * 4;                      // one [G][N] scratch array of the steps after phase A
+  if (sm) {
+    // The dictionary tables and the W_b fragments are read in phase A only;
+    // the combine and look-back scratch is written only after it (a barrier
+    // separates the two), so both share one region.
+    const int tabs = K * 16 * 8 + K * 16 * 32 + (p.fold_bu ? kWbFrags * 64 * 16 : 0);
+    const int u0 = take(tabs > 6 * gn ? tabs : 6 * gn);
+    p.off_DC = u0;                                 // (row, C[row]) pairs
+    p.off_SRC = u0 + K * 16 * 8;                   // source columns of each row and their weights
+    p.off_WB = p.fold_bu ? p.off_SRC + K * 16 * 32 : 0;   // W_b MFMA fragments, one 16-byte slot per lane
+    p.off_sIdx = u0;
+    p.off_sSc = u0 + gn;
+    p.off_sB = u0 + 2 * gn;
+    p.off_pIdx = u0 + 3 * gn;
+    p.off_pSc = u0 + 4 * gn;
+    p.off_pB = u0 + 5 * gn;
+  } else {
+    p.off_DC = scan ? take(K * p.DCS * 8) : 0;    // scan: (row, C[row]) pairs
+    p.off_SRC = 0;
+    p.off_WB = 0;
+    p.off_sIdx = scan ? take(gn) : 0;
+    p.off_sSc = scan ? take(gn) : 0;
+    p.off_sB = scan ? take(gn) : 0;
+    p.off_pIdx = scan ? take(gn) : 0;
+    p.off_pSc = scan ? take(gn) : 0;
+    p.off_pB = scan ? take(gn) : 0;
+  }
   p.off_H = take(64 * 4);
   p.off_tmp = take(64 * 4);
-  p.off_WB = p.fold_bu ? take(kWbFrags * 64 * 16) : 0;   // W_b MFMA fragments, one 16-byte slot per lane
   p.off_misc = take(16);
   p.lds_bytes = off;
 
