@@ -407,7 +407,7 @@ int pdssm_scan_states(const pdssm_dims* dims, int32_t chunk, const int32_t* k_st
   int rc = check_dims(dims, chunk);
   if (rc) return rc;
   Plan p;
-  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk))) return rc;
+  if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk, 0, 2))) return rc;
   if (workspace_bytes < p.ws_bytes)
     return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 p.ws_bytes);

@@ -1478,7 +1478,7 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
 // summary and the output weights w_t = C Phi_t, exactly as the fused
 // step-major pass does.  Everything after phase A is chunk_tail.
 // ---------------------------------------------------------------------------
-template <int PMAP, int NOUT>
+template <int PMAP, int NOUT, int STATES>
 __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) {
   constexpr int SMAX = 32;                         // steps per group
   const Plan& p = a.p;
@@ -1641,12 +1641,57 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
   }
   __syncthreads();                                 // the tables' bytes become the scratch of the steps below
   chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);
+  if constexpr (STATES && !PMAP && NOUT == 1) {
+    {
+      // The state after every step as well: each group runs its sub-chunk
+      // again from its true entering state (left in the slots by the steps
+      // above; the plan keeps the tables for this), writing h_t directly.
+      const float* slots = (const float*)(smem + p.off_slot);
+      float hj = act ? slots[gam * 16 + j] : 0.f;
+      const rsrc_t hr = make_rsrc(a.H_all + gbase * N, rows);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        mi[q] = buf_i32(mr, map_off(q));
+        dv[q] = buf_f32(dr, row_off(q));
+        bu[q] = buf_f32(bur, row_off(q));
+      }
+      auto rblock = [&](auto full_tag, const int k) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int nb = FULL ? 4 : nst - 4 * k;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool valid = FULL || r < nb;
+          const int q = (4 * k + r) & 15, kt = mi[q];
+          const float hn = se_gather(SE[kt * 16 + j], SW[kt * 16 + j], __float_as_int(dv[q] * hj), lb4, bu[q]);
+          if (valid) hj = hn;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hj), hr,
+                                                (valid && act) ? row_lane + (uint32_t)((4 * k + r) * N * 4) : kNoLoad,
+                                                0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t q = 4 * k + 16 + r;
+          mi[(4 * k + r) & 15] = buf_i32(mr, map_lane + q * 4);
+          dv[(4 * k + r) & 15] = buf_f32(dr, row_lane + q * N * 4);
+          bu[(4 * k + r) & 15] = buf_f32(bur, row_lane + q * N * 4);
+        }
+      };
+#pragma unroll
+      for (int k = 0; k < SMAX / 4; ++k) {
+        if (k >= nblk) break;
+        if (4 * k + 4 <= nst_last)
+          rblock(std::true_type{}, k);
+        else
+          rblock(std::false_type{}, k);
+      }
+    }
+  }
 }
 
-template <int PMAP, int NOUT = 1>
+template <int PMAP, int NOUT = 1, int STATES = 0>
 __global__ __launch_bounds__(kThreads, 3) void pdssm_step16_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  step16_body<PMAP, NOUT>(a, smem);
+  step16_body<PMAP, NOUT, STATES>(a, smem);
 }
 
 // (several rows of C need more registers: two waves per SIMD then)

@@ -23,7 +23,9 @@ void launch_clear(const Args& a, hipStream_t st) {
 hipError_t launch_scan(const Args& a, hipStream_t st) {
   launch_clear(a, st);
   if (a.p.step16) {
-    if (a.p.n_out > 1)
+    if (a.H_all)
+      hipLaunchKernelGGL((pdssm_step16_kernel<0, 1, 1>), dim3(a.p.tasks), dim3(kThreads), a.p.lds_bytes, st, a);
+    else if (a.p.n_out > 1)
       hipLaunchKernelGGL((pdssm_step16_kernel<0, kMaxOut>), dim3(a.p.tasks), dim3(kThreads), a.p.lds_bytes, st, a);
     else if (a.P_in)
       hipLaunchKernelGGL(pdssm_step16_kernel<1>, dim3(a.p.tasks), dim3(kThreads), a.p.lds_bytes, st, a);

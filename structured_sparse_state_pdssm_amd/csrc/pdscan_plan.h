@@ -39,7 +39,7 @@ struct Plan {
   int mma_bf16;  // score GEMM on bf16 MFMA (else fp32 MFMA)
   int fused16;   // fused pass with step-major MFMA tiles (N, K <= 16; see below)
   int fold_bu;   // fused16: Bu = W_b u from a third MFMA tile instead of an input
-  int step16;    // scan alone with the step-major layout (N <= 16, no per-step states)
+  int step16;    // scan alone with the step-major layout (N <= 16); 2: also writes every state
   int n_out;     // outputs per head, rows of C (> 1: step-major paths only)
   int YS;        // stride of the per-output local-output rows
   int tasks;     // workgroups
@@ -76,7 +76,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.fold_bu = (p.fused16 && fold_bu) ? 1 : 0;
   // the scan alone on the same layout: maps streamed per step (at most 32
   // steps per group, as above)
-  p.step16 = (mode == kModeScan && step16 && N <= 16 && K <= 16 && (chunk < L ? chunk : L) <= 512) ? 1 : 0;
+  p.step16 = (mode == kModeScan && step16 && N <= 16 && K <= 16 && (chunk < L ? chunk : L) <= 512) ? step16 : 0;
   const bool sm = p.fused16 || p.step16;
   p.NP = sm ? 16 : next_pow2(N);
   p.G = kThreads / p.NP;
@@ -118,20 +118,23 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.off_slot = take(kThreads * 4);
   const int gn = p.G * N * 4;                      // one [G][N] scratch array of the steps after phase A
   if (sm) {
-    // The dictionary tables and the W_b fragments are read in phase A only;
-    // the combine and look-back scratch is written only after it (a barrier
-    // separates the two), so both share one region.
+    // The dictionary tables and the W_b fragments are read in phase A only
+    // (and, when every state is written, again after the carries are known);
+    // the combine and look-back scratch is written only after phase A (a
+    // barrier separates the two), so without the states replay both share
+    // one region.
     const int tabs = K * 16 * 8 + K * 16 * 32 + (p.fold_bu ? kWbFrags * 64 * 16 : 0);
-    const int u0 = take(tabs > 6 * gn ? tabs : 6 * gn);
+    const int u0 = take(p.step16 == 2 ? tabs + 6 * gn : (tabs > 6 * gn ? tabs : 6 * gn));
+    const int s0 = p.step16 == 2 ? u0 + tabs : u0;
     p.off_DC = u0;                                 // (row, C[row]) pairs
     p.off_SRC = u0 + K * 16 * 8;                   // source columns of each row and their weights
     p.off_WB = p.fold_bu ? p.off_SRC + K * 16 * 32 : 0;   // W_b MFMA fragments, one 16-byte slot per lane
-    p.off_sIdx = u0;
-    p.off_sSc = u0 + gn;
-    p.off_sB = u0 + 2 * gn;
-    p.off_pIdx = u0 + 3 * gn;
-    p.off_pSc = u0 + 4 * gn;
-    p.off_pB = u0 + 5 * gn;
+    p.off_sIdx = s0;
+    p.off_sSc = s0 + gn;
+    p.off_sB = s0 + 2 * gn;
+    p.off_pIdx = s0 + 3 * gn;
+    p.off_pSc = s0 + 4 * gn;
+    p.off_pB = s0 + 5 * gn;
   } else {
     p.off_DC = scan ? take(K * p.DCS * 8) : 0;    // scan: (row, C[row]) pairs
     p.off_SRC = 0;
