@@ -177,7 +177,7 @@ def _is_kernel(name, which):
     if which == "sens":
         return "pdssm_sens_kernel" in name
     if which == "soft":
-        return "pdssm_soft_kernel" in name
+        return "pdssm_soft_kernel" in name or "pdssm_step16_kernel<1" in name
     if which == "scan":
         return "pdssm_step16_kernel" in name or ("pdssm_kernel<1," in name)
     if which == "select":
@@ -195,15 +195,20 @@ def pmc_summary(fetch_dir, write_dir, workload, which="fwd"):
     for counter, d, probe_bytes in (("FETCH_SIZE", fetch_dir, COPY_PROBE_BYTES),
                                     ("WRITE_SIZE", write_dir, COPY_PROBE_BYTES)):
         rows = _pmc_rows(d, counter)
-        kern = [float(r["Counter_Value"]) for r in rows if _is_kernel(r["Kernel_Name"], which)]
+        # per kernel of the pass, the mean over its dispatches; a call that
+        # launches several (the soft path: selection, then scan) sums them
+        per = {}
+        for r in rows:
+            if _is_kernel(r["Kernel_Name"], which):
+                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         probe = [float(r["Counter_Value"]) for r in rows if "neg" in r["Kernel_Name"]]
-        if not kern or not probe:
+        if not per or not probe:
             raise SystemExit(f"{counter}: no {which} kernel or copy-probe dispatches under {d}")
-        names = sorted({r["Kernel_Name"] for r in rows if _is_kernel(r["Kernel_Name"], which)})
+        kib = sum(mean(v) for v in per.values())
         scale = probe_bytes / (mean(probe) * 1024.0)
-        out[counter] = {"kernel_kib": mean(kern), "probe_kib": mean(probe),
-                        "scale": scale, "bytes": mean(kern) * 1024.0 * scale,
-                        "dispatches": len(kern), "kernels": names}
+        out[counter] = {"kernel_kib": kib, "probe_kib": mean(probe),
+                        "scale": scale, "bytes": kib * 1024.0 * scale,
+                        "dispatches": sum(len(v) for v in per.values()), "kernels": sorted(per)}
     total = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
     rec = {"workload": workload, "pass": which, "kernel_hash": kernel_hash(which),
            "hbm_bytes_per_launch": round(total), "counters": out,
