@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from pdssm_inputs import dense_dictionary, generate, get_config
-from tests._gpu import assert_within, host, lib, proj_dev, to_dev
+from tests._gpu import assert_within, host, lib, proj_dev, to_dev, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -142,3 +142,30 @@ def test_soft_select_deterministic():
     a, b = _gpu_soft(inp, M), _gpu_soft(inp, M)
     for n in ("M_t", "P_idx", "D"):
         assert np.array_equal(host(a[n]), host(b[n])), n
+
+
+@pytest.mark.slow
+def test_soft_full_impulse_sampled_heads():
+    """Full impulse shape in the bench's configuration (chunk 512): the whole
+    soft forward on the GPU, two heads compared with the oracle over all
+    131072 steps (selection element by element, then the scan on the GPU's
+    own maps)."""
+    torch = torch_mod()
+    P = lib()
+    inp = generate(get_config("impulse"))
+    c = inp.cfg
+    M = dense_dictionary(c.H, c.K, c.N, c.seed)
+    print("[gpu] soft forward impulse full size", flush=True)
+    out = _gpu_soft(inp, M)
+    y, hL = P.pdssm_scan_fwd_pidx(out["P_idx"], out["D"], to_dev(inp.Bu), to_dev(inp.C), to_dev(inp.h0),
+                                  chunk=c.chunk)
+    torch.cuda.synchronize()
+    for h in (0, 17):
+        sl = slice(h, h + 1)
+        ref = oracle.soft_select(inp.u[:, sl], inp.W_sel[sl], M[sl], inp.W_d[sl], inp.b_d[sl])
+        got = {k: out[k][:, sl] for k in ("M_t", "P_idx", "D")}
+        pidx = _check_selection(got, ref, f"head {h}")
+        yr, hr = oracle.scan_pidx(pidx, host(out["D"][:, sl]).astype(np.float64), inp.Bu[:, sl], inp.C[sl],
+                                  inp.h0[:, sl])
+        assert_within(host(y[:, sl]), yr, f"head {h} y")
+        assert_within(host(hL[:, sl]), hr, f"head {h} h_L")
