@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void pdssm_soft_kernel(SoftArgs a) {
       wd[m] = soft_load4(zr, c16 < N ? (uint32_t)(c16 * d + 16 * m + 4 * g) : kNoLoad, bf);
     }
   }
-  float mb[kSoftMaxN][kSoftMaxK / 4];
+  float mb[kSoftMaxN][kSoftMaxK / 4];             // dictionary fragments: matrix g + 4 kb, row i, column c16
   {
     const rsrc_t mr = make_rsrc(a.M + (size_t)h * K * N * N, (uint32_t)(K * N * N * 4));
 #pragma unroll
@@ -152,8 +152,9 @@ __global__ __launch_bounds__(kThreads) void pdssm_soft_kernel(SoftArgs a) {
       }
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
+      const float inv = 1.f / sum;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = al[r] / sum;
+      for (int r = 0; r < 4; ++r) al[r] *= inv;
     }
 
     // mixture, row by row: lane (g, c16) gets M_t[t0 + c16][i][4 g + r]; the
@@ -162,6 +163,8 @@ __global__ __launch_bounds__(kThreads) void pdssm_soft_kernel(SoftArgs a) {
     const uint32_t rowo = (uint32_t)t * N;         // element offset of step t's first row/entry
     f4v best = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     int bi[4] = {0, 0, 0, 0};
+    uint32_t ob = (rowo * N + 4 * g) * 4;          // byte offset of M_t[t][i][4 g], row i = 0
+    const uint32_t ostep = (uint32_t)N * 4;
 #pragma unroll
     for (int i = 0; i < kSoftMaxN; ++i) {
       if (i < N) {                                 // a guard, not an exit: every index stays constant
@@ -175,16 +178,16 @@ __global__ __launch_bounds__(kThreads) void pdssm_soft_kernel(SoftArgs a) {
             best[r] = acc[r];
             bi[r] = i;
           }
-        const uint32_t o = (rowo + i) * N + 4 * g;  // M_t element [t][i][4 g]
+        const uint32_t o = ob / 4;                  // M_t element [t][i][4 g]
         if (vec) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, acc), mtr,
-                                                 4 * g < N ? o * 4 : kNoLoad, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, acc), mtr, 4 * g < N ? ob : kNoLoad, 0, 0);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), mtr,
                                                   4 * g + r < N ? (o + r) * 4 : kNoLoad, 0, 0);
         }
+        ob += ostep;
       }
     }
     f4v dv;
