@@ -259,6 +259,11 @@ def test_argmax_ties_on_gpu(bf16, d):
     dict(B=3, H=2, L=129, N=12, K=7, d=40, chunk=128),
     dict(B=1, H=1, L=1000, N=64, K=32, d=128, chunk=64),
     dict(B=2, H=2, L=300, N=33, K=2, d=256, chunk=100),
+    # the largest shapes the library accepts: K + N = 128, d = 8192 (fp32 and
+    # the bf16 deep selection path)
+    dict(B=1, H=2, L=150, N=64, K=64, d=64, chunk=64),
+    dict(B=1, H=1, L=40, N=16, K=16, d=8192, chunk=16),
+    dict(B=1, H=1, L=64, N=64, K=64, d=8192, chunk=32, dtype="bf16"),
 ])
 def test_edge_shapes(shape):
     chunk = shape.pop("chunk")
