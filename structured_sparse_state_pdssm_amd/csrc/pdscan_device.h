@@ -891,7 +891,7 @@ template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT>
 __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   const Plan& p = a.p;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = p.N, K = p.K, S = p.S, T = p.chunk, TS = p.TS, G = p.G;
+  const int N = p.N, K = p.K, S = p.S, T = p.chunk, TS = p.TS;
   // NPT != 0: compile-time group width equal to N (every lane owns a row)
   const int NP = NPT ? NPT : p.NP;
   const int BH = p.B * p.H;
@@ -903,19 +903,8 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   i2v* DC = (i2v*)(smem + p.off_DC);
   float* Cs = (float*)(smem + p.off_C);
   float* slots = (float*)(smem + p.off_slot);
-  int* sIdx = (int*)(smem + p.off_sIdx);
-  float* sSc = (float*)(smem + p.off_sSc);
-  float* sB = (float*)(smem + p.off_sB);
-  int* pIdx = (int*)(smem + p.off_pIdx);
-  float* pSc = (float*)(smem + p.off_pSc);
-  float* pB = (float*)(smem + p.off_pB);
-  float* Hs = (float*)(smem + p.off_H);
-  float* tmp = (float*)(smem + p.off_tmp);
   int* misc = (int*)(smem + p.off_misc);
-
   uint32_t* hdr = (uint32_t*)a.ws;
-  uint64_t* agg = (uint64_t*)(a.ws + p.ws_agg);
-  uint64_t* inc = (uint64_t*)(a.ws + p.ws_inc);
 
   // ---- task: chunk-major tickets so that predecessors always started first
   int task;
@@ -1539,7 +1528,6 @@ __device__ __forceinline__ void step16_body(const Args& a, unsigned char* smem) 
 #pragma unroll
     for (int o = 0; o < NOUT; ++o) cjo[o] = buf_f32(cr, (act && o < P) ? (uint32_t)(o * N + j) * 4u : kNoLoad);
   }
-  const float cj = cjo[0];
   if (tid < 16) {
 #pragma unroll
     for (int o = 0; o < NOUT; ++o) Cs[o * 16 + j] = cjo[o];

@@ -65,7 +65,6 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
   const int c0 = c * T;
   const int Tc = min(T, q.L - c0);
   const size_t gbase = (size_t)s * q.L + c0;
-  const int ND = N * d;
 
   // ---- staging: every load of the task is issued before the first wait
   // (buffer loads; a lane with nothing to load reads zero through an
