@@ -84,7 +84,10 @@ def select(u, W_sel, W_d, b_d, u_shared=False):
 
     Returns (k_star int32 [B,H,L], D fp64 [B,H,L,N], s fp64 [B,H,L,K])."""
     s = scores(u, W_sel, u_shared)
-    k_star = np.argmax(s, axis=-1).astype(np.int32)      # first maximum wins
+    # the decision is taken on the scores rounded to fp32: the pages fix no
+    # precision for the scores, and fp32 is the one the kernel decides in;
+    # the first maximum wins
+    k_star = np.argmax(s.astype(np.float32), axis=-1).astype(np.int32)
     z = scores(u, W_d, u_shared) + np.asarray(b_d, dtype=F64)[None, :, None, :]
     return k_star, sigmoid(z), s
 

@@ -369,6 +369,22 @@ def test_argmax_ties_lowest_index():
     assert (k_star == k1).all()
 
 
+def test_argmax_decided_on_fp32_scores():
+    """Two scores that differ in fp64 by less than half an fp32 ulp round to
+    the same fp32 value: the decision, taken in fp32, is a tie and goes to the
+    lower index (an fp64 argmax would take the higher one)."""
+    H, K, d, L = 1, 3, 2, 1
+    u = np.zeros((1, H, L, d))
+    u[..., 0] = 1.0
+    u[..., 1] = 2.0 ** -30
+    W = np.zeros((H, K, d))
+    W[0, 0] = [1.0, 0.0]                 # score 1
+    W[0, 2] = [1.0, 1.0]                 # score 1 + 2^-30: distinct in fp64, equal in fp32
+    k_star, _, s = oracle.select(u, W, np.zeros((H, 1, d)), np.zeros((H, 1)))
+    assert s[0, 0, 0, 2] > s[0, 0, 0, 0] and np.float32(s[0, 0, 0, 2]) == np.float32(s[0, 0, 0, 0])
+    assert k_star[0, 0, 0] == 0
+
+
 # --------------------------------------------------------------------------
 # F10: logistic identities
 # --------------------------------------------------------------------------
