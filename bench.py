@@ -161,6 +161,34 @@ def copy_probe(torch):
     print(f"[bench] copy probe: 3 x neg over {COPY_PROBE_BYTES} B", file=sys.stderr, flush=True)
 
 
+def add_box(rec, torch, np):
+    """The box the line was measured on: device properties as the runtime
+    reports them, and a same-box copy bandwidth (1 GiB read + 1 GiB written
+    by a device-to-device copy, median of 10 event-timed reps), against which
+    an HBM-bound line's achieved bandwidth is also given."""
+    prop = torch.cuda.get_device_properties(0)
+    n = COPY_PROBE_BYTES // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    del src, dst
+    copy_gbps = 2 * COPY_PROBE_BYTES / float(np.median(ts)) / 1e9
+    rec["box"] = {"device": prop.name, "arch": getattr(prop, "gcnArchName", ""),
+                  "compute_units": prop.multi_processor_count,
+                  "memory_GB": round(prop.total_memory / 1e9, 1), "copy_GBps": round(copy_gbps, 1)}
+    roof = rec.get("roofline", {})
+    if roof.get("unit") == "GB/s":
+        roof["frac_of_copy"] = round(roof["achieved"] / copy_gbps, 4)
+
+
 def _pmc_rows(d, counter):
     import csv
     import glob
@@ -318,6 +346,7 @@ def bench_bwd(args, torch, np, P):
         "timing": timing,
         "kernel_hash": kernel_hash("bwd"),
     }
+    add_box(rec, torch, np)
     if args.copy_probe:
         copy_probe(torch)
     if not args.no_cpu_baseline:
@@ -402,6 +431,7 @@ def bench_sens(args, torch, np, P):
         "timing": timing,
         "kernel_hash": kernel_hash("sens"),
     }
+    add_box(rec, torch, np)
     if args.copy_probe:
         copy_probe(torch)
     if not args.no_cpu_baseline:
@@ -509,6 +539,7 @@ def bench_soft(args, torch, np, P):
         "soft_over_hard_time": round(launch_s * 1e6 / hard_us, 3),
         "kernel_hash": kernel_hash("soft"),
     }
+    add_box(rec, torch, np)
     if args.copy_probe:
         copy_probe(torch)
     if not args.no_cpu_baseline:
@@ -603,6 +634,7 @@ def bench_part(args, torch, np, P):
         "timing": timing,
         "kernel_hash": kernel_hash(args.which),
     }
+    add_box(rec, torch, np)
     if args.copy_probe:
         copy_probe(torch)
     if not args.no_cpu_baseline:
@@ -744,6 +776,7 @@ def main():
         "timing": timing,
         "kernel_hash": kernel_hash(args.which),
     }
+    add_box(rec, torch, np)
     if args.copy_probe:
         copy_probe(torch)
     if not args.no_cpu_baseline:
