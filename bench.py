@@ -14,7 +14,8 @@ sensitivity dy_t/du_0 (pdssm_impulse_sens); ``--pass soft`` times the
 soft-selection comparison path (pdssm_soft_select + pdssm_scan_fwd_pidx) with
 the hard-selection forward pass beside it; ``--pass scan`` and ``--pass
 select`` time the two stages of the forward pass alone (pdssm_scan_fwd given
-the selections, pdssm_select).
+the selections, pdssm_select); ``--pass multi [--n-out P]`` times
+pdssm_fwd_wb_multi (the folded pass with P rows of C per head).
 ``timing`` in the JSON line gives the median, p10 and p90 of the per-call
 event durations with warm caches ("hot") and with a 1 GiB fill before each
 call ("cold").
@@ -56,10 +57,11 @@ SOURCES["soft"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_soft_plan.h", "pd
 SOURCES["sens"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_sens_plan.h", "pdscan_sens.h",
                    "pdscan_launch_sens.hip")
 SOURCES["scan"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_scan.hip")
+SOURCES["multi"] = SOURCES["fwd"]
 SOURCES["select"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_select.hip")
 # stem of the committed counter summary of each pass
 TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd", "fold": "pdssm_fold", "sens": "pdssm_sens",
-                "soft": "pdssm_soft", "scan": "pdssm_scan", "select": "pdssm_select"}
+                "soft": "pdssm_soft", "scan": "pdssm_scan", "select": "pdssm_select", "multi": "pdssm_multi"}
 COLD_FILL_BYTES = 1 << 30       # written before each cold-cache rep (beyond L2 and MALL)
 
 
@@ -657,6 +659,93 @@ def bench_part(args, torch, np, P):
     print(json.dumps(rec), flush=True)
 
 
+def bench_multi(args, torch, np, P):
+    """Time pdssm_fwd_wb_multi: the folded forward pass with n_out rows of C
+    per head (the layer call: u in, y [B,H,L,n_out] out), at the longest
+    chunk its on-chip output rows allow unless --chunk is given."""
+    from pdssm_inputs import generate, get_config
+    cfg = get_config(args.workload)
+    P_out = args.n_out
+    chunk = args.chunk or (256 if P_out <= 2 else 128)
+    t0 = time.time()
+    inp = generate(cfg)
+    print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    bf = cfg.dtype == "bf16"
+    pdt = torch.bfloat16 if bf else torch.float32
+
+    def dev(x, dt=None):
+        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+
+    B, H, L, N, K, d = cfg.B, cfg.H, cfg.L, cfg.N, cfg.K, cfg.d
+    rng = np.random.default_rng(100 + P_out)
+    Cm = (rng.standard_normal((H, P_out, N)) / np.sqrt(N)).astype(np.float32)
+    u, W_sel, W_d, W_b = dev(inp.u, pdt), dev(inp.W_sel, pdt), dev(inp.W_d, pdt), dev(inp.W_b, pdt)
+    b_d, dic, C, h0 = dev(inp.b_d), dev(inp.dict_idx), dev(Cm), dev(inp.h0)
+    dims = P.make_dims(B, H, L, N, K, d, cfg.u_shared, bf)
+    ws = torch.empty(P.fwd_workspace_bytes(dims, chunk), dtype=torch.uint8, device="cuda")
+    out = {"y": torch.empty((B, H, L, P_out), device="cuda"), "h_L": torch.empty((B, H, N), device="cuda")}
+
+    def step():
+        P.pdssm_fwd_wb_multi(u, W_sel, dic, W_d, b_d, W_b, C, h0, chunk=chunk, workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    wall, hot, timing = time_calls(torch, np, step, args.steps, stream)
+    if P.workspace_error_flag(ws):
+        raise RuntimeError("look-back wait gave up during timing")
+    launch_s = float(np.mean(hot)) / 1e6
+    ms_step = wall * 1e3 / args.steps
+    es = 2 if bf else 4
+    steps = B * H * L
+    alg = (B * (1 if cfg.u_shared else H) * L * d * es + steps * 4 * P_out + 2 * B * H * N * 4
+           + H * K * d * es + 2 * H * N * d * es + H * N * 4 + H * K * N * 4 + H * P_out * N * 4)
+    flops = 2 * (K + 2 * N) * d * steps
+    peak_mma = PEAK_BF16_TFLOPS if (bf and d >= 128) else PEAK_FP32_TFLOPS
+    if flops / (peak_mma * 1e12) > alg / (PEAK_HBM_GBPS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(flops / launch_s / 1e12, 2), "peak": peak_mma,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(alg / launch_s / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic_from_profile(cfg.name, "multi")
+    roof["algorithmic_bytes"] = alg
+    roof["launch_us"] = round(launch_s * 1e6, 2)
+    rec = {
+        "metric": f"state-updates/sec (B·H·L·N) PD-SSM fwd select+scan with Bu = W_b u folded and {P_out} "
+                  "outputs per head (C [H,n_out,N])",
+        "value": cfg.state_updates / (ms_step / 1e3),
+        "unit": "state-updates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} multi-output: B={B} H={H} L={L} N={N} K={K} d={d} n_out={P_out} "
+                               f"chunk={chunk}",
+                   "B": B, "H": H, "L": L, "N": N, "K": K, "d_in": d, "n_out": P_out, "chunk": chunk},
+        "roofline": roof,
+        "timing": timing,
+        "kernel_hash": kernel_hash("multi"),
+    }
+    add_box(rec, torch, np)
+    if args.copy_probe:
+        copy_probe(torch)
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        oracle.forward_wb_multi(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, Cm, inp.h0,
+                                cfg.u_shared)
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": steps * N / dt, "unit": "state-updates/s", "cores": cores,
+                               "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": f"whole {cfg.name} workload ({B}x{H}x{L} steps, N={N}, n_out={P_out}), "
+                                         "one run"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -665,12 +754,14 @@ def main():
     ap.add_argument("--workload", default="impulse")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fold", "sens", "soft", "scan", "select"),
-                    default="fwd",
+    ap.add_argument("--pass", dest="which",
+                    choices=("fwd", "bwd", "fold", "sens", "soft", "scan", "select", "multi"), default="fwd",
                     help="forward pass (default), the gradient pass through the scan, the "
                          "forward pass with the drive Bu = W_b u folded into the selection GEMM, "
                          "the impulse sensitivity dy_t/du_0, the soft-selection comparison path, "
-                         "or one stage of the forward pass alone (scan, select)")
+                         "one stage of the forward pass alone (scan, select), or the folded pass "
+                         "with several outputs per head (multi)")
+    ap.add_argument("--n-out", type=int, default=2, help="rows of C per head for --pass multi (1..4)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain copy kernel of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -700,6 +791,8 @@ def main():
         return bench_soft(args, torch, np, P)
     if args.which in ("scan", "select"):
         return bench_part(args, torch, np, P)
+    if args.which == "multi":
+        return bench_multi(args, torch, np, P)
     cfg = get_config(args.workload)
     chunk = args.chunk or cfg.chunk
     t0 = time.time()

@@ -1682,9 +1682,9 @@ __global__ __launch_bounds__(kThreads, 3) void pdssm_step16_kernel(Args a) {
   step16_body<PMAP, NOUT, STATES>(a, smem);
 }
 
-// (several rows of C need more registers: two waves per SIMD then)
+// (more than two rows of C need more registers: two waves per SIMD then)
 template <int IN_BF16, int MMA_BF16, int KCH, int SPLIT, int FOLD = 0, int NOUT = 1>
-__global__ __launch_bounds__(kThreads, NOUT > 1 ? 2 : 3) void pdssm_fused16_kernel(Args a) {
+__global__ __launch_bounds__(kThreads, NOUT > 2 ? 2 : 3) void pdssm_fused16_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   fused16_body<IN_BF16, MMA_BF16, KCH, SPLIT, FOLD, NOUT>(a, smem);
 }

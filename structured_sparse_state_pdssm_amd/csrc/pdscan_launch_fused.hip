@@ -26,6 +26,18 @@ hipError_t launch_fused(const Args& a, hipStream_t st) {
   const Plan& p = a.p;
   const int path = sel_path(p), npt = npt_of(p);
   launch_clear(a, st);
+  if (p.fused16 && p.fold_bu && p.n_out == 2) {
+    const dim3 grid(p.tasks), block(kThreads);
+    if (p.in_bf16)
+      hipLaunchKernelGGL((pdssm_fused16_kernel<1, 1, 4, 0, 1, 2>), grid, block, p.lds_bytes, st, a);
+    else if (p.d == 64)
+      hipLaunchKernelGGL((pdssm_fused16_kernel<0, 0, 4, 1, 1, 2>), grid, block, p.lds_bytes, st, a);
+    else if (p.d == 32)
+      hipLaunchKernelGGL((pdssm_fused16_kernel<0, 0, 2, 1, 1, 2>), grid, block, p.lds_bytes, st, a);
+    else
+      hipLaunchKernelGGL((pdssm_fused16_kernel<0, 0, 1, 0, 1, 2>), grid, block, p.lds_bytes, st, a);
+    return hipGetLastError();
+  }
   if (p.fused16 && p.fold_bu && p.n_out > 1) {
     const dim3 grid(p.tasks), block(kThreads);
     if (p.in_bf16)
