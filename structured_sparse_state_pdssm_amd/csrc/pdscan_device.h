@@ -320,10 +320,13 @@ constexpr int kChanBlock = MMA_BF16 ? 32 : 16;
 
 // Epilogue of one tile: argmax over score columns, logistic of the
 // pre-activations, stores.  rows >= rlim are not stored.
+// Column of tile t: 16 t + i when kt < 0 (scores then pre-activations,
+// contiguous); with kt >= 0 the first kt tiles hold the scores and tile
+// t >= kt holds pre-activation 16 (t - kt) + i, i.e. column K + 16 (t - kt) + i.
 template <int NCT>
 __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, const float* bdr,
                                               int row0, int rlim, int lane, const SelDst& o,
-                                              int ct0 = 0) {
+                                              int ct0 = 0, int kt = -1) {
   // ct0: the first column tile held in acc; the score columns (K <= 64, at
   // most four tiles) are always in the pass that starts at 0
   const bool with_k = ct0 == 0;
@@ -370,7 +373,7 @@ __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, con
   }
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const int col = 16 * (ct0 + ct) + i;
+    const int col = (kt < 0 || ct0 + ct < kt) ? 16 * (ct0 + ct) + i : K + 16 * (ct0 + ct - kt) + i;
     if (col >= K && col < K + N) {
       const int n = col - K;
       f4v dv;
@@ -523,7 +526,12 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
   const int i = lane & 15, g = lane >> 4;
   const int K = p.K, N = p.N, d = p.d;
   const int KB = d >> 5;                           // 32-channel blocks
-  constexpr int CP = NCT < 4 ? NCT : 4;            // column tiles per pass
+  // tiles: the first KT hold score columns (rows of W_sel), the rest
+  // pre-activation columns (rows of W_d), so that every tile reads one
+  // matrix and its loads need no branch (a branch between loads into one
+  // register makes the compiler drain every load in flight)
+  const int KT = (K + 15) >> 4;
+  constexpr int CP = NCT <= 6 ? NCT : 4;           // column tiles per pass
   const rsrc_t rs = make_rsrc((const uint16_t*)a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
   const rsrc_t rz = make_rsrc((const uint16_t*)a.W_d + (size_t)h * N * d, (uint32_t)(N * d * 2));
   const int Tc = min(p.chunk, p.L - c0);
@@ -538,19 +546,21 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
     }
 #pragma unroll
     for (int ct0 = 0; ct0 < NCT; ct0 += CP) {
-      // weight rows: W_sel for columns < K, W_d for K <= column < K + N.  The
-      // buffer descriptor must be uniform, so a tile reads W_sel, W_d, or
-      // (the one tile that straddles K) both with the other lanes zeroed.
+      // weight rows: tile t < KT reads row 16 t + i of W_sel, tile t >= KT
+      // row 16 (t - KT) + i of W_d; the descriptor choice is uniform
       float bdr[CP];
-      uint32_t soff[CP], zoff[CP];                 // byte offsets (kNoLoad: none)
+      uint32_t woff[CP];                           // byte offsets (kNoLoad: none)
+      rsrc_t wr[CP];
 #pragma unroll
       for (int ct = 0; ct < CP; ++ct) {
-        const int col = 16 * (ct0 + ct) + i;
-        soff[ct] = col < K ? (uint32_t)((col * d + 8 * g) * 2) : kNoLoad;
-        zoff[ct] = (col >= K && col < K + N) ? (uint32_t)(((col - K) * d + 8 * g) * 2) : kNoLoad;
-        bdr[ct] = (col >= K && col < K + N) ? a.b_d[(size_t)h * N + col - K] : 0.f;
+        const bool sc = ct0 + ct < KT;
+        const int m = sc ? 16 * (ct0 + ct) + i : 16 * (ct0 + ct - KT) + i;
+        const bool ok = m < (sc ? K : N);
+        woff[ct] = ok ? (uint32_t)((m * d + 8 * g) * 2) : kNoLoad;
+        bdr[ct] = (ok && !sc) ? a.b_d[(size_t)h * N + m] : 0.f;
+        wr[ct] = sc ? rs : rz;
       }
-      constexpr int RING = 3;                      // blocks in flight
+      constexpr int RING = CP > 4 ? 2 : 3;         // blocks in flight
       u4v Ar[RING][2], Br[RING][CP];
       auto issue = [&](int slot_m, u4v* A2, u4v* Bn) {
         const bool ok = slot_m < KB;
@@ -560,19 +570,9 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
           A2[rt] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
                                                ur, (ok && uoff[rt] != kNoLoad) ? uoff[rt] + mo : kNoLoad, 0, 0));
 #pragma unroll
-        for (int ct = 0; ct < CP; ++ct) {
-          const int c16 = 16 * (ct0 + ct);         // uniform
-          const uint32_t so = (ok && soff[ct] != kNoLoad) ? soff[ct] + mo : kNoLoad;
-          const uint32_t zo = (ok && zoff[ct] != kNoLoad) ? zoff[ct] + mo : kNoLoad;
-          if (c16 + 16 <= K) {
-            Bn[ct] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0));
-          } else if (c16 >= K) {
-            Bn[ct] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0));
-          } else {
-            Bn[ct] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0)) |
-                     __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0));
-          }
-        }
+        for (int ct = 0; ct < CP; ++ct)
+          Bn[ct] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                               wr[ct], (ok && woff[ct] != kNoLoad) ? woff[ct] + mo : kNoLoad, 0, 0));
       };
       f4v acc[2][CP];
 #pragma unroll
@@ -581,29 +581,33 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
         for (int ct = 0; ct < CP; ++ct) acc[rt][ct] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q = 0; q < RING - 1; ++q) issue(q, Ar[q], Br[q]);
+      // Every block of the ring is multiplied unconditionally: a block past
+      // the end was loaded as zeros and adds nothing.  (A product under a
+      // condition lets the compiler move its loads into the branch, next to
+      // their use, which leaves no load in flight while the others compute.)
       for (int mb = 0; mb < KB; mb += RING) {
 #pragma unroll
         for (int q = 0; q < RING; ++q) {
           issue(mb + q + RING - 1, Ar[(q + RING - 1) % RING], Br[(q + RING - 1) % RING]);
-          if (mb + q < KB) {
+          __builtin_amdgcn_sched_barrier(0);       // the loads stay ahead of the products
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+          for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-              for (int ct = 0; ct < CP; ++ct)
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf8v, Ar[q][rt]), __builtin_bit_cast(bf8v, Br[q][ct]), acc[rt][ct], 0, 0, 0);
-          }
+            for (int ct = 0; ct < CP; ++ct)
+              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf8v, Ar[q][rt]), __builtin_bit_cast(bf8v, Br[q][ct]), acc[rt][ct], 0, 0, 0);
         }
       }
-      tile_epilogue<CP>(p, acc[0], bdr, row0, rend, lane, o, ct0);
-      if (row0 + 16 < rend) tile_epilogue<CP>(p, acc[1], bdr, row0 + 16, rend, lane, o, ct0);
+      tile_epilogue<CP>(p, acc[0], bdr, row0, rend, lane, o, ct0, KT);
+      if (row0 + 16 < rend) tile_epilogue<CP>(p, acc[1], bdr, row0 + 16, rend, lane, o, ct0, KT);
     }
   }
 }
 
 // Shapes with a register-resident fast path.
-// kSelDeep + n: the deep bf16 path with n column tiles (n even; a shape with
-// fewer real column tiles computes zero tiles that are never written).
+// kSelDeep + n: the deep bf16 path with n column tiles, ceil(K / 16) score
+// tiles then ceil(N / 16) pre-activation tiles, rounded up to even (a shape
+// with fewer real column tiles computes zero tiles that are never written).
 enum SelPath : int { kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3, kSelDeep = 16 };
 
 template <int IN_BF16, int MMA_BF16, int PATH>
@@ -1712,7 +1716,10 @@ static inline int sel_path(const Plan& p) {
   if (!p.in_bf16 && p.d == 64 && nct == 2) return kSelF32D64N2;
   if (!p.in_bf16 && p.d == 16 && nct == 1) return kSelF32D16N1;
   if (p.in_bf16 && p.mma_bf16 && p.d == 128 && nct == 3) return kSelBF16D128N3;
-  if (p.in_bf16 && p.mma_bf16 && p.d % 32 == 0 && p.d >= 256) return kSelDeep + ((nct + 1) & ~1);
+  if (p.in_bf16 && p.mma_bf16 && p.d % 32 == 0 && p.d >= 256) {
+    const int dt = ((p.K + 15) >> 4) + ((p.N + 15) >> 4);   // at most 8 (K, N <= 64)
+    return kSelDeep + ((dt + 1) & ~1);
+  }
   return kSelAny;
 }
 

@@ -264,6 +264,11 @@ def test_argmax_ties_on_gpu(bf16, d):
     dict(B=1, H=2, L=150, N=64, K=64, d=64, chunk=64),
     dict(B=1, H=1, L=40, N=16, K=16, d=8192, chunk=16),
     dict(B=1, H=1, L=64, N=64, K=64, d=8192, chunk=32, dtype="bf16"),
+    # the bf16 deep selection path with K not a multiple of 16 (score tiles
+    # padded, then pre-activation tiles) and an odd number of 32-channel blocks
+    dict(B=2, H=2, L=300, N=33, K=17, d=256, chunk=100, dtype="bf16"),
+    dict(B=1, H=3, L=200, N=20, K=5, d=288, chunk=64, dtype="bf16"),
+    dict(B=1, H=2, L=130, N=64, K=3, d=800, chunk=128, dtype="bf16"),
 ])
 def test_edge_shapes(shape):
     chunk = shape.pop("chunk")
