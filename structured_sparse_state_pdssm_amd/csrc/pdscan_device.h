@@ -891,6 +891,73 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
   }
 }
 
+// Inverse dictionary rows for the general kernel's 32-row groups.  Entry
+// (k, i) lists the sources j of row i under entry k (dict[k][j] = i) in
+// ascending order: the first eight as lane byte offsets 4 j with bit 0 set
+// (x: sources 1-4, y: 5-8; an empty byte means no source), and bit 25 of y
+// set when the row has more than eight.  One lane per entry; a wave covers
+// two entries (lanes 0-31 and 32-63), and lane i of an entry builds row i
+// from ballots of its sources' target bits.
+__device__ __forceinline__ void build_rows32(i2v* SE, const int* dict_h, int K, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int q0 = wave * 64; q0 < K * 32; q0 += kThreads) {   // uniform in the wave
+    const int q = q0 + lane;
+    const bool on = q < K * 32;
+    const int tg = on ? dict_h[q] : 0;
+    const int i = q & 31;
+    uint64_t m = __builtin_amdgcn_ballot_w64(on) & ((lane & 32) ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull);
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+      const uint64_t bb = __builtin_amdgcn_ballot_w64(on && ((tg >> b) & 1));
+      m &= ((i >> b) & 1) ? bb : ~bb;
+    }
+    const int deg = __builtin_popcountll(m);
+    unsigned x = 0, y = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const unsigned s = m ? (unsigned)__builtin_ctzll(m) : 0u;
+      const unsigned byt = m ? ((s & 31u) << 2) | 1u : 0u;
+      if (r < 4) x |= byt << (8 * r);
+      else y |= byt << (8 * (r - 4));
+      m &= m - 1;
+    }
+    if (deg > 8) y |= 2u << 24;
+    if (on) SE[q] = i2v{(int)x, (int)y};          // entry k * 32 + i = q
+  }
+}
+
+// h'_i = hn + sum over the sources j of row i (ascending) of the value vj of
+// lane j of this 32-lane group; lb is the group's lane-0 byte offset.  Rows
+// with more than four sources take a second round of permutes, rows with more
+// than eight a scan of the dictionary row (DCk: entry k of the (row, C) table).
+__device__ __forceinline__ float gather_rows32(const i2v se, int vj, int lb, float hn, const i2v* DCk, int i) {
+  const unsigned x = (unsigned)se.x, y = (unsigned)se.y;
+  float gv[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(lb | (int)((x >> (8 * m)) & 0xFCu), vj));
+#pragma unroll
+  for (int m = 0; m < 4; ++m) hn += ((x >> (8 * m)) & 1u) ? gv[m] : 0.f;
+  if (__builtin_amdgcn_ballot_w64(y & 1u)) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(lb | (int)((y >> (8 * m)) & 0xFCu), vj));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) hn += ((y >> (8 * m)) & 1u) ? gv[m] : 0.f;
+    if (__builtin_amdgcn_ballot_w64((y >> 25) & 1u)) {
+      const bool more = (y >> 25) & 1u;
+      int cnt = 0;
+      for (int s = 0; s < 32; ++s) {
+        const bool src = DCk[s].x == i;
+        const float g = __int_as_float(__builtin_amdgcn_ds_bpermute(lb | (s << 2), vj));
+        cnt += src ? 1 : 0;
+        hn += (more && src && cnt > 8) ? g : 0.f;
+      }
+    }
+  }
+  return hn;
+}
+
 template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT>
 __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   const Plan& p = a.p;
@@ -966,6 +1033,8 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         const int r = a.dict[(size_t)h * K * N + q];
         DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
       }
+      if constexpr (NPT == 32)
+        if (p.gse) build_rows32((i2v*)(smem + p.off_SRC), a.dict + (size_t)h * K * N, K, tid);
     }
   }
   if constexpr (MODE == kModeScan) {
@@ -1002,6 +1071,13 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   const float cj = act ? Cs[j] : 0.f;
   float hl = 0.f, msc = 1.f;
   int midx = jj;
+  // NPT = 32 with the inverse-row table: h' = Bu + gather of D h over the
+  // sources of each row (permutes); otherwise a scatter with LDS atomics
+  [[maybe_unused]] const bool gs = NPT == 32 && MODE != kModeSelect && p.gse && !(MODE == kModeScan && a.P_in);
+  [[maybe_unused]] const i2v* SE = (const i2v*)(smem + p.off_SRC);
+  [[maybe_unused]] const int lb = (lane & 32) << 2;
+  auto phase_a = [&](auto gs_tag) {
+  constexpr bool GS = decltype(gs_tag)::value;
   for (int blk = 0; blk < nst; blk += kBuBlock) {
     float bn[kBuBlock];
 #pragma unroll
@@ -1016,9 +1092,11 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
       const int t0 = tb + blk + q4;
       const i4v k4 = *(const i4v*)(kbuf + t0);
       const f4v d4 = act ? *(const f4v*)(Dbuf + j * TS + t0) : f4v{1.f, 1.f, 1.f, 1.f};
-      int own[4];
+      [[maybe_unused]] int own[4];
+      if constexpr (!GS) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) own[r] = DC[(r < nb ? k4[r] : 0) * p.DCS + jj].x;
+        for (int r = 0; r < 4; ++r) own[r] = DC[(r < nb ? k4[r] : 0) * p.DCS + jj].x;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool valid = r < nb;
@@ -1027,10 +1105,16 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         // next factor of the running map, gathered at its current rows
         const i2v e = DC[k * p.DCS + midx];
         const float dm = Dbuf[midx * TS + t];
-        // h' = Bu + scatter(D h); one wave, so its LDS operations stay in order
-        slot[j] = valid ? bu[q4 + r] : 0.f;
-        atomicAdd(&slot[(valid && act) ? own[r] : j], (valid ? d4[r] : 1.f) * hl);
-        hl = slot[j];
+        if constexpr (GS) {
+          const float hn = gather_rows32(SE[k * 32 + j], __float_as_int(d4[r] * hl), lb, bu[q4 + r],
+                                         DC + k * p.DCS, j);
+          hl = valid ? hn : hl;
+        } else {
+          // h' = Bu + scatter(D h); one wave, so its LDS operations stay in order
+          slot[j] = valid ? bu[q4 + r] : 0.f;
+          atomicAdd(&slot[(valid && act) ? own[r] : j], (valid ? d4[r] : 1.f) * hl);
+          hl = slot[j];
+        }
         // compose, and record w_t = C Phi_t over column t (all lanes of the
         // group have read column t above)
         if (valid) {
@@ -1045,6 +1129,13 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     }
 #pragma unroll
     for (int q = 0; q < kBuBlock; ++q) bu[q] = bn[q];
+  }
+  };
+  if constexpr (NPT == 32 && MODE != kModeSelect) {
+    if (gs) phase_a(std::true_type{});
+    else phase_a(std::false_type{});
+  } else {
+    phase_a(std::false_type{});
   }
 
   chunk_tail<false>(a, smem, c, s, Tc, gbase, NP, gam, j, act, midx, msc, hl);

@@ -41,6 +41,7 @@ struct Plan {
   int fold_bu;   // fused16: Bu = W_b u from a third MFMA tile instead of an input
   int step16;    // scan alone with the step-major layout (N <= 16); 2: also writes every state
   int n_out;     // outputs per head, rows of C (> 1: step-major paths only)
+  int gse;       // general kernel, N = 32: phase A gathers over inverse dictionary rows (table at off_SRC)
   int YS;        // stride of the per-output local-output rows
   int tasks;     // workgroups
   // LDS byte offsets
@@ -58,10 +59,8 @@ inline int next_pow2(int x) {
 
 inline int align_up(int x, int a) { return (x + a - 1) / a * a; }
 
-// Fills `p` for one call.  `mode` selects which parts exist.  Returns false
-// when the plan needs more than kMaxLds bytes of LDS.
-inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int d, int u_shared,
-                      int in_bf16, int chunk, int fold_bu = 0, int step16 = 0, int n_out = 1) {
+inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K, int d, int u_shared,
+                           int in_bf16, int chunk, int fold_bu, int step16, int n_out, int allow_gse) {
   p.B = B; p.H = H; p.L = L; p.N = N; p.K = K; p.d = d;
   p.u_shared = u_shared; p.in_bf16 = in_bf16;
   // a chunk longer than the sequence behaves exactly like chunk = L
@@ -96,6 +95,10 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
     if (p.TS % 32 != 4) p.TS += (36 - p.TS % 32) % 32;
   }
   p.DCS = sm ? 16 : N + 1;   // the step-major kernels index with a shift
+  // general kernel with two 32-row groups per wave: phase A's scatter is a
+  // gather over the sources of each row (a per-task table of 8 bytes per
+  // dictionary entry and row)
+  p.gse = (allow_gse && mode != kModeSelect && !sm && N == 32) ? 1 : 0;
   p.nC = (L + p.chunk - 1) / p.chunk;
   p.NC = align_up(K + N, 16);
   p.KP = align_up(K, 4);
@@ -137,7 +140,7 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
     p.off_pB = s0 + 5 * gn;
   } else {
     p.off_DC = scan ? take(K * p.DCS * 8) : 0;    // scan: (row, C[row]) pairs
-    p.off_SRC = 0;
+    p.off_SRC = p.gse ? take(K * N * 8) : 0;      // first eight sources of each row
     p.off_WB = 0;
     p.off_sIdx = scan ? take(gn) : 0;
     p.off_sSc = scan ? take(gn) : 0;
@@ -159,6 +162,16 @@ inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int 
   p.ws_bytes = (mode == kModeSelect) ? 0 : p.ws_inc + seqchunks * N * sizeof(uint64_t);
   if (n_out < 1 || n_out > kMaxOut || (n_out > 1 && !sm)) return false;
   return p.lds_bytes <= kMaxLds;
+}
+
+// Fills `p` for one call.  `mode` selects which parts exist.  Returns false
+// when the plan needs more than kMaxLds bytes of LDS (the gather table is
+// dropped first: phase A then scatters with LDS atomics).
+inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int d, int u_shared,
+                      int in_bf16, int chunk, int fold_bu = 0, int step16 = 0, int n_out = 1) {
+  if (make_plan_once(p, mode, B, H, L, N, K, d, u_shared, in_bf16, chunk, fold_bu, step16, n_out, 1))
+    return true;
+  return p.gse && make_plan_once(p, mode, B, H, L, N, K, d, u_shared, in_bf16, chunk, fold_bu, step16, n_out, 0);
 }
 
 // Everything a kernel launch reads.

@@ -4,6 +4,8 @@ Bars: selections bit-exact; y and h_L within 1e-4 (1 + |ref|) elementwise;
 D within 2e-6 absolute (diagnostic); automata runs bit-exact.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -87,6 +89,34 @@ def test_scan_standalone(name):
                              to_dev(inp.Bu), to_dev(inp.C), to_dev(inp.h0), chunk=inp.cfg.chunk)
     assert_within(host(y), y_ref, f"{name} y")
     assert_within(host(hL), h_ref, f"{name} h_L")
+
+
+def _skewed_dictionaries(H, N):
+    """Column-one-hot entries with rows of every in-degree: all columns into
+    row 0, three sources per row, a permutation, and ten sources in row 0
+    with rows 1-9 empty."""
+    j = np.arange(N)
+    one = np.stack([np.zeros(N, np.int64), j // 3, (j * 7) % N, np.where(j < 10, 0, j)])
+    return np.broadcast_to(one, (H, 4, N)).astype(np.int32).copy()
+
+
+@pytest.mark.parametrize("N", [32, 64, 20])
+def test_high_in_degree_rows(N):
+    """Rows with up to N sources (the gather over inverse rows with N = 32
+    takes its second and third rounds; other N scatter): fused forward and
+    scan alone against the oracle."""
+    cfg = get_config("timeseries", B=2, H=2, L=500, N=N, K=4)
+    inp = dataclasses.replace(generate(cfg), dict_idx=_skewed_dictionaries(2, N))
+    ref = oracle.forward_inputs(inp)
+    _check_fwd(inp, ref, 128, f"skewed dictionaries N={N}")
+    P = lib()
+    D32 = ref["D"].astype(np.float32)
+    y_ref, h_ref = oracle.scan(ref["k_star"], inp.dict_idx, D32, inp.Bu, inp.C, inp.h0)
+    print(f"[gpu] pdssm_scan_fwd skewed dictionaries N={N}", flush=True)
+    y, hL = P.pdssm_scan_fwd(to_dev(ref["k_star"]), to_dev(inp.dict_idx), to_dev(D32),
+                             to_dev(inp.Bu), to_dev(inp.C), to_dev(inp.h0), chunk=128)
+    assert_within(host(y), y_ref, f"skewed N={N} scan y")
+    assert_within(host(hL), h_ref, f"skewed N={N} scan h_L")
 
 
 @pytest.mark.parametrize("chunk", [1, 3, 16, 100, 512, 700])
