@@ -215,6 +215,7 @@ struct SelDst {
   int32_t* P_out; // global, optional
   const int* dic; // LDS dictionary [K][N] (for P_out)
   size_t gbase;   // global row index of chunk row 0 = s*L + c0
+  unsigned char* wst;  // deep path: LDS stages for the weight blocks, or nullptr
 };
 
 template <int IN_BF16, int MMA_BF16>
@@ -604,6 +605,122 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
   }
 }
 
+// The deep path with the weight blocks staged through LDS: each 32-channel
+// block of the score and pre-activation weights is read from memory once per
+// workgroup, each wave loading one or two of its 16-column tiles, instead
+// of once per wave.  Every wave of the workgroup takes part whatever its rows
+// (rows past rend load zeros and store nothing), with one barrier per block.
+// One pass (NCT <= 6), at most 32 rows per wave.  The two stages hold 16 NCT
+// columns of 64 bytes each, at a stride of 80 bytes so that the 16 lanes of a
+// fragment read hit distinct banks.  They lie in the region D is written to
+// afterwards, so a barrier separates their last read from the epilogues.
+// u blocks are loaded two ahead into registers, weight blocks two ahead into
+// registers and then one ahead into a stage.
+template <int NCT>
+__device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int h, int c0, int rbeg,
+                                                     int rend, int lane, const SelDst& o) {
+  const Plan& p = a.p;
+  // the wave index through lane 0: the descriptor and branch choices below
+  // are then scalar (a descriptor the compiler cannot prove uniform turns a
+  // load into a loop over lanes)
+  const int i = lane & 15, g = lane >> 4, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int K = p.K, N = p.N, d = p.d;
+  const int KB = d >> 5;
+  const int KT = (K + 15) >> 4;
+  constexpr int kRow = 80, kStage = 16 * NCT * kRow;
+  constexpr int TPW = (NCT + kWaves - 1) / kWaves;   // tiles this wave stages
+  unsigned char* wst = o.wst;
+  const rsrc_t rs = make_rsrc((const uint16_t*)a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
+  const rsrc_t rz = make_rsrc((const uint16_t*)a.W_d + (size_t)h * N * d, (uint32_t)(N * d * 2));
+  const int Tc = min(p.chunk, p.L - c0);
+  const rsrc_t ur = make_rsrc((const uint16_t*)a.u + ((size_t)s_u * p.L + c0) * d, (uint32_t)(Tc * d * 2));
+
+  uint32_t uoff[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = rbeg + 16 * rt + i;
+    uoff[rt] = row < rend ? (uint32_t)((row * d + 8 * g) * 2) : kNoLoad;
+  }
+  // tile t < KT: row 16 t + i of W_sel; tile t >= KT: row 16 (t - KT) + i of W_d
+  uint32_t toff[TPW];
+  int tlds[TPW];
+  rsrc_t tr[TPW];
+#pragma unroll
+  for (int w = 0; w < TPW; ++w) {
+    const int t = wave + kWaves * w;               // uniform in the wave
+    const bool sc = t < KT;
+    const int m = sc ? 16 * t + i : 16 * (t - KT) + i;
+    const bool ok = t < NCT && m < (sc ? K : N);
+    toff[w] = ok ? (uint32_t)((m * d + 8 * g) * 2) : kNoLoad;
+    tr[w] = sc ? rs : rz;
+    tlds[w] = (16 * t + i) * kRow + 16 * g;
+  }
+  float bdr[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int n = 16 * (ct - KT) + i;
+    bdr[ct] = (ct >= KT && n < N) ? a.b_d[(size_t)h * N + n] : 0.f;
+  }
+
+  u4v Ar[3][2], Wr[2][TPW];
+  auto load_u = [&](int m, u4v* A2) {
+    const bool ok = m < KB;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+      A2[rt] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                           ur, (ok && uoff[rt] != kNoLoad) ? uoff[rt] + (uint32_t)m * 64u : kNoLoad, 0, 0));
+  };
+  auto load_w = [&](int m, u4v* W) {
+    const bool ok = m < KB;
+#pragma unroll
+    for (int w = 0; w < TPW; ++w)
+      W[w] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                          tr[w], (ok && toff[w] != kNoLoad) ? toff[w] + (uint32_t)m * 64u : kNoLoad, 0, 0));
+  };
+  auto put_w = [&](int m, const u4v* W) {
+    unsigned char* st = wst + (m & 1) * kStage;
+#pragma unroll
+    for (int w = 0; w < TPW; ++w)
+      if (wave + kWaves * w < NCT) *(u4v*)(st + tlds[w]) = W[w];
+  };
+
+  f4v acc[2][NCT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+  load_u(0, Ar[0]);
+  load_u(1, Ar[1]);
+  load_w(0, Wr[0]);
+  load_w(1, Wr[1]);
+  put_w(0, Wr[0]);
+  load_w(2, Wr[0]);
+  // blocks past the end load zeros, stage zeros and add nothing
+  for (int m0 = 0; m0 < KB; m0 += 6) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const int m = m0 + q;
+      __syncthreads();                             // stage m written; stage m - 1 read by every wave
+      load_u(m + 2, Ar[(q + 2) % 3]);
+      put_w(m + 1, Wr[(q + 1) & 1]);
+      load_w(m + 3, Wr[(q + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);           // the loads stay ahead of the products
+      const unsigned char* st = wst + (m & 1) * kStage;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const u4v bf = *(const u4v*)(st + (16 * ct + i) * kRow + 16 * g);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf8v, Ar[q % 3][rt]), __builtin_bit_cast(bf8v, bf), acc[rt][ct], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();                                 // the stages are D's region from here
+  tile_epilogue<NCT>(p, acc[0], bdr, rbeg, rend, lane, o, 0, KT);
+  tile_epilogue<NCT>(p, acc[1], bdr, rbeg + 16, rend, lane, o, 0, KT);
+}
+
 // Shapes with a register-resident fast path.
 // kSelDeep + n: the deep bf16 path with n column tiles, ceil(K / 16) score
 // tiles then ceil(N / 16) pre-activation tiles, rounded up to even (a shape
@@ -619,8 +736,15 @@ __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, i
     select_rows<0, 0, 1, 1>(a, s_u, h, c0, rbeg, rend, lane, o);
   else if constexpr (PATH == kSelBF16D128N3 && IN_BF16 && MMA_BF16)
     select_rows<1, 1, 4, 3>(a, s_u, h, c0, rbeg, rend, lane, o);
-  else if constexpr (PATH > kSelDeep && IN_BF16 && MMA_BF16)
+  else if constexpr (PATH > kSelDeep && IN_BF16 && MMA_BF16) {
+    if constexpr (PATH - kSelDeep <= 6) {
+      if (o.wst) {
+        select_rows_deep_lds<PATH - kSelDeep>(a, s_u, h, c0, rbeg, rend, lane, o);
+        return;
+      }
+    }
     select_rows_deep<PATH - kSelDeep>(a, s_u, h, c0, rbeg, rend, lane, o);
+  }
   else
     select_rows_any<IN_BF16, MMA_BF16>(a, s_u, h, c0, rbeg, rend, lane, o);
 }
@@ -1058,6 +1182,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     o.P_out = a.P_out;
     o.dic = dic;
     o.gbase = gbase;
+    o.wst = (MODE == kModeFused && p.wst) ? smem + p.off_D : nullptr;
     const int wr0 = min(wave * gpw * S, Tc), wr1 = min(wr0 + gpw * S, Tc);
     select_dispatch<IN_BF16, MMA_BF16, PATH>(a, s_u, h, c0, wr0, wr1, lane, o);
   }

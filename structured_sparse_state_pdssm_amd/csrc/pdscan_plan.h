@@ -42,6 +42,7 @@ struct Plan {
   int step16;    // scan alone with the step-major layout (N <= 16); 2: also writes every state
   int n_out;     // outputs per head, rows of C (> 1: step-major paths only)
   int gse;       // general kernel, N = 32: phase A gathers over inverse dictionary rows (table at off_SRC)
+  int wst;       // fused deep bf16 selection: weight blocks staged through LDS (in D's region)
   int YS;        // stride of the per-output local-output rows
   int tasks;     // workgroups
   // LDS byte offsets
@@ -113,6 +114,14 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   p.n_out = n_out;
   p.YS = align_up(T + p.G, 4);
   p.off_D = scan ? take(n_out * N * p.TS * 4) : 0;
+  // fused deep bf16 selection (d a multiple of 32, at least 256) in one pass
+  // over at most six column tiles with at most 32 rows per wave: two stages
+  // of 16 columns x 80 bytes per tile in D's region, if it is large enough
+  {
+    const int dt = ((K + 15) >> 4) + ((N + 15) >> 4), nct = (dt + 1) & ~1;
+    const bool deep = mode == kModeFused && !sm && in_bf16 && p.mma_bf16 && d % 32 == 0 && d >= 256;
+    p.wst = (deep && nct <= 6 && (64 / p.NP) * p.S <= 32 && n_out * N * p.TS * 4 >= 2 * 16 * nct * 80) ? 1 : 0;
+  }
   p.off_k = (scan && !sm) ? take(align_up(T, 4) * 4) : 0;   // the step-major kernels keep k* in registers
   p.off_yl = scan ? take(n_out * p.YS * 4) : 0;
   p.off_dict = scan ? 0 : take(K * N * 4);   // selection: P_idx gathers
