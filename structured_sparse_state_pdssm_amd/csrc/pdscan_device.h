@@ -179,6 +179,24 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// The same sum, complete only in the group's last 16-lane row (lanes
+// NP - 16 .. NP - 1; NP <= 16: every lane): rows are joined by DPP row
+// broadcasts (lane 15 of a row into the next row, lane 31 into rows 2 and 3)
+// instead of cross-lane permutes through the LDS unit.
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+template <int NP>
+__device__ __forceinline__ float group_sum_last(float v) {
+  v = group_sum<NP < 16 ? NP : 16>(v);
+  if constexpr (NP >= 32)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppRowBcast15,
+                                                               0xA, 0xF, false));
+  if constexpr (NP >= 64)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppRowBcast31,
+                                                               0xC, 0xF, false));
+  return v;
+}
+
 __device__ __forceinline__ float group_sum_rt(float v, int NP) {
   switch (NP) {
     case 1: return v;
@@ -1248,8 +1266,13 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         }
         if (valid && act) Dbuf[j * TS + t] = __int_as_float(e.y) * msc;
         // local output C h'
-        const float yl = NPT ? group_sum<NPT ? NPT : 1>(cj * hl) : group_sum_rt(cj * hl, NP);
-        if (valid && j == 0) yloc[t] = yl;
+        if constexpr (NPT != 0) {
+          const float yl = group_sum_last<NPT>(cj * hl);
+          if (valid && j == NPT - 1) yloc[t] = yl;
+        } else {
+          const float yl = group_sum_rt(cj * hl, NP);
+          if (valid && j == 0) yloc[t] = yl;
+        }
       }
     }
 #pragma unroll
