@@ -1039,33 +1039,30 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
 // (x: sources 1-4, y: 5-8; an empty byte means no source), and bit 25 of y
 // set when the row has more than eight.  One lane per entry; a wave covers
 // two entries (lanes 0-31 and 32-63), and lane i of an entry builds row i
-// from ballots of its sources' target bits.
-__device__ __forceinline__ void build_rows32(i2v* SE, const int* dict_h, int K, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-  for (int q0 = wave * 64; q0 < K * 32; q0 += kThreads) {   // uniform in the wave
-    const int q = q0 + lane;
-    const bool on = q < K * 32;
-    const int tg = on ? dict_h[q] : 0;
-    const int i = q & 31;
-    uint64_t m = __builtin_amdgcn_ballot_w64(on) & ((lane & 32) ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull);
+// from ballots of its sources' target bits (the loop over entries must be
+// uniform in the wave: q = 64 w + lane).
+__device__ __forceinline__ i2v row32_entry(int tg, bool on, int q, int lane) {
+  // lane = q % 64 holds target tg = dict[k][j] of source j = q % 32 under
+  // entry k = q / 32, and builds row i = q % 32 of the same entry
+  const int i = q & 31;
+  uint64_t m = __builtin_amdgcn_ballot_w64(on) & ((lane & 32) ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull);
 #pragma unroll
-    for (int b = 0; b < 5; ++b) {
-      const uint64_t bb = __builtin_amdgcn_ballot_w64(on && ((tg >> b) & 1));
-      m &= ((i >> b) & 1) ? bb : ~bb;
-    }
-    const int deg = __builtin_popcountll(m);
-    unsigned x = 0, y = 0;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const unsigned s = m ? (unsigned)__builtin_ctzll(m) : 0u;
-      const unsigned byt = m ? ((s & 31u) << 2) | 1u : 0u;
-      if (r < 4) x |= byt << (8 * r);
-      else y |= byt << (8 * (r - 4));
-      m &= m - 1;
-    }
-    if (deg > 8) y |= 2u << 24;
-    if (on) SE[q] = i2v{(int)x, (int)y};          // entry k * 32 + i = q
+  for (int b = 0; b < 5; ++b) {
+    const uint64_t bb = __builtin_amdgcn_ballot_w64(on && ((tg >> b) & 1));
+    m &= ((i >> b) & 1) ? bb : ~bb;
   }
+  const int deg = __builtin_popcountll(m);
+  unsigned x = 0, y = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const unsigned s = m ? (unsigned)__builtin_ctzll(m) : 0u;
+    const unsigned byt = m ? ((s & 31u) << 2) | 1u : 0u;
+    if (r < 4) x |= byt << (8 * r);
+    else y |= byt << (8 * (r - 4));
+    m &= m - 1;
+  }
+  if (deg > 8) y |= 2u << 24;
+  return i2v{(int)x, (int)y};
 }
 
 // h'_i = hn + sum over the sources j of row i (ascending) of the value vj of
@@ -1170,13 +1167,22 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         const int r = a.P_in[gbase * N + q];
         DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
       }
+    } else if (NPT == 32 && p.gse) {
+      // the (row, C) pairs and the inverse rows from one read of the dictionary
+      i2v* SE = (i2v*)(smem + p.off_SRC);
+      for (int q0 = wave * 64; q0 < K * N; q0 += kThreads) {   // uniform in the wave
+        const int q = q0 + lane;
+        const bool on = q < K * N;
+        const int r = on ? a.dict[(size_t)h * K * N + q] : 0;
+        if (on) DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
+        const i2v e = row32_entry(r, on, q, lane);
+        if (on) SE[q] = e;
+      }
     } else {
       for (int q = tid; q < K * N; q += kThreads) {
         const int r = a.dict[(size_t)h * K * N + q];
         DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
       }
-      if constexpr (NPT == 32)
-        if (p.gse) build_rows32((i2v*)(smem + p.off_SRC), a.dict + (size_t)h * K * N, K, tid);
     }
   }
   if constexpr (MODE == kModeScan) {
