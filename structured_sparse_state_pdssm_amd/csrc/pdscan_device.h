@@ -988,14 +988,14 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
       // sub-chunk from the state entering it (the step of phase A, now from
       // the true state), writing the states and the outputs directly.
       const int* kbuf = (const int*)(smem + p.off_k);
-      const i2v* DC = (const i2v*)(smem + p.off_DC);
+      const unsigned char* DR = smem + p.off_DC;
       const float* Cs = (const float*)(smem + p.off_C);
       float* scr = (float*)sIdx + gam * NP;        // free since phase B
       float hj = act ? slots[gam * NP + j] : 0.f;
       const int tb = gam * S, te = min(tb + S, Tc);
       for (int t = tb; t < te; ++t) {
         const size_t row = (gbase + t) * N;
-        const int r = act ? DC[kbuf[t] * p.DCS + j].x : j;
+        const int r = act ? (int)DR[kbuf[t] * p.DCS + j] : j;
         const float dj = act ? a.D_in[row + j] : 0.f;
         scr[j] = act ? a.Bu[row + j] : 0.f;
         // one wave holds the group, so its LDS operations stay in order
@@ -1033,21 +1033,24 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
   }
 }
 
-// Inverse dictionary rows for the general kernel's 32-row groups.  Entry
-// (k, i) lists the sources j of row i under entry k (dict[k][j] = i) in
-// ascending order: the first eight as lane byte offsets 4 j with bit 0 set
-// (x: sources 1-4, y: 5-8; an empty byte means no source), and bit 25 of y
-// set when the row has more than eight.  One lane per entry; a wave covers
-// two entries (lanes 0-31 and 32-63), and lane i of an entry builds row i
-// from ballots of its sources' target bits (the loop over entries must be
-// uniform in the wave: q = 64 w + lane).
-__device__ __forceinline__ i2v row32_entry(int tg, bool on, int q, int lane) {
-  // lane = q % 64 holds target tg = dict[k][j] of source j = q % 32 under
-  // entry k = q / 32, and builds row i = q % 32 of the same entry
-  const int i = q & 31;
-  uint64_t m = __builtin_amdgcn_ballot_w64(on) & ((lane & 32) ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull);
+// Inverse dictionary rows for the general kernel's groups of NG = 32 or 64
+// rows.  Entry (k, i) lists the sources j of row i under entry k
+// (dict[k][j] = i) in ascending order: the first eight as lane byte offsets
+// 4 j with bit 0 set (x: sources 1-4, y: 5-8; an empty byte means no
+// source), and bit 25 of y set when the row has more than eight.  One lane
+// per entry; a wave covers 64 / NG entries, and lane i of an entry builds
+// row i from ballots of its sources' target bits (the loop over entries must
+// be uniform in the wave: q = 64 w + lane).
+template <int NG>
+__device__ __forceinline__ i2v row_entry(int tg, bool on, int q, int lane) {
+  // lane = q % 64 holds target tg = dict[k][j] of source j = q % NG under
+  // entry k = q / NG, and builds row i = q % NG of the same entry
+  constexpr int LB = NG == 32 ? 5 : 6;
+  const int i = q & (NG - 1);
+  uint64_t m = __builtin_amdgcn_ballot_w64(on);
+  if constexpr (NG == 32) m &= (lane & 32) ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull;
 #pragma unroll
-  for (int b = 0; b < 5; ++b) {
+  for (int b = 0; b < LB; ++b) {
     const uint64_t bb = __builtin_amdgcn_ballot_w64(on && ((tg >> b) & 1));
     m &= ((i >> b) & 1) ? bb : ~bb;
   }
@@ -1056,7 +1059,7 @@ __device__ __forceinline__ i2v row32_entry(int tg, bool on, int q, int lane) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const unsigned s = m ? (unsigned)__builtin_ctzll(m) : 0u;
-    const unsigned byt = m ? ((s & 31u) << 2) | 1u : 0u;
+    const unsigned byt = m ? ((s & (unsigned)(NG - 1)) << 2) | 1u : 0u;
     if (r < 4) x |= byt << (8 * r);
     else y |= byt << (8 * (r - 4));
     m &= m - 1;
@@ -1066,10 +1069,12 @@ __device__ __forceinline__ i2v row32_entry(int tg, bool on, int q, int lane) {
 }
 
 // h'_i = hn + sum over the sources j of row i (ascending) of the value vj of
-// lane j of this 32-lane group; lb is the group's lane-0 byte offset.  Rows
+// lane j of this NG-lane group; lb is the group's lane-0 byte offset.  Rows
 // with more than four sources take a second round of permutes, rows with more
-// than eight a scan of the dictionary row (DCk: entry k of the (row, C) table).
-__device__ __forceinline__ float gather_rows32(const i2v se, int vj, int lb, float hn, const i2v* DCk, int i) {
+// than eight a scan of the dictionary row (DRk: the target rows of entry k).
+template <int NG>
+__device__ __forceinline__ float gather_rows(const i2v se, int vj, int lb, float hn, const unsigned char* DRk,
+                                             int i) {
   const unsigned x = (unsigned)se.x, y = (unsigned)se.y;
   float gv[4];
 #pragma unroll
@@ -1086,8 +1091,8 @@ __device__ __forceinline__ float gather_rows32(const i2v se, int vj, int lb, flo
     if (__builtin_amdgcn_ballot_w64((y >> 25) & 1u)) {
       const bool more = (y >> 25) & 1u;
       int cnt = 0;
-      for (int s = 0; s < 32; ++s) {
-        const bool src = DCk[s].x == i;
+      for (int s = 0; s < NG; ++s) {
+        const bool src = (int)DRk[s] == i;
         const float g = __int_as_float(__builtin_amdgcn_ds_bpermute(lb | (s << 2), vj));
         cnt += src ? 1 : 0;
         hn += (more && src && cnt > 8) ? g : 0.f;
@@ -1110,7 +1115,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   int* kbuf = (int*)(smem + p.off_k);
   float* yloc = (float*)(smem + p.off_yl);
   int* dic = (int*)(smem + p.off_dict);
-  i2v* DC = (i2v*)(smem + p.off_DC);
+  unsigned char* DR = smem + p.off_DC;       // DR[k][m] = dict[k][m] (a byte: N <= 64)
   float* Cs = (float*)(smem + p.off_C);
   float* slots = (float*)(smem + p.off_slot);
   int* misc = (int*)(smem + p.off_misc);
@@ -1160,29 +1165,26 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   } else {
     for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
     __syncthreads();
-    // DC[k][m] = (dict[k][m], C[dict[k][m]]): target row and its output weight;
-    // with per-step maps, entry t is step t's map and k*_t = t
+    // DR[k][m] = dict[k][m]: the target row of source m under entry k; with
+    // per-step maps, entry t is step t's map and k*_t = t
     if (MODE == kModeScan && a.P_in) {
-      for (int q = tid; q < Tc * N; q += kThreads) {
-        const int r = a.P_in[gbase * N + q];
-        DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
-      }
-    } else if (NPT == 32 && p.gse) {
-      // the (row, C) pairs and the inverse rows from one read of the dictionary
+      for (int q = tid; q < Tc * N; q += kThreads)
+        DR[(q / N) * p.DCS + q % N] = (unsigned char)a.P_in[gbase * N + q];
+    } else if ((NPT == 32 || NPT == 64) && p.gse) {
+      // the target rows and the inverse rows from one read of the dictionary
+      constexpr int NG = NPT == 64 ? 64 : 32;
       i2v* SE = (i2v*)(smem + p.off_SRC);
       for (int q0 = wave * 64; q0 < K * N; q0 += kThreads) {   // uniform in the wave
         const int q = q0 + lane;
         const bool on = q < K * N;
         const int r = on ? a.dict[(size_t)h * K * N + q] : 0;
-        if (on) DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
-        const i2v e = row32_entry(r, on, q, lane);
+        if (on) DR[(q / N) * p.DCS + q % N] = (unsigned char)r;
+        const i2v e = row_entry<NG>(r, on, q, lane);
         if (on) SE[q] = e;
       }
     } else {
-      for (int q = tid; q < K * N; q += kThreads) {
-        const int r = a.dict[(size_t)h * K * N + q];
-        DC[(q / N) * p.DCS + q % N] = i2v{r, __float_as_int(Cs[r])};
-      }
+      for (int q = tid; q < K * N; q += kThreads)
+        DR[(q / N) * p.DCS + q % N] = (unsigned char)a.dict[(size_t)h * K * N + q];
     }
   }
   if constexpr (MODE == kModeScan) {
@@ -1222,9 +1224,10 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   int midx = jj;
   // NPT = 32 with the inverse-row table: h' = Bu + gather of D h over the
   // sources of each row (permutes); otherwise a scatter with LDS atomics
-  [[maybe_unused]] const bool gs = NPT == 32 && MODE != kModeSelect && p.gse && !(MODE == kModeScan && a.P_in);
+  [[maybe_unused]] const bool gs = (NPT == 32 || NPT == 64) && MODE != kModeSelect && p.gse &&
+                                   !(MODE == kModeScan && a.P_in);
   [[maybe_unused]] const i2v* SE = (const i2v*)(smem + p.off_SRC);
-  [[maybe_unused]] const int lb = (lane & 32) << 2;
+  [[maybe_unused]] const int lb = NPT == 32 ? (lane & 32) << 2 : 0;
   auto phase_a = [&](auto gs_tag) {
   constexpr bool GS = decltype(gs_tag)::value;
   for (int blk = 0; blk < nst; blk += kBuBlock) {
@@ -1244,7 +1247,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
       [[maybe_unused]] int own[4];
       if constexpr (!GS) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) own[r] = DC[(r < nb ? k4[r] : 0) * p.DCS + jj].x;
+        for (int r = 0; r < 4; ++r) own[r] = DR[(r < nb ? k4[r] : 0) * p.DCS + jj];
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1252,11 +1255,12 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         const int t = t0 + r;
         const int k = valid ? k4[r] : 0;
         // next factor of the running map, gathered at its current rows
-        const i2v e = DC[k * p.DCS + midx];
+        const int nrow = DR[k * p.DCS + midx];
         const float dm = Dbuf[midx * TS + t];
         if constexpr (GS) {
-          const float hn = gather_rows32(SE[k * 32 + j], __float_as_int(d4[r] * hl), lb, bu[q4 + r],
-                                         DC + k * p.DCS, j);
+          constexpr int NG = NPT == 64 ? 64 : 32;
+          const float hn = gather_rows<NG>(SE[k * NG + j], __float_as_int(d4[r] * hl), lb, bu[q4 + r],
+                                           DR + k * p.DCS, j);
           hl = valid ? hn : hl;
         } else {
           // h' = Bu + scatter(D h); one wave, so its LDS operations stay in order
@@ -1268,9 +1272,9 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         // group have read column t above)
         if (valid) {
           msc *= dm;
-          midx = e.x;
+          midx = nrow;
         }
-        if (valid && act) Dbuf[j * TS + t] = __int_as_float(e.y) * msc;
+        if (valid && act) Dbuf[j * TS + t] = Cs[midx] * msc;
         // local output C h'
         if constexpr (NPT != 0) {
           const float yl = group_sum_last<NPT>(cj * hl);
@@ -1285,7 +1289,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     for (int q = 0; q < kBuBlock; ++q) bu[q] = bn[q];
   }
   };
-  if constexpr (NPT == 32 && MODE != kModeSelect) {
+  if constexpr ((NPT == 32 || NPT == 64) && MODE != kModeSelect) {
     if (gs) phase_a(std::true_type{});
     else phase_a(std::false_type{});
   } else {

@@ -41,7 +41,7 @@ struct Plan {
   int fold_bu;   // fused16: Bu = W_b u from a third MFMA tile instead of an input
   int step16;    // scan alone with the step-major layout (N <= 16); 2: also writes every state
   int n_out;     // outputs per head, rows of C (> 1: step-major paths only)
-  int gse;       // general kernel, N = 32: phase A gathers over inverse dictionary rows (table at off_SRC)
+  int gse;       // general kernel, N = 32 or 64: phase A gathers over inverse dictionary rows (table at off_SRC)
   int wst;       // fused deep bf16 selection: weight blocks staged through LDS (in D's region)
   int YS;        // stride of the per-output local-output rows
   int tasks;     // workgroups
@@ -96,10 +96,10 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
     if (p.TS % 32 != 4) p.TS += (36 - p.TS % 32) % 32;
   }
   p.DCS = sm ? 16 : N + 1;   // the step-major kernels index with a shift
-  // general kernel with two 32-row groups per wave: phase A's scatter is a
-  // gather over the sources of each row (a per-task table of 8 bytes per
-  // dictionary entry and row)
-  p.gse = (allow_gse && mode != kModeSelect && !sm && N == 32) ? 1 : 0;
+  // general kernel with 32- or 64-row groups: phase A's scatter is a gather
+  // over the sources of each row (a per-task table of 8 bytes per dictionary
+  // entry and row)
+  p.gse = (allow_gse && mode != kModeSelect && !sm && (N == 32 || N == 64)) ? 1 : 0;
   p.nC = (L + p.chunk - 1) / p.chunk;
   p.NC = align_up(K + N, 16);
   p.KP = align_up(K, 4);
@@ -148,7 +148,7 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
     p.off_pSc = s0 + 4 * gn;
     p.off_pB = s0 + 5 * gn;
   } else {
-    p.off_DC = scan ? take(K * p.DCS * 8) : 0;    // scan: (row, C[row]) pairs
+    p.off_DC = scan ? take(K * p.DCS) : 0;        // scan: target row of each source (a byte)
     p.off_SRC = p.gse ? take(K * N * 8) : 0;      // first eight sources of each row
     p.off_WB = 0;
     p.off_sIdx = scan ? take(gn) : 0;
