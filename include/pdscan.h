@@ -36,6 +36,18 @@
  *     no global mutable state: scratch memory comes from the caller's
  *     workspace.  Two calls that share one workspace must be ordered on one
  *     stream.
+ *   - Workspace header.  Every call that takes a workspace clears it first;
+ *     its 32-bit word at byte offset 4 is then nonzero when a look-back wait
+ *     of that call (the inter-chunk carry, phase B) gave up after about 4M
+ *     window reads.  The affected chunks then continued from the zero carry
+ *     (h0 in the forward scans), so y, h_L and every gradient or sensitivity
+ *     output of that call are wrong.  A wait ends only when the preceding
+ *     chunks have published, which every launch order the runtime uses
+ *     guarantees; the word guards against a stalled device.  Read it with
+ *     pdssm_workspace_status after the call, on the same stream.
+ *     (Test hook: with PDSSM_TEST_LOOKBACK_GIVEUP=1 in the environment every
+ *     wait ignores the carries it finds and gives up after two reads, so a
+ *     test can set the word on purpose.  Never set it in normal use.)
  *   - Arguments are validated on the host before any HIP call.  On failure
  *     nothing is enqueued and a negative pdssm_status is returned; the
  *     calling thread's pdssm_last_error() then describes the problem.
@@ -108,7 +120,15 @@ int pdssm_fwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* byt
 
 /* Fused selection + chunked scan in one pass over u and Bu.  Arguments as in
  * pdssm_select and pdssm_scan_fwd; k_star [B,H,L] and D [B,H,L,N] are
- * optional outputs (NULL: not written). */
+ * optional outputs (NULL: not written).
+ * Score precision.  fp32 inputs on the step-major kernel (per-head u, N <= 16,
+ * K <= 16, d_in in {32, 64}) form every product on the bf16 matrix cores from
+ * an exact three-piece split of each fp32 operand (x = x0 + x1 + x2, each
+ * piece the next eight significant bits), keeping the six piece products
+ * whose weight is at least 2^-16 of |x w| and accumulating in fp32: the
+ * dropped terms are below 2^-23 |x w|, so the scores carry fp32 accuracy.
+ * Other fp32 shapes use fp32 MFMA; bf16 inputs use bf16 MFMA (d_in >= 128)
+ * or exact fp32 MFMA products (d_in < 128). */
 int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
               const int32_t* dict_idx, const void* W_d, const float* b_d,
               const float* Bu, const float* C, const float* h0,
@@ -193,7 +213,9 @@ int pdssm_scan_fwd_multi(const pdssm_dims* dims, int32_t chunk, int32_t n_out, c
                          void* stream);
 
 /* Bytes of workspace pdssm_impulse_sens needs for these dims and chunk length
- * (about nC * B * H * N * (d_in + 2) * 8 bytes: one tangent state per chunk). */
+ * (256 + nC * B * H * 4 * N * 8 bytes: per chunk, its composed PD map and the
+ * inclusive map entering the next chunk, 2 N tagged words each; no tangent
+ * state crosses a chunk). */
 int pdssm_impulse_sens_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes);
 
 /* Sensitivity of every output to the first input, dY[b,h,t,:] = dy_t / du_0,
@@ -222,7 +244,7 @@ int pdssm_impulse_sens(const pdssm_dims* dims, int32_t chunk, const int32_t* k_s
  * pdssm_scan_workspace_bytes.  With N <= 16 and chunk <= 512 the maps stream
  * through registers; otherwise an on-chip table holds one map per step of a
  * chunk (chunk * (N + 1) * 8 bytes), and a chunk whose table does not fit
- * (N = 16: above 512; N = 20: above 192) returns PDSSM_EUNSUPPORTED. */
+ * (N = 16: above 512; N = 20: above 548) returns PDSSM_EUNSUPPORTED. */
 int pdssm_scan_fwd_pidx(const pdssm_dims* dims, int32_t chunk, const int32_t* P_idx, const float* D,
                         const float* Bu, const float* C, const float* h0, float* y, float* h_L,
                         void* workspace, size_t workspace_bytes, void* stream);
@@ -256,6 +278,20 @@ const char* pdssm_last_error(void);
 
 /* PDSSM_ABI_VERSION of the loaded library. */
 int pdssm_abi_version(void);
+
+/* Look-back status of the most recent call on `workspace` (any of the calls
+ * above that take a workspace): enqueues on `stream` a one-lane kernel that
+ * ORs the workspace error word (see "Workspace header" above; nonzero = some
+ * look-back wait of that call gave up and its outputs are wrong) into
+ * status[0].  Order it after the call on the same stream and read status
+ * after synchronising; zero status[0] first, or keep ORing the words of
+ * several calls into it to check them all at once.
+ *   workspace: the call's workspace (16-byte aligned, at least 256 bytes).
+ *   status: one uint32 in device memory or in pinned host memory visible to
+ *     the device (4-byte aligned); owned by the caller.
+ * Returns PDSSM_EINVAL for NULL or misaligned pointers, PDSSM_EWORKSPACE for
+ * fewer than 256 bytes. */
+int pdssm_workspace_status(const void* workspace, size_t workspace_bytes, uint32_t* status, void* stream);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,7 @@ def _load():
         "pdssm_status_str": [ctypes.c_int],
         "pdssm_last_error": [],
         "pdssm_abi_version": [],
+        "pdssm_workspace_status": [vp, sz, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

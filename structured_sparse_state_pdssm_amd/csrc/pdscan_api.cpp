@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "pdscan.h"
@@ -25,6 +26,7 @@ hipError_t launch_bwd(const BwdArgs& a, float* g_C, hipStream_t st);
 hipError_t launch_sens(const SensArgs& a, hipStream_t st);
 hipError_t launch_soft(const SoftArgs& a, hipStream_t st);
 hipError_t launch_dict_hardmax(const float* M, int32_t* dict, int HK, int N, hipStream_t st);
+hipError_t launch_status(const void* ws, uint32_t* status, hipStream_t st);
 }
 
 using pdscan::Plan;
@@ -75,6 +77,15 @@ int check_dims(const pdssm_dims* d, int32_t chunk) {
   return PDSSM_OK;
 }
 
+// Test hook: with PDSSM_TEST_LOOKBACK_GIVEUP=1 in the environment every
+// look-back wait ignores the carries it finds and gives up after two window
+// reads, so the workspace error word is set on purpose while every kernel
+// still ends normally.  Never set in normal use.
+bool lookback_giveup_hook() {
+  const char* v = getenv("PDSSM_TEST_LOOKBACK_GIVEUP");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
 int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_bu = 0, int step16 = 0,
                int n_out = 1) {
   const int c = (mode == pdscan::kModeSelect) ? pdscan::kSelectRows : chunk;
@@ -85,6 +96,10 @@ int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_b
                 d->N, p.lds_bytes, pdscan::kMaxLds);
   if ((uint64_t)p.nC * d->B * d->H > 0x7fffffffull)
     return fail(PDSSM_EUNSUPPORTED, "too many chunks");
+  if (lookback_giveup_hook()) {
+    p.force_giveup = 1;
+    p.spin_limit = 2;
+  }
   return PDSSM_OK;
 }
 
@@ -166,6 +181,10 @@ int sens_plan(pdscan::SensPlan& q, const pdssm_dims* dims, int32_t chunk) {
                 dims->d_in, q.S, pdscan::kSensMaxS, q.bytes, pdscan::kMaxLds);
   if ((uint64_t)q.nC * dims->B * dims->H > 0x7fffffffull)
     return fail(PDSSM_EUNSUPPORTED, "too many chunks");
+  if (lookback_giveup_hook()) {
+    q.force_giveup = 1;
+    q.spin_limit = 2;
+  }
   return PDSSM_OK;
 }
 
@@ -246,6 +265,19 @@ int check_n_out(int32_t n_out) {
 extern "C" {
 
 int pdssm_abi_version(void) { return PDSSM_ABI_VERSION; }
+
+int pdssm_workspace_status(const void* workspace, size_t workspace_bytes, uint32_t* status, void* stream) {
+  if (!workspace) return fail(PDSSM_EINVAL, "workspace is NULL");
+  if (!status) return fail(PDSSM_EINVAL, "status is NULL");
+  if ((uintptr_t)workspace & 15) return fail(PDSSM_EINVAL, "workspace is not 16-byte aligned");
+  if ((uintptr_t)status & 3) return fail(PDSSM_EINVAL, "status is not 4-byte aligned");
+  if (workspace_bytes < 256)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes is smaller than its 256-byte header", workspace_bytes);
+  const hipError_t e = pdscan::launch_status(workspace, status, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return PDSSM_OK;
+}
 
 const char* pdssm_last_error(void) { return g_err; }
 
@@ -384,6 +416,10 @@ int pdssm_scan_fwd_pidx(const pdssm_dims* dims, int32_t chunk, const int32_t* P_
                          dd.in_dtype == PDSSM_BF16, chunk, 0, sm ? 1 : 0))
     return fail(PDSSM_EUNSUPPORTED, "chunk=%d with N=%d needs %d bytes of on-chip memory with per-step "
                 "maps (limit %d); use a shorter chunk", chunk, dd.N, p.lds_bytes, pdscan::kMaxLds);
+  if (lookback_giveup_hook()) {
+    p.force_giveup = 1;
+    p.spin_limit = 2;
+  }
   if (workspace_bytes < p.ws_bytes)
     return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 p.ws_bytes);

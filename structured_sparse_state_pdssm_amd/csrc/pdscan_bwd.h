@@ -306,8 +306,9 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_bwd_kernel(BwdArgs a) {
       if (f & 1) { hit = q; break; }
       if (!(f & 2)) break;
     }
-    if (hit >= 0) break;
-    if (spins >= kSpinLimit) {
+    if (hit >= 0 && !a.p.force_giveup) break;
+    if (spins >= a.p.spin_limit) {                 // give up: zero carry, flag the call
+      hit = -1;
       if (tid == 0) atomicOr(&hdr[kWsError], 1u);
       break;
     }

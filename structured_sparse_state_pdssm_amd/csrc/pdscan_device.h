@@ -47,7 +47,6 @@ typedef int i4v __attribute__((ext_vector_type(4)));
 typedef int i2v __attribute__((ext_vector_type(2)));
 
 constexpr uint64_t kTagValid = 1ull << 32;
-constexpr int kSpinLimit = 1 << 22;
 constexpr int kBuBlock = 16;   // phase-A steps whose drive terms sit in registers
 
 // Compiler-level ordering point between LDS accesses of different lanes of
@@ -902,8 +901,9 @@ __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, i
       if (f & 1) { hit = q; break; }
       if (!(f & 2)) break;
     }
-    if (hit >= 0) break;
-    if (spins >= kSpinLimit) {
+    if (hit >= 0 && !p.force_giveup) break;
+    if (spins >= p.spin_limit) {                   // give up: carry h0, flag the call
+      hit = -1;
       if (tid == 0) atomicOr(&hdr[kWsError], 1u);
       break;
     }

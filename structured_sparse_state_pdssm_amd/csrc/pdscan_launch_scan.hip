@@ -20,6 +20,17 @@ void launch_clear(const Args& a, hipStream_t st) {
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)cb), dim3(256), 0, st, (uint64_t*)a.ws, words);
 }
 
+// status[0] |= the error word of the call that last used the workspace
+__global__ void status_kernel(const uint32_t* hdr, uint32_t* status) {
+  if (threadIdx.x == 0)
+    status[0] |= __hip_atomic_load(hdr + kWsError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_status(const void* ws, uint32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(status_kernel, dim3(1), dim3(64), 0, st, (const uint32_t*)ws, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const Args& a, hipStream_t st) {
   launch_clear(a, st);
   if (a.p.step16) {

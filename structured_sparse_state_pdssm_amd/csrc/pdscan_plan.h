@@ -20,6 +20,7 @@ constexpr int kSelectRows = 256;       // rows per workgroup for selection alone
 constexpr int kMaxLds = 64 * 1024;     // bytes of LDS one workgroup may use
 constexpr int kWbFrags = 6;            // W_b fragments per lane at most (fp32 d = 64: 2 blocks x 3 pieces)
 constexpr int kMaxOut = 4;             // outputs per head (rows of C) on the multi-output paths
+constexpr int kSpinLimit = 1 << 22;    // window reads before a look-back wait gives up
 
 enum Mode : int { kModeSelect = 0, kModeScan = 1, kModeFused = 2 };
 
@@ -45,6 +46,11 @@ struct Plan {
   int wst;       // fused deep bf16 selection: weight blocks staged through LDS (in D's region)
   int YS;        // stride of the per-output local-output rows
   int tasks;     // workgroups
+  // look-back: window reads before a wait gives up (sets the workspace error
+  // word and carries h0), and a test hook that ignores every carry found, so
+  // that each wait runs out after spin_limit reads while the kernel still
+  // ends normally
+  int spin_limit, force_giveup;
   // LDS byte offsets
   int off_D, off_k, off_yl, off_dict, off_DC, off_SRC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
       off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_WB, off_misc, lds_bytes;
@@ -64,6 +70,8 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
                            int in_bf16, int chunk, int fold_bu, int step16, int n_out, int allow_gse) {
   p.B = B; p.H = H; p.L = L; p.N = N; p.K = K; p.d = d;
   p.u_shared = u_shared; p.in_bf16 = in_bf16;
+  p.spin_limit = kSpinLimit;
+  p.force_giveup = 0;
   // a chunk longer than the sequence behaves exactly like chunk = L
   p.chunk = (mode == kModeSelect) ? kSelectRows : (chunk < L ? chunk : L);
   // Step-major fused path: 16-lane groups, each MFMA tile holding four steps
@@ -210,6 +218,6 @@ struct Args {
 
 // Workspace header words.
 constexpr int kWsTicket = 0;   // uint32 ticket counter
-constexpr int kWsError = 1;    // uint32: nonzero if a look-back wait gave up
+constexpr int kWsError = 1;    // uint32: nonzero if a look-back wait of this call gave up
 
 }  // namespace pdscan

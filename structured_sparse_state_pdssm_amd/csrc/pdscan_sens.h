@@ -275,8 +275,8 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_sens_kernel(SensArgs a) {
       if (f & 1) { hit = qx; break; }
       if (!(f & 2)) break;
     }
-    if (hit >= 0) break;
-    if (spins >= kSpinLimit) {
+    if (hit >= 0 && !a.q.force_giveup) break;
+    if (spins >= a.q.spin_limit) {                 // give up: flag the call
       if (tid == 0) atomicOr(&hdr[kWsError], 1u);
       hit = 0;
       break;

@@ -16,6 +16,7 @@ constexpr int kSensMaxS = 32;    // steps per lane group at most (chunk <= 512)
 struct SensPlan {
   int B, H, L, N, K, d, in_bf16, chunk;
   int S, G, GS, nC, tasks;
+  int spin_limit, force_giveup;   // look-back give-up, as in Plan
   int off_dk, off_C, off_k, off_W, off_cb, off_P, off_V, off_win, off_misc, bytes;
   size_t ws_agg, ws_inc, ws_bytes;
 };
@@ -24,6 +25,8 @@ inline bool make_sens_plan(SensPlan& q, int B, int H, int L, int N, int K, int d
                            int chunk) {
   q.B = B; q.H = H; q.L = L; q.N = N; q.K = K; q.d = d; q.in_bf16 = in_bf16;
   q.chunk = chunk < L ? chunk : L;
+  q.spin_limit = kSpinLimit;
+  q.force_giveup = 0;
   q.G = kThreads / 16;
   q.S = align_up((q.chunk + q.G - 1) / q.G, 4);
   q.GS = q.S * kSensRow + kSensRow;               // group stride, 16 (mod 64) words

@@ -190,3 +190,17 @@ def test_multi_output_validation(P):
                                   A + 4 * big, A + 5 * big, A + 6 * big, None, None, None, A + 7 * big,
                                   A + 8 * big, A + 9 * big, 0, None)
     assert rc == -3
+
+
+def test_workspace_status_validation(P):
+    """pdssm_workspace_status: NULL or misaligned pointers are invalid, a
+    buffer shorter than the 256-byte header is a workspace error; all are
+    rejected before anything is enqueued."""
+    st = A + (10 << 30)
+    fn = P.lib.pdssm_workspace_status
+    assert fn(None, 4096, st, None) == -1 and b"workspace" in P.lib.pdssm_last_error()
+    assert fn(A, 4096, None, None) == -1 and b"status" in P.lib.pdssm_last_error()
+    assert fn(A + 8, 4096, st, None) == -1 and b"aligned" in P.lib.pdssm_last_error()
+    assert fn(A, 4096, st + 2, None) == -1 and b"aligned" in P.lib.pdssm_last_error()
+    assert fn(A, 255, st, None) == -3 and b"header" in P.lib.pdssm_last_error()
+

@@ -90,9 +90,8 @@ def test_soft_forward_parity(key):
 @pytest.mark.parametrize("N", [16, 5, 20])
 def test_scan_pidx_chunk_independence(chunk, N):
     """N <= 16 with chunks up to 512: maps streamed through registers (the
-    step-major scan); N = 20: one on-chip table entry per step."""
-    if N == 20 and chunk > 192:
-        pytest.skip("the per-step table of N = 20 exceeds on-chip memory past 192 steps")
+    step-major scan); N = 20: one on-chip table entry per step (it fits up to
+    548 steps: 512 takes 61.7 KB of the 64 KiB)."""
     rng = np.random.default_rng(chunk + 1000 * N)
     B, H, L = 2, 3, 600
     pidx = rng.integers(0, N, (B, H, L, N)).astype(np.int32)
@@ -108,12 +107,14 @@ def test_scan_pidx_chunk_independence(chunk, N):
     assert_within(host(hL), hr, f"chunk {chunk} h_L")
 
 
-def test_scan_pidx_rejects_a_chunk_too_long_for_its_table():
+@pytest.mark.parametrize("N,chunk", [(16, 1024), (20, 549), (20, 1024)])
+def test_scan_pidx_rejects_a_chunk_too_long_for_its_table(N, chunk):
+    """The header's limits: N = 16 above 512 steps, N = 20 above 548."""
     P = lib()
-    z = np.zeros((1, 1, 2048, 16), dtype=np.float32)
+    z = np.zeros((1, 1, 2048, N), dtype=np.float32)
     with pytest.raises(P.PdssmError) as e:
-        P.pdssm_scan_fwd_pidx(to_dev(z.astype(np.int32)), to_dev(z), to_dev(z), to_dev(np.zeros((1, 16), np.float32)),
-                              chunk=1024)
+        P.pdssm_scan_fwd_pidx(to_dev(z.astype(np.int32)), to_dev(z), to_dev(z), to_dev(np.zeros((1, N), np.float32)),
+                              chunk=chunk)
     assert e.value.status == P.PDSSM_EUNSUPPORTED
 
 
