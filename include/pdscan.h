@@ -135,6 +135,32 @@ int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* 
               int32_t* k_star, float* D, float* y, float* h_L,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Look-back scratch the allocation-free call below holds on each device. */
+#define PDSSM_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* pdssm_fwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Arguments and outputs as in pdssm_fwd; the look-back
+ * scratch (pdssm_fwd_workspace_bytes of it) lives in a 16 MiB device array
+ * that the library holds on each GPU it runs on, until the process ends.
+ *   status: optional (NULL: not written); one uint32 in device memory or
+ *     pinned host memory, 4-byte aligned.  The call ORs its look-back error
+ *     word into status[0] (nonzero = a wait gave up; see "Workspace header").
+ * Every call on a GPU uses that GPU's one array (the array of the device
+ * current at the call): two calls that may overlap on one GPU (different
+ * streams, or host threads without ordering) race and give wrong results;
+ * order them on one stream.  Each call clears the part of the array it uses
+ * first, so nothing carries over from the previous call.  The array is found
+ * on the first call on each device; calls allocate nothing.
+ * Returns PDSSM_EUNSUPPORTED when the call needs more scratch than
+ * PDSSM_NOALLOC_SCRATCH_BYTES (pdssm_fwd_workspace_bytes above 16 MiB), with
+ * the other statuses as pdssm_fwd. */
+int pdssm_fwd_noalloc(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
+                      const int32_t* dict_idx, const void* W_d, const float* b_d,
+                      const float* Bu, const float* C, const float* h0,
+                      int32_t* k_star, float* D, float* y, float* h_L,
+                      uint32_t* status, void* stream);
+
 /* pdssm_fwd with the drive term computed in the same pass: Bu_t = W_b u_t
  * (the input map B of the state-space recurrence, "Flash PD-SSM" summary,
  * methodology item 1) is a third column tile of the selection GEMM, so Bu is

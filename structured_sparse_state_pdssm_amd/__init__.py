@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     PDSSM_EUNSUPPORTED,
     PDSSM_EWORKSPACE,
     PDSSM_F32,
+    PDSSM_NOALLOC_SCRATCH_BYTES,
     PDSSM_OK,
     PdssmDims,
     PdssmError,
@@ -254,6 +255,28 @@ def pdssm_fwd(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0=None, chunk=128, want_k=Fa
                          _ptr(W_d), _ptr(b_d), _ptr(Bu), _ptr(C), _ptr(h0),
                          _ptr(res.get("k_star")), _ptr(res.get("D")), _ptr(res["y"]),
                          _ptr(res["h_L"]), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev)))
+    return res
+
+
+def pdssm_fwd_noalloc(u, W_sel, dict_idx, W_d, b_d, Bu, C, h0=None, chunk=128, want_k=False,
+                      want_D=False, status=None, out=None):
+    """pdssm_fwd without a workspace: the look-back scratch is the library's
+    own per-device array (calls on one GPU must not overlap).  ``status`` (a
+    device int32 tensor of one element, optional) receives the look-back
+    error word ORed in.  Returns dict(y, h_L[, k_star][, D])."""
+    torch = _torch()
+    dims, B, H, L, N, K, d = _fwd_common(u, W_sel, W_d)
+    dev = u.device
+    res = _fwd_outputs(out or {}, B, H, L, N, want_k, want_D, dev)
+    _args((u, "u", None, None), (W_sel, "W_sel", None, None), (W_d, "W_d", None, None),
+          (dict_idx, "dict_idx", (H, K, N), torch.int32), (b_d, "b_d", (H, N), torch.float32),
+          (Bu, "Bu", (B, H, L, N), torch.float32), (C, "C", (H, N), torch.float32),
+          (h0, "h0", (B, H, N), torch.float32), (status, "status", (1,), torch.int32),
+          *_fwd_out_specs(res, B, H, L, N))
+    _check(lib.pdssm_fwd_noalloc(ctypes.byref(dims), int(chunk), _ptr(u), _ptr(W_sel), _ptr(dict_idx),
+                                 _ptr(W_d), _ptr(b_d), _ptr(Bu), _ptr(C), _ptr(h0),
+                                 _ptr(res.get("k_star")), _ptr(res.get("D")), _ptr(res["y"]),
+                                 _ptr(res["h_L"]), _ptr(status), _stream(dev)))
     return res
 
 
@@ -493,4 +516,4 @@ def workspace_error_flag(workspace):
     return int(st.item())
 
 
-__all__ += ["pdssm_workspace_status", "workspace_error_flag"]
+__all__ += ["pdssm_workspace_status", "workspace_error_flag", "pdssm_fwd_noalloc"]

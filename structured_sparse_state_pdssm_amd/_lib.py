@@ -13,6 +13,7 @@ PDSSM_EWORKSPACE = -3
 PDSSM_EHIP = -4
 PDSSM_F32 = 0
 PDSSM_BF16 = 1
+PDSSM_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class PdssmDims(ctypes.Structure):
@@ -59,6 +60,7 @@ def _load():
         "pdssm_last_error": [],
         "pdssm_abi_version": [],
         "pdssm_workspace_status": [vp, sz, vp, vp],
+        "pdssm_fwd_noalloc": [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -27,6 +27,7 @@ hipError_t launch_sens(const SensArgs& a, hipStream_t st);
 hipError_t launch_soft(const SoftArgs& a, hipStream_t st);
 hipError_t launch_dict_hardmax(const float* M, int32_t* dict, int HK, int N, hipStream_t st);
 hipError_t launch_status(const void* ws, uint32_t* status, hipStream_t st);
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 }
 
 using pdscan::Plan;
@@ -378,6 +379,48 @@ int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* 
   a.Bu = Bu; a.C = C; a.h0 = h0; a.k_out = k_star; a.D_out = D;
   a.y = y; a.hL = h_L; a.ws = (unsigned char*)workspace;
   return dispatch(pdscan::kModeFused, a, stream);
+}
+
+int pdssm_fwd_noalloc(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
+                      const int32_t* dict_idx, const void* W_d, const float* b_d, const float* Bu,
+                      const float* C, const float* h0, int32_t* k_star, float* D, float* y, float* h_L,
+                      uint32_t* status, void* stream) {
+  int rc = check_dims(dims, chunk);
+  if (rc) return rc;
+  Plan p;
+  if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk))) return rc;
+  if (p.ws_bytes > (size_t)PDSSM_NOALLOC_SCRATCH_BYTES)
+    return fail(PDSSM_EUNSUPPORTED, "this call needs %zu bytes of look-back scratch, more than the %zu the "
+                "allocation-free entry point holds per device (use pdssm_fwd with a workspace, or a longer "
+                "chunk)", p.ws_bytes, (size_t)PDSSM_NOALLOC_SCRATCH_BYTES);
+  if (status && ((uintptr_t)status & 3)) return fail(PDSSM_EINVAL, "status is not 4-byte aligned");
+  const Sizes z = sizes(dims);
+  const Range in[] = {{"u", u, z.u},         {"W_sel", W_sel, z.Wsel}, {"dict_idx", dict_idx, z.dict},
+                      {"W_d", W_d, z.Wd},    {"b_d", b_d, z.bd},       {"Bu", Bu, z.Bu},
+                      {"C", C, z.C},         {"h0", h0, z.h0}};
+  const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y}, {"h_L", h_L, z.hL}};
+  static const char* const req[] = {"u", "W_sel", "dict_idx", "W_d", "b_d", "Bu", "C", "y", "h_L", nullptr};
+  if ((rc = check_ptrs(in, 8, out, 4, req))) return rc;
+  for (const Range& r : in)
+    if (overlap({"status", status, 4}, r)) return fail(PDSSM_EINVAL, "status overlaps input %s", r.name);
+  for (const Range& r : out)
+    if (overlap({"status", status, 4}, r)) return fail(PDSSM_EINVAL, "status overlaps output %s", r.name);
+  void* scratch = nullptr;
+  size_t cap = 0;
+  hipError_t e = pdscan::noalloc_scratch(&scratch, &cap);
+  if (e != hipSuccess) return fail(PDSSM_EHIP, "device scratch lookup failed: %s", hipGetErrorString(e));
+  if (p.ws_bytes > cap) return fail(PDSSM_EUNSUPPORTED, "scratch of %zu bytes < %zu needed", cap, p.ws_bytes);
+  pdscan::Args a = {};
+  a.p = p;
+  a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx;
+  a.Bu = Bu; a.C = C; a.h0 = h0; a.k_out = k_star; a.D_out = D;
+  a.y = y; a.hL = h_L; a.ws = (unsigned char*)scratch;
+  if ((rc = dispatch(pdscan::kModeFused, a, stream))) return rc;
+  if (status) {
+    e = pdscan::launch_status(scratch, status, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return PDSSM_OK;
 }
 
 int pdssm_fwd_wb(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,

@@ -27,6 +27,7 @@ hipError_t launch_sens(const SensArgs&, hipStream_t) { return stub("sens"); }
 hipError_t launch_soft(const SoftArgs&, hipStream_t) { return stub("soft"); }
 hipError_t launch_dict_hardmax(const float*, int32_t*, int, int, hipStream_t) { return stub("dict_hardmax"); }
 hipError_t launch_status(const void*, uint32_t*, hipStream_t) { return stub("status"); }
+hipError_t noalloc_scratch(void**, size_t*) { return stub("noalloc_scratch"); }
 }  // namespace pdscan
 
 extern "C" const char* hipGetErrorString(hipError_t) { return "stub"; }

@@ -204,3 +204,25 @@ def test_workspace_status_validation(P):
     assert fn(A, 4096, st + 2, None) == -1 and b"aligned" in P.lib.pdssm_last_error()
     assert fn(A, 255, st, None) == -3 and b"header" in P.lib.pdssm_last_error()
 
+
+def test_noalloc_validation(P):
+    """The allocation-free entry point validates like pdssm_fwd and refuses,
+    before any HIP call, a call whose look-back scratch would exceed its
+    per-device array."""
+    big = 1 << 30
+    fn = P.lib.pdssm_fwd_noalloc
+    d = _dims(P, B=8, L=131072)                      # 256 chunks x 256 sequences: 32 MiB of scratch
+    assert P.fwd_workspace_bytes(d, 512) > P.PDSSM_NOALLOC_SCRATCH_BYTES
+    args = [A, A + big, A + 2 * big, A + 3 * big, A + 4 * big, A + 5 * big, A + 6 * big, None, None, None,
+            A + 7 * big, A + 8 * big, None, None]
+    assert fn(ctypes.byref(d), 512, *args) == -2 and b"scratch" in P.lib.pdssm_last_error()
+    d = _dims(P, L=2048)
+    bad = list(args)
+    bad[5] = None                                    # Bu
+    assert fn(ctypes.byref(d), 128, *bad) == -1 and b"Bu" in P.lib.pdssm_last_error()
+    bad = list(args)
+    bad[12] = A + 9 * big + 2                        # misaligned status
+    assert fn(ctypes.byref(d), 128, *bad) == -1 and b"status" in P.lib.pdssm_last_error()
+    bad = list(args)
+    bad[12] = A + 7 * big                            # status inside y
+    assert fn(ctypes.byref(d), 128, *bad) == -1 and b"overlaps" in P.lib.pdssm_last_error()
