@@ -697,7 +697,7 @@ def bench_multi(args, torch, np, P):
     from pdssm_inputs import generate, get_config
     cfg = get_config(args.workload)
     P_out = args.n_out
-    chunk = args.chunk or (256 if P_out <= 2 else 128)
+    chunk = args.chunk or min(cfg.chunk, 256 if P_out <= 2 else 128)
     t0 = time.time()
     inp = generate(cfg)
     print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)

@@ -163,15 +163,22 @@ int pdssm_fwd_noalloc(const pdssm_dims* dims, int32_t chunk, const void* u, cons
 
 /* pdssm_fwd with the drive term computed in the same pass: Bu_t = W_b u_t
  * (the input map B of the state-space recurrence, "Flash PD-SSM" summary,
- * methodology item 1) is a third column tile of the selection GEMM, so Bu is
- * never read from or written to memory.
+ * problem statement and methodology item 1) is a third set of columns of the
+ * selection GEMM, so Bu is never read from or written to memory.
  *   W_b [H,N,d_in] (in, u's dtype): row n holds the weights of state row n.
  *   All other arguments, the workspace (pdssm_fwd_workspace_bytes) and the
- *   outputs as in pdssm_fwd.  The products are formed like the scores (fp32
- *   for fp32 inputs, bf16 x bf16 with fp32 accumulation for bf16 inputs).
- * Shapes: the step-major kernel only (per-head u, N <= 16, K <= 16,
- * chunk <= 512, fp32 d_in in {16, 32, 64} or bf16 d_in = 128); anything else
- * returns PDSSM_EUNSUPPORTED. */
+ *   outputs as in pdssm_fwd (u per head or shared by the heads).  The
+ *   products are formed like the scores (fp32 for fp32 inputs, bf16 x bf16
+ *   with fp32 accumulation for bf16 inputs with d_in >= 128).
+ * Shapes: the step-major kernel (per-head u, N <= 16, K <= 16, chunk <= 512,
+ * fp32 d_in in {16, 32, 64} or bf16 d_in = 128: W_b is a third MFMA tile) and
+ * the general kernel (every other shape: the drive terms of a chunk go to an
+ * on-chip [N][chunk] buffer) when its selection GEMM holds the columns:
+ * K + 2N <= 128, or for bf16 inputs with d_in >= 256 (a multiple of 32)
+ * ceil(K/16) + 2 ceil(N/16) <= 10 tiles (N = 64 with K <= 32).  On the
+ * general kernel the chunk's on-chip footprint (about chunk * (2N + 2) * 4
+ * bytes plus the dictionary tables) may take up to the 160 KiB LDS of one
+ * compute unit.  Anything else returns PDSSM_EUNSUPPORTED. */
 int pdssm_fwd_wb(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
                  const int32_t* dict_idx, const void* W_d, const float* b_d,
                  const void* W_b, const float* C, const float* h0,
@@ -220,19 +227,22 @@ int pdssm_scan_bwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
  *   C      [H,n_out,N] fp32 (in): row o of head h is C[h,o,:];
  *   y      [B,H,L,n_out] fp32 (out): y[b,h,t,o] = C[h,o,:] . h_t.
  * Everything else, the workspace (pdssm_fwd_workspace_bytes) and the shape
- * limits as in pdssm_fwd_wb.  The on-chip output weights grow with n_out, so
- * the chunk shrinks with it (N = 16: n_out = 2 up to chunk 256, n_out = 3 or 4
- * up to chunk 128); a chunk that does not fit returns PDSSM_EUNSUPPORTED. */
+ * limits as in pdssm_fwd_wb.  The on-chip output weights grow with n_out
+ * (n_out * N * chunk * 4 bytes), so the longest chunk shrinks with it
+ * (step-major kernel, N = 16: n_out = 2 up to chunk 256, n_out = 3 or 4 up to
+ * 128; general kernel within 160 KiB, e.g. N = 64 with d_in = 768 and the
+ * drive folded: n_out = 2 up to chunk 128); a chunk that does not fit returns
+ * PDSSM_EUNSUPPORTED. */
 int pdssm_fwd_wb_multi(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const void* u,
                        const void* W_sel, const int32_t* dict_idx, const void* W_d, const float* b_d,
                        const void* W_b, const float* C, const float* h0, int32_t* k_star, float* D,
                        float* y, float* h_L, void* workspace, size_t workspace_bytes, void* stream);
 
 /* pdssm_scan_fwd with several outputs per head: C [H,n_out,N] and
- * y [B,H,L,n_out] as in pdssm_fwd_wb_multi; 1 <= n_out <= 4.  Runs on the
- * step-major scan only (N <= 16, K <= 16, chunk <= 512 and fitting on chip as
- * above); otherwise PDSSM_EUNSUPPORTED.  Workspace as
- * pdssm_scan_workspace_bytes. */
+ * y [B,H,L,n_out] as in pdssm_fwd_wb_multi; 1 <= n_out <= 4.  The step-major
+ * scan (N <= 16, K <= 16, chunk <= 512) or the general one; a chunk whose
+ * per-output on-chip rows do not fit returns PDSSM_EUNSUPPORTED.  Workspace
+ * as pdssm_scan_workspace_bytes. */
 int pdssm_scan_fwd_multi(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const int32_t* k_star,
                          const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
                          const float* h0, float* y, float* h_L, void* workspace, size_t workspace_bytes,

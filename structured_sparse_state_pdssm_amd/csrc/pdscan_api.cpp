@@ -94,7 +94,7 @@ int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_b
                          d->in_dtype == PDSSM_BF16, c, fold_bu, step16, n_out))
     return fail(PDSSM_EUNSUPPORTED,
                 "chunk=%d with N=%d needs %d bytes of on-chip memory per workgroup (limit %d)", c,
-                d->N, p.lds_bytes, pdscan::kMaxLds);
+                d->N, p.lds_bytes, p.lds_limit);
   if ((uint64_t)p.nC * d->B * d->H > 0x7fffffffull)
     return fail(PDSSM_EUNSUPPORTED, "too many chunks");
   if (lookback_giveup_hook()) {
@@ -201,9 +201,6 @@ int scan_fwd_impl(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const in
   if (rc) return rc;
   Plan p;
   if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk, 0, 1, n_out))) return rc;
-  if (n_out > 1 && !p.step16)
-    return fail(PDSSM_EUNSUPPORTED, "several outputs per head need the step-major scan: N <= 16, K <= 16, "
-                "chunk <= 512 (got N=%d K=%d chunk=%d)", dims->N, dims->K, chunk);
   if (workspace_bytes < p.ws_bytes)
     return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 p.ws_bytes);
@@ -231,10 +228,10 @@ int fwd_wb_impl(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const void
   if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk, 1, 0, n_out))) return rc;
   if (!p.fold_bu)
     return fail(PDSSM_EUNSUPPORTED,
-                "the drive term is folded into the step-major kernel only: per-head u, N <= 16, "
-                "K <= 16, chunk <= 512, fp32 d in {16, 32, 64} or bf16 d = 128 (got u_shared=%d "
-                "N=%d K=%d d=%d %s)", dims->u_shared, dims->N, dims->K, dims->d_in,
-                dims->in_dtype == PDSSM_BF16 ? "bf16" : "fp32");
+                "the drive term cannot be folded for this shape: the selection GEMM would need more "
+                "column tiles than the kernel holds (K + 2N <= 128, or with bf16 d >= 256 at most %d "
+                "tiles of 16; got N=%d K=%d d=%d %s)", pdscan::kFoldMaxTiles, dims->N, dims->K,
+                dims->d_in, dims->in_dtype == PDSSM_BF16 ? "bf16" : "fp32");
   if (workspace_bytes < p.ws_bytes)
     return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 p.ws_bytes);
@@ -328,8 +325,20 @@ int pdssm_fwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* byt
   int rc = check_dims(dims, chunk);
   if (rc) return rc;
   if (!bytes) return fail(PDSSM_EINVAL, "bytes is NULL");
+  // The size depends only on the chunk count; the shape is accepted when
+  // any of the fused calls that take this workspace (pdssm_fwd, pdssm_fwd_wb,
+  // pdssm_fwd_wb_multi) can run it, whose on-chip budgets differ.
   Plan p;
-  if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk))) return rc;
+  rc = build_plan(p, pdscan::kModeFused, dims, chunk);
+  for (int n_out = 1; rc == PDSSM_EUNSUPPORTED && n_out <= pdscan::kMaxOut; ++n_out) {
+    Plan q;
+    if (build_plan(q, pdscan::kModeFused, dims, chunk, 1, 0, n_out) == PDSSM_OK && q.fold_bu) {
+      p = q;
+      rc = PDSSM_OK;
+      g_err[0] = 0;
+    }
+  }
+  if (rc) return rc;
   *bytes = p.ws_bytes;
   return PDSSM_OK;
 }

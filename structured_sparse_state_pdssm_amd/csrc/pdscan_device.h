@@ -233,6 +233,7 @@ struct SelDst {
   const int* dic; // LDS dictionary [K][N] (for P_out)
   size_t gbase;   // global row index of chunk row 0 = s*L + c0
   unsigned char* wst;  // deep path: LDS stages for the weight blocks, or nullptr
+  float* Bubuf;   // drive folded: [N][TS] drive terms of the chunk (fused), or nullptr
 };
 
 template <int IN_BF16, int MMA_BF16>
@@ -337,10 +338,13 @@ template <int MMA_BF16>
 constexpr int kChanBlock = MMA_BF16 ? 32 : 16;
 
 // Epilogue of one tile: argmax over score columns, logistic of the
-// pre-activations, stores.  rows >= rlim are not stored.
-// Column of tile t: 16 t + i when kt < 0 (scores then pre-activations,
-// contiguous); with kt >= 0 the first kt tiles hold the scores and tile
-// t >= kt holds pre-activation 16 (t - kt) + i, i.e. column K + 16 (t - kt) + i.
+// pre-activations, drive terms (drive folded), stores.  rows >= rlim are not
+// stored.  Columns: [0, K) scores, [K, K + N) pre-activations, [K + N,
+// K + 2N) drive terms.  Column of tile t: 16 t + i when kt < 0 (the three
+// segments contiguous); with kt >= 0 the first kt tiles hold the scores,
+// the next ceil(N / 16) the pre-activations (column K + 16 (t - kt) + i) and
+// the ones after them the drive terms, so that no tile straddles two weight
+// matrices.
 template <int NCT>
 __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, const float* bdr,
                                               int row0, int rlim, int lane, const SelDst& o,
@@ -389,9 +393,19 @@ __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, con
     if (o.k_out)
       for (int r = 0; r < 4; ++r) if (rb + r < rlim) o.k_out[o.gbase + rb + r] = bk[r];
   }
+  const int nt = (N + 15) >> 4;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const int col = (kt < 0 || ct0 + ct < kt) ? 16 * (ct0 + ct) + i : K + 16 * (ct0 + ct - kt) + i;
+    const int t = ct0 + ct;
+    const int col = (kt < 0 || t < kt) ? 16 * t + i
+                                       : (t < kt + nt ? K + 16 * (t - kt) + i : K + N + 16 * (t - kt - nt) + i);
+    if (o.Bubuf && col >= K + N && col < K + 2 * N) {
+      // drive term Bu_t[n] = W_b[n, :] u_t, raw
+      float* dst = o.Bubuf + (col - K - N) * o.TS + rb;
+      if (full) *(f4v*)dst = acc[ct];
+      else
+        for (int r = 0; r < 4; ++r) if (rb + r < rlim) dst[r] = acc[ct][r];
+    }
     if (col >= K && col < K + N) {
       const int n = col - K;
       f4v dv;
@@ -436,12 +450,14 @@ __device__ __forceinline__ void select_rows(const Args& a, int s_u, int h, int c
   for (int ct = 0; ct < NCT; ++ct) {
     const int col = 16 * ct + i;
     const bool sc = col < K, zc = col >= K && col < K + N;
-    const void* wb = sc ? a.W_sel : a.W_d;
-    const size_t wrow = sc ? ((size_t)h * K + col) * d : ((size_t)h * N + (col - K)) * d;
+    const bool bc = p.fold_bu && col >= K + N && col < K + 2 * N;   // drive folded: rows of W_b
+    const void* wb = sc ? a.W_sel : (zc ? a.W_d : a.W_b);
+    const size_t wrow = sc ? ((size_t)h * K + col) * d
+                           : (zc ? ((size_t)h * N + (col - K)) * d : ((size_t)h * N + (col - K - N)) * d);
 #pragma unroll
     for (int m = 0; m < KCH; ++m) {
       const int ch = m * CB + PER * g;
-      wf[ct][m] = load_frag<IN_BF16, MMA_BF16>(wb, wrow + ch, (sc || zc) && ch < d);
+      wf[ct][m] = load_frag<IN_BF16, MMA_BF16>(wb, wrow + ch, (sc || zc || bc) && ch < d);
     }
     bdr[ct] = zc ? a.b_d[(size_t)h * N + col - K] : 0.f;
   }
@@ -512,9 +528,11 @@ __device__ __forceinline__ void select_rows_any(const Args& a, int s_u, int h, i
         if (ct < NCT) {
           const int col = 16 * ct + i;
           const bool sc = col < K, zc = col >= K && col < K + N;
-          const void* wb = sc ? a.W_sel : a.W_d;
-          const size_t wrow = sc ? ((size_t)h * K + col) * d : ((size_t)h * N + (col - K)) * d;
-          const FT bw = load_frag<IN_BF16, MMA_BF16>(wb, wrow + ch, (sc || zc) && ch < d);
+          const bool bc = p.fold_bu && col >= K + N && col < K + 2 * N;
+          const void* wb = sc ? a.W_sel : (zc ? a.W_d : a.W_b);
+          const size_t wrow = sc ? ((size_t)h * K + col) * d
+                                 : (zc ? ((size_t)h * N + (col - K)) * d : ((size_t)h * N + (col - K - N)) * d);
+          const FT bw = load_frag<IN_BF16, MMA_BF16>(wb, wrow + ch, (sc || zc || bc) && ch < d);
           mma_step<IN_BF16, MMA_BF16>(acc[ct], av, bw);
         }
       }
@@ -548,10 +566,13 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
   // pre-activation columns (rows of W_d), so that every tile reads one
   // matrix and its loads need no branch (a branch between loads into one
   // register makes the compiler drain every load in flight)
-  const int KT = (K + 15) >> 4;
+  const int KT = (K + 15) >> 4, NT = (N + 15) >> 4;
   constexpr int CP = NCT <= 6 ? NCT : 4;           // column tiles per pass
   const rsrc_t rs = make_rsrc((const uint16_t*)a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
   const rsrc_t rz = make_rsrc((const uint16_t*)a.W_d + (size_t)h * N * d, (uint32_t)(N * d * 2));
+  // drive folded: tiles KT + NT .. KT + 2 NT - 1 read rows of W_b
+  const rsrc_t rbw = make_rsrc(p.fold_bu ? (const uint16_t*)a.W_b + (size_t)h * N * d : nullptr,
+                               p.fold_bu ? (uint32_t)(N * d * 2) : 0u);
   const int Tc = min(p.chunk, p.L - c0);
   const rsrc_t ur = make_rsrc((const uint16_t*)a.u + ((size_t)s_u * p.L + c0) * d, (uint32_t)(Tc * d * 2));
 
@@ -571,12 +592,13 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
       rsrc_t wr[CP];
 #pragma unroll
       for (int ct = 0; ct < CP; ++ct) {
-        const bool sc = ct0 + ct < KT;
-        const int m = sc ? 16 * (ct0 + ct) + i : 16 * (ct0 + ct - KT) + i;
-        const bool ok = m < (sc ? K : N);
+        const int t = ct0 + ct;
+        const int seg = t < KT ? 0 : (t < KT + NT ? 1 : 2);   // W_sel, W_d, W_b
+        const int m = seg == 0 ? 16 * t + i : (seg == 1 ? 16 * (t - KT) + i : 16 * (t - KT - NT) + i);
+        const bool ok = seg == 0 ? m < K : (seg == 1 ? m < N : (p.fold_bu && t < KT + 2 * NT && m < N));
         woff[ct] = ok ? (uint32_t)((m * d + 8 * g) * 2) : kNoLoad;
-        bdr[ct] = (ok && !sc) ? a.b_d[(size_t)h * N + m] : 0.f;
-        wr[ct] = sc ? rs : rz;
+        bdr[ct] = (ok && seg == 1) ? a.b_d[(size_t)h * N + m] : 0.f;
+        wr[ct] = seg == 0 ? rs : (seg == 1 ? rz : rbw);
       }
       constexpr int RING = CP > 4 ? 2 : 3;         // blocks in flight
       u4v Ar[RING][2], Br[RING][CP];
@@ -643,12 +665,14 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
   const int i = lane & 15, g = lane >> 4, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int K = p.K, N = p.N, d = p.d;
   const int KB = d >> 5;
-  const int KT = (K + 15) >> 4;
+  const int KT = (K + 15) >> 4, NT = (N + 15) >> 4;
   constexpr int kRow = 80, kStage = 16 * NCT * kRow;
   constexpr int TPW = (NCT + kWaves - 1) / kWaves;   // tiles this wave stages
   unsigned char* wst = o.wst;
   const rsrc_t rs = make_rsrc((const uint16_t*)a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
   const rsrc_t rz = make_rsrc((const uint16_t*)a.W_d + (size_t)h * N * d, (uint32_t)(N * d * 2));
+  const rsrc_t rbw = make_rsrc(p.fold_bu ? (const uint16_t*)a.W_b + (size_t)h * N * d : nullptr,
+                               p.fold_bu ? (uint32_t)(N * d * 2) : 0u);
   const int Tc = min(p.chunk, p.L - c0);
   const rsrc_t ur = make_rsrc((const uint16_t*)a.u + ((size_t)s_u * p.L + c0) * d, (uint32_t)(Tc * d * 2));
 
@@ -658,25 +682,26 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
     const int row = rbeg + 16 * rt + i;
     uoff[rt] = row < rend ? (uint32_t)((row * d + 8 * g) * 2) : kNoLoad;
   }
-  // tile t < KT: row 16 t + i of W_sel; tile t >= KT: row 16 (t - KT) + i of W_d
+  // tile t < KT: row 16 t + i of W_sel; KT <= t < KT + NT: row 16 (t - KT) + i
+  // of W_d; after them (drive folded) row 16 (t - KT - NT) + i of W_b
   uint32_t toff[TPW];
   int tlds[TPW];
   rsrc_t tr[TPW];
 #pragma unroll
   for (int w = 0; w < TPW; ++w) {
     const int t = wave + kWaves * w;               // uniform in the wave
-    const bool sc = t < KT;
-    const int m = sc ? 16 * t + i : 16 * (t - KT) + i;
-    const bool ok = t < NCT && m < (sc ? K : N);
+    const int seg = t < KT ? 0 : (t < KT + NT ? 1 : 2);
+    const int m = seg == 0 ? 16 * t + i : (seg == 1 ? 16 * (t - KT) + i : 16 * (t - KT - NT) + i);
+    const bool ok = t < NCT && (seg == 0 ? m < K : (seg == 1 ? m < N : (p.fold_bu && t < KT + 2 * NT && m < N)));
     toff[w] = ok ? (uint32_t)((m * d + 8 * g) * 2) : kNoLoad;
-    tr[w] = sc ? rs : rz;
+    tr[w] = seg == 0 ? rs : (seg == 1 ? rz : rbw);
     tlds[w] = (16 * t + i) * kRow + 16 * g;
   }
   float bdr[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const int n = 16 * (ct - KT) + i;
-    bdr[ct] = (ct >= KT && n < N) ? a.b_d[(size_t)h * N + n] : 0.f;
+    bdr[ct] = (ct >= KT && ct < KT + NT && n < N) ? a.b_d[(size_t)h * N + n] : 0.f;
   }
 
   u4v Ar[3][2], Wr[2][TPW];
@@ -742,7 +767,9 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
 // kSelDeep + n: the deep bf16 path with n column tiles, ceil(K / 16) score
 // tiles then ceil(N / 16) pre-activation tiles, rounded up to even (a shape
 // with fewer real column tiles computes zero tiles that are never written).
-enum SelPath : int { kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3, kSelDeep = 16 };
+enum SelPath : int {
+  kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3, kSelBF16D128N5 = 4, kSelDeep = 16
+};
 
 template <int IN_BF16, int MMA_BF16, int PATH>
 __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, int c0, int rbeg,
@@ -753,8 +780,10 @@ __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, i
     select_rows<0, 0, 1, 1>(a, s_u, h, c0, rbeg, rend, lane, o);
   else if constexpr (PATH == kSelBF16D128N3 && IN_BF16 && MMA_BF16)
     select_rows<1, 1, 4, 3>(a, s_u, h, c0, rbeg, rend, lane, o);
+  else if constexpr (PATH == kSelBF16D128N5 && IN_BF16 && MMA_BF16)
+    select_rows<1, 1, 4, 5>(a, s_u, h, c0, rbeg, rend, lane, o);
   else if constexpr (PATH > kSelDeep && IN_BF16 && MMA_BF16) {
-    if constexpr (PATH - kSelDeep <= 6) {
+    if constexpr (PATH - kSelDeep <= kFoldMaxTiles) {
       if (o.wst) {
         select_rows_deep_lds<PATH - kSelDeep>(a, s_u, h, c0, rbeg, rend, lane, o);
         return;
@@ -1116,10 +1145,14 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   float* yloc = (float*)(smem + p.off_yl);
   int* dic = (int*)(smem + p.off_dict);
   unsigned char* DR = smem + p.off_DC;       // DR[k][m] = dict[k][m] (a byte: N <= 64)
-  float* Cs = (float*)(smem + p.off_C);
+  float* Cs = (float*)(smem + p.off_C);            // row o of C at N o
   float* slots = (float*)(smem + p.off_slot);
   int* misc = (int*)(smem + p.off_misc);
   uint32_t* hdr = (uint32_t*)a.ws;
+  // drive folded (fused mode): the selection writes the drive terms here
+  const bool fold = MODE == kModeFused && p.fold_bu;
+  float* Bubuf = (float*)(smem + p.off_Bu);
+  const int P = p.n_out;                           // rows of C (outputs per step)
 
   // ---- task: chunk-major tickets so that predecessors always started first
   int task;
@@ -1145,9 +1178,11 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   const int jj = act ? j : 0;              // row index that is safe to look up
 
   // ---- phase-A drive terms of the first block: issued first, used last
-  // (selection mode never reads Bu; its pointer may be null there)
-  const rsrc_t bur = make_rsrc(MODE == kModeSelect ? (const float*)nullptr : a.Bu + gbase * N,
-                               MODE == kModeSelect ? 0u : (uint32_t)(Tc * N * 4));
+  // (selection mode never reads Bu, and with the drive folded it is formed
+  // on chip: Bu may be null there, and the empty descriptor loads zeros)
+  const bool no_bu = MODE == kModeSelect || fold;
+  const rsrc_t bur = make_rsrc(no_bu ? (const float*)nullptr : a.Bu + gbase * N,
+                               no_bu ? 0u : (uint32_t)(Tc * N * 4));
   // (the deep selection path needs the registers itself: its first block
   // follows the selection instead)
   float bu[kBuBlock];
@@ -1163,7 +1198,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     if (a.P_out)
       for (int q = tid; q < K * N; q += kThreads) dic[q] = a.dict[(size_t)h * K * N + q];
   } else {
-    for (int q = tid; q < N; q += kThreads) Cs[q] = a.C[(size_t)h * N + q];
+    for (int q = tid; q < P * N; q += kThreads) Cs[q] = a.C[(size_t)h * P * N + q];
     __syncthreads();
     // DR[k][m] = dict[k][m]: the target row of source m under entry k; with
     // per-step maps, entry t is step t's map and k*_t = t
@@ -1209,6 +1244,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     o.dic = dic;
     o.gbase = gbase;
     o.wst = (MODE == kModeFused && p.wst) ? smem + p.off_D : nullptr;
+    o.Bubuf = fold ? Bubuf : nullptr;
     const int wr0 = min(wave * gpw * S, Tc), wr1 = min(wr0 + gpw * S, Tc);
     select_dispatch<IN_BF16, MMA_BF16, PATH>(a, s_u, h, c0, wr0, wr1, lane, o);
   }
@@ -1219,7 +1255,9 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   // ---- phase A: each lane group runs its sub-chunk [tb, te) from a zero
   // state.  Padding steps (past te) act as the identity map.
   float* slot = slots + gam * NP;
-  const float cj = act ? Cs[j] : 0.f;
+  float cjo[kMaxOut];
+#pragma unroll
+  for (int o = 0; o < kMaxOut; ++o) cjo[o] = (act && o < P) ? Cs[o * N + j] : 0.f;
   float hl = 0.f, msc = 1.f;
   int midx = jj;
   // NPT = 32 with the inverse-row table: h' = Bu + gather of D h over the
@@ -1244,6 +1282,8 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
       const int t0 = tb + blk + q4;
       const i4v k4 = *(const i4v*)(kbuf + t0);
       const f4v d4 = act ? *(const f4v*)(Dbuf + j * TS + t0) : f4v{1.f, 1.f, 1.f, 1.f};
+      // drive terms: the register ring, or (drive folded) this row of the chunk's on-chip drive
+      const f4v b4 = (fold && act) ? *(const f4v*)(Bubuf + j * TS + t0) : f4v{0.f, 0.f, 0.f, 0.f};
       [[maybe_unused]] int own[4];
       if constexpr (!GS) {
 #pragma unroll
@@ -1257,14 +1297,15 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         // next factor of the running map, gathered at its current rows
         const int nrow = DR[k * p.DCS + midx];
         const float dm = Dbuf[midx * TS + t];
+        const float bt = fold ? b4[r] : bu[q4 + r];
         if constexpr (GS) {
           constexpr int NG = NPT == 64 ? 64 : 32;
-          const float hn = gather_rows<NG>(SE[k * NG + j], __float_as_int(d4[r] * hl), lb, bu[q4 + r],
+          const float hn = gather_rows<NG>(SE[k * NG + j], __float_as_int(d4[r] * hl), lb, bt,
                                            DR + k * p.DCS, j);
           hl = valid ? hn : hl;
         } else {
           // h' = Bu + scatter(D h); one wave, so its LDS operations stay in order
-          slot[j] = valid ? bu[q4 + r] : 0.f;
+          slot[j] = valid ? bt : 0.f;
           atomicAdd(&slot[(valid && act) ? own[r] : j], (valid ? d4[r] : 1.f) * hl);
           hl = slot[j];
         }
@@ -1274,14 +1315,24 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
           msc *= dm;
           midx = nrow;
         }
-        if (valid && act) Dbuf[j * TS + t] = Cs[midx] * msc;
-        // local output C h'
-        if constexpr (NPT != 0) {
-          const float yl = group_sum_last<NPT>(cj * hl);
-          if (valid && j == NPT - 1) yloc[t] = yl;
-        } else {
-          const float yl = group_sum_rt(cj * hl, NP);
-          if (valid && j == 0) yloc[t] = yl;
+        // (row o of w_t at D's rows + N o: one [N][TS] block per row of C)
+        if (valid && act) {
+#pragma unroll
+          for (int o = 0; o < kMaxOut; ++o)
+            if (o < P) Dbuf[(o * N + j) * TS + t] = Cs[o * N + midx] * msc;
+        }
+        // local outputs C h'
+#pragma unroll
+        for (int o = 0; o < kMaxOut; ++o) {
+          if (o < P) {
+            if constexpr (NPT != 0) {
+              const float yl = group_sum_last<NPT>(cjo[o] * hl);
+              if (valid && j == NPT - 1) yloc[o * p.YS + t] = yl;
+            } else {
+              const float yl = group_sum_rt(cjo[o] * hl, NP);
+              if (valid && j == 0) yloc[o * p.YS + t] = yl;
+            }
+          }
         }
       }
     }
@@ -1965,8 +2016,11 @@ static inline int sel_path(const Plan& p) {
   if (!p.in_bf16 && p.d == 64 && nct == 2) return kSelF32D64N2;
   if (!p.in_bf16 && p.d == 16 && nct == 1) return kSelF32D16N1;
   if (p.in_bf16 && p.mma_bf16 && p.d == 128 && nct == 3) return kSelBF16D128N3;
+  if (p.in_bf16 && p.mma_bf16 && p.d == 128 && nct == 5) return kSelBF16D128N5;
   if (p.in_bf16 && p.mma_bf16 && p.d % 32 == 0 && p.d >= 256) {
-    const int dt = ((p.K + 15) >> 4) + ((p.N + 15) >> 4);   // at most 8 (K, N <= 64)
+    // at most 8 tiles (K, N <= 64), or kFoldMaxTiles with the drive folded
+    const int nt = (p.N + 15) >> 4;
+    const int dt = ((p.K + 15) >> 4) + nt + (p.fold_bu ? nt : 0);
     return kSelDeep + ((dt + 1) & ~1);
   }
   return kSelAny;

@@ -18,7 +18,8 @@ static void launch_deep(const Args& a, hipStream_t st, int nct, int npt) {
     case 2: launch_deep_n<MODE, 2>(a, st, npt); break;
     case 4: launch_deep_n<MODE, 4>(a, st, npt); break;
     case 6: launch_deep_n<MODE, 6>(a, st, npt); break;
-    default: launch_deep_n<MODE, 8>(a, st, npt); break;
+    case 8: launch_deep_n<MODE, 8>(a, st, npt); break;
+    default: launch_deep_n<MODE, kFoldMaxTiles>(a, st, npt); break;   // drive folded
   }
 }
 
@@ -79,6 +80,10 @@ hipError_t launch_fused(const Args& a, hipStream_t st) {
       launch_kernel<kModeFused, 1, 1, kSelBF16D128N3, 32, true>(a, st);
     else if (path == kSelBF16D128N3)
       launch_kernel<kModeFused, 1, 1, kSelBF16D128N3, 0, true>(a, st);
+    else if (path == kSelBF16D128N5 && npt == 32)            // drive folded, N = 32
+      launch_kernel<kModeFused, 1, 1, kSelBF16D128N5, 32, true>(a, st);
+    else if (path == kSelBF16D128N5)
+      launch_kernel<kModeFused, 1, 1, kSelBF16D128N5, 0, true>(a, st);
     else if (path > kSelDeep)
       launch_deep<kModeFused>(a, st, path - kSelDeep, npt);
     else if (npt == 64)

@@ -17,7 +17,9 @@ namespace pdscan {
 constexpr int kThreads = 256;          // lanes per workgroup
 constexpr int kWaves = kThreads / 64;  // wave64
 constexpr int kSelectRows = 256;       // rows per workgroup for selection alone
-constexpr int kMaxLds = 64 * 1024;     // bytes of LDS one workgroup may use
+constexpr int kMaxLds = 64 * 1024;     // bytes of LDS one workgroup uses on the established paths (2 per CU)
+constexpr int kMaxLdsGfx950 = 160 * 1024;   // the whole LDS of one gfx950 CU: one workgroup may take all of it
+constexpr int kFoldMaxTiles = 10;      // general kernel, drive folded: column tiles of the selection GEMM
 constexpr int kWbFrags = 6;            // W_b fragments per lane at most (fp32 d = 64: 2 blocks x 3 pieces)
 constexpr int kMaxOut = 4;             // outputs per head (rows of C) on the multi-output paths
 constexpr int kSpinLimit = 1 << 22;    // window reads before a look-back wait gives up
@@ -39,7 +41,8 @@ struct Plan {
   int KP;    // score staging width
   int mma_bf16;  // score GEMM on bf16 MFMA (else fp32 MFMA)
   int fused16;   // fused pass with step-major MFMA tiles (N, K <= 16; see below)
-  int fold_bu;   // fused16: Bu = W_b u from a third MFMA tile instead of an input
+  int fold_bu;   // Bu = W_b u formed on chip instead of read: a third MFMA tile (fused16) or a third
+                 // column segment of the selection GEMM written to an on-chip [N][TS] buffer (general kernel)
   int step16;    // scan alone with the step-major layout (N <= 16); 2: also writes every state
   int n_out;     // outputs per head, rows of C (> 1: step-major paths only)
   int gse;       // general kernel, N = 32 or 64: phase A gathers over inverse dictionary rows (table at off_SRC)
@@ -53,7 +56,8 @@ struct Plan {
   int spin_limit, force_giveup;
   // LDS byte offsets
   int off_D, off_k, off_yl, off_dict, off_DC, off_SRC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
-      off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_WB, off_misc, lds_bytes;
+      off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_WB, off_Bu, off_misc, lds_bytes;
+  int lds_limit;   // the plan's LDS budget (kMaxLds, or kMaxLdsGfx950 for the folded / multi-output general plans)
   // workspace byte offsets (scan / fused)
   size_t ws_agg, ws_inc, ws_bytes;
 };
@@ -81,7 +85,13 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   const int kch = in_bf16 ? (d >= 128 ? (d == 128 ? 4 : 0) : 0) : (d == 16 || d == 32 || d == 64 ? d / 16 : 0);
   p.fused16 = (mode == kModeFused && !u_shared && N <= 16 && K <= 16 && kch > 0 &&
                (chunk < L ? chunk : L) <= 512) ? 1 : 0;
-  p.fold_bu = (p.fused16 && fold_bu) ? 1 : 0;
+  // the general kernel folds the drive as a third column segment of its
+  // selection GEMM (at most kFoldMaxTiles column tiles)
+  const int KT = (K + 15) >> 4, NT = (N + 15) >> 4;
+  const bool deep_sel = in_bf16 && d % 32 == 0 && d >= 256;   // the deep bf16 selection
+  const bool gen_fold = mode == kModeFused && !p.fused16 && fold_bu &&
+                        (deep_sel ? ((KT + 2 * NT + 1) & ~1) <= kFoldMaxTiles : align_up(K + 2 * N, 16) <= 128);
+  p.fold_bu = ((p.fused16 || gen_fold) && fold_bu) ? 1 : 0;
   // the scan alone on the same layout: maps streamed per step (at most 32
   // steps per group, as above)
   p.step16 = (mode == kModeScan && step16 && N <= 16 && K <= 16 && (chunk < L ? chunk : L) <= 512) ? step16 : 0;
@@ -109,7 +119,7 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   // entry and row)
   p.gse = (allow_gse && mode != kModeSelect && !sm && (N == 32 || N == 64)) ? 1 : 0;
   p.nC = (L + p.chunk - 1) / p.chunk;
-  p.NC = align_up(K + N, 16);
+  p.NC = align_up(K + N + (p.fold_bu && !sm ? N : 0), 16);   // scores, pre-activations, drive terms
   p.KP = align_up(K, 4);
   p.mma_bf16 = (in_bf16 && d >= 128) ? 1 : 0;
   p.tasks = p.nC * B * H;
@@ -125,15 +135,20 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   // fused deep bf16 selection (d a multiple of 32, at least 256) in one pass
   // over at most six column tiles with at most 32 rows per wave: two stages
   // of 16 columns x 80 bytes per tile in D's region, if it is large enough
+  // (folded: up to kFoldMaxTiles tiles, the drive tiles after the others)
   {
-    const int dt = ((K + 15) >> 4) + ((N + 15) >> 4), nct = (dt + 1) & ~1;
+    const int dt = KT + NT + (p.fold_bu && !sm ? NT : 0), nct = (dt + 1) & ~1;
     const bool deep = mode == kModeFused && !sm && in_bf16 && p.mma_bf16 && d % 32 == 0 && d >= 256;
-    p.wst = (deep && nct <= 6 && (64 / p.NP) * p.S <= 32 && n_out * N * p.TS * 4 >= 2 * 16 * nct * 80) ? 1 : 0;
+    p.wst = (deep && nct <= (p.fold_bu ? kFoldMaxTiles : 6) && (64 / p.NP) * p.S <= 32 &&
+             n_out * N * p.TS * 4 >= 2 * 16 * nct * 80) ? 1 : 0;
   }
+  // general kernel, drive folded: the drive terms of the chunk, [N][TS]
+  p.off_Bu = (p.fold_bu && !sm) ? take(N * p.TS * 4) : 0;
   p.off_k = (scan && !sm) ? take(align_up(T, 4) * 4) : 0;   // the step-major kernels keep k* in registers
   p.off_yl = scan ? take(n_out * p.YS * 4) : 0;
   p.off_dict = scan ? 0 : take(K * N * 4);   // selection: P_idx gathers
-  p.off_C = take((N > 16 * n_out ? N : 16 * n_out) * 4);   // step-major: row o of C at 16 o
+  // step-major: row o of C at 16 o; general kernel: at N o
+  p.off_C = take((sm ? (N > 16 * n_out ? N : 16 * n_out) : N * n_out) * 4);
   p.off_bd = take(N * 4);
   p.off_slot = take(kThreads * 4);
   const int gn = p.G * N * 4;                      // one [G][N] scratch array of the steps after phase A
@@ -177,13 +192,19 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   p.ws_agg = 256;
   p.ws_inc = p.ws_agg + seqchunks * 3 * N * sizeof(uint64_t);
   p.ws_bytes = (mode == kModeSelect) ? 0 : p.ws_inc + seqchunks * N * sizeof(uint64_t);
-  if (n_out < 1 || n_out > kMaxOut || (n_out > 1 && !sm)) return false;
-  return p.lds_bytes <= kMaxLds;
+  // several outputs per head: the step-major paths, and the general kernel in
+  // the fused and scan modes
+  if (n_out < 1 || n_out > kMaxOut || (n_out > 1 && mode == kModeSelect)) return false;
+  // The folded and multi-output general plans may take the whole LDS of a
+  // CU (one workgroup per CU); every other plan keeps to kMaxLds, so that
+  // two workgroups share a CU.
+  p.lds_limit = (!sm && (p.fold_bu || n_out > 1)) ? kMaxLdsGfx950 : kMaxLds;
+  return p.lds_bytes <= p.lds_limit;
 }
 
 // Fills `p` for one call.  `mode` selects which parts exist.  Returns false
-// when the plan needs more than kMaxLds bytes of LDS (the gather table is
-// dropped first: phase A then scatters with LDS atomics).
+// when the plan needs more LDS than its budget (lds_limit; the gather table
+// is dropped first: phase A then scatters with LDS atomics).
 inline bool make_plan(Plan& p, int mode, int B, int H, int L, int N, int K, int d, int u_shared,
                       int in_bf16, int chunk, int fold_bu = 0, int step16 = 0, int n_out = 1) {
   if (make_plan_once(p, mode, B, H, L, N, K, d, u_shared, in_bf16, chunk, fold_bu, step16, n_out, 1))

@@ -180,8 +180,12 @@ def test_multi_output_validation(P):
                                (2, 256, -3)):
         rc = P.lib.pdssm_scan_fwd_multi(ctypes.byref(d), chunk, n_out, *args(0))
         assert rc == want, (n_out, chunk, rc, P.lib.pdssm_last_error())
+    # the general scan takes several outputs too (N = 17): here it stops at the empty workspace,
+    # and past its on-chip budget (N = 64, four outputs at chunk 512) the shape is unsupported
     d17 = _dims(P, L=4096, N=17)
-    assert P.lib.pdssm_scan_fwd_multi(ctypes.byref(d17), 128, 2, *args(1 << 20)) == -2
+    assert P.lib.pdssm_scan_fwd_multi(ctypes.byref(d17), 128, 2, *args(0)) == -3
+    d64 = _dims(P, L=4096, N=64, K=32)
+    assert P.lib.pdssm_scan_fwd_multi(ctypes.byref(d64), 512, 4, *args(0)) == -2
     rc = P.lib.pdssm_fwd_wb_multi(ctypes.byref(d), 512, 2, A, A + big, A + 2 * big, A + 3 * big,
                                   A + 4 * big, A + 5 * big, A + 6 * big, None, None, None, A + 7 * big,
                                   A + 8 * big, A + 9 * big, 0, None)
@@ -226,3 +230,14 @@ def test_noalloc_validation(P):
     bad = list(args)
     bad[12] = A + 7 * big                            # status inside y
     assert fn(ctypes.byref(d), 128, *bad) == -1 and b"overlaps" in P.lib.pdssm_last_error()
+
+
+def test_workspace_query_accepts_shapes_only_the_folded_plans_hold(P):
+    """The fused workspace size depends only on the chunk count, and the
+    query accepts a shape when any fused call can run it: the LM-layer shape
+    at chunk 256 exceeds pdssm_fwd's on-chip budget but not that of the
+    folded general kernel (one workgroup per compute unit)."""
+    d = P.make_dims(16, 24, 2048, 64, 32, 768, True, True)
+    n = P.fwd_workspace_bytes(d, 256)
+    assert n == 256 + 8 * 16 * 24 * 4 * 64 * 8
+    assert P.lib.pdssm_last_error() == b""

@@ -15,13 +15,24 @@ from tests._gpu import assert_within, host, lib, proj_dev, to_dev, torch_mod
 pytestmark = pytest.mark.gpu
 
 # shapes of the step-major kernel: fp32 d = 64 (split products), fp32 d = 32,
-# fp32 d = 16 (fp32 MFMA), bf16 d = 128 (bf16 MFMA); ragged last chunks
+# fp32 d = 16 (fp32 MFMA), bf16 d = 128 (bf16 MFMA); and of the general
+# kernel, where the drive terms are a third column segment of the selection
+# GEMM written to an on-chip buffer: the time-series shape (N = 32, bf16
+# d = 128, register-resident weights), the LM-layer shape (N = 64, u shared
+# by the heads, bf16 d = 768: deep selection with LDS-staged weights, and at
+# chunk 64 without the staging), shared fp32 inputs and an odd N (generic
+# selection); ragged last chunks
 CASES = {
     "impulse": ("impulse", dict(H=3, L=1300)),
     "base": ("base", dict(B=2, H=3, L=700)),
     "base_d32": ("base", dict(B=1, H=2, L=450, d=32)),
     "tiny": ("tiny", dict(L=250)),
     "bf16_d128": ("timeseries", dict(B=1, H=2, L=600, N=16, K=8)),
+    "timeseries": ("timeseries", dict(B=2, H=2, L=600)),
+    "lm_layer": ("lm_layer", dict(B=2, H=5, L=300)),
+    "shared_f32": ("lm_layer", dict(B=2, H=3, L=200, N=16, K=8, d=64, dtype="f32")),
+    "odd_n20": ("base", dict(B=1, H=2, L=333, N=20, K=5, d=24)),
+    "lm_n32_k16": ("lm_layer", dict(B=1, H=3, L=260, N=32, K=16)),
 }
 
 _cache = {}
@@ -71,6 +82,17 @@ def test_fold_chunk_independence(chunk):
     _check(_run(_dev(inp), chunk), ref, f"chunk {chunk}")
 
 
+@pytest.mark.parametrize("key,chunk", [("lm_layer", 64), ("lm_layer", 100), ("lm_layer", 32),
+                                       ("timeseries", 128), ("timeseries", 64), ("timeseries", 7)])
+def test_fold_general_chunk_independence(key, chunk):
+    """The general kernel's folded drive at other chunks: the LM-layer shape
+    without the LDS weight staging (chunk 64, 32), a ragged chunk (100), and
+    the time-series shape at shorter chunks (one ragged: 7)."""
+    inp, ref = _case(key)
+    print(f"[gpu] pdssm_fwd_wb {key} chunk={chunk}", flush=True)
+    _check(_run(_dev(inp), chunk), ref, f"{key} chunk {chunk}")
+
+
 def test_fold_without_selection_outputs_or_h0():
     inp, _ = _case("base")
     ref = oracle.forward_wb(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, inp.C, None)
@@ -101,10 +123,12 @@ def test_fold_deterministic():
         assert np.array_equal(host(a[n]), host(b[n])), n
 
 
-@pytest.mark.parametrize("name,kw", [("lm_layer", dict(B=1, H=2, L=64)),
-                                     ("timeseries", dict(B=1, H=2, L=64)),
-                                     ("base", dict(B=1, H=2, L=64, N=17))])
-def test_fold_rejects_shapes_outside_the_step_major_kernel(name, kw):
+@pytest.mark.parametrize("name,kw", [("lm_layer", dict(B=1, H=2, L=64, K=64)),
+                                     ("base", dict(B=1, H=2, L=64, N=64, K=8, d=64))])
+def test_fold_rejects_shapes_whose_gemm_does_not_fit(name, kw):
+    """Too many columns for the folded selection GEMM: bf16 d = 768 with
+    K = 64, N = 64 (12 tiles of 16, the kernel holds 10) and fp32 with
+    K + 2N = 136 > 128."""
     P = lib()
     inp = generate(get_config(name, **kw))
     with pytest.raises(P.PdssmError) as e:
@@ -112,12 +136,24 @@ def test_fold_rejects_shapes_outside_the_step_major_kernel(name, kw):
     assert e.value.status == P.PDSSM_EUNSUPPORTED
 
 
+def test_fold_general_deterministic():
+    inp, _ = _case("lm_layer")
+    d = _dev(inp)
+    a, b = _run(d, 128), _run(d, 128)
+    for n in ("y", "h_L", "k_star", "D"):
+        assert np.array_equal(host(a[n]), host(b[n])), n
+
+
 @pytest.mark.slow
-def test_fold_full_impulse():
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["impulse", "timeseries", "lm_layer"])
+def test_fold_full_size(name):
+    """Full workloads in the benchmark's launch configuration (their chunk)."""
     torch = torch_mod()
-    inp = generate(get_config("impulse"))
-    ref = oracle.forward_wb(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, inp.C, inp.h0)
-    print("[gpu] pdssm_fwd_wb impulse full size", flush=True)
+    inp = generate(get_config(name))
+    ref = oracle.forward_wb(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, inp.C, inp.h0,
+                            inp.cfg.u_shared)
+    print(f"[gpu] pdssm_fwd_wb {name} full size", flush=True)
     out = _run(_dev(inp), inp.cfg.chunk)
     torch.cuda.synchronize()
-    _check(out, ref, "impulse full")
+    _check(out, ref, f"{name} full")

@@ -23,6 +23,13 @@ CASES = {
     "tiny_p4": ("tiny", dict(L=250), 4, 64),
     "bf16_d128_p2": ("timeseries", dict(B=1, H=2, L=600, N=16, K=8), 2, 256),
     "n5_p3": ("base", dict(B=1, H=2, L=333, N=5, K=3), 3, 128),
+    # the general kernel: time-series (N = 32) and LM-layer (N = 64, shared
+    # u) shapes, an odd N with fp32 inputs
+    "timeseries_p2": ("timeseries", dict(B=2, H=2, L=600), 2, 256),
+    "timeseries_p3_c128": ("timeseries", dict(B=1, H=2, L=500), 3, 128),
+    "lm_layer_p2": ("lm_layer", dict(B=2, H=3, L=300), 2, 128),
+    "lm_layer_p4_c64": ("lm_layer", dict(B=1, H=3, L=300), 4, 64),
+    "n20_p2": ("base", dict(B=1, H=2, L=333, N=20, K=5, d=24), 2, 100),
 }
 
 _cache = {}
@@ -91,6 +98,40 @@ def test_multi_deterministic():
     a = P.pdssm_fwd_wb_multi(*args, chunk=chunk)
     b = P.pdssm_fwd_wb_multi(*args, chunk=chunk)
     assert np.array_equal(host(a["y"]), host(b["y"])) and np.array_equal(host(a["h_L"]), host(b["h_L"]))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,P", [("timeseries", 2), ("lm_layer", 2)])
+def test_multi_full_size(name, P):
+    """Full workloads, two outputs per head, at the workload's chunk."""
+    inp = generate(get_config(name))
+    rng = np.random.default_rng(100 + P)
+    C = (rng.standard_normal((inp.cfg.H, P, inp.cfg.N)) / np.sqrt(inp.cfg.N)).astype(np.float32)
+    ref = oracle.forward_wb_multi(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, C, inp.h0,
+                                  inp.cfg.u_shared)
+    bf = inp.cfg.dtype == "bf16"
+    Pl = lib()
+    print(f"[gpu] pdssm_fwd_wb_multi {name} full size n_out={P}", flush=True)
+    out = Pl.pdssm_fwd_wb_multi(proj_dev(inp.u, bf), proj_dev(inp.W_sel, bf), to_dev(inp.dict_idx),
+                                proj_dev(inp.W_d, bf), to_dev(inp.b_d), proj_dev(inp.W_b, bf), to_dev(C),
+                                to_dev(inp.h0), chunk=inp.cfg.chunk, want_k=True)
+    assert np.array_equal(host(out["k_star"]), ref["k_star"])
+    assert_within(host(out["y"]), ref["y"], f"{name} y")
+    assert_within(host(out["h_L"]), ref["h_L"], f"{name} h_L")
+
+
+def test_multi_general_rejects_outputs_beyond_on_chip_memory():
+    """LM-layer shape, drive folded, four outputs at chunk 128: 182 KB of
+    on-chip rows, more than the 160 KiB of a compute unit."""
+    inp = generate(get_config("lm_layer", B=1, H=2, L=256))
+    P = lib()
+    C = np.zeros((inp.cfg.H, 4, inp.cfg.N), np.float32)
+    with pytest.raises(P.PdssmError) as e:
+        P.pdssm_fwd_wb_multi(proj_dev(inp.u, True), proj_dev(inp.W_sel, True), to_dev(inp.dict_idx),
+                             proj_dev(inp.W_d, True), to_dev(inp.b_d), proj_dev(inp.W_b, True), to_dev(C),
+                             to_dev(inp.h0), chunk=128)
+    assert e.value.status == P.PDSSM_EUNSUPPORTED
 
 
 def test_multi_rejects_a_chunk_too_long_for_its_outputs():
