@@ -1097,41 +1097,26 @@ __device__ __forceinline__ i2v row_entry(int tg, bool on, int q, int lane) {
   return i2v{(int)x, (int)y};
 }
 
-// h'_i = hn + sum over the sources j of row i (ascending) of the value vj of
-// lane j of this NG-lane group; lb is the group's lane-0 byte offset.  Rows
-// with more than four sources take a second round of permutes, rows with more
-// than eight a scan of the dictionary row (DRk: the target rows of entry k).
-template <int NG>
-__device__ __forceinline__ float gather_rows(const i2v se, int vj, int lb, float hn, const unsigned char* DRk,
-                                             int i) {
-  const unsigned x = (unsigned)se.x, y = (unsigned)se.y;
-  float gv[4];
+// Sum over four sources of one row: sx holds four source bytes (lane byte
+// offset 4 j with the presence bit 0 set, the group's lane-0 offset ORed into
+// bit 7), vj the value of lane j of the group.  The permute ignores the low
+// two bits of its address; the presence bits become weights 1.0 / 0.0 through
+// byte-to-float conversions, and fma(g, 1, h) = h + g, fma(g, 0, h) = h, so
+// the sum equals the selected additions in source order.
+__device__ __forceinline__ float gather4w(unsigned sx, int vj, float hn) {
+  float g[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
-    gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(lb | (int)((x >> (8 * m)) & 0xFCu), vj));
+    g[m] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)((sx >> (8 * m)) & 0xFFu), vj));
+  const unsigned wb = sx & 0x01010101u;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) hn += ((x >> (8 * m)) & 1u) ? gv[m] : 0.f;
-  if (__builtin_amdgcn_ballot_w64(y & 1u)) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute(lb | (int)((y >> (8 * m)) & 0xFCu), vj));
-#pragma unroll
-    for (int m = 0; m < 4; ++m) hn += ((y >> (8 * m)) & 1u) ? gv[m] : 0.f;
-    if (__builtin_amdgcn_ballot_w64((y >> 25) & 1u)) {
-      const bool more = (y >> 25) & 1u;
-      int cnt = 0;
-      for (int s = 0; s < NG; ++s) {
-        const bool src = (int)DRk[s] == i;
-        const float g = __int_as_float(__builtin_amdgcn_ds_bpermute(lb | (s << 2), vj));
-        cnt += src ? 1 : 0;
-        hn += (more && src && cnt > 8) ? g : 0.f;
-      }
-    }
-  }
+  for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(g[m], (float)((wb >> (8 * m)) & 0xFFu), hn);
   return hn;
 }
 
-template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT>
+// NOUT: rows of C the instantiation handles (1, or kMaxOut for the
+// multi-output plans, which take p.n_out of them).
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1>
 __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   const Plan& p = a.p;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1152,7 +1137,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   // drive folded (fused mode): the selection writes the drive terms here
   const bool fold = MODE == kModeFused && p.fold_bu;
   float* Bubuf = (float*)(smem + p.off_Bu);
-  const int P = p.n_out;                           // rows of C (outputs per step)
+  const int P = NOUT > 1 ? p.n_out : 1;           // rows of C (outputs per step)
 
   // ---- task: chunk-major tickets so that predecessors always started first
   int task;
@@ -1255,9 +1240,9 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   // ---- phase A: each lane group runs its sub-chunk [tb, te) from a zero
   // state.  Padding steps (past te) act as the identity map.
   float* slot = slots + gam * NP;
-  float cjo[kMaxOut];
+  float cjo[NOUT];
 #pragma unroll
-  for (int o = 0; o < kMaxOut; ++o) cjo[o] = (act && o < P) ? Cs[o * N + j] : 0.f;
+  for (int o = 0; o < NOUT; ++o) cjo[o] = (act && o < P) ? Cs[o * N + j] : 0.f;
   float hl = 0.f, msc = 1.f;
   int midx = jj;
   // NPT = 32 with the inverse-row table: h' = Bu + gather of D h over the
@@ -1266,8 +1251,8 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
                                    !(MODE == kModeScan && a.P_in);
   [[maybe_unused]] const i2v* SE = (const i2v*)(smem + p.off_SRC);
   [[maybe_unused]] const int lb = NPT == 32 ? (lane & 32) << 2 : 0;
-  auto phase_a = [&](auto gs_tag) {
-  constexpr bool GS = decltype(gs_tag)::value;
+  // Scatter path (any N, or no gather table): LDS atomics into a per-group row.
+  auto phase_a = [&]() {
   for (int blk = 0; blk < nst; blk += kBuBlock) {
     float bn[kBuBlock];
 #pragma unroll
@@ -1284,11 +1269,9 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
       const f4v d4 = act ? *(const f4v*)(Dbuf + j * TS + t0) : f4v{1.f, 1.f, 1.f, 1.f};
       // drive terms: the register ring, or (drive folded) this row of the chunk's on-chip drive
       const f4v b4 = (fold && act) ? *(const f4v*)(Bubuf + j * TS + t0) : f4v{0.f, 0.f, 0.f, 0.f};
-      [[maybe_unused]] int own[4];
-      if constexpr (!GS) {
+      int own[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) own[r] = DR[(r < nb ? k4[r] : 0) * p.DCS + jj];
-      }
+      for (int r = 0; r < 4; ++r) own[r] = DR[(r < nb ? k4[r] : 0) * p.DCS + jj];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool valid = r < nb;
@@ -1298,17 +1281,10 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         const int nrow = DR[k * p.DCS + midx];
         const float dm = Dbuf[midx * TS + t];
         const float bt = fold ? b4[r] : bu[q4 + r];
-        if constexpr (GS) {
-          constexpr int NG = NPT == 64 ? 64 : 32;
-          const float hn = gather_rows<NG>(SE[k * NG + j], __float_as_int(d4[r] * hl), lb, bt,
-                                           DR + k * p.DCS, j);
-          hl = valid ? hn : hl;
-        } else {
-          // h' = Bu + scatter(D h); one wave, so its LDS operations stay in order
-          slot[j] = valid ? bt : 0.f;
-          atomicAdd(&slot[(valid && act) ? own[r] : j], (valid ? d4[r] : 1.f) * hl);
-          hl = slot[j];
-        }
+        // h' = Bu + scatter(D h); one wave, so its LDS operations stay in order
+        slot[j] = valid ? bt : 0.f;
+        atomicAdd(&slot[(valid && act) ? own[r] : j], (valid ? d4[r] : 1.f) * hl);
+        hl = slot[j];
         // compose, and record w_t = C Phi_t over column t (all lanes of the
         // group have read column t above)
         if (valid) {
@@ -1318,12 +1294,12 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         // (row o of w_t at D's rows + N o: one [N][TS] block per row of C)
         if (valid && act) {
 #pragma unroll
-          for (int o = 0; o < kMaxOut; ++o)
+          for (int o = 0; o < NOUT; ++o)
             if (o < P) Dbuf[(o * N + j) * TS + t] = Cs[o * N + midx] * msc;
         }
         // local outputs C h'
 #pragma unroll
-        for (int o = 0; o < kMaxOut; ++o) {
+        for (int o = 0; o < NOUT; ++o) {
           if (o < P) {
             if constexpr (NPT != 0) {
               const float yl = group_sum_last<NPT>(cjo[o] * hl);
@@ -1340,11 +1316,98 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     for (int q = 0; q < kBuBlock; ++q) bu[q] = bn[q];
   }
   };
+  // Gather path, groups of NG = 32 or 64 rows (every lane a row, the
+  // dictionary stride NG): step t of a group reads its map row (k*_t and the
+  // composed path), gathers D_t h over each row's sources, and takes D_t and
+  // C at the path's current row from the lanes that hold them (permutes), so
+  // no on-chip read lands on a random row.  With NG = 64 the group is the
+  // wave and k*_t a scalar.  Blocks of four steps that lie wholly inside every
+  // group of the wave skip the per-step validity selects.
+  [[maybe_unused]] auto phase_a_gather = [&]() {
+    constexpr int NG = NPT == 64 ? 64 : 32;
+    constexpr int LG = NG == 64 ? 6 : 5;
+    const unsigned lb4 = (unsigned)lb * 0x01010101u;
+    const int lbm = lb;                            // byte offset of the group's lane 0
+    auto steps = [&](auto full_tag, const i4v k4, const f4v d4, const f4v b4, int t0, int q4, int nb) {
+      constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = FULL || r < nb;
+        const int t = t0 + r;
+        int k = valid ? k4[r] : 0;
+        if constexpr (NG == 64) k = __builtin_amdgcn_readfirstlane(k);   // one group per wave
+        const int nrow = DR[(k << LG) + midx];
+        const float dm = __int_as_float(__builtin_amdgcn_ds_bpermute(lbm + (midx << 2), __float_as_int(d4[r])));
+        const float bt = fold ? b4[r] : bu[q4 + r];
+        const i2v se = SE[(k << LG) + j];
+        const int vj = __float_as_int(d4[r] * hl);
+        float hn = gather4w((unsigned)se.x | lb4, vj, bt);
+        if (__builtin_amdgcn_ballot_w64(se.y & 1)) {      // rows with five to eight sources
+          // (bit 25, the more-than-eight flag, is bit 1 of byte 3: the permute ignores it)
+          hn = gather4w((unsigned)se.y | lb4, vj, hn);
+          if (__builtin_amdgcn_ballot_w64((se.y >> 25) & 1u)) {   // more than eight: scan the map row
+            const bool more = (se.y >> 25) & 1u;
+            const unsigned char* DRk = DR + (k << LG);
+            int cnt = 0;
+            for (int q = 0; q < NG; ++q) {
+              const bool src = (int)DRk[q] == j;
+              const float gq = __int_as_float(__builtin_amdgcn_ds_bpermute(lbm | (q << 2), vj));
+              cnt += src ? 1 : 0;
+              hn += (more && src && cnt > 8) ? gq : 0.f;
+            }
+          }
+        }
+        if (valid) {
+          hl = hn;
+          msc *= dm;
+          midx = nrow;
+        }
+        // w_t = C Phi_t, row o of C from the lane that holds C[o][midx]
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) {
+          if (o < P) {
+            const float cw = __int_as_float(__builtin_amdgcn_ds_bpermute(lbm + (midx << 2), __float_as_int(cjo[o])));
+            if (valid) Dbuf[(o * N + j) * TS + t] = cw * msc;
+          }
+        }
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) {
+          if (o < P) {
+            const float yl = group_sum_last<NG>(cjo[o] * hl);
+            if (valid && j == NG - 1) yloc[o * p.YS + t] = yl;
+          }
+        }
+      }
+    };
+    for (int blk = 0; blk < nst; blk += kBuBlock) {
+      float bn[kBuBlock];
+#pragma unroll
+      for (int q = 0; q < kBuBlock; ++q) {
+        const int tt = blk + kBuBlock + q;
+        bn[q] = buf_f32(bur, (tt < nst) ? (uint32_t)((tb + tt) * N + j) * 4u : kNoLoad);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < kBuBlock; q4 += 4) {
+        const int nb = nst - blk - q4;             // steps left, uniform in the group
+        if (!__builtin_amdgcn_ballot_w64(nb > 0)) break;
+        const int t0 = tb + blk + q4;
+        const i4v k4 = *(const i4v*)(kbuf + t0);
+        const f4v d4 = *(const f4v*)(Dbuf + j * TS + t0);
+        const f4v b4 = fold ? *(const f4v*)(Bubuf + j * TS + t0) : f4v{0.f, 0.f, 0.f, 0.f};
+        if (!__builtin_amdgcn_ballot_w64(nb < 4))
+          steps(std::true_type{}, k4, d4, b4, t0, q4, nb);
+        else
+          steps(std::false_type{}, k4, d4, b4, t0, q4, nb);
+      }
+#pragma unroll
+      for (int q = 0; q < kBuBlock; ++q) bu[q] = bn[q];
+    }
+  };
   if constexpr ((NPT == 32 || NPT == 64) && MODE != kModeSelect) {
-    if (gs) phase_a(std::true_type{});
-    else phase_a(std::false_type{});
+    if (gs) phase_a_gather();
+    else phase_a();
   } else {
-    phase_a(std::false_type{});
+    phase_a();
   }
 
   chunk_tail<false>(a, smem, c, s, Tc, gbase, NP, gam, j, act, midx, msc, hl);
@@ -1996,16 +2059,16 @@ __global__ __launch_bounds__(kThreads, NOUT > 2 ? 2 : 3) void pdssm_fused16_kern
 // Two entry points over one body: the register-resident fp32 selection paths
 // fit three waves per SIMD; the other paths get the larger register budget
 // of two waves per SIMD.
-template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT>
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1>
 __global__ __launch_bounds__(kThreads, 3) void pdssm_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT>(a, smem);
+  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT>(a, smem);
 }
 
-template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT>
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1>
 __global__ __launch_bounds__(kThreads, 2) void pdssm_kernel_wide(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT>(a, smem);
+  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT>(a, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2032,13 +2095,13 @@ static inline int npt_of(const Plan& p) {
   return (p.N == p.NP && (p.N == 8 || p.N == 16 || p.N == 32 || p.N == 64)) ? p.N : 0;
 }
 
-template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, bool WIDE>
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, bool WIDE, int NOUT = 1>
 static inline void launch_kernel(const Args& a, hipStream_t st) {
   if constexpr (WIDE)
-    hipLaunchKernelGGL((pdssm_kernel_wide<MODE, IN_BF16, MMA_BF16, PATH, NPT>), dim3(a.p.tasks),
+    hipLaunchKernelGGL((pdssm_kernel_wide<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT>), dim3(a.p.tasks),
                        dim3(kThreads), a.p.lds_bytes, st, a);
   else
-    hipLaunchKernelGGL((pdssm_kernel<MODE, IN_BF16, MMA_BF16, PATH, NPT>), dim3(a.p.tasks),
+    hipLaunchKernelGGL((pdssm_kernel<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT>), dim3(a.p.tasks),
                        dim3(kThreads), a.p.lds_bytes, st, a);
 }
 

@@ -44,6 +44,14 @@ hipError_t launch_scan(const Args& a, hipStream_t st) {
       hipLaunchKernelGGL(pdssm_step16_kernel<0>, dim3(a.p.tasks), dim3(kThreads), a.p.lds_bytes, st, a);
     return hipGetLastError();
   }
+  if (a.p.n_out > 1) {                             // several rows of C (general scan)
+    switch (npt_of(a.p)) {
+      case 32: launch_kernel<kModeScan, 0, 0, kSelAny, 32, false, kMaxOut>(a, st); break;
+      case 64: launch_kernel<kModeScan, 0, 0, kSelAny, 64, false, kMaxOut>(a, st); break;
+      default: launch_kernel<kModeScan, 0, 0, kSelAny, 0, false, kMaxOut>(a, st); break;
+    }
+    return hipGetLastError();
+  }
   switch (npt_of(a.p)) {
     case 8: launch_kernel<kModeScan, 0, 0, kSelAny, 8, false>(a, st); break;
     case 16: launch_kernel<kModeScan, 0, 0, kSelAny, 16, false>(a, st); break;

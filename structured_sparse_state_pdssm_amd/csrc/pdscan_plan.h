@@ -118,6 +118,7 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   // over the sources of each row (a per-task table of 8 bytes per dictionary
   // entry and row)
   p.gse = (allow_gse && mode != kModeSelect && !sm && (N == 32 || N == 64)) ? 1 : 0;
+  if (p.gse) p.DCS = N;      // the gather path indexes the map rows with a shift
   p.nC = (L + p.chunk - 1) / p.chunk;
   p.NC = align_up(K + N + (p.fold_bu && !sm ? N : 0), 16);   // scores, pre-activations, drive terms
   p.KP = align_up(K, 4);
