@@ -653,7 +653,7 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
 // columns of 64 bytes each, at a stride of 80 bytes so that the 16 lanes of a
 // fragment read hit distinct banks.  They lie in the region D is written to
 // afterwards, so a barrier separates their last read from the epilogues.
-// u blocks are loaded two ahead into registers, weight blocks two ahead into
+// u blocks are loaded three ahead into registers, weight blocks two ahead into
 // registers and then one ahead into a stage.
 template <int NCT>
 __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int h, int c0, int rbeg,
@@ -704,7 +704,7 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
     bdr[ct] = (ct >= KT && ct < KT + NT && n < N) ? a.b_d[(size_t)h * N + n] : 0.f;
   }
 
-  u4v Ar[3][2], Wr[2][TPW];
+  u4v Ar[4][2], Wr[2][TPW];
   auto load_u = [&](int m, u4v* A2) {
     const bool ok = m < KB;
 #pragma unroll
@@ -733,17 +733,19 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
     for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f4v{0.f, 0.f, 0.f, 0.f};
   load_u(0, Ar[0]);
   load_u(1, Ar[1]);
+  load_u(2, Ar[2]);
   load_w(0, Wr[0]);
   load_w(1, Wr[1]);
   put_w(0, Wr[0]);
   load_w(2, Wr[0]);
-  // blocks past the end load zeros, stage zeros and add nothing
-  for (int m0 = 0; m0 < KB; m0 += 6) {
+  // blocks past the end load zeros, stage zeros and add nothing (u blocks
+  // three ahead in a four-slot ring)
+  for (int m0 = 0; m0 < KB; m0 += 4) {
 #pragma unroll
-    for (int q = 0; q < 6; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const int m = m0 + q;
       __syncthreads();                             // stage m written; stage m - 1 read by every wave
-      load_u(m + 2, Ar[(q + 2) % 3]);
+      load_u(m + 3, Ar[(q + 3) & 3]);
       put_w(m + 1, Wr[(q + 1) & 1]);
       load_w(m + 3, Wr[(q + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);           // the loads stay ahead of the products
@@ -754,7 +756,7 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
           acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf8v, Ar[q % 3][rt]), __builtin_bit_cast(bf8v, bf), acc[rt][ct], 0, 0, 0);
+              __builtin_bit_cast(bf8v, Ar[q & 3][rt]), __builtin_bit_cast(bf8v, bf), acc[rt][ct], 0, 0, 0);
       }
     }
   }
@@ -1191,13 +1193,25 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
       for (int q = tid; q < Tc * N; q += kThreads)
         DR[(q / N) * p.DCS + q % N] = (unsigned char)a.P_in[gbase * N + q];
     } else if ((NPT == 32 || NPT == 64) && p.gse) {
-      // the target rows and the inverse rows from one read of the dictionary
+      // the target rows and the inverse rows from one read of the dictionary;
+      // every load of the wave is issued before the first ballot waits
       constexpr int NG = NPT == 64 ? 64 : 32;
+      constexpr int kIt = 64 * 64 / kThreads;      // K * N / kThreads at most (K <= 64)
       i2v* SE = (i2v*)(smem + p.off_SRC);
-      for (int q0 = wave * 64; q0 < K * N; q0 += kThreads) {   // uniform in the wave
+      const rsrc_t dr = make_rsrc(a.dict + (size_t)h * K * N, (uint32_t)(K * N * 4));
+      int rv[kIt];
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int q = wave * 64 + it * kThreads + lane;
+        rv[it] = buf_i32(dr, q < K * N ? (uint32_t)q * 4u : kNoLoad);
+      }
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int q0 = wave * 64 + it * kThreads;   // uniform in the wave
+        if (q0 >= K * N) break;
         const int q = q0 + lane;
         const bool on = q < K * N;
-        const int r = on ? a.dict[(size_t)h * K * N + q] : 0;
+        const int r = on ? rv[it] : 0;
         if (on) DR[(q / N) * p.DCS + q % N] = (unsigned char)r;
         const i2v e = row_entry<NG>(r, on, q, lane);
         if (on) SE[q] = e;
@@ -1209,9 +1223,23 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   }
   if constexpr (MODE == kModeScan) {
     for (int q = tid; q < Tc; q += kThreads) kbuf[q] = a.P_in ? q : a.k_in[gbase + q];
-    for (int q = tid; q < Tc * N; q += kThreads) {
-      const int t = q / N, n = q - t * N;
-      Dbuf[n * TS + t] = a.D_in[gbase * N + q];
+    // D of the chunk, eight loads in flight per lane at a time
+    const rsrc_t dd = make_rsrc(a.D_in + gbase * N, (uint32_t)(Tc * N * 4));
+    for (int q0 = 0; q0 < Tc * N; q0 += 8 * kThreads) {
+      float dv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = q0 + e * kThreads + tid;
+        dv[e] = buf_f32(dd, q < Tc * N ? (uint32_t)q * 4u : kNoLoad);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = q0 + e * kThreads + tid;
+        if (q < Tc * N) {
+          const int t = q / N, n = q - t * N;
+          Dbuf[n * TS + t] = dv[e];
+        }
+      }
     }
   }
   __syncthreads();
