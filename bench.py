@@ -50,7 +50,7 @@ CSRC = os.path.join(ROOT, "structured_sparse_state_pdssm_amd", "csrc")
 # the sources each benchmarked kernel is built from
 SOURCES = {
     "fwd": ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_general.h", "pdscan_launch_fused.hip",
-            "pdscan_launch_fused16.hip", "pdscan_launch_fused_multi.hip"),
+            "pdscan_launch_fused16.hip", "pdscan_launch_fused_multi.hip", "pdscan_launch_fused_fold.hip"),
     "bwd": ("pdscan_device.h", "pdscan_plan.h", "pdscan_bwd_plan.h", "pdscan_bwd.h",
             "pdscan_launch_bwd.hip"),
 }

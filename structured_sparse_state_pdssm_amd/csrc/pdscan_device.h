@@ -433,7 +433,7 @@ __device__ __forceinline__ void tile_epilogue(const Plan& p, const f4v* acc, con
   }
 }
 
-template <int IN_BF16, int MMA_BF16, int KCH, int NCT>
+template <int IN_BF16, int MMA_BF16, int KCH, int NCT, int FOLD>
 __device__ __forceinline__ void select_rows(const Args& a, int s_u, int h, int c0, int rbeg,
                                             int rend, int lane, const SelDst& o) {
   typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
@@ -450,7 +450,7 @@ __device__ __forceinline__ void select_rows(const Args& a, int s_u, int h, int c
   for (int ct = 0; ct < NCT; ++ct) {
     const int col = 16 * ct + i;
     const bool sc = col < K, zc = col >= K && col < K + N;
-    const bool bc = p.fold_bu && col >= K + N && col < K + 2 * N;   // drive folded: rows of W_b
+    const bool bc = FOLD && col >= K + N && col < K + 2 * N;   // drive folded: rows of W_b
     const void* wb = sc ? a.W_sel : (zc ? a.W_d : a.W_b);
     const size_t wrow = sc ? ((size_t)h * K + col) * d
                            : (zc ? ((size_t)h * N + (col - K)) * d : ((size_t)h * N + (col - K - N)) * d);
@@ -497,7 +497,7 @@ __device__ __forceinline__ void select_rows(const Args& a, int s_u, int h, int c
 }
 
 // Any shape: operands loaded per 16-row tile, up to 8 column tiles.
-template <int IN_BF16, int MMA_BF16>
+template <int IN_BF16, int MMA_BF16, int FOLD>
 __device__ __forceinline__ void select_rows_any(const Args& a, int s_u, int h, int c0, int rbeg,
                                                 int rend, int lane, const SelDst& o) {
   typedef typename Frag<IN_BF16, MMA_BF16>::T FT;
@@ -528,7 +528,7 @@ __device__ __forceinline__ void select_rows_any(const Args& a, int s_u, int h, i
         if (ct < NCT) {
           const int col = 16 * ct + i;
           const bool sc = col < K, zc = col >= K && col < K + N;
-          const bool bc = p.fold_bu && col >= K + N && col < K + 2 * N;
+          const bool bc = FOLD && col >= K + N && col < K + 2 * N;
           const void* wb = sc ? a.W_sel : (zc ? a.W_d : a.W_b);
           const size_t wrow = sc ? ((size_t)h * K + col) * d
                                  : (zc ? ((size_t)h * N + (col - K)) * d : ((size_t)h * N + (col - K - N)) * d);
@@ -555,7 +555,7 @@ __device__ __forceinline__ void select_rows_any(const Args& a, int s_u, int h, i
 // column tiles per pass, with the u and weight fragments of the next two
 // 32-channel blocks in flight in a three-slot register ring while the current
 // block multiplies.
-template <int NCT>
+template <int NCT, int FOLD>
 __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, int c0, int rbeg,
                                                  int rend, int lane, const SelDst& o) {
   const Plan& p = a.p;
@@ -571,8 +571,8 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
   const rsrc_t rs = make_rsrc((const uint16_t*)a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
   const rsrc_t rz = make_rsrc((const uint16_t*)a.W_d + (size_t)h * N * d, (uint32_t)(N * d * 2));
   // drive folded: tiles KT + NT .. KT + 2 NT - 1 read rows of W_b
-  const rsrc_t rbw = make_rsrc(p.fold_bu ? (const uint16_t*)a.W_b + (size_t)h * N * d : nullptr,
-                               p.fold_bu ? (uint32_t)(N * d * 2) : 0u);
+  const rsrc_t rbw = make_rsrc(FOLD ? (const uint16_t*)a.W_b + (size_t)h * N * d : nullptr,
+                               FOLD ? (uint32_t)(N * d * 2) : 0u);
   const int Tc = min(p.chunk, p.L - c0);
   const rsrc_t ur = make_rsrc((const uint16_t*)a.u + ((size_t)s_u * p.L + c0) * d, (uint32_t)(Tc * d * 2));
 
@@ -595,7 +595,7 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
         const int t = ct0 + ct;
         const int seg = t < KT ? 0 : (t < KT + NT ? 1 : 2);   // W_sel, W_d, W_b
         const int m = seg == 0 ? 16 * t + i : (seg == 1 ? 16 * (t - KT) + i : 16 * (t - KT - NT) + i);
-        const bool ok = seg == 0 ? m < K : (seg == 1 ? m < N : (p.fold_bu && t < KT + 2 * NT && m < N));
+        const bool ok = seg == 0 ? m < K : (seg == 1 ? m < N : (FOLD && t < KT + 2 * NT && m < N));
         woff[ct] = ok ? (uint32_t)((m * d + 8 * g) * 2) : kNoLoad;
         bdr[ct] = (ok && seg == 1) ? a.b_d[(size_t)h * N + m] : 0.f;
         wr[ct] = seg == 0 ? rs : (seg == 1 ? rz : rbw);
@@ -655,7 +655,7 @@ __device__ __forceinline__ void select_rows_deep(const Args& a, int s_u, int h, 
 // afterwards, so a barrier separates their last read from the epilogues.
 // u blocks are loaded three ahead into registers, weight blocks two ahead into
 // registers and then one ahead into a stage.
-template <int NCT>
+template <int NCT, int FOLD>
 __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int h, int c0, int rbeg,
                                                      int rend, int lane, const SelDst& o) {
   const Plan& p = a.p;
@@ -671,8 +671,8 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
   unsigned char* wst = o.wst;
   const rsrc_t rs = make_rsrc((const uint16_t*)a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
   const rsrc_t rz = make_rsrc((const uint16_t*)a.W_d + (size_t)h * N * d, (uint32_t)(N * d * 2));
-  const rsrc_t rbw = make_rsrc(p.fold_bu ? (const uint16_t*)a.W_b + (size_t)h * N * d : nullptr,
-                               p.fold_bu ? (uint32_t)(N * d * 2) : 0u);
+  const rsrc_t rbw = make_rsrc(FOLD ? (const uint16_t*)a.W_b + (size_t)h * N * d : nullptr,
+                               FOLD ? (uint32_t)(N * d * 2) : 0u);
   const int Tc = min(p.chunk, p.L - c0);
   const rsrc_t ur = make_rsrc((const uint16_t*)a.u + ((size_t)s_u * p.L + c0) * d, (uint32_t)(Tc * d * 2));
 
@@ -692,7 +692,7 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
     const int t = wave + kWaves * w;               // uniform in the wave
     const int seg = t < KT ? 0 : (t < KT + NT ? 1 : 2);
     const int m = seg == 0 ? 16 * t + i : (seg == 1 ? 16 * (t - KT) + i : 16 * (t - KT - NT) + i);
-    const bool ok = t < NCT && (seg == 0 ? m < K : (seg == 1 ? m < N : (p.fold_bu && t < KT + 2 * NT && m < N)));
+    const bool ok = t < NCT && (seg == 0 ? m < K : (seg == 1 ? m < N : (FOLD && t < KT + 2 * NT && m < N)));
     toff[w] = ok ? (uint32_t)((m * d + 8 * g) * 2) : kNoLoad;
     tr[w] = seg == 0 ? rs : (seg == 1 ? rz : rbw);
     tlds[w] = (16 * t + i) * kRow + 16 * g;
@@ -773,28 +773,28 @@ enum SelPath : int {
   kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3, kSelBF16D128N5 = 4, kSelDeep = 16
 };
 
-template <int IN_BF16, int MMA_BF16, int PATH>
+template <int IN_BF16, int MMA_BF16, int PATH, int FOLD = 0>
 __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, int c0, int rbeg,
                                                 int rend, int lane, const SelDst& o) {
   if constexpr (PATH == kSelF32D64N2 && !IN_BF16 && !MMA_BF16)
-    select_rows<0, 0, 4, 2>(a, s_u, h, c0, rbeg, rend, lane, o);
+    select_rows<0, 0, 4, 2, FOLD>(a, s_u, h, c0, rbeg, rend, lane, o);
   else if constexpr (PATH == kSelF32D16N1 && !IN_BF16 && !MMA_BF16)
-    select_rows<0, 0, 1, 1>(a, s_u, h, c0, rbeg, rend, lane, o);
+    select_rows<0, 0, 1, 1, FOLD>(a, s_u, h, c0, rbeg, rend, lane, o);
   else if constexpr (PATH == kSelBF16D128N3 && IN_BF16 && MMA_BF16)
-    select_rows<1, 1, 4, 3>(a, s_u, h, c0, rbeg, rend, lane, o);
+    select_rows<1, 1, 4, 3, FOLD>(a, s_u, h, c0, rbeg, rend, lane, o);
   else if constexpr (PATH == kSelBF16D128N5 && IN_BF16 && MMA_BF16)
-    select_rows<1, 1, 4, 5>(a, s_u, h, c0, rbeg, rend, lane, o);
+    select_rows<1, 1, 4, 5, FOLD>(a, s_u, h, c0, rbeg, rend, lane, o);
   else if constexpr (PATH > kSelDeep && IN_BF16 && MMA_BF16) {
     if constexpr (PATH - kSelDeep <= kFoldMaxTiles) {
       if (o.wst) {
-        select_rows_deep_lds<PATH - kSelDeep>(a, s_u, h, c0, rbeg, rend, lane, o);
+        select_rows_deep_lds<PATH - kSelDeep, FOLD>(a, s_u, h, c0, rbeg, rend, lane, o);
         return;
       }
     }
-    select_rows_deep<PATH - kSelDeep>(a, s_u, h, c0, rbeg, rend, lane, o);
+    select_rows_deep<PATH - kSelDeep, FOLD>(a, s_u, h, c0, rbeg, rend, lane, o);
   }
   else
-    select_rows_any<IN_BF16, MMA_BF16>(a, s_u, h, c0, rbeg, rend, lane, o);
+    select_rows_any<IN_BF16, MMA_BF16, FOLD>(a, s_u, h, c0, rbeg, rend, lane, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -1118,7 +1118,7 @@ __device__ __forceinline__ float gather4w(unsigned sx, int vj, float hn) {
 
 // NOUT: rows of C the instantiation handles (1, or kMaxOut for the
 // multi-output plans, which take p.n_out of them).
-template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1>
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1, int FOLD = 0>
 __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   const Plan& p = a.p;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1137,7 +1137,8 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   int* misc = (int*)(smem + p.off_misc);
   uint32_t* hdr = (uint32_t*)a.ws;
   // drive folded (fused mode): the selection writes the drive terms here
-  const bool fold = MODE == kModeFused && p.fold_bu;
+  // (FOLD: the instantiation for plans with fold_bu set)
+  constexpr bool fold = MODE == kModeFused && FOLD;
   float* Bubuf = (float*)(smem + p.off_Bu);
   const int P = NOUT > 1 ? p.n_out : 1;           // rows of C (outputs per step)
 
@@ -1259,7 +1260,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     o.wst = (MODE == kModeFused && p.wst) ? smem + p.off_D : nullptr;
     o.Bubuf = fold ? Bubuf : nullptr;
     const int wr0 = min(wave * gpw * S, Tc), wr1 = min(wr0 + gpw * S, Tc);
-    select_dispatch<IN_BF16, MMA_BF16, PATH>(a, s_u, h, c0, wr0, wr1, lane, o);
+    select_dispatch<IN_BF16, MMA_BF16, PATH, FOLD>(a, s_u, h, c0, wr0, wr1, lane, o);
   }
   if constexpr (MODE == kModeSelect) return;
   if constexpr (PATH >= kSelDeep) first_bu();
@@ -2087,16 +2088,16 @@ __global__ __launch_bounds__(kThreads, NOUT > 2 ? 2 : 3) void pdssm_fused16_kern
 // Two entry points over one body: the register-resident fp32 selection paths
 // fit three waves per SIMD; the other paths get the larger register budget
 // of two waves per SIMD.
-template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1>
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1, int FOLD = 0>
 __global__ __launch_bounds__(kThreads, 3) void pdssm_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT>(a, smem);
+  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT, FOLD>(a, smem);
 }
 
-template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1>
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1, int FOLD = 0>
 __global__ __launch_bounds__(kThreads, 2) void pdssm_kernel_wide(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT>(a, smem);
+  pdssm_body<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT, FOLD>(a, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2123,13 +2124,13 @@ static inline int npt_of(const Plan& p) {
   return (p.N == p.NP && (p.N == 8 || p.N == 16 || p.N == 32 || p.N == 64)) ? p.N : 0;
 }
 
-template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, bool WIDE, int NOUT = 1>
+template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, bool WIDE, int NOUT = 1, int FOLD = 0>
 static inline void launch_kernel(const Args& a, hipStream_t st) {
   if constexpr (WIDE)
-    hipLaunchKernelGGL((pdssm_kernel_wide<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT>), dim3(a.p.tasks),
+    hipLaunchKernelGGL((pdssm_kernel_wide<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT, FOLD>), dim3(a.p.tasks),
                        dim3(kThreads), a.p.lds_bytes, st, a);
   else
-    hipLaunchKernelGGL((pdssm_kernel<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT>), dim3(a.p.tasks),
+    hipLaunchKernelGGL((pdssm_kernel<MODE, IN_BF16, MMA_BF16, PATH, NPT, NOUT, FOLD>), dim3(a.p.tasks),
                        dim3(kThreads), a.p.lds_bytes, st, a);
 }
 
