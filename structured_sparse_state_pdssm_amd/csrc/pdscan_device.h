@@ -1595,6 +1595,19 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
     drow[jq] = ok ? v : -1;
   }
 
+  // rows of C and the logistic biases next (the table build waits for C only,
+  // so every load issued after it stays in flight)
+  const float bdz = buf_f32(make_rsrc(a.b_d + (size_t)h * N, (uint32_t)(N * 4)), i < N ? (uint32_t)i * 4u : kNoLoad);
+  // rows of C (NOUT > 1: p.n_out of them, C[h][o][j]); row 0 also feeds DC
+  const int P = NOUT > 1 ? p.n_out : 1;
+  float cjo[NOUT];
+  {
+    const rsrc_t cr = make_rsrc(a.C + (size_t)h * P * N, (uint32_t)(P * N * 4));
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) cjo[o] = buf_f32(cr, (act && o < P) ? (uint32_t)(o * N + j) * 4u : kNoLoad);
+  }
+  const float cj = cjo[0];
+
   // weight fragments: tile 0 = pre-activation columns, tile 1 = score columns
   // (split into bf16 pieces once per task when the products are emulated)
   constexpr int KB = SPLIT ? KCH / 2 : 1;          // 32-channel blocks
@@ -1657,16 +1670,6 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
       }
     }
   }
-  const float bdz = buf_f32(make_rsrc(a.b_d + (size_t)h * N, (uint32_t)(N * 4)), i < N ? (uint32_t)i * 4u : kNoLoad);
-  // rows of C (NOUT > 1: p.n_out of them, C[h][o][j]); row 0 also feeds DC
-  const int P = NOUT > 1 ? p.n_out : 1;
-  float cjo[NOUT];
-  {
-    const rsrc_t cr = make_rsrc(a.C + (size_t)h * P * N, (uint32_t)(P * N * 4));
-#pragma unroll
-    for (int o = 0; o < NOUT; ++o) cjo[o] = buf_f32(cr, (act && o < P) ? (uint32_t)(o * N + j) * 4u : kNoLoad);
-  }
-  const float cj = cjo[0];
 
   // u rows of tile k for this lane's A operand: group i / 4 of the wave,
   // step 4k + i % 4 of that group's sub-chunk
@@ -1692,8 +1695,11 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
   const int wave_nst = max(min(wave * 4 * S + S, Tc) - wave * 4 * S, 0);
   const int nblk = (wave_nst + 3) >> 2;            // uniform in the wave
   FT U[2][KCH];
-  if (nblk > 0) load_tile(U[0], 0);
-  if (nblk > 1) load_tile(U[1], 1);
+  // unconditional (rows past the wave's steps load zeros): a load under a
+  // branch makes the wait before the table build below count only the loads
+  // issued on every path, which drains these tiles too
+  load_tile(U[0], 0);
+  load_tile(U[1], 1);
 
   // drive terms: a ring of four blocks of four steps; each block's slots are
   // refilled four blocks ahead
