@@ -48,6 +48,9 @@
  *     (Test hook: with PDSSM_TEST_LOOKBACK_GIVEUP=1 in the environment every
  *     wait ignores the carries it finds and gives up after two reads, so a
  *     test can set the word on purpose.  Never set it in normal use.)
+ *   - Tuning hook: PDSSM_XCD_HEAD_GROUPS = 0, 1, 2, 4 or 8 in the environment
+ *     overrides how the general fused kernel groups its (b, h) sequences
+ *     over the eight dies (0: no grouping).  Results do not depend on it.
  *   - Arguments are validated on the host before any HIP call.  On failure
  *     nothing is enqueued and a negative pdssm_status is returned; the
  *     calling thread's pdssm_last_error() then describes the problem.

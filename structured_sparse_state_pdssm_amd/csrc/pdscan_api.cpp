@@ -87,6 +87,16 @@ bool lookback_giveup_hook() {
   return v && v[0] == '1' && v[1] == 0;
 }
 
+// Tuning and test hook: PDSSM_XCD_HEAD_GROUPS = 0, 1, 2, 4 or 8 overrides
+// the die grouping the general fused kernel picks (0: none; a value that
+// would leave a die class empty also gives none).  The results do not depend
+// on it.  Returns -1 when unset.
+int xcd_groups_hook() {
+  const char* v = getenv("PDSSM_XCD_HEAD_GROUPS");
+  if (!v || !v[0] || v[1]) return -1;
+  return (v[0] == '0' || v[0] == '1' || v[0] == '2' || v[0] == '4' || v[0] == '8') ? v[0] - '0' : -1;
+}
+
 int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_bu = 0, int step16 = 0,
                int n_out = 1) {
   const int c = (mode == pdscan::kModeSelect) ? pdscan::kSelectRows : chunk;
@@ -97,6 +107,15 @@ int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_b
                 d->N, p.lds_bytes, p.lds_limit);
   if ((uint64_t)p.nC * d->B * d->H > 0x7fffffffull)
     return fail(PDSSM_EUNSUPPORTED, "too many chunks");
+  if (mode == pdscan::kModeFused && !p.fused16) {
+    int hg = pdscan::xcd_head_groups(p.B, p.H, p.L, p.N, p.K, p.d, p.u_shared, p.in_bf16, p.fold_bu, p.nC);
+    const int forced = xcd_groups_hook();
+    if (forced >= 0) hg = (forced && forced <= p.H && pdscan::kXcds / forced <= p.B) ? forced : 0;
+    if (hg && pdscan::xcd_tasks(p, hg) <= 0x7fffffffll) {
+      p.xhg = hg;
+      p.tasks = (int)pdscan::xcd_tasks(p, hg);
+    }
+  }
   if (lookback_giveup_hook()) {
     p.force_giveup = 1;
     p.spin_limit = 2;

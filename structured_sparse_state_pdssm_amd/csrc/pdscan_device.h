@@ -1143,15 +1143,30 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   const int P = NOUT > 1 ? p.n_out : 1;           // rows of C (outputs per step)
 
   // ---- task: chunk-major tickets so that predecessors always started first
-  int task;
+  // (with the die grouping, tickets of this die's class: see xcd_head_groups)
+  int c, s;
   if constexpr (MODE == kModeSelect) {
-    task = blockIdx.x;
+    c = blockIdx.x / BH;
+    s = blockIdx.x % BH;
   } else {
-    if (tid == 0) misc[0] = (int)atomicAdd(&hdr[kWsTicket], 1u);
+    const int hg = p.xhg, cls = blockIdx.x & (kXcds - 1);
+    if (tid == 0) misc[0] = (int)atomicAdd(&hdr[hg ? kWsClassTicket + cls : kWsTicket], 1u);
     __syncthreads();
-    task = misc[0];
+    const int task = misc[0];
+    if (hg) {
+      const int bg = kXcds / hg, hgi = cls % hg, bgi = cls / hg;
+      const int hlo = p.H * hgi / hg, nh = p.H * (hgi + 1) / hg - hlo;
+      const int blo = p.B * bgi / bg, nb = p.B * (bgi + 1) / bg - blo;
+      const int sz = nh * nb;
+      if (task >= sz * p.nC) return;               // past the class's tasks (uniform in the workgroup)
+      c = task / sz;
+      const int r = task - c * sz;
+      s = (blo + r / nh) * p.H + hlo + r % nh;
+    } else {
+      c = task / BH;
+      s = task % BH;
+    }
   }
-  const int c = task / BH, s = task % BH;
   const int b = s / p.H, h = s % p.H;
   const int c0 = c * T;
   const int Tc = min(T, p.L - c0);

@@ -23,6 +23,8 @@ constexpr int kFoldMaxTiles = 10;      // general kernel, drive folded: column t
 constexpr int kWbFrags = 6;            // W_b fragments per lane at most (fp32 d = 64: 2 blocks x 3 pieces)
 constexpr int kMaxOut = 4;             // outputs per head (rows of C) on the multi-output paths
 constexpr int kSpinLimit = 1 << 22;    // window reads before a look-back wait gives up
+constexpr int kXcds = 8;               // accelerator dies (XCDs); workgroup i is dispatched to die i mod 8
+constexpr double kL2WeightBudget = 2.5 * 1024 * 1024;   // bytes of one die's 4 MiB L2 the weights may hold
 
 enum Mode : int { kModeSelect = 0, kModeScan = 1, kModeFused = 2 };
 
@@ -49,6 +51,8 @@ struct Plan {
   int wst;       // fused deep bf16 selection: weight blocks staged through LDS (in D's region)
   int YS;        // stride of the per-output local-output rows
   int tasks;     // workgroups
+  int xhg;       // general fused kernel: head groups of the die grouping (0: one ticket counter; see
+                 // xcd_head_groups)
   // look-back: window reads before a wait gives up (sets the workspace error
   // word and carries h0), and a test hook that ignores every carry found, so
   // that each wait runs out after spin_limit reads while the kernel still
@@ -124,6 +128,7 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   p.KP = align_up(K, 4);
   p.mma_bf16 = (in_bf16 && d >= 128) ? 1 : 0;
   p.tasks = p.nC * B * H;
+  p.xhg = 0;
 
   const int T = p.chunk;
   int off = 0;
@@ -203,6 +208,45 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   return p.lds_bytes <= p.lds_limit;
 }
 
+// Die grouping of the general fused kernel.  Each of the eight dies has its
+// own L2, and workgroup i runs on die i mod 8, so a workgroup takes its task
+// from a ticket counter of its die's class: class x owns the (b, h) sequences
+// with b in batch group x / hg and h in head group x mod hg (hg head groups,
+// 8 / hg batch groups, contiguous near-equal ranges), in chunk-major order.
+// The weights of a head are then read by 8 / hg dies instead of all eight and
+// a shared input row u[b, t] by hg dies: hg is picked to minimise the bytes
+// the dies fetch beyond their L2, with a head group's weights expected to stay
+// in L2 across chunks only when they take at most kL2WeightBudget.  A
+// predecessor chunk of a task has a lower ticket of the same counter, so the
+// look-back only waits on workgroups that have started.  0 (one counter, the
+// plain chunk-major order) when no sharing is worth it or a class would be
+// empty.
+inline int xcd_head_groups(int B, int H, int L, int N, int K, int d, int u_shared, int in_bf16, int fold,
+                           int nC) {
+  const double es = in_bf16 ? 2 : 4;
+  const double Wt = (double)H * (K + N * (fold ? 2 : 1)) * d * es;   // selection weights of every head
+  const double Ut = u_shared ? (double)B * L * d * es : 0.0;          // the shared input
+  if (!u_shared && Wt <= 1024.0 * 1024.0) return 0;
+  int best = 0;
+  double best_cost = 0;
+  for (int hg = 1; hg <= kXcds; hg *= 2) {
+    const int bg = kXcds / hg;
+    if (hg > H || bg > B) continue;
+    double cost = hg * Ut + bg * Wt;
+    if (Wt / hg > kL2WeightBudget) cost += (nC - 1) * bg * Wt;
+    if (!best || cost < best_cost) { best = hg; best_cost = cost; }
+  }
+  return best;
+}
+
+// Workgroups of a plan with hg head groups (0: none): eight classes padded to
+// the largest; a workgroup whose ticket is past its class's tasks exits.
+inline long long xcd_tasks(const Plan& p, int hg) {
+  if (!hg) return (long long)p.nC * p.B * p.H;
+  const int bg = kXcds / hg;
+  return (long long)kXcds * ((p.B + bg - 1) / bg) * ((p.H + hg - 1) / hg) * p.nC;
+}
+
 // Fills `p` for one call.  `mode` selects which parts exist.  Returns false
 // when the plan needs more LDS than its budget (lds_limit; the gather table
 // is dropped first: phase A then scatters with LDS atomics).
@@ -241,5 +285,6 @@ struct Args {
 // Workspace header words.
 constexpr int kWsTicket = 0;   // uint32 ticket counter
 constexpr int kWsError = 1;    // uint32: nonzero if a look-back wait of this call gave up
+constexpr int kWsClassTicket = 8;   // uint32 x 8: the die classes' ticket counters (die grouping)
 
 }  // namespace pdscan

@@ -4,7 +4,8 @@
   fp32 three-piece split and with bf16 products, and the general kernel's
   register-resident and deep selections): the lowest index must win;
 * run-to-run bit identity of the general kernel on the time-series and
-  LM-layer shapes (many chunks, so the look-back is exercised);
+  LM-layer shapes (many chunks, so the look-back is exercised), and bit
+  identity across its groupings of the sequences over the dies;
 * score accuracy of the three-piece split on inputs whose channels span a
   wide exponent range, and on products of values near the bottom of the
   normal range, against the fp64 definition;
@@ -88,6 +89,42 @@ def test_general_kernel_bit_identical_runs(name, kw):
         a = host(runs[0][key])
         for r in runs[1:]:
             assert np.array_equal(a, host(r[key])), f"{name}: {key} differs between runs"
+
+
+# ----------------------------------------------------------------------------
+# die grouping of the general fused kernel
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,kw", [
+    ("lm_layer", dict(B=8, H=8, L=300)),           # u shared; every grouping possible
+    ("lm_layer", dict(B=3, H=5, L=260, N=32, K=16)),   # ragged groups, padded classes
+    ("timeseries", dict(B=8, H=8, L=600, d=512)),  # u per head, weights of 1.5 MiB
+])
+def test_die_grouping_does_not_change_results(name, kw, monkeypatch):
+    """The general kernel's (b, h) grouping over the dies (forced through the
+    PDSSM_XCD_HEAD_GROUPS hook; a grouping that would leave a die class empty
+    falls back to none) changes only which workgroup runs which task: every
+    output is bit-identical to the ungrouped order, and within the tolerance
+    of the oracle."""
+    inp = generate(get_config(name, **kw))
+    ref = oracle.forward_inputs(inp)
+    dev = upload(inp)
+    chunk = inp.cfg.chunk
+    outs = {}
+    for hg in ("0", "1", "2", "4", "8"):
+        monkeypatch.setenv("PDSSM_XCD_HEAD_GROUPS", hg)
+        print(f"[gpu] die grouping {name} {kw} head groups {hg}", flush=True)
+        outs[hg] = run_fwd(dev, chunk)
+    monkeypatch.delenv("PDSSM_XCD_HEAD_GROUPS")
+    print(f"[gpu] die grouping {name} {kw} default", flush=True)
+    outs["default"] = run_fwd(dev, chunk)
+    base = {k: host(v) for k, v in outs["0"].items()}
+    assert np.array_equal(base["k_star"], ref["k_star"])
+    assert_within(base["y"], ref["y"], f"{name} y")
+    assert_within(base["h_L"], ref["h_L"], f"{name} h_L")
+    for hg, o in outs.items():
+        for key in ("y", "h_L", "k_star", "D"):
+            assert np.array_equal(base[key], host(o[key])), f"{name}: {key} differs with head groups {hg}"
 
 
 # ----------------------------------------------------------------------------

@@ -144,6 +144,22 @@ def test_fold_general_deterministic():
         assert np.array_equal(host(a[n]), host(b[n])), n
 
 
+def test_fold_die_grouping_does_not_change_results(monkeypatch):
+    """The folded general pass under every grouping of the sequences over the
+    dies (PDSSM_XCD_HEAD_GROUPS; 1 would leave die classes empty at B = 4
+    and falls back to none): bit-identical outputs."""
+    inp = generate(get_config("lm_layer", B=4, H=8, L=300))
+    d = _dev(inp)
+    outs = {}
+    for hg in ("0", "1", "2", "4", "8"):
+        monkeypatch.setenv("PDSSM_XCD_HEAD_GROUPS", hg)
+        print(f"[gpu] pdssm_fwd_wb lm_layer head groups {hg}", flush=True)
+        outs[hg] = _run(d, inp.cfg.chunk)
+    for hg, o in outs.items():
+        for n in ("y", "h_L", "k_star", "D"):
+            assert np.array_equal(host(outs["0"][n]), host(o[n])), f"{n} differs with head groups {hg}"
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["impulse", "timeseries", "lm_layer"])
