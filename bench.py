@@ -695,10 +695,10 @@ def bench_multi(args, torch, np, P):
     """Time pdssm_fwd_wb_multi: the folded forward pass with n_out rows of C
     per head (the layer call: u in, y [B,H,L,n_out] out), at the longest
     chunk its on-chip output rows allow unless --chunk is given."""
-    from pdssm_inputs import generate, get_config
+    from pdssm_inputs import generate, get_config, launch_chunk
     cfg = get_config(args.workload)
     P_out = args.n_out
-    chunk = args.chunk or min(cfg.chunk, 256 if P_out <= 2 else 128)
+    chunk = args.chunk or min(launch_chunk("multi", cfg), 256 if P_out <= 2 else 128)
     t0 = time.time()
     inp = generate(cfg)
     print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -814,7 +814,7 @@ def main():
     import torch
 
     import structured_sparse_state_pdssm_amd as P
-    from pdssm_inputs import generate, get_config
+    from pdssm_inputs import generate, get_config, launch_chunk
 
     torch.cuda.set_device(0)
     if args.which == "bwd":
@@ -828,7 +828,7 @@ def main():
     if args.which == "multi":
         return bench_multi(args, torch, np, P)
     cfg = get_config(args.workload)
-    chunk = args.chunk or cfg.chunk
+    chunk = args.chunk or launch_chunk(args.which, cfg)
     t0 = time.time()
     inp = generate(cfg)
     print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)

@@ -18,7 +18,7 @@ Workloads follow the pages' experiment descriptions only loosely (they print no
 inputs); the recipes are synthetic stand-ins, see ``configs.py``.
 """
 
-from .configs import CONFIGS, Config, get_config  # noqa: F401
+from .configs import CONFIGS, Config, get_config, launch_chunk  # noqa: F401
 from .gen import (  # noqa: F401
     GAP,
     Inputs,

@@ -87,3 +87,17 @@ def get_config(name: str, **overrides) -> Config:
     parity sizes: e.g. ``get_config("impulse", L=3000)``)."""
     c = CONFIGS[name]
     return c.with_(**overrides) if overrides else c
+
+
+# Launch chunk of a pass where it differs from the workload's own.  The
+# folded and multi-output calls on the LM-layer shape hold the drive terms
+# (and the extra output rows) on chip: at the workload's chunk of 128 one
+# workgroup fills a CU, and these are the longest chunks at which two share
+# one (78.6 KB and 79.9 KB of LDS each).  The results do not depend on the
+# chunk beyond rounding.
+LAUNCH_CHUNK = {("fold", "lm_layer"): 96, ("multi", "lm_layer"): 64}
+
+
+def launch_chunk(pass_name: str, cfg: Config) -> int:
+    """Chunk at which the benchmark runs `pass_name` on workload `cfg`."""
+    return LAUNCH_CHUNK.get((pass_name, cfg.name), cfg.chunk)

@@ -1372,18 +1372,32 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     constexpr int LG = NG == 64 ? 6 : 5;
     const unsigned lb4 = (unsigned)lb * 0x01010101u;
     const int lbm = lb;                            // byte offset of the group's lane 0
+    // The table rows of the block's four entries are read before the first
+    // step (they depend on k* alone), and with one row of C the block's w_t
+    // are written after its last step: each step then waits on LDS once, for
+    // its gather, instead of also on its table row and on its permute of C.
+    constexpr bool kDeferW = NOUT == 1;
     auto steps = [&](auto full_tag, const i4v k4, const f4v d4, const f4v b4, int t0, int q4, int nb) {
       constexpr bool FULL = decltype(full_tag)::value;
+      int kk[4];
+      i2v se4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int k = (FULL || r < nb) ? k4[r] : 0;
+        if constexpr (NG == 64) k = __builtin_amdgcn_readfirstlane(k);   // one group per wave
+        kk[r] = k;
+        se4[r] = SE[(k << LG) + j];
+      }
+      [[maybe_unused]] float cwv[4], msv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool valid = FULL || r < nb;
         const int t = t0 + r;
-        int k = valid ? k4[r] : 0;
-        if constexpr (NG == 64) k = __builtin_amdgcn_readfirstlane(k);   // one group per wave
+        const int k = kk[r];
         const int nrow = DR[(k << LG) + midx];
         const float dm = __int_as_float(__builtin_amdgcn_ds_bpermute(lbm + (midx << 2), __float_as_int(d4[r])));
         const float bt = fold ? b4[r] : bu[q4 + r];
-        const i2v se = SE[(k << LG) + j];
+        const i2v se = se4[r];
         const int vj = __float_as_int(d4[r] * hl);
         float hn = gather4w((unsigned)se.x | lb4, vj, bt);
         if (__builtin_amdgcn_ballot_w64(se.y & 1)) {      // rows with five to eight sources
@@ -1407,11 +1421,16 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
           midx = nrow;
         }
         // w_t = C Phi_t, row o of C from the lane that holds C[o][midx]
+        if constexpr (kDeferW) {
+          cwv[r] = __int_as_float(__builtin_amdgcn_ds_bpermute(lbm + (midx << 2), __float_as_int(cjo[0])));
+          msv[r] = msc;
+        } else {
 #pragma unroll
-        for (int o = 0; o < NOUT; ++o) {
-          if (o < P) {
-            const float cw = __int_as_float(__builtin_amdgcn_ds_bpermute(lbm + (midx << 2), __float_as_int(cjo[o])));
-            if (valid) Dbuf[(o * N + j) * TS + t] = cw * msc;
+          for (int o = 0; o < NOUT; ++o) {
+            if (o < P) {
+              const float cw = __int_as_float(__builtin_amdgcn_ds_bpermute(lbm + (midx << 2), __float_as_int(cjo[o])));
+              if (valid) Dbuf[(o * N + j) * TS + t] = cw * msc;
+            }
           }
         }
 #pragma unroll
@@ -1421,6 +1440,11 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
             if (valid && j == NG - 1) yloc[o * p.YS + t] = yl;
           }
         }
+      }
+      if constexpr (kDeferW) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (FULL || r < nb) Dbuf[j * TS + t0 + r] = cwv[r] * msv[r];
       }
     };
     for (int blk = 0; blk < nst; blk += kBuBlock) {

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from pdssm_inputs import generate, get_config
+from pdssm_inputs import generate, get_config, launch_chunk
 from tests._gpu import assert_within, host, lib, proj_dev, to_dev, torch_mod
 
 pytestmark = pytest.mark.gpu
@@ -82,7 +82,7 @@ def test_fold_chunk_independence(chunk):
     _check(_run(_dev(inp), chunk), ref, f"chunk {chunk}")
 
 
-@pytest.mark.parametrize("key,chunk", [("lm_layer", 64), ("lm_layer", 100), ("lm_layer", 32),
+@pytest.mark.parametrize("key,chunk", [("lm_layer", 64), ("lm_layer", 96), ("lm_layer", 100), ("lm_layer", 32),
                                        ("timeseries", 128), ("timeseries", 64), ("timeseries", 7)])
 def test_fold_general_chunk_independence(key, chunk):
     """The general kernel's folded drive at other chunks: the LM-layer shape
@@ -164,12 +164,14 @@ def test_fold_die_grouping_does_not_change_results(monkeypatch):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["impulse", "timeseries", "lm_layer"])
 def test_fold_full_size(name):
-    """Full workloads in the benchmark's launch configuration (their chunk)."""
+    """Full workloads in the benchmark's launch configuration (its chunk for
+    the folded pass: 96 on the LM-layer shape, else the workload's)."""
     torch = torch_mod()
     inp = generate(get_config(name))
     ref = oracle.forward_wb(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, inp.C, inp.h0,
                             inp.cfg.u_shared)
-    print(f"[gpu] pdssm_fwd_wb {name} full size", flush=True)
-    out = _run(_dev(inp), inp.cfg.chunk)
+    chunk = launch_chunk("fold", inp.cfg)
+    print(f"[gpu] pdssm_fwd_wb {name} full size chunk={chunk}", flush=True)
+    out = _run(_dev(inp), chunk)
     torch.cuda.synchronize()
     _check(out, ref, f"{name} full")
