@@ -93,9 +93,12 @@ def get_config(name: str, **overrides) -> Config:
 # folded and multi-output calls on the LM-layer shape hold the drive terms
 # (and the extra output rows) on chip: at the workload's chunk of 128 one
 # workgroup fills a CU, and these are the longest chunks at which two share
-# one (78.6 KB and 79.9 KB of LDS each).  The results do not depend on the
-# chunk beyond rounding.
-LAUNCH_CHUNK = {("fold", "lm_layer"): 96, ("multi", "lm_layer"): 64}
+# one (78.6 KB and 79.9 KB of LDS each).  The base shape (32 sequences of
+# 4096 steps) at 128 makes 1024 chunk tasks, more than one round of the 768
+# workgroups the chip holds, each paying the per-task set-up; at 256 the 512
+# tasks run in one round.  The results do not depend on the chunk beyond
+# rounding.
+LAUNCH_CHUNK = {("fold", "lm_layer"): 96, ("multi", "lm_layer"): 64, ("fwd", "base"): 256}
 
 
 def launch_chunk(pass_name: str, cfg: Config) -> int:

@@ -178,6 +178,27 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Group sums of four values at once (NP = 32 or 64): lane l ends with the
+// sum over its group of v[l & 3].  Two exchange levels inside each quad leave
+// every lane the quad sum of one value (l & 3), rotations by 4 and 8 finish
+// each 16-lane row, and permutes join the rows: 6 or 7 exchanges instead of
+// 4 x 6 for four separate sums.  The order of the additions is fixed.
+constexpr int kDppRor4 = 0x124;        // row_ror:4
+constexpr int kDppRor8 = 0x128;        // row_ror:8
+template <int NP>
+__device__ __forceinline__ float group_sum4(const float (&v)[4], int lane) {
+  static_assert(NP == 32 || NP == 64, "rows joined by permutes");
+  const bool o1 = lane & 1, o2 = lane & 2;
+  const float a = (o1 ? v[1] : v[0]) + dpp_f<kDppXor1>(o1 ? v[0] : v[1]);
+  const float b = (o1 ? v[3] : v[2]) + dpp_f<kDppXor1>(o1 ? v[2] : v[3]);
+  float c = (o2 ? b : a) + dpp_f<kDppXor2>(o2 ? a : b);
+  c += dpp_f<kDppRor4>(c);
+  c += dpp_f<kDppRor8>(c);
+  c += __shfl_xor(c, 16, 64);
+  if constexpr (NP == 64) c += __shfl_xor(c, 32, 64);
+  return c;
+}
+
 // The same sum, complete only in the group's last 16-lane row (lanes
 // NP - 16 .. NP - 1; NP <= 16: every lane): rows are joined by DPP row
 // broadcasts (lane 15 of a row into the next row, lane 31 into rows 2 and 3)
@@ -1105,12 +1126,16 @@ __device__ __forceinline__ i2v row_entry(int tg, bool on, int q, int lane) {
 // two bits of its address; the presence bits become weights 1.0 / 0.0 through
 // byte-to-float conversions, and fma(g, 1, h) = h + g, fma(g, 0, h) = h, so
 // the sum equals the selected additions in source order.
-__device__ __forceinline__ float gather4w(unsigned sx, int vj, float hn) {
+// pm is the presence mask 0x01010101 from the plan, opaque to the compiler:
+// with a literal it knows that each masked byte is 0 or 1 and extracts the bit
+// before converting (two instructions per weight instead of one
+// v_cvt_f32_ubyteN).
+__device__ __forceinline__ float gather4w(unsigned sx, int vj, float hn, unsigned pm) {
   float g[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
     g[m] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)((sx >> (8 * m)) & 0xFFu), vj));
-  const unsigned wb = sx & 0x01010101u;
+  const unsigned wb = sx & pm;
 #pragma unroll
   for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(g[m], (float)((wb >> (8 * m)) & 0xFFu), hn);
   return hn;
@@ -1372,10 +1397,13 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     constexpr int LG = NG == 64 ? 6 : 5;
     const unsigned lb4 = (unsigned)lb * 0x01010101u;
     const int lbm = lb;                            // byte offset of the group's lane 0
+    const unsigned pm = (unsigned)p.pmask;
     // The table rows of the block's four entries are read before the first
     // step (they depend on k* alone), and with one row of C the block's w_t
     // are written after its last step: each step then waits on LDS once, for
     // its gather, instead of also on its table row and on its permute of C.
+    // With one row of C the four local outputs are also summed together after
+    // the last step (group_sum4).
     constexpr bool kDeferW = NOUT == 1;
     auto steps = [&](auto full_tag, const i4v k4, const f4v d4, const f4v b4, int t0, int q4, int nb) {
       constexpr bool FULL = decltype(full_tag)::value;
@@ -1388,7 +1416,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         kk[r] = k;
         se4[r] = SE[(k << LG) + j];
       }
-      [[maybe_unused]] float cwv[4], msv[4];
+      [[maybe_unused]] float cwv[4], msv[4], ylv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool valid = FULL || r < nb;
@@ -1399,10 +1427,10 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         const float bt = fold ? b4[r] : bu[q4 + r];
         const i2v se = se4[r];
         const int vj = __float_as_int(d4[r] * hl);
-        float hn = gather4w((unsigned)se.x | lb4, vj, bt);
+        float hn = gather4w((unsigned)se.x | lb4, vj, bt, pm);
         if (__builtin_amdgcn_ballot_w64(se.y & 1)) {      // rows with five to eight sources
           // (bit 25, the more-than-eight flag, is bit 1 of byte 3: the permute ignores it)
-          hn = gather4w((unsigned)se.y | lb4, vj, hn);
+          hn = gather4w((unsigned)se.y | lb4, vj, hn, pm);
           if (__builtin_amdgcn_ballot_w64((se.y >> 25) & 1u)) {   // more than eight: scan the map row
             const bool more = (se.y >> 25) & 1u;
             const unsigned char* DRk = DR + (k << LG);
@@ -1433,11 +1461,15 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
             }
           }
         }
+        if constexpr (kDeferW) {
+          ylv[r] = cjo[0] * hl;
+        } else {
 #pragma unroll
-        for (int o = 0; o < NOUT; ++o) {
-          if (o < P) {
-            const float yl = group_sum_last<NG>(cjo[o] * hl);
-            if (valid && j == NG - 1) yloc[o * p.YS + t] = yl;
+          for (int o = 0; o < NOUT; ++o) {
+            if (o < P) {
+              const float yl = group_sum_last<NG>(cjo[o] * hl);
+              if (valid && j == NG - 1) yloc[o * p.YS + t] = yl;
+            }
           }
         }
       }
@@ -1445,6 +1477,9 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (FULL || r < nb) Dbuf[j * TS + t0 + r] = cwv[r] * msv[r];
+        // the block's local outputs: lane j < 4 of the group writes step t0 + j
+        const float yl = group_sum4<NG>(ylv, lane);
+        if (j < 4 && (FULL || j < nb)) yloc[t0 + j] = yl;
       }
     };
     for (int blk = 0; blk < nst; blk += kBuBlock) {

@@ -58,6 +58,7 @@ struct Plan {
   // that each wait runs out after spin_limit reads while the kernel still
   // ends normally
   int spin_limit, force_giveup;
+  int pmask;     // 0x01010101: the gather's source-presence mask, passed at run time (see gather4w)
   // LDS byte offsets
   int off_D, off_k, off_yl, off_dict, off_DC, off_SRC, off_C, off_bd, off_slot, off_sIdx, off_sSc, off_sB,
       off_pIdx, off_pSc, off_pB, off_H, off_tmp, off_WB, off_Bu, off_misc, lds_bytes;
@@ -80,6 +81,7 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   p.u_shared = u_shared; p.in_bf16 = in_bf16;
   p.spin_limit = kSpinLimit;
   p.force_giveup = 0;
+  p.pmask = 0x01010101;
   // a chunk longer than the sequence behaves exactly like chunk = L
   p.chunk = (mode == kModeSelect) ? kSelectRows : (chunk < L ? chunk : L);
   // Step-major fused path: 16-lane groups, each MFMA tile holding four steps

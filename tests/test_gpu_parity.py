@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from pdssm_inputs import generate, get_config
+from pdssm_inputs import generate, get_config, launch_chunk
 from tests._gpu import TOL, assert_within, host, lib, run_fwd, to_dev, torch_mod, upload
 
 pytestmark = pytest.mark.gpu
@@ -335,6 +335,10 @@ def test_h0_none_equals_zeros():
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["tiny", "base", "timeseries", "impulse", "lm_layer"])
 def test_full_size(name):
+    """Every workload at full size, at its own chunk and, where the benchmark
+    launches at another (base: 256), at that one too."""
     inp = generate(get_config(name))
     ref = oracle.forward_inputs(inp)
-    _check_fwd(inp, ref, inp.cfg.chunk, f"full {name}")
+    for chunk in sorted({inp.cfg.chunk, launch_chunk("fwd", inp.cfg)}):
+        print(f"[gpu] full {name} chunk={chunk}", flush=True)
+        _check_fwd(inp, ref, chunk, f"full {name} chunk {chunk}")
