@@ -45,6 +45,7 @@ typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u2v __attribute__((ext_vector_type(2)));
 typedef int i4v __attribute__((ext_vector_type(4)));
 typedef int i2v __attribute__((ext_vector_type(2)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr uint64_t kTagValid = 1ull << 32;
 constexpr int kBuBlock = 16;   // phase-A steps whose drive terms sit in registers
@@ -791,7 +792,8 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
 // tiles then ceil(N / 16) pre-activation tiles, rounded up to even (a shape
 // with fewer real column tiles computes zero tiles that are never written).
 enum SelPath : int {
-  kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3, kSelBF16D128N5 = 4, kSelDeep = 16
+  kSelAny = 0, kSelF32D64N2 = 1, kSelF32D16N1 = 2, kSelBF16D128N3 = 3, kSelBF16D128N5 = 4, kSelStep32 = 5,
+  kSelDeep = 16
 };
 
 template <int IN_BF16, int MMA_BF16, int PATH, int FOLD = 0>
@@ -1141,6 +1143,32 @@ __device__ __forceinline__ float gather4w(unsigned sx, int vj, float hn, unsigne
   return hn;
 }
 
+// k* of four steps at once (key r of each lane = score column i of step r;
+// keys past K hold the minimum): the row maximum, then the lowest column that
+// reaches it, each level applied to all four steps before the next so that
+// the DPP reads never wait on the instruction just before them.
+__device__ __forceinline__ void row_argmax4(const int (&key)[4], int i, int (&ks)[4]) {
+  int m[4], c[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = max(key[r], dpp_i<kDppXor1>(key[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = max(m[r], dpp_i<kDppXor2>(m[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = max(m[r], dpp_i<kDppHalfMirror>(m[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = max(m[r], dpp_i<kDppMirror>(m[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = key[r] == m[r] ? i : 0x7fffffff;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = min(c[r], dpp_i<kDppXor1>(c[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = min(c[r], dpp_i<kDppXor2>(c[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = min(c[r], dpp_i<kDppHalfMirror>(c[r]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ks[r] = min(c[r], dpp_i<kDppMirror>(c[r]));
+}
+
 // NOUT: rows of C the instantiation handles (1, or kMaxOut for the
 // multi-output plans, which take p.n_out of them).
 template <int MODE, int IN_BF16, int MMA_BF16, int PATH, int NPT, int NOUT = 1, int FOLD = 0>
@@ -1205,6 +1233,67 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   const bool act = NPT ? true : (j < N);
   const int jj = act ? j : 0;              // row index that is safe to look up
 
+  // ---- step-major selection (kSelStep32: N = 32, K <= 16, per-head bf16 u,
+  // d = 128, at most two tiles of 16 steps per group).  Row i of a wave's
+  // 32x32 tile kt is step 16 kt + ((i >> 3) << 2 | (i & 3)) of the wave's
+  // group (i >> 2) & 1, so output element r of lane (group g, row j) is step
+  // 16 kt + r of group g at column j.  One tile has the pre-activation
+  // columns (rows of W_d), the other the score columns (rows of W_sel,
+  // repeated in both 16-lane halves): every lane receives D_t[j] for its own
+  // steps and each 16-lane row all scores of its group's steps, so the
+  // selections never pass through LDS.  Weights and the wave's u tiles are
+  // loaded once, as MFMA operands (lane l: column or row l % 32, channels
+  // 16 m + 8 (l / 32) .. +7 of k-step m).
+  constexpr bool SM32 = PATH == kSelStep32;
+  constexpr int kS32 = 8;                          // 16-channel k-steps (d = 128)
+  [[maybe_unused]] u4v wz32[SM32 ? kS32 : 1], ws32[SM32 ? kS32 : 1], U32[SM32 ? 2 : 1][SM32 ? kS32 : 1];
+  [[maybe_unused]] float bdz32 = 0.f;
+  // steps of the wave's first group (the most in the wave), uniform
+  [[maybe_unused]] const int wave_nst = max(min(wave * gpw * S + S, Tc) - wave * gpw * S, 0);
+  [[maybe_unused]] auto issue32 = [&]() __attribute__((always_inline)) {
+    if constexpr (SM32) {
+      const int col = lane & 31, kh = lane >> 5, sc = col & 15;
+      const rsrc_t wzr = make_rsrc((const uint16_t*)a.W_d + (size_t)h * N * 128, (uint32_t)(N * 128 * 2));
+      const rsrc_t wsr = make_rsrc((const uint16_t*)a.W_sel + (size_t)h * K * 128, (uint32_t)(K * 128 * 2));
+#pragma unroll
+      for (int m = 0; m < kS32; ++m) {
+        wz32[m] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                              wzr, (uint32_t)((col * 128 + 16 * m + 8 * kh) * 2), 0, 0));
+        ws32[m] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                              wsr, sc < K ? (uint32_t)((sc * 128 + 16 * m + 8 * kh) * 2) : kNoLoad,
+                                              0, 0));
+      }
+      bdz32 = buf_f32(make_rsrc(a.b_d + (size_t)h * N, (uint32_t)(N * 4)), (uint32_t)col * 4u);
+      const rsrc_t ur = make_rsrc((const uint16_t*)a.u + gbase * 128, (uint32_t)(Tc * 128 * 2));
+      const int i = lane & 31, grp = (i >> 2) & 1, st = ((i >> 3) << 2) | (i & 3);
+      const int gtb = (wave * 2 + grp) * S;          // first step of that group
+      const int gns = max(min(gtb + S, Tc) - gtb, 0);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int m = 0; m < kS32; ++m) {
+          const bool ok = 16 * kt + st < gns;
+          U32[kt][m] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   ur, ok ? (uint32_t)(((gtb + 16 * kt + st) * 128 + 16 * m + 8 * kh) * 2)
+                                                          : kNoLoad, 0, 0));
+        }
+    }
+  };
+  // pre-activations and scores of one tile
+  [[maybe_unused]] auto mma32 = [&](f16v& aD, f16v& aS, const u4v* Ua) __attribute__((always_inline)) {
+    if constexpr (SM32) {
+      aD = f16v{};
+      aS = f16v{};
+#pragma unroll
+      for (int m = 0; m < kS32; ++m) {
+        aD = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8v, Ua[m]), __builtin_bit_cast(bf8v, wz32[m]),
+                                                     aD, 0, 0, 0);
+        aS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8v, Ua[m]), __builtin_bit_cast(bf8v, ws32[m]),
+                                                     aS, 0, 0, 0);
+      }
+    }
+  };
+
   // ---- phase-A drive terms of the first block: issued first, used last
   // (selection mode never reads Bu, and with the drive folded it is formed
   // on chip: Bu may be null there, and the empty descriptor loads zeros)
@@ -1246,6 +1335,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         const int q = wave * 64 + it * kThreads + lane;
         rv[it] = buf_i32(dr, q < K * N ? (uint32_t)q * 4u : kNoLoad);
       }
+      issue32();                                   // step-major selection operands (the table build waits only for rv)
 #pragma unroll
       for (int it = 0; it < kIt; ++it) {
         const int q0 = wave * 64 + it * kThreads;   // uniform in the wave
@@ -1285,8 +1375,9 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   }
   __syncthreads();
 
-  // ---- selection for this wave's rows
-  if constexpr (MODE != kModeScan) {
+  // ---- selection for this wave's rows (the step-major path selects tile by
+  // tile inside phase A)
+  if constexpr (MODE != kModeScan && !SM32) {
     const int s_u = p.u_shared ? b : s;
     SelDst o;
     o.kbuf = (MODE == kModeFused) ? kbuf : nullptr;
@@ -1482,7 +1573,9 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         if (j < 4 && (FULL || j < nb)) yloc[t0 + j] = yl;
       }
     };
-    for (int blk = 0; blk < nst; blk += kBuBlock) {
+    // one block of kBuBlock steps; the step-major path passes the block's
+    // selections in registers (kr, dr), the others read them from LDS
+    auto run_block = [&](int blk, const int* kr, const float* dr) __attribute__((always_inline)) {
       float bn[kBuBlock];
 #pragma unroll
       for (int q = 0; q < kBuBlock; ++q) {
@@ -1494,8 +1587,15 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         const int nb = nst - blk - q4;             // steps left, uniform in the group
         if (!__builtin_amdgcn_ballot_w64(nb > 0)) break;
         const int t0 = tb + blk + q4;
-        const i4v k4 = *(const i4v*)(kbuf + t0);
-        const f4v d4 = *(const f4v*)(Dbuf + j * TS + t0);
+        i4v k4;
+        f4v d4;
+        if constexpr (SM32) {
+          k4 = i4v{kr[q4], kr[q4 + 1], kr[q4 + 2], kr[q4 + 3]};
+          d4 = f4v{dr[q4], dr[q4 + 1], dr[q4 + 2], dr[q4 + 3]};
+        } else {
+          k4 = *(const i4v*)(kbuf + t0);
+          d4 = *(const f4v*)(Dbuf + j * TS + t0);
+        }
         const f4v b4 = fold ? *(const f4v*)(Bubuf + j * TS + t0) : f4v{0.f, 0.f, 0.f, 0.f};
         if (!__builtin_amdgcn_ballot_w64(nb < 4))
           steps(std::true_type{}, k4, d4, b4, t0, q4, nb);
@@ -1504,6 +1604,56 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
       }
 #pragma unroll
       for (int q = 0; q < kBuBlock; ++q) bu[q] = bn[q];
+    };
+    if constexpr (SM32) {
+      // D_t = logistic(pre-activation) per lane, k*_t by a row argmax over the
+      // score columns of each 16-lane row (both rows of a group hold the same
+      // scores), for the tile's 16 steps
+      auto sel32 = [&](int blk, const f16v& aD, const f16v& aS, int* ks, float* Dr) __attribute__((always_inline)) {
+        const int ci = lane & 15;
+        int key[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          Dr[r] = logistic(aD[r] + bdz32);
+          key[r] = ci < K ? order_key(aS[r]) : (int)0x80000000;
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 16; r4 += 4) {
+          const int kq[4] = {key[r4], key[r4 + 1], key[r4 + 2], key[r4 + 3]};
+          int kw[4];
+          row_argmax4(kq, ci, kw);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ks[r4 + e] = kw[e];
+        }
+        if (a.k_out && j == 0)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (blk + r < nst) a.k_out[gbase + tb + blk + r] = ks[r];
+        if (a.D_out)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (blk + r < nst) a.D_out[(gbase + tb + blk + r) * N + j] = Dr[r];
+      };
+      // both tiles' products are issued first: the second runs on the matrix
+      // cores while the first tile's steps run on the vector units.  One copy
+      // of the block code serves both tiles (the second tile's accumulators
+      // move into the first's), which keeps the hot loop within the
+      // instruction cache.
+      f16v aD, aS, nD, nS;
+      mma32(aD, aS, U32[0]);
+      const int ntile = wave_nst > 16 ? 2 : 1;     // uniform in the wave
+      if (ntile == 2) mma32(nD, nS, U32[1]);
+      int ks[16];
+      float Dr[16];
+#pragma nounroll
+      for (int kt = 0; kt < ntile; ++kt) {
+        sel32(16 * kt, aD, aS, ks, Dr);
+        run_block(16 * kt, ks, Dr);
+        aD = nD;
+        aS = nS;
+      }
+    } else {
+      for (int blk = 0; blk < nst; blk += kBuBlock) run_block(blk, nullptr, nullptr);
     }
   };
   if constexpr ((NPT == 32 || NPT == 64) && MODE != kModeSelect) {
@@ -1573,31 +1723,6 @@ __device__ __forceinline__ float se_gather(const i4v se, const f4v wt, int vj, u
   return hn;
 }
 
-// k* of four steps at once (key r of each lane = score column i of step r;
-// keys past K hold the minimum): the row maximum, then the lowest column that
-// reaches it, each level applied to all four steps before the next so that
-// the DPP reads never wait on the instruction just before them.
-__device__ __forceinline__ void row_argmax4(const int (&key)[4], int i, int (&ks)[4]) {
-  int m[4], c[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) m[r] = max(key[r], dpp_i<kDppXor1>(key[r]));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) m[r] = max(m[r], dpp_i<kDppXor2>(m[r]));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) m[r] = max(m[r], dpp_i<kDppHalfMirror>(m[r]));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) m[r] = max(m[r], dpp_i<kDppMirror>(m[r]));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) c[r] = key[r] == m[r] ? i : 0x7fffffff;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) c[r] = min(c[r], dpp_i<kDppXor1>(c[r]));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) c[r] = min(c[r], dpp_i<kDppXor2>(c[r]));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) c[r] = min(c[r], dpp_i<kDppHalfMirror>(c[r]));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) ks[r] = min(c[r], dpp_i<kDppMirror>(c[r]));
-}
 
 // ---------------------------------------------------------------------------
 // Fused pass with step-major tiles (N <= 16, K <= 16, per-head u).
@@ -2184,6 +2309,7 @@ __global__ __launch_bounds__(kThreads, 2) void pdssm_kernel_wide(Args a) {
 // host launchers
 // ---------------------------------------------------------------------------
 static inline int sel_path(const Plan& p) {
+  if (p.step32) return kSelStep32;
   const int nct = p.NC >> 4;
   if (!p.in_bf16 && p.d == 64 && nct == 2) return kSelF32D64N2;
   if (!p.in_bf16 && p.d == 16 && nct == 1) return kSelF32D16N1;

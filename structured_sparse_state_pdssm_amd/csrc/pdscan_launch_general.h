@@ -33,7 +33,9 @@ static hipError_t launch_general(const Args& a, hipStream_t st) {
   const Plan& p = a.p;
   const int path = sel_path(p), npt = npt_of(p);
   if (p.in_bf16 && p.mma_bf16) {
-    if (path == kSelBF16D128N3 && npt == 32)
+    if (path == kSelStep32) {                      // step-major selection tiles (one output, unfolded)
+      if constexpr (NOUT == 1 && !FOLD) launch_kernel<kModeFused, 1, 1, kSelStep32, 32, true, 1, 0>(a, st);
+    } else if (path == kSelBF16D128N3 && npt == 32)
       launch_kernel<kModeFused, 1, 1, kSelBF16D128N3, 32, true, NOUT, FOLD>(a, st);
     else if (path == kSelBF16D128N3)
       launch_kernel<kModeFused, 1, 1, kSelBF16D128N3, 0, true, NOUT, FOLD>(a, st);

@@ -46,6 +46,7 @@ struct Plan {
   int fold_bu;   // Bu = W_b u formed on chip instead of read: a third MFMA tile (fused16) or a third
                  // column segment of the selection GEMM written to an on-chip [N][TS] buffer (general kernel)
   int step16;    // scan alone with the step-major layout (N <= 16); 2: also writes every state
+  int step32;    // general fused kernel with step-major selection tiles (32-lane groups, see below)
   int n_out;     // outputs per head, rows of C (> 1: step-major paths only)
   int gse;       // general kernel, N = 32 or 64: phase A gathers over inverse dictionary rows (table at off_SRC)
   int wst;       // fused deep bf16 selection: weight blocks staged through LDS (in D's region)
@@ -98,13 +99,20 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
   const bool gen_fold = mode == kModeFused && !p.fused16 && fold_bu &&
                         (deep_sel ? ((KT + 2 * NT + 1) & ~1) <= kFoldMaxTiles : align_up(K + 2 * N, 16) <= 128);
   p.fold_bu = ((p.fused16 || gen_fold) && fold_bu) ? 1 : 0;
+  // General fused kernel, N = 32: the selection as 32x32 MFMA tiles whose
+  // rows are (group, step) pairs, so that D and the scores of a group's steps
+  // land in its lanes' registers (per-head bf16 u, d = 128, K <= 16, unfolded,
+  // one output, at most two tiles of 16 steps per group: chunk <= 256; the
+  // inverse-row gather is required)
+  p.step32 = (mode == kModeFused && !p.fused16 && !u_shared && in_bf16 && d == 128 && N == 32 && K <= 16 &&
+              !p.fold_bu && n_out == 1 && allow_gse && (chunk < L ? chunk : L) <= 256) ? 1 : 0;
   // the scan alone on the same layout: maps streamed per step (at most 32
   // steps per group, as above)
   p.step16 = (mode == kModeScan && step16 && N <= 16 && K <= 16 && (chunk < L ? chunk : L) <= 512) ? step16 : 0;
   const bool sm = p.fused16 || p.step16;
   p.NP = sm ? 16 : next_pow2(N);
   p.G = kThreads / p.NP;
-  p.S = align_up((p.chunk + p.G - 1) / p.G, 4);
+  p.S = align_up((p.chunk + p.G - 1) / p.G, p.step32 ? 16 : 4);   // step32: whole tiles of 16 steps
   // t-contiguous rows; a stride of 4 (mod 32) words spreads the rows of one
   // column over distinct LDS banks while keeping 16-byte alignment
   // Column layout.  fused16: group g's step t goes to column t + g and the

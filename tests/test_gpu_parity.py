@@ -152,6 +152,19 @@ def test_chunk_size_independence(chunk):
     _check_fwd(inp, ref, chunk, f"base chunk {chunk}")
 
 
+@pytest.mark.parametrize("chunk", [7, 16, 48, 100, 200, 256])
+@pytest.mark.parametrize("kw", [dict(B=1, H=3, L=700), dict(B=2, H=2, L=430, K=5)],
+                         ids=["K16", "K5"])
+def test_step_major_n32_tiles(kw, chunk):
+    """The time-series shape's step-major selection tiles (N = 32, bf16
+    d = 128): one or two 16-step tiles per group, last chunks whose wave
+    groups hold different step counts (700 and 430 are not multiples of the
+    chunk), K below 16 (score columns past K hold the minimum key), k* and D
+    written out, against the oracle."""
+    inp, ref = _case("timeseries", **kw)
+    _check_fwd(inp, ref, chunk, f"step-major N=32 {kw}")
+
+
 def test_deterministic_runs():
     inp, _ = _case("impulse", **REDUCED["impulse"])
     dev = upload(inp)
