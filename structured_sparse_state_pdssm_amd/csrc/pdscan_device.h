@@ -1124,8 +1124,9 @@ __device__ __forceinline__ i2v row_entry(int tg, bool on, int q, int lane) {
 
 // Sum over four sources of one row: sx holds four source bytes (lane byte
 // offset 4 j with the presence bit 0 set, the group's lane-0 offset ORed into
-// bit 7), vj the value of lane j of the group.  The permute ignores the low
-// two bits of its address; the presence bits become weights 1.0 / 0.0 through
+// bit 7), vj the value of lane j of the group.  The permute selects its lane
+// from address bits 2 to 7 alone (checked on gfx950), so byte m of sx needs
+// only a shift, and the presence bits become weights 1.0 / 0.0 through
 // byte-to-float conversions, and fma(g, 1, h) = h + g, fma(g, 0, h) = h, so
 // the sum equals the selected additions in source order.
 // pm is the presence mask 0x01010101 from the plan, opaque to the compiler:
@@ -1136,7 +1137,7 @@ __device__ __forceinline__ float gather4w(unsigned sx, int vj, float hn, unsigne
   float g[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
-    g[m] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)((sx >> (8 * m)) & 0xFFu), vj));
+    g[m] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(sx >> (8 * m)), vj));
   const unsigned wb = sx & pm;
 #pragma unroll
   for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(g[m], (float)((wb >> (8 * m)) & 0xFFu), hn);
@@ -1697,7 +1698,8 @@ __device__ __forceinline__ void write_se(i4v* SE, f4v* SW, int tid, const int (&
 // h'_i = hn + sum over the sources j of row i (entries se, wt) of the value
 // vj of lane j of this 16-lane group, gathered in ascending j.  lb4 holds the
 // group's lane-0 byte offset in each of its four bytes (a multiple of 64, and
-// a slot offset is below 64, so one OR places all four addresses).  Rows
+// a slot offset is below 64, so one OR places all four addresses; the permute
+// reads address bits 2 to 7 only, so each byte needs just a shift).  Rows
 // with more than four sources take a loop that the whole wave enters only
 // when some lane needs it.
 __device__ __forceinline__ float se_gather(const i4v se, const f4v wt, int vj, unsigned lb4, float hn) {
@@ -1705,7 +1707,7 @@ __device__ __forceinline__ float se_gather(const i4v se, const f4v wt, int vj, u
   float gv[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
-    gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)__builtin_amdgcn_ubfe(ax, 8 * m, 8), vj));
+    gv[m] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(ax >> (8 * m)), vj));
 #pragma unroll
   for (int m = 0; m < 4; ++m) hn = __builtin_fmaf(gv[m], wt[m], hn);
   const unsigned aw = (unsigned)se.w;
