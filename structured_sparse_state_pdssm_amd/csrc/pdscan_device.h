@@ -787,6 +787,126 @@ __device__ __forceinline__ void select_rows_deep_lds(const Args& a, int s_u, int
   tile_epilogue<NCT>(p, acc[1], bdr, rbeg + 16, rend, lane, o, 0, KT);
 }
 
+// The deep path with 64-channel blocks (unfolded, at most six column tiles,
+// d a multiple of 64; chosen when its stages fit D's region).  A 32-channel
+// block reads half of each 128-byte line of u and of the weights, and the
+// other half, read one block later, has often left the L1 by then: on the
+// LM-layer shape about 40 % of those lines crossed from L2 twice.  Here each
+// block reads whole lines, with half as many blocks and barriers.  u is one
+// block ahead in a two-slot ring; weight blocks are two ahead in registers,
+// then one ahead in a stage of 16 NCT columns x 128 bytes at a 144-byte
+// stride (the same bank spread as the 80-byte stride of the 32-channel
+// stages).
+template <int NCT>
+__device__ __forceinline__ void select_rows_deep_lds64(const Args& a, int s_u, int h, int c0, int rbeg,
+                                                       int rend, int lane, const SelDst& o) {
+  const Plan& p = a.p;
+  const int i = lane & 15, g = lane >> 4, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int K = p.K, N = p.N, d = p.d;
+  const int KB = d >> 6;                           // 64-channel blocks
+  const int KT = (K + 15) >> 4, NT = (N + 15) >> 4;
+  constexpr int kRow = 144, kStage = 16 * NCT * kRow;
+  constexpr int TPW = (NCT + kWaves - 1) / kWaves;   // tiles this wave stages
+  unsigned char* wst = o.wst;
+  const rsrc_t rs = make_rsrc((const uint16_t*)a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
+  const rsrc_t rz = make_rsrc((const uint16_t*)a.W_d + (size_t)h * N * d, (uint32_t)(N * d * 2));
+  const int Tc = min(p.chunk, p.L - c0);
+  const rsrc_t ur = make_rsrc((const uint16_t*)a.u + ((size_t)s_u * p.L + c0) * d, (uint32_t)(Tc * d * 2));
+
+  uint32_t uoff[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = rbeg + 16 * rt + i;
+    uoff[rt] = row < rend ? (uint32_t)((row * d + 8 * g) * 2) : kNoLoad;
+  }
+  // tile t < KT: row 16 t + i of W_sel; KT <= t < KT + NT: row 16 (t - KT) + i of W_d
+  uint32_t toff[TPW];
+  int tlds[TPW];
+  rsrc_t tr[TPW];
+#pragma unroll
+  for (int w = 0; w < TPW; ++w) {
+    const int t = wave + kWaves * w;               // uniform in the wave
+    const bool sc = t < KT;
+    const int m = sc ? 16 * t + i : 16 * (t - KT) + i;
+    const bool ok = t < NCT && (sc ? m < K : (t < KT + NT && m < N));
+    toff[w] = ok ? (uint32_t)((m * d + 8 * g) * 2) : kNoLoad;
+    tr[w] = sc ? rs : rz;
+    tlds[w] = (16 * t + i) * kRow + 16 * g;
+  }
+  float bdr[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int n = 16 * (ct - KT) + i;
+    bdr[ct] = (ct >= KT && ct < KT + NT && n < N) ? a.b_d[(size_t)h * N + n] : 0.f;
+  }
+
+  u4v Ar[2][2][2], Wr[2][TPW][2];                  // [slot][row tile or column tile][32-channel half]
+  auto load_u = [&](int m, u4v (*A)[2]) {
+    const bool ok = m < KB;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        A[rt][hf] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+            ur, (ok && uoff[rt] != kNoLoad) ? uoff[rt] + (uint32_t)m * 128u + 64u * hf : kNoLoad, 0, 0));
+  };
+  auto load_w = [&](int m, u4v (*W)[2]) {
+    const bool ok = m < KB;
+#pragma unroll
+    for (int w = 0; w < TPW; ++w)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        W[w][hf] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+            tr[w], (ok && toff[w] != kNoLoad) ? toff[w] + (uint32_t)m * 128u + 64u * hf : kNoLoad, 0, 0));
+  };
+  auto put_w = [&](int m, const u4v (*W)[2]) {
+    unsigned char* st = wst + (m & 1) * kStage;
+#pragma unroll
+    for (int w = 0; w < TPW; ++w)
+      if (wave + kWaves * w < NCT) {
+        *(u4v*)(st + tlds[w]) = W[w][0];
+        *(u4v*)(st + tlds[w] + 64) = W[w][1];
+      }
+  };
+
+  f4v acc[2][NCT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f4v{0.f, 0.f, 0.f, 0.f};
+  load_u(0, Ar[0]);
+  load_w(0, Wr[0]);
+  load_w(1, Wr[1]);
+  put_w(0, Wr[0]);
+  load_w(2, Wr[0]);
+  // blocks past the end load zeros, stage zeros and add nothing
+  for (int m0 = 0; m0 < KB; m0 += 2) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int m = m0 + q;
+      __syncthreads();                             // stage m written; stage m - 1 read by every wave
+      load_u(m + 1, Ar[(q + 1) & 1]);
+      put_w(m + 1, Wr[(q + 1) & 1]);
+      load_w(m + 3, Wr[(q + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);           // the loads stay ahead of the products
+      const unsigned char* st = wst + (m & 1) * kStage;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const u4v bf = *(const u4v*)(st + (16 * ct + i) * kRow + 16 * g + 64 * hf);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf8v, Ar[q & 1][rt][hf]), __builtin_bit_cast(bf8v, bf), acc[rt][ct], 0, 0, 0);
+        }
+    }
+  }
+  __syncthreads();                                 // the stages are D's region from here
+  tile_epilogue<NCT>(p, acc[0], bdr, rbeg, rend, lane, o, 0, KT);
+  tile_epilogue<NCT>(p, acc[1], bdr, rbeg + 16, rend, lane, o, 0, KT);
+}
+
 // Shapes with a register-resident fast path.
 // kSelDeep + n: the deep bf16 path with n column tiles, ceil(K / 16) score
 // tiles then ceil(N / 16) pre-activation tiles, rounded up to even (a shape
@@ -810,6 +930,12 @@ __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, i
   else if constexpr (PATH > kSelDeep && IN_BF16 && MMA_BF16) {
     if constexpr (PATH - kSelDeep <= kFoldMaxTiles) {
       if (o.wst) {
+        if constexpr (!FOLD && PATH - kSelDeep <= 6) {
+          if (a.p.wst == 2) {                      // 64-channel stages fit
+            select_rows_deep_lds64<PATH - kSelDeep>(a, s_u, h, c0, rbeg, rend, lane, o);
+            return;
+          }
+        }
         select_rows_deep_lds<PATH - kSelDeep, FOLD>(a, s_u, h, c0, rbeg, rend, lane, o);
         return;
       }

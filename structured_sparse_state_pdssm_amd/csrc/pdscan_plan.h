@@ -49,7 +49,8 @@ struct Plan {
   int step32;    // general fused kernel with step-major selection tiles (32-lane groups, see below)
   int n_out;     // outputs per head, rows of C (> 1: step-major paths only)
   int gse;       // general kernel, N = 32 or 64: phase A gathers over inverse dictionary rows (table at off_SRC)
-  int wst;       // fused deep bf16 selection: weight blocks staged through LDS (in D's region)
+  int wst;       // fused deep bf16 selection: weight blocks staged through LDS (in D's region);
+                 // 2: in 64-channel blocks
   int YS;        // stride of the per-output local-output rows
   int tasks;     // workgroups
   int xhg;       // general fused kernel: head groups of the die grouping (0: one ticket counter; see
@@ -157,6 +158,9 @@ inline bool make_plan_once(Plan& p, int mode, int B, int H, int L, int N, int K,
     const bool deep = mode == kModeFused && !sm && in_bf16 && p.mma_bf16 && d % 32 == 0 && d >= 256;
     p.wst = (deep && nct <= (p.fold_bu ? kFoldMaxTiles : 6) && (64 / p.NP) * p.S <= 32 &&
              n_out * N * p.TS * 4 >= 2 * 16 * nct * 80) ? 1 : 0;
+    // unfolded, d a multiple of 64: 64-channel blocks (whole 128-byte lines
+    // per block) when their stages (144-byte rows) fit as well
+    if (p.wst && !p.fold_bu && d % 64 == 0 && n_out * N * p.TS * 4 >= 2 * 16 * nct * 144) p.wst = 2;
   }
   // general kernel, drive folded: the drive terms of the chunk, [N][TS]
   p.off_Bu = (p.fold_bu && !sm) ? take(N * p.TS * 4) : 0;

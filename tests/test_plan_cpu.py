@@ -4,7 +4,8 @@ dispatcher's choices for the benchmark shapes.
 
 Checked: which kernel takes each workload (the step-major N <= 16 kernel for
 the impulse and base shapes, the step-major N = 32 selection tiles for the
-time-series shape at chunk <= 256, the general kernel otherwise), the on-chip
+time-series shape at chunk <= 256, the general kernel otherwise, and the
+deep selection's weight stages: 64-channel blocks unfolded, 32 folded), the on-chip
 budgets (64 KiB, or 160 KiB for the folded and multi-output general plans,
 with the folded LM-layer plan at chunk 96 small enough for two workgroups
 per CU), and the die grouping's choice of head groups: two for the LM-layer
@@ -50,7 +51,10 @@ def test_kernel_choice(plans):
     assert plans["timeseries_k17"]["step32"] == 0              # more scores than a 16-lane row
     assert plans["timeseries_fold"]["step32"] == 0 and plans["timeseries_fold"]["fold"] == 1
     assert plans["timeseries_c512"]["ok"] == 0                 # [32][516] fp32 rows exceed 64 KiB
-    assert plans["lm_layer"]["step32"] == 0 and plans["lm_layer"]["wst"] == 1
+    # the LM-layer selection stages its weights in 64-channel blocks (whole
+    # 128-byte lines); folded, its ten column tiles keep 32-channel stages
+    assert plans["lm_layer"]["step32"] == 0 and plans["lm_layer"]["wst"] == 2
+    assert plans["lm_layer_fold"]["wst"] == 1
 
 
 def test_on_chip_budgets(plans):
