@@ -58,7 +58,9 @@
  *     inputs are finite.
  *   - Shape limits (else PDSSM_EUNSUPPORTED): 1 <= N <= 64, 1 <= K <= 64,
  *     K + N <= 128, d_in % 8 == 0, d_in <= 8192, and the per-chunk on-chip
- *     footprint (about chunk * (N + 2) * 4 bytes) within 64 KiB.
+ *     footprint (about chunk * (N + 2) * 4 bytes) within 64 KiB (the folded
+ *     and multi-output calls on the general kernel: within 160 KiB, see
+ *     pdssm_fwd_wb).
  */
 #ifndef PDSCAN_H
 #define PDSCAN_H

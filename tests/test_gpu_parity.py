@@ -312,6 +312,10 @@ def test_argmax_ties_on_gpu(bf16, d):
     dict(B=2, H=2, L=300, N=33, K=17, d=256, chunk=100, dtype="bf16"),
     dict(B=1, H=3, L=200, N=20, K=5, d=288, chunk=64, dtype="bf16"),
     dict(B=1, H=2, L=130, N=64, K=3, d=800, chunk=128, dtype="bf16"),
+    # the deep path in 64-channel blocks (d a multiple of 64, unfolded, stages
+    # in D's region): an odd number of blocks, and a ragged last chunk
+    dict(B=1, H=2, L=300, N=64, K=32, d=320, chunk=128, dtype="bf16"),
+    dict(B=2, H=1, L=260, N=64, K=16, d=384, chunk=128, dtype="bf16"),
 ])
 def test_edge_shapes(shape):
     chunk = shape.pop("chunk")

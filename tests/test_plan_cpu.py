@@ -55,6 +55,9 @@ def test_kernel_choice(plans):
     # 128-byte lines); folded, its ten column tiles keep 32-channel stages
     assert plans["lm_layer"]["step32"] == 0 and plans["lm_layer"]["wst"] == 2
     assert plans["lm_layer_fold"]["wst"] == 1
+    # the GPU edge cases of the deep path take the stage variant they name
+    assert plans["edge_d320"]["wst"] == 2 and plans["edge_d384"]["wst"] == 2
+    assert plans["edge_d800"]["wst"] == 1                     # d not a multiple of 64
 
 
 def test_on_chip_budgets(plans):
