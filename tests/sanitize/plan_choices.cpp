@@ -33,6 +33,7 @@ int main() {
   show("lm_layer_multi", kModeFused, 16, 24, 2048, 64, 32, 768, 1, 1, 64, 1, 2);
   show("lm_small", kModeFused, 3, 5, 260, 32, 16, 768, 1, 1, 128);
   show("lm_b1", kModeFused, 1, 24, 2048, 64, 32, 768, 1, 1, 128);
+  show("timeseries_h96", kModeFused, 1, 96, 520, 32, 16, 128, 0, 1, 256);
   show("edge_d320", kModeFused, 1, 2, 300, 64, 32, 320, 0, 1, 128);
   show("edge_d384", kModeFused, 2, 1, 260, 64, 16, 384, 0, 1, 128);
   show("edge_d800", kModeFused, 1, 2, 130, 64, 3, 800, 0, 1, 128);

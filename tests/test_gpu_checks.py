@@ -99,6 +99,7 @@ def test_general_kernel_bit_identical_runs(name, kw):
     ("lm_layer", dict(B=8, H=8, L=300)),           # u shared; every grouping possible
     ("lm_layer", dict(B=3, H=5, L=260, N=32, K=16)),   # ragged groups, padded classes
     ("timeseries", dict(B=8, H=8, L=600, d=512)),  # u per head, weights of 1.5 MiB
+    ("timeseries", dict(B=1, H=96, L=520)),        # step-major N = 32 tiles; grouped by default (hg = 8)
 ])
 def test_die_grouping_does_not_change_results(name, kw, monkeypatch):
     """The general kernel's (b, h) grouping over the dies (forced through the

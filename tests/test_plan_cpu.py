@@ -78,3 +78,7 @@ def test_die_grouping_choice(plans):
     small = plans["lm_small"]                                  # B = 3, H = 5: padded classes
     assert small["hg"] == 4 and small["tasks"] >= small["plain"]
     assert plans["lm_b1"]["hg"] == 8                           # one batch: only head groups fill the dies
+    # per-head inputs whose weights pass 1 MiB (96 heads of 48 x 128 bf16):
+    # the step-major N = 32 path, grouped by heads
+    h96 = plans["timeseries_h96"]
+    assert h96["step32"] == 1 and h96["hg"] == 8
