@@ -104,10 +104,11 @@ def test_bwd_chunk_independence(chunk):
     assert_within(host(out["g_C"]), g_C, f"chunk {chunk} g_C")
 
 
-@pytest.mark.parametrize("N,K", [(1, 1), (5, 3), (12, 7), (16, 16), (17, 4), (40, 9)])
+@pytest.mark.parametrize("N,K", [(1, 1), (5, 3), (12, 7), (16, 16), (17, 4), (40, 9), (32, 16), (64, 32)])
 def test_bwd_state_sizes(N, K):
     """State sizes off the power-of-two grid, on both sides of the 16-row
-    nibble-path limit, with a ragged final chunk."""
+    nibble-path limit, and the time-series and LM-layer state sizes (N = 32
+    and 64), with a ragged final chunk."""
     cs = _case("base", B=1, H=2, L=333, N=N, K=K)
     d = _dev(cs)
     g_Bu, g_D, g_h0, g_C = _ref(cs)
