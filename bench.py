@@ -119,6 +119,19 @@ def traffic_from_profile(workload, which="fwd"):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _spin_cycles_per_us(torch, stream):
+    """Cycles of torch's spin kernel per microsecond (it reads the shader
+    clock, whose rate is not fixed), from one event-timed spin."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 2_000_000
+    torch.cuda._sleep(1000)
+    a.record(stream)
+    torch.cuda._sleep(n)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return n / max(a.elapsed_time(b) * 1e3, 1.0)
+
+
 def time_calls(torch, np, step, reps, stream, after=None):
     """Per-call durations (µs) from HIP events on the launch stream.
 
@@ -126,6 +139,12 @@ def time_calls(torch, np, step, reps, stream, after=None):
     read sweep over 1 GiB that evicts L2 and MALL without leaving dirty lines
     behind (a sum into one scalar), bracketed by synchronisations.  Secondary
     ("hot"): `reps` back-to-back calls with warm caches.
+
+    The GPU is kept ahead of the host so that an event never waits on the
+    host's argument marshalling (which would count host time as call time):
+    a spin kernel that touches no memory runs before each cold rep's sweep
+    (0.5 ms), and before the whole hot loop (long enough for the host to
+    queue every hot call before the first one starts).
 
     `after` (optional) is enqueued after each call's end event, outside the
     timed region (the look-back status accumulation).
@@ -136,12 +155,14 @@ def time_calls(torch, np, step, reps, stream, after=None):
     def pct(v):
         return {"median_us": round(float(np.median(v)), 2), "p10_us": round(float(np.percentile(v, 10)), 2),
                 "p90_us": round(float(np.percentile(v, 90)), 2), "mean_us": round(float(np.mean(v)), 2)}
+    cyc_us = _spin_cycles_per_us(torch, stream)
     sweep = torch.ones(EVICT_BYTES // 4, device="cuda")
     sink = torch.empty((), device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for a, b in ev:
+        torch.cuda._sleep(int(500 * cyc_us))
         torch.sum(sweep, dim=0, out=sink)
         a.record(stream)
         step()
@@ -153,8 +174,12 @@ def time_calls(torch, np, step, reps, stream, after=None):
     cold = [a.elapsed_time(b) * 1e3 for a, b in ev]
     del sweep
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    # host time per call (the cold loop's wall time less its GPU work is an
+    # upper bound); the spin covers twice that for every hot call
+    host_us = wall_cold * 1e6 / reps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    torch.cuda._sleep(int(min(2.0 * reps * host_us + 2000.0, 2e6) * cyc_us))
     for a, b in ev:
         a.record(stream)
         step()
@@ -167,7 +192,7 @@ def time_calls(torch, np, step, reps, stream, after=None):
     timing = {"reps": reps, "headline": "cold: each call after a 1 GiB read sweep (outside its events)",
               "cold": pct(cold), "hot": pct(hot),
               "cold_wall_ms_per_step_with_sweep": round(wall_cold * 1e3 / reps, 4),
-              "hot_wall_ms_per_step": round(wall_hot * 1e3 / reps, 4)}
+              "hot_wall_ms_per_step_with_lead_spin": round(wall_hot * 1e3 / reps, 4)}
     return float(np.sum(cold)) / 1e6, cold, timing
 
 
