@@ -17,9 +17,9 @@ LIB = os.path.join(PKG, "libpdscan.so")
 
 SOURCES = ["pdscan_api.cpp", "pdscan_launch_select.hip", "pdscan_launch_scan.hip",
            "pdscan_launch_fused.hip", "pdscan_launch_fused16.hip", "pdscan_launch_fused_multi.hip", "pdscan_launch_fused_fold.hip", "pdscan_launch_bwd.hip", "pdscan_launch_sens.hip", "pdscan_launch_soft.hip",
-           "pdscan_noalloc.hip"]
+           "pdscan_noalloc.hip", "pdscan_launch_gemm_sel.hip"]
 HEADERS = ["pdscan_plan.h", "pdscan_device.h", "pdscan_launch_general.h", "pdscan_bwd_plan.h", "pdscan_bwd.h",
-           "pdscan_sens_plan.h", "pdscan_sens.h", "pdscan_soft_plan.h", "pdscan_soft.h"]
+           "pdscan_sens_plan.h", "pdscan_sens.h", "pdscan_soft_plan.h", "pdscan_soft.h", "pdscan_gemm_sel.h", "pdscan_gemm_sel_plan.h"]
 
 COMPILE_FLAGS = [
     "-O3", "-std=c++17", "-fPIC",

@@ -13,6 +13,7 @@
 #include "pdscan.h"
 #include "pdscan_bwd_plan.h"
 #include "pdscan_plan.h"
+#include "pdscan_gemm_sel_plan.h"
 #include "pdscan_sens_plan.h"
 #include "pdscan_soft_plan.h"
 
@@ -21,6 +22,7 @@ namespace pdscan {
 // `st` and return the launch status; scan and fused clear the workspace first.
 hipError_t launch_select(const Args& a, hipStream_t st);
 hipError_t launch_scan(const Args& a, hipStream_t st);
+hipError_t launch_gemm_sel(const Args& a, hipStream_t st);   // pdscan_launch_gemm_sel.hip
 hipError_t launch_fused(const Args& a, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, float* g_C, hipStream_t st);
 hipError_t launch_sens(const SensArgs& a, hipStream_t st);
@@ -95,6 +97,13 @@ int xcd_groups_hook() {
   const char* v = getenv("PDSSM_XCD_HEAD_GROUPS");
   if (!v || !v[0] || v[1]) return -1;
   return (v[0] == '0' || v[0] == '1' || v[0] == '2' || v[0] == '4' || v[0] == '8') ? v[0] - '0' : -1;
+}
+
+// Test hook: PDSSM_GEMM_SEL=0 keeps pdssm_select on the per-(rows, head)
+// selection kernel for shapes the all-heads GEMM also takes.
+int gemm_sel_hook() {
+  const char* v = getenv("PDSSM_GEMM_SEL");
+  return (v && v[0] == '0' && !v[1]) ? 0 : 1;
 }
 
 int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_bu = 0, int step16 = 0,
@@ -327,6 +336,15 @@ int pdssm_select(const pdssm_dims* dims, const void* u, const void* W_sel,
   a.p = p;
   a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx;
   a.k_out = k_star; a.D_out = D; a.P_out = P_idx;
+  if (gemm_sel_hook() != 0 &&
+      pdscan::gemm_sel_fits(dims->u_shared, dims->in_dtype == PDSSM_BF16, dims->N, dims->K, dims->d_in)) {
+    // u shared by the heads: one GEMM over all tokens, the heads of a token
+    // tile on one die
+    const hipError_t e = pdscan::launch_gemm_sel(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    g_err[0] = 0;
+    return PDSSM_OK;
+  }
   return dispatch(pdscan::kModeSelect, a, stream);
 }
 
