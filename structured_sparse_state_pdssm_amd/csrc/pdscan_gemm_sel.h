@@ -16,9 +16,9 @@
 // tile 0 holds the K <= 32 score rows (rows >= K are zero and skipped by the
 // argmax), tiles 1 and 2 the N <= 64 pre-activation rows.  Each wave owns 64
 // tokens (two column tiles); the four waves share the weight rows of each
-// 64-channel block, staged through LDS in 144-byte rows (two stages), while
-// each wave loads its tokens' channels as B operands straight from memory,
-// one block ahead.
+// 64-channel block, staged through LDS in 144-byte rows (two stages); each
+// wave's u rows pass through LDS rows of its own, so that the loads read
+// whole 128-byte lines while the B operands keep the MFMA lane layout.
 //
 // Epilogue: the argmax runs over a lane's 16 score rows in increasing row
 // order (strict >, so the lowest index wins a tie) and is joined with lane
@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256, 2) void pdssm_gemm_sel_kernel(GemmSelArgs a) {
   constexpr int NT = 1 + NDT;                    // row tiles
   constexpr int R = 32 * NT;                     // staged weight rows
   __shared__ __attribute__((aligned(16))) unsigned char wl[2][R * kGsRowB];
+  __shared__ __attribute__((aligned(16))) unsigned char ul[4][64 * kGsRowB];   // each wave's tokens
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, N = a.N, K = a.K, d = a.d;
   // die-aware order: the heads of token tile T run on die T mod 8
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256, 2) void pdssm_gemm_sel_kernel(GemmSelArgs a) {
   const int T = 8 * (q / H) + x, h = q % H;
   if (T >= a.tiles) return;                      // uniform in the workgroup
   const long long ntok = (long long)a.B * a.L;
-  const int nb = d / 64;                         // channel blocks (even)
+  const int nb = d / 64;                         // channel blocks
 
   // weight rows of this head: a 16-byte piece per thread and pass
   const rsrc_t wsr = make_rsrc(a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
@@ -89,15 +90,22 @@ __global__ __launch_bounds__(256, 2) void pdssm_gemm_sel_kernel(GemmSelArgs a) {
   const long long t0 = (long long)T * kGsTok + 64 * wave;
   const rsrc_t ur = make_rsrc(a.u + t0 * d, (uint32_t)(ntok - t0 > 0 ? min(ntok - t0, 64ll) * d * 2 : 0));
   const int col = lane & 31, kh = lane >> 5;
-  u4v U0[2][4], U1[2][4];
-  auto u_load = [&](u4v (&U)[2][4], int kb) __attribute__((always_inline)) {
+  // u of one block: 64 tokens x 128 bytes per wave, loaded with eight lanes
+  // per token row (whole 128-byte lines per instruction) into registers,
+  // then written to the wave's own LDS rows, from which the B operands are
+  // read (lane l: token l % 32 of column tile s, channels 16 ks + 8 (l / 32))
+  u4v Ur[8];
+  unsigned char* uw = ul[wave];
+  auto u_load = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int i = 0; i < 8; ++i)
+      Ur[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                          ur, (uint32_t)(((8 * i + (lane >> 3)) * d + 64 * kb + 8 * (lane & 7)) * 2),
+                                          0, 0));
+  };
+  auto u_store = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        U[s][ks] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(
-                                               ur, (uint32_t)(((32 * s + col) * d + 64 * kb + 16 * ks + 8 * kh) * 2),
-                                               0, 0));
+    for (int i = 0; i < 8; ++i) *(u4v*)(uw + (8 * i + (lane >> 3)) * kGsRowB + (lane & 7) * 16) = Ur[i];
   };
 
   f16v acc[2][NT];
@@ -105,38 +113,43 @@ __global__ __launch_bounds__(256, 2) void pdssm_gemm_sel_kernel(GemmSelArgs a) {
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[s][j] = f16v{};
-  auto mma_blk = [&](const u4v (&U)[2][4], int buf) __attribute__((always_inline)) {
+  auto mma_blk = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks) {
+      u4v U[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) U[s] = *(const u4v*)(uw + (32 * s + col) * kGsRowB + (16 * ks + 8 * kh) * 2);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const u4v w = *(const u4v*)(wl[buf] + (32 * j + col) * kGsRowB + (16 * ks + 8 * kh) * 2);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
           acc[s][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8v, w),
-                                                              __builtin_bit_cast(bf8v, U[s][ks]), acc[s][j], 0, 0, 0);
+                                                              __builtin_bit_cast(bf8v, U[s]), acc[s][j], 0, 0, 0);
       }
+    }
   };
 
+  // Pipeline, one block deep: while block b multiplies, the weights and u of
+  // block b + 1 arrive in registers; they go to LDS after the block's reads
+  // (the wave's own u rows need no barrier: one wave's LDS accesses run in
+  // order; the shared weight stage alternates and a barrier ends each block).
   stage_load(0);
-  u_load(U0, 0);
+  u_load(0);
   stage_store(0);
+  u_store();
   __syncthreads();
-  for (int kb = 0; kb < nb; kb += 2) {
-    // block kb (U0, stage 0) while block kb + 1 arrives
-    stage_load(kb + 1);
-    u_load(U1, kb + 1);
-    mma_blk(U0, 0);
-    stage_store(1);
-    __syncthreads();
-    // block kb + 1 (U1, stage 1) while block kb + 2 arrives
-    const bool more = kb + 2 < nb;
+  for (int kb = 0; kb < nb; ++kb) {
+    const bool more = kb + 1 < nb;
     if (more) {
-      stage_load(kb + 2);
-      u_load(U0, kb + 2);
+      stage_load(kb + 1);
+      u_load(kb + 1);
     }
-    mma_blk(U1, 1);
-    if (more) stage_store(0);
+    mma_blk(kb & 1);
+    if (more) {
+      u_store();
+      stage_store((kb + 1) & 1);
+    }
     __syncthreads();
   }
 

@@ -1,5 +1,5 @@
 """pdssm_select on the all-heads selection GEMM (u shared by the heads, bf16,
-K <= 32, N <= 64 with N a multiple of 4, d a multiple of 128) against the
+K <= 32, N <= 64 with N a multiple of 4, d a multiple of 64) against the
 fp64 oracle's selection.
 
 Bars: k* bit-exact (the generator keeps the top two scores 1e-3 apart; the
@@ -58,10 +58,12 @@ def _near_ties(s):
 CASES = [
     # B, H, L, N, K, d
     (2, 5, 300, 64, 32, 768),     # reduced LM-layer shape: ragged last tile
-    (1, 3, 257, 32, 5, 128),      # one tile of pre-activation rows, one block pair
+    (1, 3, 257, 32, 5, 128),      # one tile of pre-activation rows, two channel blocks
     (3, 2, 100, 60, 32, 256),     # N not a multiple of 32
     (2, 1, 513, 64, 1, 384),      # one score row
     (1, 7, 2048, 4, 17, 128),     # smallest N, more tiles than dies
+    (2, 3, 200, 64, 32, 64),      # one channel block
+    (1, 2, 300, 48, 8, 320),      # an odd number of channel blocks
 ]
 
 
