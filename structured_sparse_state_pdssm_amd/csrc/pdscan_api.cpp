@@ -336,7 +336,7 @@ int pdssm_select(const pdssm_dims* dims, const void* u, const void* W_sel,
   a.p = p;
   a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx;
   a.k_out = k_star; a.D_out = D; a.P_out = P_idx;
-  if (gemm_sel_hook() != 0 &&
+  if (gemm_sel_hook() != 0 && (long long)dims->B * dims->L < (1ll << 31) &&
       pdscan::gemm_sel_fits(dims->u_shared, dims->in_dtype == PDSSM_BF16, dims->N, dims->K, dims->d_in)) {
     // u shared by the heads: one GEMM over all tokens, the heads of a token
     // tile on one die

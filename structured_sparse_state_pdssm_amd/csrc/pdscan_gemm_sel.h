@@ -23,7 +23,9 @@
 // Epilogue: the argmax runs over a lane's 16 score rows in increasing row
 // order (strict >, so the lowest index wins a tie) and is joined with lane
 // l ^ 32, which holds the other 16; the pre-activations get b_d and the
-// logistic and leave as 16-byte stores of four consecutive n.
+// logistic and leave as 16-byte stores of four consecutive n (the partial
+// lines meet in L2; staging them through LDS into whole rows measured no
+// faster, and non-temporal stores, which skip that merge, far slower).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -170,8 +172,9 @@ __global__ __launch_bounds__(256, 2) void pdssm_gemm_sel_kernel(GemmSelArgs a) {
   for (int s = 0; s < 2; ++s) {
     const long long t = t0 + 32 * s + col;       // this lane's token
     const bool live = t < ntok;
-    const long long b = live ? t / a.L : 0, l = live ? t % a.L : 0;
-    const size_t seq = (size_t)(b * H + h) * a.L + l;   // index of (b, h, l)
+    // token counts below 2^31 (checked by the caller): 32-bit division
+    const uint32_t b = live ? (uint32_t)t / (uint32_t)a.L : 0u, l = live ? (uint32_t)t % (uint32_t)a.L : 0u;
+    const size_t seq = ((size_t)b * H + h) * a.L + l;   // index of (b, h, l)
     // argmax over the lane's 16 score rows, then over the pair of lanes
     float best = 0.f;
     int bi = -1;
