@@ -62,17 +62,36 @@ SOURCES["sens"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_sens_plan.h", "pd
 SOURCES["scan"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_scan.hip")
 SOURCES["multi"] = SOURCES["fwd"]
 SOURCES["select"] = ("pdscan_device.h", "pdscan_plan.h", "pdscan_launch_select.hip")
+# u shared by the heads (bf16, N > 32 for the forward pass): the all-heads
+# selection GEMM, and for the forward pass the chunked scan after it (the
+# host code that picks the route is part of it)
+SOURCES["select_gemm"] = ("pdscan_device.h", "pdscan_gemm_sel.h", "pdscan_gemm_sel_plan.h",
+                          "pdscan_launch_gemm_sel.hip", "pdscan_api.cpp")
+SOURCES["fwd_two_pass"] = SOURCES["select_gemm"] + ("pdscan_plan.h", "pdscan_launch_scan.hip")
 # stem of the committed counter summary of each pass
 TRAFFIC_STEM = {"fwd": "pdssm_fused", "bwd": "pdssm_bwd", "fold": "pdssm_fold", "sens": "pdssm_sens",
                 "soft": "pdssm_soft", "scan": "pdssm_scan", "select": "pdssm_select", "multi": "pdssm_multi"}
 EVICT_BYTES = 1 << 30           # read before each cold-cache rep (beyond L2 and MALL)
 
 
-def kernel_hash(which="fwd") -> str:
+def source_key(which, workload=None):
+    """Which source set a pass runs from on a workload: the forward pass and
+    the selection on the LM-layer shape (u shared by the heads, bf16, N = 64)
+    take the all-heads selection GEMM (and, forward, the scan after it)."""
+    if workload is not None and which in ("fwd", "select"):
+        from pdssm_inputs import get_config
+        cfg = get_config(workload)
+        if cfg.u_shared and cfg.dtype == "bf16" and cfg.K <= 32 and cfg.N <= 64 and cfg.N % 4 == 0 \
+                and cfg.d % 64 == 0 and (which == "select" or cfg.N > 32):
+            return "select_gemm" if which == "select" else "fwd_two_pass"
+    return which
+
+
+def kernel_hash(which="fwd", workload=None) -> str:
     """Hash of a kernel's sources: ties a stored counter summary to the kernel
     it was measured on."""
     h = hashlib.sha256()
-    for name in SOURCES[which]:
+    for name in SOURCES[source_key(which, workload)]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -114,7 +133,7 @@ def traffic_from_profile(workload, which="fwd"):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_hash") != kernel_hash(which):
+    if rec.get("kernel_hash") != kernel_hash(which, workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -260,7 +279,7 @@ def _is_kernel(name, which):
     if which == "scan":
         return "pdssm_step16_kernel" in name or ("pdssm_kernel<1," in name)
     if which == "select":
-        return "pdssm_kernel<0," in name or "pdssm_kernel_wide<0," in name
+        return "pdssm_kernel<0," in name or "pdssm_kernel_wide<0," in name or "pdssm_gemm_sel_kernel" in name
     return "pdssm_" in name and "clear" not in name and "bwd" not in name and "fill" not in name.lower()
 
 
@@ -289,7 +308,7 @@ def pmc_summary(fetch_dir, write_dir, workload, which="fwd"):
                         "scale": scale, "bytes": kib * 1024.0 * scale,
                         "dispatches": sum(len(v) for v in per.values()), "kernels": sorted(per)}
     total = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
-    rec = {"workload": workload, "pass": which, "kernel_hash": kernel_hash(which),
+    rec = {"workload": workload, "pass": which, "kernel_hash": kernel_hash(which, workload),
            "hbm_bytes_per_launch": round(total), "counters": out,
            "copy_probe_bytes": COPY_PROBE_BYTES}
     path = os.path.join(ROOT, "profiles", f"{TRAFFIC_STEM[which]}_{workload}_traffic.json")
@@ -691,7 +710,7 @@ def bench_part(args, torch, np, P):
                    "B": B, "H": H, "L": L, "N": N, "K": K, "d_in": d, "chunk": chunk},
         "roofline": roof,
         "timing": timing,
-        "kernel_hash": kernel_hash(args.which),
+        "kernel_hash": kernel_hash(args.which, cfg.name),
     }
     add_box(rec, torch, np)
     if args.copy_probe:
@@ -928,7 +947,7 @@ def main():
         "hbm_GBps": round(alg_bytes / avg_launch_s / 1e9, 1),
         "roofline": roof,
         "timing": timing,
-        "kernel_hash": kernel_hash(args.which),
+        "kernel_hash": kernel_hash(args.which, cfg.name),
     }
     # secondary line: the same calls back to back with warm caches
     hot_s = timing["hot"]["mean_us"] / 1e6

@@ -90,7 +90,9 @@ typedef struct {
   int32_t in_dtype; /* pdssm_dtype of u, W_sel and W_d                               */
 } pdssm_dims;
 
-/* Selection: scores, argmax and the logistic diagonal for every (b,h,t).
+/* Selection: scores, argmax and the logistic diagonal for every (b,h,t)
+ * ("Flash PD-SSM" summary, Methodology 1: fp32 scores over the K dictionary
+ * entries, the argmax with ties to the lowest index, D = sigmoid(W_d u + b_d)).
  *   u [B,H,L,d] | [B,L,d]; W_sel [H,K,d]; W_d [H,N,d]; b_d [H,N]
  *   k_star [B,H,L] int32 (out, required); D [B,H,L,N] fp32 (out, required)
  *   dict_idx [H,K,N] int32 and P_idx [B,H,L,N] int32: optional pair.  When
@@ -99,7 +101,10 @@ typedef struct {
  *   NULL.
  * Score GEMMs run as fp32 MFMA for fp32 inputs and for bf16 inputs with
  * d_in < 128 (bf16 products are exact in fp32), and as bf16 MFMA with fp32
- * accumulation for bf16 inputs with d_in >= 128. */
+ * accumulation for bf16 inputs with d_in >= 128.  With u shared by the heads
+ * in bf16 (K <= 32, N <= 64 a multiple of 4, d_in a multiple of 64, B*L below
+ * 2^31) the selection runs as one bf16 GEMM over all tokens and heads (the
+ * heads of each 256-token tile on one die, so the tile is read from HBM once). */
 int pdssm_select(const pdssm_dims* dims, const void* u, const void* W_sel,
                  const int32_t* dict_idx, const void* W_d, const float* b_d,
                  int32_t* k_star, float* D, int32_t* P_idx, void* stream);
@@ -120,12 +125,20 @@ int pdssm_scan_fwd(const pdssm_dims* dims, int32_t chunk, const int32_t* k_star,
                    const float* C, const float* h0, float* y, float* h_L,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pdssm_fwd needs for these dims and chunk length. */
+/* Bytes of workspace pdssm_fwd needs for these dims and chunk length.  For
+ * the shapes pdssm_fwd runs as two passes (below) this includes room for k*
+ * and D: B*H*L*(N+1)*4 bytes beyond the look-back words. */
 int pdssm_fwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes);
 
-/* Fused selection + chunked scan in one pass over u and Bu.  Arguments as in
- * pdssm_select and pdssm_scan_fwd; k_star [B,H,L] and D [B,H,L,N] are
- * optional outputs (NULL: not written).
+/* Selection + chunked scan.  Arguments as in pdssm_select and
+ * pdssm_scan_fwd; k_star [B,H,L] and D [B,H,L,N] are optional outputs (NULL:
+ * not written).
+ * Passes.  One fused kernel reads u and Bu once, except for u shared by the
+ * heads with N > 32 and the shapes of pdssm_select's all-heads GEMM: there
+ * the GEMM writes k* and D (into the caller's outputs, or the workspace) and
+ * the chunked scan of pdssm_scan_fwd reads them, on the same stream.  Results
+ * agree to the tolerances of both paths (k* identical; y and h_L differ by
+ * rounding order only).
  * Score precision.  fp32 inputs on the step-major kernel (per-head u, N <= 16,
  * K <= 16, d_in in {32, 64}) form every product on the bf16 matrix cores from
  * an exact three-piece split of each fp32 operand (x = x0 + x1 + x2, each
@@ -145,9 +158,10 @@ int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* 
 
 /* pdssm_fwd without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
- * forbid allocation).  Arguments and outputs as in pdssm_fwd; the look-back
- * scratch (pdssm_fwd_workspace_bytes of it) lives in a 16 MiB device array
- * that the library holds on each GPU it runs on, until the process ends.
+ * forbid allocation).  Arguments and outputs as in pdssm_fwd, always on the
+ * single fused kernel (never the two-pass route, whose k* and D would need
+ * room); its look-back scratch lives in a 16 MiB device array that the
+ * library holds on each GPU it runs on, until the process ends.
  *   status: optional (NULL: not written); one uint32 in device memory or
  *     pinned host memory, 4-byte aligned.  The call ORs its look-back error
  *     word into status[0] (nonzero = a wait gave up; see "Workspace header").
@@ -158,8 +172,8 @@ int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* 
  * first, so nothing carries over from the previous call.  The array is found
  * on the first call on each device; calls allocate nothing.
  * Returns PDSSM_EUNSUPPORTED when the call needs more scratch than
- * PDSSM_NOALLOC_SCRATCH_BYTES (pdssm_fwd_workspace_bytes above 16 MiB), with
- * the other statuses as pdssm_fwd. */
+ * PDSSM_NOALLOC_SCRATCH_BYTES (the fused kernel's look-back words above 16
+ * MiB), with the other statuses as pdssm_fwd. */
 int pdssm_fwd_noalloc(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
                       const int32_t* dict_idx, const void* W_d, const float* b_d,
                       const float* Bu, const float* C, const float* h0,

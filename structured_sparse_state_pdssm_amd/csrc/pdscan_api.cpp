@@ -106,6 +106,13 @@ int gemm_sel_hook() {
   return (v && v[0] == '0' && !v[1]) ? 0 : 1;
 }
 
+// Test hook: PDSSM_FWD_TWO_PASS=0 keeps pdssm_fwd on the fused kernel where
+// it would otherwise run the selection GEMM and the scan as two passes.
+int two_pass_hook() {
+  const char* v = getenv("PDSSM_FWD_TWO_PASS");
+  return (v && v[0] == '0' && !v[1]) ? 0 : 1;
+}
+
 int build_plan(Plan& p, int mode, const pdssm_dims* d, int32_t chunk, int fold_bu = 0, int step16 = 0,
                int n_out = 1) {
   const int c = (mode == pdscan::kModeSelect) ? pdscan::kSelectRows : chunk;
@@ -358,6 +365,29 @@ int pdssm_scan_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* by
   return PDSSM_OK;
 }
 
+// pdssm_fwd as two passes: the all-heads selection GEMM writes k* and D,
+// then the chunked scan reads them.  Taken for u shared by the heads with more
+// than 32 state rows (the general fused kernel's deep selection there re-reads
+// each token once per head and chunk task; the GEMM reads it from one die's L2
+// for every head).  Workspace: the scan's look-back words, then k* and D
+// (used when the caller does not ask for them).
+bool fwd_two_pass(const pdssm_dims* d) {
+  return two_pass_hook() && d->N > 32 && (long long)d->B * d->L < (1ll << 31) &&
+         pdscan::gemm_sel_fits(d->u_shared, d->in_dtype == PDSSM_BF16, d->N, d->K, d->d_in);
+}
+struct TwoPassWs {
+  size_t scan, k, D, total;   // byte offsets of k* and D, and the size
+};
+TwoPassWs two_pass_ws(const pdssm_dims* d, const Plan& scan) {
+  TwoPassWs w;
+  const size_t align = 256;
+  w.scan = scan.ws_bytes;
+  w.k = (w.scan + align - 1) / align * align;
+  w.D = (w.k + (size_t)d->B * d->H * d->L * 4 + align - 1) / align * align;
+  w.total = w.D + (size_t)d->B * d->H * d->L * d->N * 4;
+  return w;
+}
+
 int pdssm_fwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes) {
   int rc = check_dims(dims, chunk);
   if (rc) return rc;
@@ -377,6 +407,14 @@ int pdssm_fwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* byt
   }
   if (rc) return rc;
   *bytes = p.ws_bytes;
+  if (fwd_two_pass(dims)) {
+    Plan q;
+    if (build_plan(q, pdscan::kModeScan, dims, chunk, 0, 1) == PDSSM_OK) {
+      const size_t t = two_pass_ws(dims, q).total;
+      if (t > *bytes) *bytes = t;
+    }
+    g_err[0] = 0;
+  }
   return PDSSM_OK;
 }
 
@@ -407,17 +445,40 @@ int pdssm_fwd(const pdssm_dims* dims, int32_t chunk, const void* u, const void* 
   if (rc) return rc;
   Plan p;
   if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk))) return rc;
-  if (workspace_bytes < p.ws_bytes)
-    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
-                p.ws_bytes);
   const Sizes z = sizes(dims);
   const Range in[] = {{"u", u, z.u},         {"W_sel", W_sel, z.Wsel}, {"dict_idx", dict_idx, z.dict},
                       {"W_d", W_d, z.Wd},    {"b_d", b_d, z.bd},       {"Bu", Bu, z.Bu},
                       {"C", C, z.C},         {"h0", h0, z.h0}};
-  const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y},
-                       {"h_L", h_L, z.hL},      {"workspace", workspace, p.ws_bytes}};
   static const char* const req[] = {"u",  "W_sel", "dict_idx", "W_d", "b_d",      "Bu",
                                     "C",  "y",     "h_L",      "workspace", nullptr};
+  Plan q;
+  if (fwd_two_pass(dims) && build_plan(q, pdscan::kModeScan, dims, chunk, 0, 1) == PDSSM_OK) {
+    const TwoPassWs w = two_pass_ws(dims, q);
+    if (workspace_bytes < w.total)
+      return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, w.total);
+    const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y},
+                         {"h_L", h_L, z.hL},      {"workspace", workspace, w.total}};
+    if ((rc = check_ptrs(in, 8, out, 5, req))) return rc;
+    unsigned char* ws = (unsigned char*)workspace;
+    pdscan::Args a = {};
+    a.p = q;
+    a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx;
+    a.k_out = k_star ? k_star : (int32_t*)(ws + w.k);
+    a.D_out = D ? D : (float*)(ws + w.D);
+    hipError_t e = pdscan::launch_gemm_sel(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    pdscan::Args b = {};
+    b.p = q;
+    b.dict = dict_idx; b.k_in = a.k_out; b.D_in = a.D_out; b.Bu = Bu; b.C = C; b.h0 = h0;
+    b.y = y; b.hL = h_L; b.ws = ws;
+    return dispatch(pdscan::kModeScan, b, stream);
+  }
+  g_err[0] = 0;
+  if (workspace_bytes < p.ws_bytes)
+    return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                p.ws_bytes);
+  const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y},
+                       {"h_L", h_L, z.hL},      {"workspace", workspace, p.ws_bytes}};
   if ((rc = check_ptrs(in, 8, out, 5, req))) return rc;
   pdscan::Args a = {};
   a.p = p;

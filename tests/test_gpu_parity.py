@@ -60,6 +60,21 @@ def test_fused_parity(name):
     _check_fwd(inp, ref, inp.cfg.chunk, name)
 
 
+@pytest.mark.parametrize("chunk", [96, 128])
+def test_fused_kernel_lm_layer(chunk):
+    """pdssm_fwd on the LM-layer shape runs the selection GEMM and the scan as
+    two passes; the single fused kernel it replaces there (still the path of
+    the allocation-free entry point) stays checked with the two-pass route
+    switched off."""
+    import os
+    inp, ref = _case("lm_layer", **REDUCED["lm_layer"])
+    os.environ["PDSSM_FWD_TWO_PASS"] = "0"
+    try:
+        _check_fwd(inp, ref, chunk, f"lm_layer fused kernel chunk {chunk}")
+    finally:
+        del os.environ["PDSSM_FWD_TWO_PASS"]
+
+
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_select_standalone(name):
     inp, ref = _case(name, **REDUCED[name])
