@@ -75,10 +75,11 @@ EVICT_BYTES = 1 << 30           # read before each cold-cache rep (beyond L2 and
 
 
 def source_key(which, workload=None):
-    """Which source set a pass runs from on a workload: the forward pass and
-    the selection on the LM-layer shape (u shared by the heads, bf16, N = 64)
-    take the all-heads selection GEMM (and, forward, the scan after it)."""
-    if workload is not None and which in ("fwd", "select"):
+    """Which source set a pass runs from on a workload: the forward passes
+    (plain, drive folded, several outputs) and the selection on the LM-layer
+    shape (u shared by the heads, bf16, N = 64) take the all-heads GEMMs (and,
+    forward, the scan after them)."""
+    if workload is not None and which in ("fwd", "fold", "multi", "select"):
         from pdssm_inputs import get_config
         cfg = get_config(workload)
         if cfg.u_shared and cfg.dtype == "bf16" and cfg.K <= 32 and cfg.N <= 64 and cfg.N % 4 == 0 \
@@ -805,7 +806,7 @@ def bench_multi(args, torch, np, P):
                    "B": B, "H": H, "L": L, "N": N, "K": K, "d_in": d, "n_out": P_out, "chunk": chunk},
         "roofline": roof,
         "timing": timing,
-        "kernel_hash": kernel_hash("multi"),
+        "kernel_hash": kernel_hash("multi", cfg.name),
     }
     add_box(rec, torch, np)
     if args.copy_probe:

@@ -197,7 +197,12 @@ int pdssm_fwd_noalloc(const pdssm_dims* dims, int32_t chunk, const void* u, cons
  * ceil(K/16) + 2 ceil(N/16) <= 10 tiles (N = 64 with K <= 32).  On the
  * general kernel the chunk's on-chip footprint (about chunk * (2N + 2) * 4
  * bytes plus the dictionary tables) may take up to the 160 KiB LDS of one
- * compute unit.  Anything else returns PDSSM_EUNSUPPORTED. */
+ * compute unit.  Anything else returns PDSSM_EUNSUPPORTED.
+ * Exception: u shared by the heads in bf16 with N > 32 (the shapes of
+ * pdssm_fwd's two passes) runs the all-heads selection GEMM, a second GEMM of
+ * the same tiles that writes Bu = W_b u into the workspace, then the chunked
+ * scan (pdssm_scan_fwd_multi with n_out rows): Bu passes through memory
+ * there, and the on-chip limit above does not apply. */
 int pdssm_fwd_wb(const pdssm_dims* dims, int32_t chunk, const void* u, const void* W_sel,
                  const int32_t* dict_idx, const void* W_d, const float* b_d,
                  const void* W_b, const float* C, const float* h0,

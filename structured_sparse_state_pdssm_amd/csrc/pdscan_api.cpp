@@ -23,6 +23,7 @@ namespace pdscan {
 hipError_t launch_select(const Args& a, hipStream_t st);
 hipError_t launch_scan(const Args& a, hipStream_t st);
 hipError_t launch_gemm_sel(const Args& a, hipStream_t st);   // pdscan_launch_gemm_sel.hip
+hipError_t launch_gemm_drive(const Args& a, float* Bu, hipStream_t st);
 hipError_t launch_fused(const Args& a, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, float* g_C, hipStream_t st);
 hipError_t launch_sens(const SensArgs& a, hipStream_t st);
@@ -228,6 +229,31 @@ int sens_plan(pdscan::SensPlan& q, const pdssm_dims* dims, int32_t chunk) {
 
 namespace {
 
+// The forward passes as two passes: the all-heads selection GEMM writes k*
+// and D (and, drive folded, a second GEMM writes Bu = W_b u), then the chunked
+// scan reads them.  Taken for u shared by the heads with more than 32 state
+// rows (the general fused kernel's deep selection there re-reads each token
+// once per head and chunk task; the GEMM reads it from one die's L2 for every
+// head).  Workspace: the scan's look-back words, then k*, D (used when the
+// caller does not ask for them) and Bu.
+bool fwd_two_pass(const pdssm_dims* d) {
+  return two_pass_hook() && d->N > 32 && (long long)d->B * d->L < (1ll << 31) &&
+         pdscan::gemm_sel_fits(d->u_shared, d->in_dtype == PDSSM_BF16, d->N, d->K, d->d_in);
+}
+struct TwoPassWs {
+  size_t scan, k, D, Bu, total;   // byte offsets of k*, D and Bu, and the size
+};
+TwoPassWs two_pass_ws(const pdssm_dims* d, const Plan& scan) {
+  TwoPassWs w;
+  const size_t align = 256;
+  w.scan = scan.ws_bytes;
+  w.k = (w.scan + align - 1) / align * align;
+  w.D = (w.k + (size_t)d->B * d->H * d->L * 4 + align - 1) / align * align;
+  w.Bu = (w.D + (size_t)d->B * d->H * d->L * d->N * 4 + align - 1) / align * align;
+  w.total = w.Bu + (size_t)d->B * d->H * d->L * d->N * 4;
+  return w;
+}
+
 int scan_fwd_impl(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const int32_t* k_star,
                   const int32_t* dict_idx, const float* D, const float* Bu, const float* C,
                   const float* h0, float* y, float* h_L, void* workspace, size_t workspace_bytes,
@@ -259,6 +285,37 @@ int fwd_wb_impl(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const void
                 void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_dims(dims, chunk);
   if (rc) return rc;
+  const Sizes z = sizes(dims);
+  static const char* const req[] = {"u",  "W_sel", "dict_idx", "W_d", "b_d",      "W_b",
+                                    "C",  "y",     "h_L",      "workspace", nullptr};
+  const Range in[] = {{"u", u, z.u},         {"W_sel", W_sel, z.Wsel}, {"dict_idx", dict_idx, z.dict},
+                      {"W_d", W_d, z.Wd},    {"b_d", b_d, z.bd},       {"W_b", W_b, z.Wd},
+                      {"C", C, z.C * n_out}, {"h0", h0, z.h0}};
+  Plan q;
+  if (fwd_two_pass(dims) && build_plan(q, pdscan::kModeScan, dims, chunk, 0, 1, n_out) == PDSSM_OK) {
+    // selection GEMM, drive GEMM, then the scan (with n_out rows of C)
+    const TwoPassWs w = two_pass_ws(dims, q);
+    if (workspace_bytes < w.total)
+      return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, w.total);
+    const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y * n_out},
+                         {"h_L", h_L, z.hL},      {"workspace", workspace, w.total}};
+    if ((rc = check_ptrs(in, 8, out, 5, req))) return rc;
+    unsigned char* ws = (unsigned char*)workspace;
+    pdscan::Args a = {};
+    a.p = q;
+    a.u = u; a.W_sel = W_sel; a.W_d = W_d; a.b_d = b_d; a.dict = dict_idx; a.W_b = W_b;
+    a.k_out = k_star ? k_star : (int32_t*)(ws + w.k);
+    a.D_out = D ? D : (float*)(ws + w.D);
+    hipError_t e = pdscan::launch_gemm_sel(a, (hipStream_t)stream);
+    if (e == hipSuccess) e = pdscan::launch_gemm_drive(a, (float*)(ws + w.Bu), (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PDSSM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    pdscan::Args b = {};
+    b.p = q;
+    b.dict = dict_idx; b.k_in = a.k_out; b.D_in = a.D_out; b.Bu = (const float*)(ws + w.Bu); b.C = C;
+    b.h0 = h0; b.y = y; b.hL = h_L; b.ws = ws;
+    return dispatch(pdscan::kModeScan, b, stream);
+  }
+  g_err[0] = 0;
   Plan p;
   if ((rc = build_plan(p, pdscan::kModeFused, dims, chunk, 1, 0, n_out))) return rc;
   if (!p.fold_bu)
@@ -270,14 +327,8 @@ int fwd_wb_impl(const pdssm_dims* dims, int32_t chunk, int32_t n_out, const void
   if (workspace_bytes < p.ws_bytes)
     return fail(PDSSM_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
                 p.ws_bytes);
-  const Sizes z = sizes(dims);
-  const Range in[] = {{"u", u, z.u},         {"W_sel", W_sel, z.Wsel}, {"dict_idx", dict_idx, z.dict},
-                      {"W_d", W_d, z.Wd},    {"b_d", b_d, z.bd},       {"W_b", W_b, z.Wd},
-                      {"C", C, z.C * n_out}, {"h0", h0, z.h0}};
   const Range out[] = {{"k_star", k_star, z.k}, {"D", D, z.D}, {"y", y, z.y * n_out},
                        {"h_L", h_L, z.hL},      {"workspace", workspace, p.ws_bytes}};
-  static const char* const req[] = {"u",  "W_sel", "dict_idx", "W_d", "b_d",      "W_b",
-                                    "C",  "y",     "h_L",      "workspace", nullptr};
   if ((rc = check_ptrs(in, 8, out, 5, req))) return rc;
   pdscan::Args a = {};
   a.p = p;
@@ -363,29 +414,6 @@ int pdssm_scan_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* by
   if ((rc = build_plan(p, pdscan::kModeScan, dims, chunk))) return rc;
   *bytes = p.ws_bytes;
   return PDSSM_OK;
-}
-
-// pdssm_fwd as two passes: the all-heads selection GEMM writes k* and D,
-// then the chunked scan reads them.  Taken for u shared by the heads with more
-// than 32 state rows (the general fused kernel's deep selection there re-reads
-// each token once per head and chunk task; the GEMM reads it from one die's L2
-// for every head).  Workspace: the scan's look-back words, then k* and D
-// (used when the caller does not ask for them).
-bool fwd_two_pass(const pdssm_dims* d) {
-  return two_pass_hook() && d->N > 32 && (long long)d->B * d->L < (1ll << 31) &&
-         pdscan::gemm_sel_fits(d->u_shared, d->in_dtype == PDSSM_BF16, d->N, d->K, d->d_in);
-}
-struct TwoPassWs {
-  size_t scan, k, D, total;   // byte offsets of k* and D, and the size
-};
-TwoPassWs two_pass_ws(const pdssm_dims* d, const Plan& scan) {
-  TwoPassWs w;
-  const size_t align = 256;
-  w.scan = scan.ws_bytes;
-  w.k = (w.scan + align - 1) / align * align;
-  w.D = (w.k + (size_t)d->B * d->H * d->L * 4 + align - 1) / align * align;
-  w.total = w.D + (size_t)d->B * d->H * d->L * d->N * 4;
-  return w;
 }
 
 int pdssm_fwd_workspace_bytes(const pdssm_dims* dims, int32_t chunk, size_t* bytes) {

@@ -51,9 +51,14 @@ struct GemmSelArgs {
   int tiles;              // token tiles of kGsTok
 };
 
-template <int NDT>   // tiles of pre-activation rows (N <= 32 NDT)
+// DRIVE = 0: the selection (score tile, then NDT tiles of pre-activation
+// rows; k* and D written).  DRIVE = 1: the drive term Bu = W_b u alone (W_d
+// holds W_b [H,N,d], D_out receives Bu [B,H,L,N]; NDT tiles of rows, no
+// score tile, no nonlinearity).
+template <int NDT, int DRIVE>   // tiles of N rows (N <= 32 NDT)
 __global__ __launch_bounds__(256, 2) void pdssm_gemm_sel_kernel(GemmSelArgs a) {
-  constexpr int NT = 1 + NDT;                    // row tiles
+  constexpr int ST = DRIVE ? 0 : 1;              // score tiles
+  constexpr int NT = ST + NDT;                   // row tiles
   constexpr int R = 32 * NT;                     // staged weight rows
   __shared__ __attribute__((aligned(16))) unsigned char wl[2][R * kGsRowB];
   __shared__ __attribute__((aligned(16))) unsigned char ul[4][64 * kGsRowB];   // each wave's tokens
@@ -67,17 +72,18 @@ __global__ __launch_bounds__(256, 2) void pdssm_gemm_sel_kernel(GemmSelArgs a) {
   const int nb = d / 64;                         // channel blocks
 
   // weight rows of this head: a 16-byte piece per thread and pass
-  const rsrc_t wsr = make_rsrc(a.W_sel + (size_t)h * K * d, (uint32_t)(K * d * 2));
+  const rsrc_t wsr = make_rsrc(a.W_sel + (DRIVE ? 0 : (size_t)h * K * d), DRIVE ? 0u : (uint32_t)(K * d * 2));
   const rsrc_t wdr = make_rsrc(a.W_d + (size_t)h * N * d, (uint32_t)(N * d * 2));
   u4v ws[NT];
   auto stage_load = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       const int qq = tid + 256 * m, row = qq >> 3, seg = qq & 7;
-      const int wr = m == 0 ? row : row - 32;   // score row, or pre-activation row n
-      const bool ok = m == 0 ? wr < K : wr < N;
+      const bool score = m < ST;
+      const int wr = score ? row : row - 32 * ST;   // score row, or row n of W_d (W_b)
+      const bool ok = score ? wr < K : wr < N;
       const uint32_t off = ok ? (uint32_t)((wr * d + 64 * kb + 8 * seg) * 2) : kNoLoad;
-      ws[m] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(m == 0 ? wsr : wdr, off, 0, 0));
+      ws[m] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(score ? wsr : wdr, off, 0, 0));
     }
   };
   auto stage_store = [&](int buf) __attribute__((always_inline)) {
@@ -156,6 +162,26 @@ __global__ __launch_bounds__(256, 2) void pdssm_gemm_sel_kernel(GemmSelArgs a) {
   }
 
   // ---- epilogue
+  if constexpr (DRIVE) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const long long t = t0 + 32 * s + col;
+      if (t < ntok) {
+        const uint32_t b = (uint32_t)t / (uint32_t)a.L, l = (uint32_t)t % (uint32_t)a.L;
+        float* dst = a.D_out + (((size_t)b * H + h) * a.L + l) * N;
+#pragma unroll
+        for (int j = 0; j < NDT; ++j)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int n = 32 * j + 8 * v4 + 4 * kh;
+            if (n < N)
+              *(f4v*)(dst + n) = f4v{acc[s][j][4 * v4], acc[s][j][4 * v4 + 1], acc[s][j][4 * v4 + 2],
+                                     acc[s][j][4 * v4 + 3]};
+          }
+      }
+    }
+    return;
+  }
   float bd[NDT][16];
   {
     const rsrc_t br = make_rsrc(a.b_d + (size_t)h * N, (uint32_t)(N * 4));

@@ -22,6 +22,7 @@ static hipError_t stub(const char* name) {
 hipError_t launch_select(const Args&, hipStream_t) { return stub("select"); }
 hipError_t launch_scan(const Args&, hipStream_t) { return stub("scan"); }
 hipError_t launch_gemm_sel(const Args&, hipStream_t) { return stub("gemm_sel"); }
+hipError_t launch_gemm_drive(const Args&, float*, hipStream_t) { return stub("gemm_drive"); }
 hipError_t launch_fused(const Args&, hipStream_t) { return stub("fused"); }
 hipError_t launch_bwd(const BwdArgs&, float*, hipStream_t) { return stub("bwd"); }
 hipError_t launch_sens(const SensArgs&, hipStream_t) { return stub("sens"); }

@@ -123,17 +123,33 @@ def test_multi_full_size(name, P):
     assert_within(host(out["h_L"]), ref["h_L"], f"{name} h_L")
 
 
-def test_multi_general_rejects_outputs_beyond_on_chip_memory():
-    """LM-layer shape, drive folded, four outputs at chunk 128: 182 KB of
-    on-chip rows, more than the 160 KiB of a compute unit."""
+def test_multi_general_four_outputs_at_chunk_128():
+    """LM-layer shape, drive folded, four outputs at chunk 128: the single
+    fused kernel would need 182 KB of on-chip rows, more than the 160 KiB of a
+    compute unit, and rejects the call when it is the only route; the two-pass
+    route (selection and drive GEMMs, then the scan with four rows of C) runs
+    it, within the bar of the oracle."""
+    import os
     inp = generate(get_config("lm_layer", B=1, H=2, L=256))
     P = lib()
-    C = np.zeros((inp.cfg.H, 4, inp.cfg.N), np.float32)
-    with pytest.raises(P.PdssmError) as e:
-        P.pdssm_fwd_wb_multi(proj_dev(inp.u, True), proj_dev(inp.W_sel, True), to_dev(inp.dict_idx),
-                             proj_dev(inp.W_d, True), to_dev(inp.b_d), proj_dev(inp.W_b, True), to_dev(C),
-                             to_dev(inp.h0), chunk=128)
-    assert e.value.status == P.PDSSM_EUNSUPPORTED
+    rng = np.random.default_rng(4)
+    C = (rng.standard_normal((inp.cfg.H, 4, inp.cfg.N)) / np.sqrt(inp.cfg.N)).astype(np.float32)
+    args = (proj_dev(inp.u, True), proj_dev(inp.W_sel, True), to_dev(inp.dict_idx), proj_dev(inp.W_d, True),
+            to_dev(inp.b_d), proj_dev(inp.W_b, True), to_dev(C), to_dev(inp.h0))
+    os.environ["PDSSM_FWD_TWO_PASS"] = "0"
+    try:
+        with pytest.raises(P.PdssmError) as e:
+            P.pdssm_fwd_wb_multi(*args, chunk=128)
+        assert e.value.status == P.PDSSM_EUNSUPPORTED
+    finally:
+        del os.environ["PDSSM_FWD_TWO_PASS"]
+    print("[gpu] multi lm_layer four outputs chunk 128 (two passes)", flush=True)
+    out = P.pdssm_fwd_wb_multi(*args, chunk=128, want_k=True)
+    ref = oracle.forward_wb_multi(inp.u, inp.W_sel, inp.dict_idx, inp.W_d, inp.b_d, inp.W_b, C, inp.h0,
+                                  u_shared=True)
+    assert np.array_equal(host(out["k_star"]), ref["k_star"])
+    assert_within(host(out["y"]), ref["y"], "lm_layer four outputs y")
+    assert_within(host(out["h_L"]), ref["h_L"], "lm_layer four outputs h_L")
 
 
 def test_multi_rejects_a_chunk_too_long_for_its_outputs():
