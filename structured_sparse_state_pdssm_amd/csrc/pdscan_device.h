@@ -1437,6 +1437,27 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   };
   if constexpr (MODE != kModeSelect && PATH < kSelDeep) first_bu();
 
+  // ---- scan alone, N = 32 or 64: the chunk's k* and D are requested before
+  // the tables are built (one memory round trip for all of them; written to
+  // LDS after the tables), when they fit kScanPre 16-byte loads per thread
+  constexpr int kScanPre = 8;
+  [[maybe_unused]] const bool pre = MODE == kModeScan && (NPT == 32 || NPT == 64) && !a.P_in &&
+                                    Tc <= kThreads && Tc * N <= kScanPre * 4 * kThreads;
+  [[maybe_unused]] f4v dpre[MODE == kModeScan ? kScanPre : 1];
+  [[maybe_unused]] int kpre = 0;
+  if constexpr (MODE == kModeScan && (NPT == 32 || NPT == 64)) {
+    if (pre) {
+      const rsrc_t dd = make_rsrc(a.D_in + gbase * N, (uint32_t)(Tc * N * 4));
+#pragma unroll
+      for (int e = 0; e < kScanPre; ++e) {
+        const int q = e * kThreads + tid;          // 16-byte piece q of the chunk's [Tc][N] rows
+        dpre[e] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                              dd, 4 * q < Tc * N ? (uint32_t)q * 16u : kNoLoad, 0, 0));
+      }
+      kpre = buf_i32(make_rsrc(a.k_in + gbase, (uint32_t)(Tc * 4)), tid < Tc ? (uint32_t)tid * 4u : kNoLoad);
+    }
+  }
+
   // ---- per-head constants
   if constexpr (MODE == kModeSelect) {
     if (a.P_out)
@@ -1479,7 +1500,23 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
         DR[(q / N) * p.DCS + q % N] = (unsigned char)a.dict[(size_t)h * K * N + q];
     }
   }
-  if constexpr (MODE == kModeScan) {
+  if constexpr (MODE == kModeScan && (NPT == 32 || NPT == 64)) {
+    if (pre) {
+      if (tid < Tc) kbuf[tid] = kpre;
+#pragma unroll
+      for (int e = 0; e < kScanPre; ++e) {
+        const int q = e * kThreads + tid;
+        if (4 * q < Tc * N) {
+          const int t = (4 * q) / NPT, n = (4 * q) % NPT;   // four consecutive n of step t
+          Dbuf[(n + 0) * TS + t] = dpre[e].x;
+          Dbuf[(n + 1) * TS + t] = dpre[e].y;
+          Dbuf[(n + 2) * TS + t] = dpre[e].z;
+          Dbuf[(n + 3) * TS + t] = dpre[e].w;
+        }
+      }
+    }
+  }
+  if (MODE == kModeScan && !pre) {
     for (int q = tid; q < Tc; q += kThreads) kbuf[q] = a.P_in ? q : a.k_in[gbase + q];
     // D of the chunk, eight loads in flight per lane at a time
     const rsrc_t dd = make_rsrc(a.D_in + gbase * N, (uint32_t)(Tc * N * 4));
