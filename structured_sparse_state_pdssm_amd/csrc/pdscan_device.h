@@ -1442,9 +1442,10 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   // LDS after the tables), when they fit kScanPre 16-byte loads per thread
   constexpr int kScanPre = 8;
   [[maybe_unused]] const bool pre = MODE == kModeScan && (NPT == 32 || NPT == 64) && !a.P_in &&
-                                    Tc <= kThreads && Tc * N <= kScanPre * 4 * kThreads;
+                                    Tc <= kThreads && Tc * N <= kScanPre * 4 * kThreads && P * N <= kThreads;
   [[maybe_unused]] f4v dpre[MODE == kModeScan ? kScanPre : 1];
   [[maybe_unused]] int kpre = 0;
+  [[maybe_unused]] float cpre = 0.f;             // C too (P N <= 256 here), so no wait precedes the tables
   if constexpr (MODE == kModeScan && (NPT == 32 || NPT == 64)) {
     if (pre) {
       const rsrc_t dd = make_rsrc(a.D_in + gbase * N, (uint32_t)(Tc * N * 4));
@@ -1455,6 +1456,8 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
                                               dd, 4 * q < Tc * N ? (uint32_t)q * 16u : kNoLoad, 0, 0));
       }
       kpre = buf_i32(make_rsrc(a.k_in + gbase, (uint32_t)(Tc * 4)), tid < Tc ? (uint32_t)tid * 4u : kNoLoad);
+      cpre = buf_f32(make_rsrc(a.C + (size_t)h * P * N, (uint32_t)(P * N * 4)),
+                     tid < P * N ? (uint32_t)tid * 4u : kNoLoad);
     }
   }
 
@@ -1463,8 +1466,10 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
     if (a.P_out)
       for (int q = tid; q < K * N; q += kThreads) dic[q] = a.dict[(size_t)h * K * N + q];
   } else {
-    for (int q = tid; q < P * N; q += kThreads) Cs[q] = a.C[(size_t)h * P * N + q];
-    __syncthreads();
+    if (!pre) {
+      for (int q = tid; q < P * N; q += kThreads) Cs[q] = a.C[(size_t)h * P * N + q];
+      __syncthreads();
+    }
     // DR[k][m] = dict[k][m]: the target row of source m under entry k; with
     // per-step maps, entry t is step t's map and k*_t = t
     if (MODE == kModeScan && a.P_in) {
@@ -1503,6 +1508,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   if constexpr (MODE == kModeScan && (NPT == 32 || NPT == 64)) {
     if (pre) {
       if (tid < Tc) kbuf[tid] = kpre;
+      if (tid < P * N) Cs[tid] = cpre;
 #pragma unroll
       for (int e = 0; e < kScanPre; ++e) {
         const int q = e * kThreads + tid;
