@@ -1442,10 +1442,10 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   // LDS after the tables), when they fit kScanPre 16-byte loads per thread
   constexpr int kScanPre = 8;
   [[maybe_unused]] const bool pre = MODE == kModeScan && (NPT == 32 || NPT == 64) && !a.P_in &&
-                                    Tc <= kThreads && Tc * N <= kScanPre * 4 * kThreads && P * N <= kThreads;
+                                    Tc <= kThreads && Tc * N <= kScanPre * 4 * kThreads;
   [[maybe_unused]] f4v dpre[MODE == kModeScan ? kScanPre : 1];
   [[maybe_unused]] int kpre = 0;
-  [[maybe_unused]] float cpre = 0.f;             // C too (P N <= 256 here), so no wait precedes the tables
+  [[maybe_unused]] float cpre = 0.f;
   if constexpr (MODE == kModeScan && (NPT == 32 || NPT == 64)) {
     if (pre) {
       const rsrc_t dd = make_rsrc(a.D_in + gbase * N, (uint32_t)(Tc * N * 4));
@@ -1456,17 +1456,20 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
                                               dd, 4 * q < Tc * N ? (uint32_t)q * 16u : kNoLoad, 0, 0));
       }
       kpre = buf_i32(make_rsrc(a.k_in + gbase, (uint32_t)(Tc * 4)), tid < Tc ? (uint32_t)tid * 4u : kNoLoad);
-      cpre = buf_f32(make_rsrc(a.C + (size_t)h * P * N, (uint32_t)(P * N * 4)),
-                     tid < P * N ? (uint32_t)tid * 4u : kNoLoad);
     }
   }
+  // C in a register from the start (scan and fused modes, P N <= 256), so
+  // that building the tables does not wait on it
+  [[maybe_unused]] const bool cearly = MODE != kModeSelect && P * N <= kThreads;
+  if (cearly)
+    cpre = buf_f32(make_rsrc(a.C + (size_t)h * P * N, (uint32_t)(P * N * 4)), tid < P * N ? (uint32_t)tid * 4u : kNoLoad);
 
   // ---- per-head constants
   if constexpr (MODE == kModeSelect) {
     if (a.P_out)
       for (int q = tid; q < K * N; q += kThreads) dic[q] = a.dict[(size_t)h * K * N + q];
   } else {
-    if (!pre) {
+    if (!cearly) {
       for (int q = tid; q < P * N; q += kThreads) Cs[q] = a.C[(size_t)h * P * N + q];
       __syncthreads();
     }
@@ -1508,7 +1511,6 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
   if constexpr (MODE == kModeScan && (NPT == 32 || NPT == 64)) {
     if (pre) {
       if (tid < Tc) kbuf[tid] = kpre;
-      if (tid < P * N) Cs[tid] = cpre;
 #pragma unroll
       for (int e = 0; e < kScanPre; ++e) {
         const int q = e * kThreads + tid;
@@ -1543,6 +1545,7 @@ __device__ __forceinline__ void pdssm_body(const Args& a, unsigned char* smem) {
       }
     }
   }
+  if (cearly && tid < P * N) Cs[tid] = cpre;
   __syncthreads();
 
   // ---- selection for this wave's rows (the step-major path selects tile by
