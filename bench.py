@@ -639,9 +639,9 @@ def bench_part(args, torch, np, P):
     scores, argmax, diagonal; k* and D written) or ``scan`` (pdssm_scan_fwd
     given k* and D, which come from the library's own selection call outside
     the timed region)."""
-    from pdssm_inputs import generate, get_config
+    from pdssm_inputs import generate, get_config, launch_chunk
     cfg = get_config(args.workload)
-    chunk = args.chunk or cfg.chunk
+    chunk = args.chunk or launch_chunk(args.which, cfg)
     t0 = time.time()
     inp = generate(cfg)
     print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)

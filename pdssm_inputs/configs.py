@@ -98,7 +98,7 @@ def get_config(name: str, **overrides) -> Config:
 # workgroups the chip holds, each paying the per-task set-up; at 256 the 512
 # tasks run in one round.  The results do not depend on the chunk beyond
 # rounding.
-LAUNCH_CHUNK = {("fold", "lm_layer"): 96, ("multi", "lm_layer"): 96, ("fwd", "base"): 256, ("fwd", "lm_layer"): 96}
+LAUNCH_CHUNK = {("fold", "lm_layer"): 96, ("multi", "lm_layer"): 96, ("fwd", "base"): 256, ("fwd", "lm_layer"): 96, ("scan", "lm_layer"): 96}
 
 
 def launch_chunk(pass_name: str, cfg: Config) -> int:
