@@ -241,3 +241,29 @@ def test_workspace_query_accepts_shapes_only_the_folded_plans_hold(P):
     n = P.fwd_workspace_bytes(d, 256)
     assert n == 256 + 8 * 16 * 24 * 4 * 64 * 8
     assert P.lib.pdssm_last_error() == b""
+
+
+def test_two_pass_workspace_and_validation(P):
+    """u shared by the heads in bf16 with N = 64 (the multi-head layer shape)
+    runs pdssm_fwd as two passes: the workspace query adds room for k*, D
+    and the drive term beyond the scan's look-back words, a workspace of
+    only the fused kernel's size is rejected, and the argument checks run
+    before any launch."""
+    B, H, L, N, K, d = 2, 3, 1000, 64, 32, 768
+    dims = P.make_dims(B, H, L, N, K, d, True, True)
+    n = P.fwd_workspace_bytes(dims, 96)
+    look = P.scan_workspace_bytes(dims, 96)
+    assert n >= look + B * H * L * (2 * N + 1) * 4
+    big = 1 << 30
+    args = dict(dims=dims, chunk=96, u=A, W_sel=A + big, dict_idx=A + 2 * big, W_d=A + 3 * big,
+                b_d=A + 4 * big, Bu=A + 5 * big, C=A + 6 * big, h0=None, k_star=None, D=None,
+                y=A + 7 * big, h_L=A + 8 * big, ws=A + 9 * big, ws_bytes=look, stream=None)
+    assert _call_fwd(P, args) == -3                      # the fused kernel's size is not enough here
+    assert b"workspace" in P.lib.pdssm_last_error()
+    args["ws_bytes"] = n
+    args["Bu"] = None
+    assert _call_fwd(P, args) == -1                      # Bu is required on this route too
+    args["Bu"] = A + 5 * big
+    args["y"] = A + 5 * big + 64                         # y inside Bu
+    assert _call_fwd(P, args) == -1
+    assert b"overlaps" in P.lib.pdssm_last_error()
