@@ -90,10 +90,9 @@ def get_config(name: str, **overrides) -> Config:
 
 
 # Launch chunk of a pass where it differs from the workload's own.  The
-# folded and multi-output calls on the LM-layer shape hold the drive terms
-# (and the extra output rows) on chip: at the workload's chunk of 128 one
-# workgroup fills a CU, and these are the longest chunks at which two share
-# one (78.6 KB and 79.9 KB of LDS each).  The base shape (32 sequences of
+# passes on the LM-layer shape run the selection (and drive) GEMMs and then
+# the chunked scan, which is fastest at 96 steps per chunk: three workgroups
+# of 53 KB of LDS share a CU there, two at 128.  The base shape (32 sequences of
 # 4096 steps) at 128 makes 1024 chunk tasks, more than one round of the 768
 # workgroups the chip holds, each paying the per-task set-up; at 256 the 512
 # tasks run in one round.  The results do not depend on the chunk beyond
