@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "pdscan_plan.h"
 
 namespace pdscan {
@@ -97,6 +99,13 @@ __device__ __forceinline__ float buf_f32(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ int buf_i32(rsrc_t r, uint32_t off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, n - 1>) in
+// order: a loop unrolled by construction, whatever its body's size.
+template <class F, int... Ks>
+__device__ __forceinline__ void unrolled(std::integer_sequence<int, Ks...>, F&& f) {
+  (f(std::integral_constant<int, Ks>{}), ...);
 }
 
 // DPP lane permutations inside 16-lane rows.
@@ -2214,13 +2223,29 @@ __device__ __forceinline__ void fused16_body(const Args& a, unsigned char* smem)
         if ((FULL || r < nb) && j == 0 && o < P) yrow[o * p.YS + 4 * k + r] = yl;
       }
   };
+  if constexpr (FOLD || NOUT > 1) {
+    // the same blocks unrolled by construction, each guarded by its own
+    // test: with the drive tile or several rows of C the register allocator
+    // then keeps the drive fragments and the extra outputs out of memory
+    // (three waves per SIMD with four rows of C instead of two)
+    unrolled(std::make_integer_sequence<int, SMAX / 4>{}, [&](auto kt) __attribute__((always_inline)) {
+      constexpr int k = decltype(kt)::value;
+      if (k < nblk) {
+        if (4 * k + 4 <= nst_last)
+          block(std::true_type{}, k);
+        else
+          block(std::false_type{}, k);
+      }
+    });
+  } else {
 #pragma unroll
-  for (int k = 0; k < SMAX / 4; ++k) {
-    if (k >= nblk) break;
-    if (4 * k + 4 <= nst_last)
-      block(std::true_type{}, k);
-    else
-      block(std::false_type{}, k);
+    for (int k = 0; k < SMAX / 4; ++k) {
+      if (k >= nblk) break;
+      if (4 * k + 4 <= nst_last)
+        block(std::true_type{}, k);
+      else
+        block(std::false_type{}, k);
+    }
   }
   __syncthreads();                                 // the tables' bytes become the scratch of the steps below
   chunk_tail<true>(a, smem, c, s, Tc, gbase, 16, gam, j, act, midx, msc, hl);

@@ -22,6 +22,9 @@ static void show(const char* name, int mode, int B, int H, int L, int N, int K, 
 
 int main() {
   show("impulse", kModeFused, 1, 32, 131072, 16, 8, 64, 0, 0, 512);
+  show("impulse_c640", kModeFused, 1, 32, 131072, 16, 8, 64, 0, 0, 640);
+  show("impulse_c768", kModeFused, 1, 32, 131072, 16, 8, 64, 0, 0, 768);
+  show("impulse_c640_p2", kModeFused, 1, 32, 131072, 16, 8, 64, 0, 0, 640, 0, 2);
   show("base", kModeFused, 4, 8, 4096, 16, 8, 64, 0, 0, 256);
   show("timeseries", kModeFused, 8, 16, 16384, 32, 16, 128, 0, 1, 256);
   show("timeseries_c512", kModeFused, 8, 16, 16384, 32, 16, 128, 0, 1, 512);

@@ -75,7 +75,7 @@ def test_fold_parity(key):
     _check(_run(_dev(inp), inp.cfg.chunk), ref, key)
 
 
-@pytest.mark.parametrize("chunk", [1, 4, 16, 100, 128, 512])
+@pytest.mark.parametrize("chunk", [1, 4, 16, 100, 128, 512, 640])
 def test_fold_chunk_independence(chunk):
     inp, ref = _case("impulse")
     print(f"[gpu] pdssm_fwd_wb impulse chunk={chunk}", flush=True)

@@ -19,6 +19,8 @@ CASES = {
     "impulse_p2": ("impulse", dict(H=3, L=1300), 2, 256),
     "impulse_p4": ("impulse", dict(H=3, L=1300), 4, 128),
     "impulse_p3_c100": ("impulse", dict(H=2, L=777), 3, 100),
+    # past the step-major kernel's 512 steps: the general kernel
+    "impulse_p2_c640": ("impulse", dict(H=2, L=1300), 2, 640),
     "base_d32_p2": ("base", dict(B=2, H=2, L=700, d=32), 2, 128),
     "tiny_p4": ("tiny", dict(L=250), 4, 64),
     "bf16_d128_p2": ("timeseries", dict(B=1, H=2, L=600, N=16, K=8), 2, 256),

@@ -161,10 +161,20 @@ def test_scan_deterministic():
     assert np.array_equal(host(a[0]), host(b[0])) and np.array_equal(host(a[1]), host(b[1]))
 
 
-@pytest.mark.parametrize("chunk", [1, 3, 4, 16, 64, 100, 128, 512, 700, 4096])
+@pytest.mark.parametrize("chunk", [1, 3, 4, 16, 64, 100, 128, 512, 576, 600, 640, 700, 4096])
 def test_chunk_size_independence(chunk):
     inp, ref = _case("base", **REDUCED["base"])
     _check_fwd(inp, ref, chunk, f"base chunk {chunk}")
+
+
+@pytest.mark.parametrize("chunk", [512, 513, 576, 640])
+def test_n16_chunks_at_the_step_major_limit(chunk):
+    """N = 16 shapes on either side of the step-major kernel's 512-step limit
+    (past it the general kernel takes them), on fp32 d = 64 (the three-piece
+    split) and bf16 d = 128, with a ragged last chunk."""
+    for name, kw in (("impulse", dict(H=3, L=1500)), ("timeseries", dict(B=1, H=2, L=1500, N=16, K=8))):
+        inp, ref = _case(name, **kw)
+        _check_fwd(inp, ref, chunk, f"N=16 {name} chunk {chunk}")
 
 
 @pytest.mark.parametrize("chunk", [7, 16, 48, 100, 200, 256])

@@ -45,6 +45,11 @@ def plans(tmp_path_factory):
 
 def test_kernel_choice(plans):
     assert plans["impulse"]["fused16"] == 1 and plans["base"]["fused16"] == 1
+    # the step-major kernel takes at most 32 steps per lane group (chunk 512);
+    # longer chunks of the same shapes go to the general kernel
+    assert plans["impulse"]["S"] == 32 and 3 * plans["impulse"]["lds"] <= 160 * 1024
+    for name in ("impulse_c640", "impulse_c768", "impulse_c640_p2"):
+        assert plans[name]["ok"] == 1 and plans[name]["fused16"] == 0, name
     ts = plans["timeseries"]
     assert ts["fused16"] == 0 and ts["step32"] == 1 and ts["gse"] == 1
     assert ts["S"] == 32 and ts["G"] == 8                      # two 16-step tiles per group
