@@ -964,8 +964,10 @@ __device__ __forceinline__ void select_dispatch(const Args& a, int s_u, int h, i
 // brings the summary (midx, msc, hl) of its group's sub-chunk; w_t is in the
 // [N][TS] buffer and the local outputs in yloc.
 // ---------------------------------------------------------------------------
-// Previous chunks whose states and aggregates phase B reads in one batch.
-constexpr int kLookWin = 8;
+// Previous chunks whose states and aggregates phase B reads in one batch, at
+// most (the combine's scratch bounds it: 11 chunks at N = 16, 5 at N = 32,
+// 2 at N = 64).
+constexpr int kLookWin = 16;
 
 template <bool ROW16>
 __device__ __forceinline__ void chunk_tail(const Args& a, unsigned char* smem, int c, int s, int Tc,
